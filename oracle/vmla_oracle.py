@@ -1,0 +1,287 @@
+"""CPU fp64 oracle for VideoMLA latent-cache chunk attention.
+
+TEST INFRASTRUCTURE ONLY. This module is the slow, plain reference that the
+HIP path is checked against. Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import it; the product library
+never does, and it shares no code with the HIP kernels (the only common import
+is the seeded input generator in ``workloads/``, which holds no arithmetic of
+the method).
+
+Sources (web pages about arXiv:2605.30351v1, "VideoMLA: Low-Rank Latent KV
+Cache for Minute-Scale Autoregressive Video Diffusion"):
+  [PL] paperlayer.ai section-by-section summary (the most detailed page);
+  [GI] gist.science Italian technical summary ("Riepilogo Tecnico: VideoMLA"),
+       section "Metodologia", items 1-4.
+
+What is computed, per batch element (all in float64, no intermediate
+rounding):
+  cache entry of token t   c_t = x_t W_down  (d_c)            [GI] item 1, [PL] §3
+                           k^R_t = RoPE3D(x_t W_KR, p_t)     [GI] item 3, [PL] App. D.3
+  per-head reconstruction  k^nope_{t,h} = c_t W_K_up[h]      [GI] item 2, [PL] §3
+                           v_{t,h}      = c_t W_V_up[h]
+  queries                  q = x W_Q; head h takes columns [h*d_h, (h+1)*d_h),
+                           the first d_nope are q^nope, the last d_rope are
+                           rotated: q^R = RoPE3D(., p_q)       [PL] App. D.3
+  scores                   s = (q^nope . k^nope + q^R . k^R) * scale, over every
+                           valid key of the window (no mask inside the window:
+                           the query chunk sees earlier chunks and itself)
+                                                               [PL] App. D.4
+  softmax                  p = exp(s - max s) / sum exp(s - max s)
+  output                   o_h = sum_k p_k v_{k,h}
+
+Readings of points the pages leave open (each is also listed in the design doc):
+  * RoPE3D: 16 complex pairs, the first 6 on the t axis, then 5 on h, then 5 on
+    w ([PL] App. D.3); pair j is the adjacent channels (2j, 2j+1); within an
+    axis group of width D_a (12, 10, 10) pair i turns at
+    omega_i = theta^(-2 i / D_a), theta = 10000, so i = 0 is the group's
+    highest-frequency band. PARITY UNPINNED for the table values: the pages
+    print no frequencies; only the (6,5,5) split and "highest bands first"
+    are pinned.
+  * k^R is rotated with absolute (t, h, w) when it is cached. The pages rotate
+    at window-assembly time with window-local t ([PL] App. D.5, App. E); with
+    no sink frame both give the same scores by RoPE's relative invariance,
+    which tests/test_oracle_pins.py checks.
+  * y = x @ W with W stored [in, out]; W_Q columns are head-major, each head
+    [nope | rope]; scale = 1/sqrt(d_nope + d_rope).
+  * Token n of a frame is at (h, w) = (n // grid_w, n % grid_w); t is the
+    absolute latent-frame index from 0.
+  * Ring slot of token n of frame t: (t mod W) * T + n.
+PARITY UNPINNED: final output values at the benchmark shapes (the pages print
+no worked example); they are pinned only through the identities checked in
+tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+# ---------------------------------------------------------------------------
+# Storage figures ([GI] item 4; [PL] §3 "Cache efficiency", App. D.2)
+# ---------------------------------------------------------------------------
+
+def cached_scalars_per_token(d_c: int, d_rope: int) -> int:
+    """Per-token, per-layer cached state of the latent layout: d_c + d_rope."""
+    return d_c + d_rope
+
+
+def dense_scalars_per_token(n_heads: int, d_head: int) -> int:
+    """Per-token, per-layer cached state of dense per-head KV: 2 * n_h * d_h."""
+    return 2 * n_heads * d_head
+
+
+# ---------------------------------------------------------------------------
+# 3D-RoPE ([PL] App. C.1 and App. D.3)
+# ---------------------------------------------------------------------------
+
+def rope_pair_axes(pairs=(6, 5, 5)) -> np.ndarray:
+    """Axis (0 = t, 1 = h, 2 = w) that each complex pair rotates with."""
+    return np.concatenate([np.full(n, a, dtype=np.int64) for a, n in enumerate(pairs)])
+
+
+def rope_frequencies(pairs=(6, 5, 5), axis_dims=(12, 10, 10), theta=10000.0) -> np.ndarray:
+    """Angular rate of every pair: omega_i = theta^(-2 i / D_a) within its axis group."""
+    om = []
+    for n_pairs, dim in zip(pairs, axis_dims):
+        for i in range(n_pairs):
+            om.append(float(theta) ** (-2.0 * i / dim))
+    return np.array(om, dtype=F64)
+
+
+def frame_positions(t: int, grid_h: int, grid_w: int) -> np.ndarray:
+    """(t, h, w) of every token of latent frame t, token order n = h * grid_w + w."""
+    n = np.arange(grid_h * grid_w)
+    return np.stack([np.full_like(n, t), n // grid_w, n % grid_w], axis=-1).astype(np.int64)
+
+
+def rope3d(v, pos, omega, pairs=(6, 5, 5)) -> np.ndarray:
+    """Rotate each adjacent pair (v[2j], v[2j+1]) by angle pos[axis(j)] * omega[j].
+
+    v: [..., 2 * len(omega)]; pos: [..., 3] integer positions broadcastable to
+    v's leading dims.
+    """
+    v = np.asarray(v, dtype=F64)
+    pos = np.asarray(pos, dtype=F64)
+    axes = rope_pair_axes(pairs)
+    phi = pos[..., axes] * np.asarray(omega, dtype=F64)          # [..., n_pairs]
+    cos, sin = np.cos(phi), np.sin(phi)
+    a, b = v[..., 0::2], v[..., 1::2]
+    out = np.empty(np.broadcast_shapes(v.shape, phi.shape[:-1] + (v.shape[-1],)), dtype=F64)
+    out[..., 0::2] = a * cos - b * sin
+    out[..., 1::2] = a * sin + b * cos
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Latent cache entry ([GI] items 1 and 3; [PL] §3, App. D.2)
+# ---------------------------------------------------------------------------
+
+def latent_entry(x, w_down, w_kr, pos, omega, pairs=(6, 5, 5)):
+    """Cache pair of each token: c = x W_down, k^R = RoPE3D(x W_KR, pos)."""
+    x = np.asarray(x, dtype=F64)
+    c = x @ np.asarray(w_down, dtype=F64)
+    k_r = rope3d(x @ np.asarray(w_kr, dtype=F64), pos, omega, pairs)
+    return c, k_r
+
+
+# ---------------------------------------------------------------------------
+# Explicit per-head reconstruction ([GI] item 2; [PL] §3 "On-demand reconstruction")
+# ---------------------------------------------------------------------------
+
+def reconstruct_heads(c, w_k_up, w_v_up):
+    """k^nope_{t,h} = c_t W_K_up[h]  -> [N, H, d_nope];  v_{t,h} = c_t W_V_up[h] -> [N, H, d_v]."""
+    c = np.asarray(c, dtype=F64)
+    w_k_up = np.asarray(w_k_up, dtype=F64)
+    w_v_up = np.asarray(w_v_up, dtype=F64)
+    k_nope = np.stack([c @ w_k_up[h] for h in range(w_k_up.shape[0])], axis=1)
+    v = np.stack([c @ w_v_up[h] for h in range(w_v_up.shape[0])], axis=1)
+    return k_nope, v
+
+
+def queries(x, w_q, pos, omega, n_heads, d_nope, d_rope, pairs=(6, 5, 5)):
+    """q = x W_Q split per head into q^nope [N, H, d_nope] and rotated q^R [N, H, d_rope]."""
+    q = (np.asarray(x, dtype=F64) @ np.asarray(w_q, dtype=F64)).reshape(-1, n_heads, d_nope + d_rope)
+    q_nope = q[..., :d_nope]
+    q_rope = rope3d(q[..., d_nope:], np.asarray(pos)[:, None, :], omega, pairs)
+    return q_nope, q_rope
+
+
+# ---------------------------------------------------------------------------
+# Attention over reconstructed heads
+# ---------------------------------------------------------------------------
+
+def softmax_rows(s) -> np.ndarray:
+    """Two-pass softmax over the last axis: exp(s - max) / sum exp(s - max)."""
+    s = np.asarray(s, dtype=F64)
+    e = np.exp(s - s.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def attention_explicit(q_nope, q_rope, k_nope, k_r, v, scale, row_block=256):
+    """o[q, h] = sum_k softmax_k(s[q, k, h]) v[k, h] with
+    s = (q^nope_h . k^nope_{k,h} + q^R_h . k^R_k) * scale.
+
+    Shapes: q_nope [Nq, H, dn], q_rope [Nq, H, dr], k_nope [Nk, H, dn],
+    k_r [Nk, dr] (shared by all heads), v [Nk, H, dv]  ->  [Nq, H, dv].
+    Query rows are independent; they are processed ``row_block`` at a time
+    only to bound memory.
+    """
+    nq, nh, _ = q_nope.shape
+    out = np.empty((nq, nh, v.shape[-1]), dtype=F64)
+    k_r = np.asarray(k_r, dtype=F64)
+    for h in range(nh):
+        kh = np.concatenate([k_nope[:, h, :], k_r], axis=1)          # [Nk, dn + dr]
+        vh = np.ascontiguousarray(v[:, h, :])
+        for r0 in range(0, nq, row_block):
+            qh = np.concatenate([q_nope[r0:r0 + row_block, h, :],
+                                 q_rope[r0:r0 + row_block, h, :]], axis=1)
+            p = softmax_rows((qh @ kh.T) * scale)
+            out[r0:r0 + row_block, h, :] = p @ vh
+    return out
+
+
+def attention_absorbed(q_nope, q_rope, c, k_r, w_k_up, w_v_up, scale):
+    """Latent-form inference ([PL] App. E), used only to cross-check the
+    explicit form: q~_h = q^nope_h W_K_up[h]^T scores against c directly,
+    the positional branch stays separate, the softmax-weighted latents are
+    accumulated and then projected by W_V_up[h]."""
+    c = np.asarray(c, dtype=F64)
+    k_r = np.asarray(k_r, dtype=F64)
+    nq, nh, _ = q_nope.shape
+    out = np.empty((nq, nh, w_v_up.shape[-1]), dtype=F64)
+    for h in range(nh):
+        q_lat = q_nope[:, h, :] @ np.asarray(w_k_up[h], dtype=F64).T   # [Nq, d_c]
+        s = (q_lat @ c.T + q_rope[:, h, :] @ k_r.T) * scale
+        p = softmax_rows(s)
+        out[:, h, :] = (p @ c) @ np.asarray(w_v_up[h], dtype=F64)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Sliding-window ring of latent frames ([PL] App. C.1, App. D.4)
+# ---------------------------------------------------------------------------
+
+def ring_slot(t: int, n, tokens_per_frame: int, window_frames: int):
+    """Slot of token n of absolute latent frame t: (t mod W) * T + n."""
+    return (t % window_frames) * tokens_per_frame + np.asarray(n)
+
+
+class LatentRing:
+    """Per-batch-element ring of cached pairs (c, k^R), one row per slot.
+
+    Appending frame t overwrites the slots of frame t - W (FIFO eviction);
+    appending the same frame again (a later denoising step) overwrites it in
+    place. Slots [0, n_valid_frames * T) are the valid window before the ring
+    first wraps and all slots afterwards.
+    """
+
+    def __init__(self, batch, window_frames, grid_h, grid_w, d_c, d_rope):
+        self.W, self.gh, self.gw = window_frames, grid_h, grid_w
+        self.T = grid_h * grid_w
+        self.c = np.full((batch, window_frames * self.T, d_c), np.nan, dtype=F64)
+        self.k_r = np.full((batch, window_frames * self.T, d_rope), np.nan, dtype=F64)
+
+    def append_frame(self, b, t, x_frame, w_down, w_kr, omega, pairs=(6, 5, 5)):
+        pos = frame_positions(t, self.gh, self.gw)
+        c, k_r = latent_entry(x_frame, w_down, w_kr, pos, omega, pairs)
+        slots = ring_slot(t, np.arange(self.T), self.T, self.W)
+        self.c[b, slots] = c
+        self.k_r[b, slots] = k_r
+
+    def valid(self, b, n_valid_frames):
+        n = n_valid_frames * self.T
+        return self.c[b, :n], self.k_r[b, :n]
+
+
+# ---------------------------------------------------------------------------
+# One chunk step: append the chunk, attend over the window
+# ---------------------------------------------------------------------------
+
+def window_frames(t_first: int, chunk_frames: int, window: int):
+    """Latent frames held by the window once the chunk is appended (oldest first)."""
+    t_end = t_first + chunk_frames
+    return list(range(max(0, t_end - window), t_end))
+
+
+def chunk_attention_reference(w, wts, x_of_frame, query_tokens=None):
+    """Reference output of one chunk step of workload ``w`` for one batch element.
+
+    ``wts``: dict of weights (``workloads.weights`` layout). ``x_of_frame(t)``
+    returns the [T, d_model] activations last written for frame t (the query
+    chunk's own frames included). ``query_tokens``: optional indices into the
+    chunk's N_q tokens; default all. Returns [len(query_tokens), H, d_v].
+    Keys are taken in frame order; by permutation invariance of the softmax
+    this equals the ring's slot order (checked in the pins).
+    """
+    omega = rope_frequencies(w.rope_pairs, w.rope_axis_dims, w.rope_theta)
+    frames = window_frames(w.t_first, w.chunk_frames, w.window_frames)
+    cs, krs = [], []
+    for t in frames:
+        c, k_r = latent_entry(x_of_frame(t), wts["w_down"], wts["w_kr"],
+                              frame_positions(t, w.grid_h, w.grid_w), omega, w.rope_pairs)
+        cs.append(c)
+        krs.append(k_r)
+    c = np.concatenate(cs, axis=0)
+    k_r = np.concatenate(krs, axis=0)
+    k_nope, v = reconstruct_heads(c, wts["w_k_up"], wts["w_v_up"])
+
+    chunk = list(range(w.t_first, w.t_first + w.chunk_frames))
+    xq = np.concatenate([np.asarray(x_of_frame(t), dtype=F64) for t in chunk], axis=0)
+    pos_q = np.concatenate([frame_positions(t, w.grid_h, w.grid_w) for t in chunk], axis=0)
+    if query_tokens is not None:
+        query_tokens = np.asarray(query_tokens)
+        xq, pos_q = xq[query_tokens], pos_q[query_tokens]
+    q_nope, q_rope = queries(xq, wts["w_q"], pos_q, omega, w.n_heads, w.d_nope, w.d_rope,
+                             w.rope_pairs)
+    scale = 1.0 / np.sqrt(w.d_nope + w.d_rope)
+    return attention_explicit(q_nope, q_rope, k_nope, k_r, v, scale)
+
+
+def append_reference(w, wts, x_chunk, t_first, n_frames):
+    """Cache rows [n_frames * T, d_c + d_rope] = [c | k^R] of the appended frames."""
+    omega = rope_frequencies(w.rope_pairs, w.rope_axis_dims, w.rope_theta)
+    pos = np.concatenate([frame_positions(t, w.grid_h, w.grid_w)
+                          for t in range(t_first, t_first + n_frames)], axis=0)
+    c, k_r = latent_entry(x_chunk, wts["w_down"], wts["w_kr"], pos, omega, w.rope_pairs)
+    return np.concatenate([c, k_r], axis=1)

@@ -1,0 +1,474 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each test checks the oracle against something the pages print, a closed form,
+an invariant, a library routine, or brute force on tiny inputs. The last
+group plants plausible mistakes into a copy of the oracle and shows that some
+pin fails for each one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.vmla_oracle as orc
+from workloads import config, custom, weights, x_frame
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(12345)
+
+
+def rel(a, b):
+    return float(np.linalg.norm(np.asarray(a) - np.asarray(b)) / max(np.linalg.norm(b), 1e-300))
+
+
+# ---------------------------------------------------------------------------
+# Storage figures printed on the pages
+# ---------------------------------------------------------------------------
+
+def test_storage_figures_match_pages():
+    g = json.load(open(os.path.join(GOLDEN, "storage_figures.json")))
+    d = g["dims"]["value"]
+    lat = orc.cached_scalars_per_token(d["d_c"], d["d_rope"])
+    dense = orc.dense_scalars_per_token(d["n_heads"], d["d_head"])
+    assert lat == g["latent_scalars_per_token"]["value"]
+    assert dense == g["dense_scalars_per_token"]["value"]
+    assert round(100.0 * (1.0 - lat / dense), 1) == g["reduction_percent"]["value"]
+    assert round(dense / lat, 1) == g["reduction_factor"]["value"]
+    ct = g["clip_tokens"]
+    assert ct["frames"] * ct["tokens_per_frame"] == ct["value"]
+    w = config(2)
+    assert w.window_frames * w.tokens_per_frame == ct["value"]
+    total = ct["value"] * d["n_layers"] * dense
+    assert round(total / 1e9, 2) == g["dense_cache_scalars_billions"]["value"]
+    assert round(total * g["dense_cache_gb_bf16"]["bytes_per_scalar"] / 1e9, 1) == \
+        g["dense_cache_gb_bf16"]["value"]
+    # the workload dims agree with the printed model dims
+    assert (w.d_model, w.n_heads, w.d_head, w.d_c, w.d_rope) == \
+        (d["d_model"], d["n_heads"], d["d_head"], d["d_c"], d["d_rope"])
+    assert w.cache_row == lat
+
+
+# ---------------------------------------------------------------------------
+# 3D-RoPE
+# ---------------------------------------------------------------------------
+
+OMEGA = orc.rope_frequencies()
+
+
+def _rope_complex(v, pos):
+    """Independent route: RoPE as multiplication of complex pairs by e^{i phi}."""
+    axes = [0] * 6 + [1] * 5 + [2] * 5
+    out = np.empty_like(v, dtype=np.float64)
+    for j in range(16):
+        z = complex(v[2 * j], v[2 * j + 1]) * complex(math.cos(pos[axes[j]] * OMEGA[j]),
+                                                      math.sin(pos[axes[j]] * OMEGA[j]))
+        out[2 * j], out[2 * j + 1] = z.real, z.imag
+    return out
+
+
+def test_rope_is_complex_rotation():
+    for _ in range(20):
+        v = RNG.standard_normal(32)
+        pos = RNG.integers(0, 300, size=3)
+        np.testing.assert_allclose(orc.rope3d(v, pos, OMEGA), _rope_complex(v, pos),
+                                   rtol=0, atol=1e-12)
+
+
+def test_rope_basis_vector_closed_form():
+    # pair 0 is on the t axis with omega = 1: (1, 0) at t -> (cos t, sin t)
+    v = np.zeros(32)
+    v[0] = 1.0
+    out = orc.rope3d(v, np.array([3, 0, 0]), OMEGA)
+    np.testing.assert_allclose(out[:2], [math.cos(3.0), math.sin(3.0)], atol=1e-15)
+    np.testing.assert_allclose(out[2:], 0.0, atol=0)
+
+
+def test_rope_norm_identity_group_law():
+    v = RNG.standard_normal((50, 32))
+    p = RNG.integers(0, 500, size=(50, 3))
+    p2 = RNG.integers(0, 500, size=(50, 3))
+    r = orc.rope3d(v, p, OMEGA)
+    np.testing.assert_allclose(np.linalg.norm(r, axis=1), np.linalg.norm(v, axis=1), rtol=1e-13)
+    np.testing.assert_allclose(orc.rope3d(v, np.zeros((50, 3), int), OMEGA), v, atol=0)
+    np.testing.assert_allclose(orc.rope3d(r, p2, OMEGA), orc.rope3d(v, p + p2, OMEGA),
+                               rtol=0, atol=1e-11)
+
+
+def test_rope_relative_position_invariance():
+    q = RNG.standard_normal((40, 32))
+    k = RNG.standard_normal((40, 32))
+    pq = RNG.integers(0, 200, size=(40, 3))
+    pk = RNG.integers(0, 200, size=(40, 3))
+    shift = RNG.integers(-100, 100, size=(40, 3))
+    a = np.sum(orc.rope3d(q, pq, OMEGA) * orc.rope3d(k, pk, OMEGA), axis=1)
+    b = np.sum(orc.rope3d(q, pq + shift, OMEGA) * orc.rope3d(k, pk + shift, OMEGA), axis=1)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-11)
+
+
+def test_rope_axis_split_6_5_5_and_highest_bands():
+    # [PL] App. D.3: 16 complex pairs split (6, 5, 5) over t, h, w, using each
+    # axis group's highest-frequency bands.
+    assert list(orc.rope_pair_axes()) == [0] * 6 + [1] * 5 + [2] * 5
+    assert OMEGA.shape == (16,)
+    for lo, hi in ((0, 6), (6, 11), (11, 16)):
+        assert OMEGA[lo] == 1.0                          # highest band of the group
+        assert np.all(np.diff(OMEGA[lo:hi]) < 0)         # bands decrease within a group
+    v = RNG.standard_normal(32)
+    for axis, (lo, hi) in enumerate(((0, 6), (6, 11), (11, 16))):
+        pos = np.zeros(3, int)
+        pos[axis] = 7
+        out = orc.rope3d(v, pos, OMEGA)
+        moved = np.flatnonzero(np.abs(out - v).reshape(16, 2).max(axis=1) > 1e-12)
+        assert list(moved) == list(range(lo, hi))
+
+
+def test_frame_positions_token_order():
+    p = orc.frame_positions(5, 3, 4)
+    assert p.shape == (12, 3)
+    for n in range(12):
+        assert tuple(p[n]) == (5, n // 4, n % 4)
+
+
+# ---------------------------------------------------------------------------
+# Attention core
+# ---------------------------------------------------------------------------
+
+def _rand_heads(nq, nk, H=3, dn=5, dr=4, dv=6, scale_q=1.0):
+    q_nope = RNG.standard_normal((nq, H, dn)) * scale_q
+    q_rope = RNG.standard_normal((nq, H, dr)) * scale_q
+    k_nope = RNG.standard_normal((nk, H, dn))
+    k_r = RNG.standard_normal((nk, dr))
+    v = RNG.standard_normal((nk, H, dv))
+    return q_nope, q_rope, k_nope, k_r, v
+
+
+def test_attention_matches_torch_sdpa_fp64():
+    q_nope, q_rope, k_nope, k_r, v = _rand_heads(7, 33)
+    H = q_nope.shape[1]
+    d = q_nope.shape[2] + q_rope.shape[2]
+    out = orc.attention_explicit(q_nope, q_rope, k_nope, k_r, v, 1.0 / math.sqrt(d))
+    Q = torch.from_numpy(np.concatenate([q_nope, q_rope], -1)).permute(1, 0, 2)[None]
+    K = torch.from_numpy(np.concatenate([k_nope, np.repeat(k_r[:, None], H, 1)], -1)).permute(1, 0, 2)[None]
+    V = torch.from_numpy(v).permute(1, 0, 2)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V)   # default scale 1/sqrt(d)
+    np.testing.assert_allclose(out, ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    q_nope, q_rope, k_nope, k_r, v = _rand_heads(4, 9)
+    # zero queries -> uniform weights -> mean of the values
+    out = orc.attention_explicit(0 * q_nope, 0 * q_rope, k_nope, k_r, v, 0.3)
+    np.testing.assert_allclose(out, np.broadcast_to(v.mean(axis=0), out.shape), atol=1e-14)
+    # one key -> that key's value
+    out1 = orc.attention_explicit(q_nope, q_rope, k_nope[:1], k_r[:1], v[:1], 0.3)
+    np.testing.assert_allclose(out1, np.broadcast_to(v[0], out1.shape), atol=1e-14)
+    # a dominant key takes all the weight
+    k2 = k_nope.copy()
+    out2 = orc.attention_explicit(np.ones_like(q_nope), 0 * q_rope, np.where(
+        np.arange(9)[:, None, None] == 4, 50.0, 0.0) + 0 * k2, 0 * k_r, v, 1.0)
+    np.testing.assert_allclose(out2, np.broadcast_to(v[4], out2.shape), atol=1e-12)
+
+
+def test_softmax_rows_sum_to_one():
+    s = RNG.standard_normal((20, 300)) * 30
+    p = orc.softmax_rows(s)
+    assert np.all(p >= 0)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-14)
+    np.testing.assert_allclose(orc.softmax_rows(s + 1234.5), p, atol=1e-14)   # shift invariance
+
+
+def test_absorbed_equals_explicit():
+    # [PL] App. E: latent-form inference keeps the training-time computation.
+    H, dn, dr, dc, dv = 3, 6, 4, 7, 5
+    c = RNG.standard_normal((41, dc))
+    k_r = RNG.standard_normal((41, dr))
+    w_k_up = RNG.standard_normal((H, dc, dn))
+    w_v_up = RNG.standard_normal((H, dc, dv))
+    q_nope = RNG.standard_normal((11, H, dn))
+    q_rope = RNG.standard_normal((11, H, dr))
+    k_nope, v = orc.reconstruct_heads(c, w_k_up, w_v_up)
+    a = orc.attention_explicit(q_nope, q_rope, k_nope, k_r, v, 0.4)
+    b = orc.attention_absorbed(q_nope, q_rope, c, k_r, w_k_up, w_v_up, 0.4)
+    assert rel(b, a) < 1e-12
+
+
+def test_mla_reduces_to_dense_mha_with_selection_up_projections():
+    # d_c = H (d_nope + d_v): W_down holds every head's dense key and value
+    # weights side by side; W_K_up / W_V_up select a head's block. MLA is then
+    # exactly a dense MHA whose positional key is shared by all heads.
+    D, H, dn, dr, dv = 10, 2, 3, 4, 5
+    dc = H * (dn + dv)
+    wk = [RNG.standard_normal((D, dn)) for _ in range(H)]
+    wv = [RNG.standard_normal((D, dv)) for _ in range(H)]
+    w_down = np.concatenate(wk + wv, axis=1)
+    w_k_up = np.zeros((H, dc, dn))
+    w_v_up = np.zeros((H, dc, dv))
+    for h in range(H):
+        w_k_up[h, h * dn:(h + 1) * dn, :] = np.eye(dn)
+        w_v_up[h, H * dn + h * dv:H * dn + (h + 1) * dv, :] = np.eye(dv)
+    w_kr = RNG.standard_normal((D, dr * 8))[:, :dr]
+    w_q = RNG.standard_normal((D, H * (dn + dr)))
+    xk = RNG.standard_normal((13, D))
+    xq = RNG.standard_normal((6, D))
+    # dr = 4 means 2 complex pairs: one on t, one on h
+    pairs, dims = (1, 1, 0), (2, 2, 2)
+    om = orc.rope_frequencies(pairs, dims)
+    pk = RNG.integers(0, 20, size=(13, 3))
+    pq = RNG.integers(0, 20, size=(6, 3))
+
+    c, k_r = orc.latent_entry(xk, w_down, w_kr, pk, om, pairs)
+    k_nope, v = orc.reconstruct_heads(c, w_k_up, w_v_up)
+    q_nope, q_rope = orc.queries(xq, w_q, pq, om, H, dn, dr, pairs)
+    out = orc.attention_explicit(q_nope, q_rope, k_nope, k_r, v, 1 / math.sqrt(dn + dr))
+
+    # dense MHA built directly, RoPE by complex multiplication, SDPA from torch
+    def crot(a, p):
+        z = a[..., 0::2] + 1j * a[..., 1::2]
+        phi = np.stack([p[..., 0] * om[0], p[..., 1] * om[1]], -1)
+        z = z * np.exp(1j * phi)
+        r = np.empty_like(a)
+        r[..., 0::2], r[..., 1::2] = z.real, z.imag
+        return r
+    krot = crot(xk @ w_kr, pk)
+    Qs, Ks, Vs = [], [], []
+    for h in range(H):
+        qh = xq @ w_q[:, h * (dn + dr):(h + 1) * (dn + dr)]
+        Qs.append(np.concatenate([qh[:, :dn], crot(qh[:, dn:], pq)], 1))
+        Ks.append(np.concatenate([xk @ wk[h], krot], 1))
+        Vs.append(xk @ wv[h])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.stack(Qs))[None], torch.from_numpy(np.stack(Ks))[None],
+        torch.from_numpy(np.stack(Vs))[None])[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-11)
+
+
+def test_mla_equals_dense_mha_with_composed_weights_real_dims():
+    # At the real widths: W_K,h := W_down W_K_up[h], W_V,h := W_down W_V_up[h].
+    w = custom(2, 3, window_frames=2, chunk_frames=1, t_first=1, dtype="f32")
+    wt = weights(w)
+    xs = {t: x_frame(w, t) for t in range(2)}
+    out = orc.chunk_attention_reference(w, wt, lambda t: xs[t])
+    om = orc.rope_frequencies()
+    H, dn = w.n_heads, w.d_nope
+    xk = np.concatenate([xs[0], xs[1]]).astype(np.float64)
+    pk = np.concatenate([orc.frame_positions(t, 2, 3) for t in (0, 1)])
+    xq = xs[1].astype(np.float64)
+    pq = orc.frame_positions(1, 2, 3)
+    krot = np.stack([_rope_complex(r, p) for r, p in zip(xk @ wt["w_kr"].astype(np.float64), pk)])
+    Qs, Ks, Vs = [], [], []
+    for h in range(H):
+        WK = wt["w_down"].astype(np.float64) @ wt["w_k_up"][h].astype(np.float64)
+        WV = wt["w_down"].astype(np.float64) @ wt["w_v_up"][h].astype(np.float64)
+        qh = xq @ wt["w_q"][:, h * 128:(h + 1) * 128].astype(np.float64)
+        qr = np.stack([_rope_complex(r, p) for r, p in zip(qh[:, dn:], pq)])
+        Qs.append(np.concatenate([qh[:, :dn], qr], 1))
+        Ks.append(np.concatenate([xk @ WK, krot], 1))
+        Vs.append(xk @ WV)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.stack(Qs))[None], torch.from_numpy(np.stack(Ks))[None],
+        torch.from_numpy(np.stack(Vs))[None])[0].permute(1, 0, 2).numpy()
+    assert rel(out, ref) < 1e-12
+
+
+def test_brute_force_scalar_loops_tiny():
+    # Tiny dims, every sum written as a scalar loop with math.cos / math.exp.
+    D, H, dn, dr, dc, dv = 3, 2, 2, 4, 3, 2
+    pairs, dims = (1, 1, 0), (2, 2, 2)
+    om = orc.rope_frequencies(pairs, dims)
+    w_q = RNG.standard_normal((D, H * (dn + dr)))
+    w_down = RNG.standard_normal((D, dc))
+    w_kr = RNG.standard_normal((D, dr))
+    w_k_up = RNG.standard_normal((H, dc, dn))
+    w_v_up = RNG.standard_normal((H, dc, dv))
+    xk = RNG.standard_normal((5, D))
+    xq = RNG.standard_normal((2, D))
+    pk = RNG.integers(0, 9, size=(5, 3))
+    pq = RNG.integers(0, 9, size=(2, 3))
+    scale = 1 / math.sqrt(dn + dr)
+
+    def mv(x, W, j):
+        return sum(x[i] * W[i][j] for i in range(len(x)))
+
+    def rot(vec, p):
+        ang = [p[0] * om[0], p[1] * om[1]]
+        o = list(vec)
+        for j in range(2):
+            a, b = vec[2 * j], vec[2 * j + 1]
+            o[2 * j] = a * math.cos(ang[j]) - b * math.sin(ang[j])
+            o[2 * j + 1] = a * math.sin(ang[j]) + b * math.cos(ang[j])
+        return o
+
+    ref = np.zeros((2, H, dv))
+    for qi in range(2):
+        qfull = [mv(xq[qi], w_q, j) for j in range(H * (dn + dr))]
+        for h in range(H):
+            qn = qfull[h * (dn + dr):h * (dn + dr) + dn]
+            qr = rot(qfull[h * (dn + dr) + dn:(h + 1) * (dn + dr)], pq[qi])
+            s, vals = [], []
+            for k in range(5):
+                c = [mv(xk[k], w_down, j) for j in range(dc)]
+                kr = rot([mv(xk[k], w_kr, j) for j in range(dr)], pk[k])
+                kn = [sum(c[i] * w_k_up[h][i][j] for i in range(dc)) for j in range(dn)]
+                vv = [sum(c[i] * w_v_up[h][i][j] for i in range(dc)) for j in range(dv)]
+                s.append(scale * (sum(qn[j] * kn[j] for j in range(dn)) +
+                                  sum(qr[j] * kr[j] for j in range(dr))))
+                vals.append(vv)
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            z = sum(e)
+            for j in range(dv):
+                ref[qi, h, j] = sum(e[k] / z * vals[k][j] for k in range(5))
+
+    c, k_r = orc.latent_entry(xk, w_down, w_kr, pk, om, pairs)
+    k_nope, v = orc.reconstruct_heads(c, w_k_up, w_v_up)
+    q_nope, q_rope = orc.queries(xq, w_q, pq, om, H, dn, dr, pairs)
+    out = orc.attention_explicit(q_nope, q_rope, k_nope, k_r, v, scale)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Positional caching and the ring
+# ---------------------------------------------------------------------------
+
+def test_absolute_rotation_equals_window_local_rotation():
+    # [PL] App. D.5 / App. E rotate cached keys at read time with window-local
+    # t; rotating at append time with absolute t gives the same scores when
+    # queries use the same origin (no sink frame).
+    w = custom(2, 3, window_frames=4, chunk_frames=2, t_first=7, dtype="f32")
+    wt = weights(w)
+    xs = {t: x_frame(w, t) for t in range(3, 9)}
+    absolute = orc.chunk_attention_reference(w, wt, lambda t: xs[t])
+    t0 = 5   # oldest frame of the window
+    wl = w.with_(t_first=w.t_first - t0)
+    local = orc.chunk_attention_reference(wl, wt, lambda t: xs[t + t0])
+    assert rel(local, absolute) < 1e-12
+
+
+def test_ring_after_wrap_equals_linear_window_and_slot_order_is_irrelevant():
+    w = custom(2, 2, window_frames=3, chunk_frames=1, t_first=0, dtype="f32")
+    wt = weights(w)
+    om = orc.rope_frequencies()
+    ring = orc.LatentRing(1, 3, 2, 2, w.d_c, w.d_rope)
+    xs = {}
+    for t in range(8):                      # wraps twice; frames 5, 6, 7 remain
+        xs[t] = x_frame(w, t)
+        ring.append_frame(0, t, xs[t], wt["w_down"], wt["w_kr"], om)
+    c, k_r = ring.valid(0, 3)
+    # slots: frame 6 -> 0, frame 7 -> 1, frame 5 -> 2
+    assert [orc.ring_slot(t, 0, 4, 3) for t in (5, 6, 7)] == [8, 0, 4]
+    lin_c, lin_kr = [], []
+    for t in (5, 6, 7):
+        cc, kk = orc.latent_entry(xs[t], wt["w_down"], wt["w_kr"], orc.frame_positions(t, 2, 2), om)
+        lin_c.append(cc)
+        lin_kr.append(kk)
+    order = np.concatenate([np.arange(8, 12), np.arange(0, 4), np.arange(4, 8)])
+    np.testing.assert_array_equal(c[order], np.concatenate(lin_c))
+    np.testing.assert_array_equal(k_r[order], np.concatenate(lin_kr))
+    # attention in ring order equals attention in frame order
+    wl = w.with_(t_first=7)
+    ref = orc.chunk_attention_reference(wl, wt, lambda t: xs[t])
+    q_nope, q_rope = orc.queries(xs[7], wt["w_q"], orc.frame_positions(7, 2, 2), om,
+                                 w.n_heads, w.d_nope, w.d_rope)
+    kn, vv = orc.reconstruct_heads(c, wt["w_k_up"], wt["w_v_up"])
+    ring_out = orc.attention_explicit(q_nope, q_rope, kn, k_r, vv, 1 / math.sqrt(128))
+    assert rel(ring_out, ref) < 1e-13
+
+
+def test_key_permutation_invariance():
+    q_nope, q_rope, k_nope, k_r, v = _rand_heads(5, 40)
+    perm = RNG.permutation(40)
+    a = orc.attention_explicit(q_nope, q_rope, k_nope, k_r, v, 0.5)
+    b = orc.attention_explicit(q_nope, q_rope, k_nope[perm], k_r[perm], v[perm], 0.5)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+def test_reappend_overwrites_in_place():
+    w = custom(1, 3, window_frames=2, chunk_frames=1, t_first=0, dtype="f32")
+    wt = weights(w)
+    om = orc.rope_frequencies()
+    ring = orc.LatentRing(1, 2, 1, 3, w.d_c, w.d_rope)
+    for step in range(3):
+        ring.append_frame(0, 1, x_frame(w, 1, step=step), wt["w_down"], wt["w_kr"], om)
+    c, _ = ring.valid(0, 2)
+    cc, _ = orc.latent_entry(x_frame(w, 1, step=2), wt["w_down"], wt["w_kr"],
+                             orc.frame_positions(1, 1, 3), om)
+    np.testing.assert_array_equal(c[3:6], cc)
+    assert np.isnan(c[:3]).all()            # frame 0 never written
+
+
+def test_append_reference_rows_layout():
+    w = custom(2, 3, window_frames=2, chunk_frames=2, t_first=4, dtype="f32")
+    wt = weights(w)
+    x = np.concatenate([x_frame(w, 4), x_frame(w, 5)])
+    rows = orc.append_reference(w, wt, x, 4, 2)
+    assert rows.shape == (12, 224)
+    np.testing.assert_allclose(rows[:, :192], x.astype(np.float64) @ wt["w_down"], rtol=1e-13, atol=1e-13)
+    kr = x.astype(np.float64) @ wt["w_kr"]
+    pos = np.concatenate([orc.frame_positions(4, 2, 3), orc.frame_positions(5, 2, 3)])
+    for i in range(12):
+        np.testing.assert_allclose(rows[i, 192:], _rope_complex(kr[i], pos[i]), atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: every one of them must trip at least one pin
+# ---------------------------------------------------------------------------
+
+def _wrong_sign_rope(v, pos, omega, pairs=(6, 5, 5)):
+    v = np.asarray(v, dtype=np.float64)
+    phi = np.asarray(pos, dtype=np.float64)[..., orc.rope_pair_axes(pairs)] * omega
+    out = np.empty(np.broadcast_shapes(v.shape, phi.shape[:-1] + (v.shape[-1],)))
+    a, b = v[..., 0::2], v[..., 1::2]
+    out[..., 0::2] = a * np.cos(phi) + b * np.sin(phi)
+    out[..., 1::2] = -a * np.sin(phi) + b * np.cos(phi)
+    return out
+
+
+def _attention_no_rope_term(q_nope, q_rope, k_nope, k_r, v, scale, row_block=256):
+    return _ORIG_ATT(q_nope, 0 * q_rope, k_nope, k_r, v, scale, row_block)
+
+
+def _attention_wrong_scale(q_nope, q_rope, k_nope, k_r, v, scale, row_block=256):
+    return _ORIG_ATT(q_nope, q_rope, k_nope, k_r, v, scale * math.sqrt(2.0), row_block)
+
+
+def _reconstruct_transposed_value(c, w_k_up, w_v_up):
+    k, v = _ORIG_REC(c, w_k_up, w_v_up)
+    return k, v[:, ::-1, :]          # heads' values swapped
+
+
+def _positions_hw_swapped(t, grid_h, grid_w):
+    p = _ORIG_POS(t, grid_h, grid_w)
+    return p[:, [0, 2, 1]]
+
+
+_ORIG_ATT = orc.attention_explicit
+_ORIG_REC = orc.reconstruct_heads
+_ORIG_POS = orc.frame_positions
+
+PINS = [test_rope_is_complex_rotation, test_attention_matches_torch_sdpa_fp64,
+        test_mla_reduces_to_dense_mha_with_selection_up_projections,
+        test_mla_equals_dense_mha_with_composed_weights_real_dims,
+        test_brute_force_scalar_loops_tiny, test_append_reference_rows_layout,
+        test_frame_positions_token_order, test_absorbed_equals_explicit]
+
+
+@pytest.mark.parametrize("name,patch", [
+    ("rope rotation sign", ("rope3d", _wrong_sign_rope)),
+    ("dropped positional score term", ("attention_explicit", _attention_no_rope_term)),
+    ("wrong softmax scale", ("attention_explicit", _attention_wrong_scale)),
+    ("values of the wrong head", ("reconstruct_heads", _reconstruct_transposed_value)),
+    ("h and w swapped in positions", ("frame_positions", _positions_hw_swapped)),
+])
+def test_planted_mistake_is_caught(monkeypatch, name, patch):
+    attr, fn = patch
+    monkeypatch.setattr(orc, attr, fn)
+    caught = 0
+    for pin in PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught > 0, f"no pin catches: {name}"

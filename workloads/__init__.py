@@ -1,0 +1,15 @@
+"""Seeded synthetic workloads for latent-cache chunk attention.
+
+This package only describes shapes and draws seeded random inputs. It holds
+none of the method's arithmetic, so both the CPU oracle (``oracle/``) and the
+HIP path's tests and benchmark can use it without sharing any computation.
+"""
+from .configs import Workload, CONFIGS, config, custom
+from .seeded import (ROLE_WQ, ROLE_WDOWN, ROLE_WKR, ROLE_WKUP, ROLE_WVUP, ROLE_X,
+                     round_bf16, bf16_bits, weights, x_frame, x_frames)
+
+__all__ = [
+    "Workload", "CONFIGS", "config", "custom",
+    "ROLE_WQ", "ROLE_WDOWN", "ROLE_WKR", "ROLE_WKUP", "ROLE_WVUP", "ROLE_X",
+    "round_bf16", "bf16_bits", "weights", "x_frame", "x_frames",
+]
