@@ -1,0 +1,167 @@
+/*
+ * vmla.h -- C ABI of the latent-KV chunk-attention library for AMD MI355X (gfx950).
+ *
+ * The library implements the inference hot path of VideoMLA (arXiv:2605.30351v1,
+ * "VideoMLA: Low-Rank Latent KV Cache for Minute-Scale Autoregressive Video
+ * Diffusion"; citations below refer to the paperlayer.ai section-by-section
+ * summary of that paper as [PL]): every cached token keeps only a shared
+ * content latent c (d_c scalars) and one head-shared 3D-RoPE positional key
+ * k_R (d_rope scalars), and attention runs directly on those latents.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller (allocated and
+ *    freed by the caller, e.g. through PyTorch). The library allocates nothing,
+ *    keeps no global state, and is re-entrant. Every pointer must be 16-byte
+ *    aligned. All tensors are dense and row-major ("C order").
+ *  - Weights follow y = x @ W with W stored [in, out].
+ *  - dtype: one element type per call for x, the weights, the cache and the
+ *    output: VMLA_BF16 (bf16 storage; bf16 matrix-core products with fp32
+ *    accumulation) or VMLA_F32 (fp32 storage; values are converted to bf16
+ *    when they enter a matrix-core product, accumulation stays fp32).
+ *  - stream: a hipStream_t passed as void* (NULL = the default stream). Calls
+ *    are asynchronous on that stream and never synchronise the host.
+ *  - Errors: every argument is validated on the host before any HIP call; a
+ *    negative vmla_status is returned and nothing is launched. A failed launch
+ *    returns VMLA_ERR_HIP. No exception or abort crosses the ABI.
+ *  - Supported geometry in this version: d_nope = 96, d_rope = 32, d_c = 192,
+ *    d_v = 128 (the defaults of [PL] App. D.2-D.3), rope_pairs summing to
+ *    d_rope / 2, d_model a multiple of 64, 1 <= n_heads <= 64.
+ *
+ * Token and position convention: token n of a latent frame sits at grid
+ * position (h, w) = (n / grid_w, n % grid_w); t is the absolute latent-frame
+ * index counted from 0. Ring slot of token n of frame t: (t mod W) * T + n,
+ * with T = grid_h * grid_w tokens per frame and W = window_frames.
+ */
+#ifndef VMLA_H
+#define VMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VMLA_ABI_VERSION 1
+
+typedef enum vmla_status {
+  VMLA_OK = 0,
+  VMLA_ERR_NULL = -1,       /* a required pointer is NULL */
+  VMLA_ERR_SHAPE = -2,      /* unsupported or inconsistent dimensions */
+  VMLA_ERR_DTYPE = -3,      /* unknown dtype, or cache dtype differs from the call's */
+  VMLA_ERR_ALIGN = -4,      /* a pointer is not 16-byte aligned */
+  VMLA_ERR_RANGE = -5,      /* t_first / n_frames / n_valid_frames out of range */
+  VMLA_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than vmla_attention_workspace_bytes */
+  VMLA_ERR_HIP = -7         /* a HIP launch failed (hipGetLastError after the launch) */
+} vmla_status;
+
+typedef enum vmla_dtype { VMLA_F32 = 0, VMLA_BF16 = 1 } vmla_dtype;
+
+/* Layer geometry ([PL] §4, App. C.1, App. D.2-D.3). */
+typedef struct vmla_dims {
+  int32_t d_model;          /* hidden width of x (1536 for Wan2.1-T2V-1.3B) */
+  int32_t n_heads;          /* attention heads (12) */
+  int32_t d_nope;           /* per-head content width of q and k (96) */
+  int32_t d_rope;           /* width of the head-shared positional key (32) */
+  int32_t d_c;              /* width of the shared content latent (192) */
+  int32_t d_v;              /* per-head value width (128) */
+  int32_t rope_pairs[3];    /* complex pairs rotated by t, h, w: {6, 5, 5} ([PL] App. D.3) */
+  int32_t rope_axis_dims[3];/* width D_a of each axis group in the frequency law
+                               omega_i = theta^(-2 i / D_a), i = 0 .. pairs_a - 1: {12, 10, 10} */
+  float rope_theta;         /* 10000 */
+  float scale;              /* softmax scale applied to the full score, 1/sqrt(d_nope + d_rope) */
+} vmla_dims;
+
+/* Sliding-window ring of cached latent frames ([PL] App. C.1, App. D.4).
+ * data: [batch, window_frames * grid_h * grid_w, d_c + d_rope]; row of a slot =
+ * [c (d_c) | k_R rotated by 3D-RoPE at its absolute (t, h, w) (d_rope)]. */
+typedef struct vmla_cache {
+  void* data;
+  int32_t dtype;            /* vmla_dtype */
+  int32_t batch;
+  int32_t window_frames;    /* W */
+  int32_t grid_h;
+  int32_t grid_w;
+} vmla_cache;
+
+/* Fills *dims with the Wan2.1-T2V-1.3B VideoMLA defaults listed above. */
+void vmla_default_dims(vmla_dims* dims);
+
+/*
+ * vmla_cache_append -- write the latent cache entries of one chunk of frames.
+ *
+ * Defined by: the shared content latent c_t = x_t W_down ([PL] §3 "Shared
+ * low-rank KV cache"; App. D.2) and the head-shared positional key
+ * k_R_t = RoPE3D(x_t W_KR, (t, h, w)) ([PL] §3 "Decoupled positional
+ * encoding"; App. D.3); the pair (c_t, k_R_t) is what the cache stores
+ * ([PL] App. D.2), in a fixed-size window of latent frames with FIFO eviction
+ * ([PL] App. D.4).
+ *
+ *   x       [batch, n_frames * T, d_model]  activations of frames
+ *                                           t_first .. t_first + n_frames - 1
+ *   w_down  [d_model, d_c]
+ *   w_kr    [d_model, d_rope]
+ *   cache   ring written in place: exactly the slots of the chunk's frames,
+ *           (t mod W) * T + n, are (over)written; no other slot is touched.
+ *           Appending a frame again (a later denoising step) overwrites it.
+ *
+ * Errors: VMLA_ERR_NULL (any pointer NULL), VMLA_ERR_ALIGN, VMLA_ERR_DTYPE
+ * (dtype invalid or != cache->dtype), VMLA_ERR_SHAPE (unsupported dims,
+ * non-positive grid/batch/window), VMLA_ERR_RANGE (t_first < 0, n_frames < 1,
+ * n_frames > window_frames), VMLA_ERR_HIP.
+ */
+int32_t vmla_cache_append(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                          const void* x, const void* w_down, const void* w_kr,
+                          int32_t t_first, int32_t n_frames, void* stream);
+
+/* Bytes of device workspace vmla_chunk_attention needs for batch and n_q query
+ * tokens (the absorbed, pre-scaled bf16 queries [batch, n_heads, n_q, d_c + d_rope]).
+ * Returns 0 for invalid arguments. */
+size_t vmla_attention_workspace_bytes(const vmla_dims* dims, int32_t batch, int32_t n_q);
+
+/*
+ * vmla_chunk_attention -- attention of one query chunk over the latent window.
+ *
+ * Defined by: latent-form inference ([PL] App. E): queries q = x W_Q split per
+ * head into q_nope (d_nope) and q_rope (d_rope, rotated by 3D-RoPE at the
+ * token's absolute (t, h, w)); the content score uses the absorbed query
+ * q_nope W_K_up[h]^T against c ("Content-path absorption"), the positional
+ * score q_rope . k_R stays separate ("RoPE branch"); softmax over every valid
+ * key of the window, the query chunk included (no mask: chunk-causal attention,
+ * [PL] App. D.4); the softmax-weighted latents are accumulated and projected by
+ * W_V_up[h] ("Value-path absorption"). The result equals explicit per-head
+ * reconstruction k_nope = c W_K_up[h], v = c W_V_up[h] ([PL] §3) up to rounding.
+ *
+ *   x        [batch, n_q, d_model], n_q = n_frames * T: activations of the
+ *            query chunk (frames t_first .. t_first + n_frames - 1)
+ *   w_q      [d_model, n_heads * (d_nope + d_rope)]: head-major columns,
+ *            each head [nope (d_nope) | rope (d_rope)]
+ *   w_k_up   [n_heads, d_c, d_nope]
+ *   w_v_up   [n_heads, d_c, d_v]
+ *   n_valid_frames  must equal min(t_first + n_frames, window_frames): keys are
+ *            the ring slots [0, n_valid_frames * T) of each batch element
+ *   out      [batch, n_q, n_heads, d_v] (dtype of the call)
+ *   workspace >= vmla_attention_workspace_bytes(dims, batch, n_q) bytes; its
+ *            contents are scratch owned by the call until it completes on stream.
+ *
+ * Errors: as vmla_cache_append, plus VMLA_ERR_RANGE when n_valid_frames is not
+ * min(t_first + n_frames, window_frames), VMLA_ERR_WORKSPACE.
+ */
+int32_t vmla_chunk_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                             const void* x, const void* w_q, const void* w_k_up,
+                             const void* w_v_up, int32_t t_first, int32_t n_frames,
+                             int32_t n_valid_frames, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* vmla_status_string(int32_t status);
+
+/* VMLA_ABI_VERSION of the built library. */
+int32_t vmla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VMLA_H */

@@ -1,0 +1,19 @@
+"""Latent-KV chunk attention (VideoMLA hot path) on AMD MI355X.
+
+The compute lives in ``libvmla.so`` (hand-written HIP kernels for gfx950 behind
+the C ABI in include/vmla.h); this package is its ctypes binding. Build the
+library with ``python -m latent_kv_attention_cache_amd.build``.
+"""
+from ._binding import (VMLA_OK, VMLA_ERR_NULL, VMLA_ERR_SHAPE, VMLA_ERR_DTYPE, VMLA_ERR_ALIGN,
+                       VMLA_ERR_RANGE, VMLA_ERR_WORKSPACE, VMLA_ERR_HIP, VMLA_F32, VMLA_BF16,
+                       EXPORTED, LatentCache, VmlaError, default_dims, load_library, vmla_cache,
+                       vmla_dims, vmla_attention_workspace_bytes, vmla_cache_append,
+                       vmla_chunk_attention, vmla_status_string)
+
+__all__ = [
+    "VMLA_OK", "VMLA_ERR_NULL", "VMLA_ERR_SHAPE", "VMLA_ERR_DTYPE", "VMLA_ERR_ALIGN",
+    "VMLA_ERR_RANGE", "VMLA_ERR_WORKSPACE", "VMLA_ERR_HIP", "VMLA_F32", "VMLA_BF16", "EXPORTED",
+    "LatentCache", "VmlaError", "default_dims", "load_library", "vmla_cache", "vmla_dims",
+    "vmla_attention_workspace_bytes", "vmla_cache_append", "vmla_chunk_attention",
+    "vmla_status_string",
+]

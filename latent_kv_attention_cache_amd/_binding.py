@@ -1,0 +1,229 @@
+"""ctypes binding of ``libvmla.so`` (the C ABI in include/vmla.h).
+
+Argument marshalling only: torch tensors supply device pointers, shapes and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels. There is no fallback: if the library is missing, or a tensor is not
+on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+from .build import LIB_PATH
+
+VMLA_OK = 0
+VMLA_ERR_NULL = -1
+VMLA_ERR_SHAPE = -2
+VMLA_ERR_DTYPE = -3
+VMLA_ERR_ALIGN = -4
+VMLA_ERR_RANGE = -5
+VMLA_ERR_WORKSPACE = -6
+VMLA_ERR_HIP = -7
+
+VMLA_F32 = 0
+VMLA_BF16 = 1
+
+_TORCH_DTYPE = {VMLA_F32: torch.float32, VMLA_BF16: torch.bfloat16}
+_VMLA_DTYPE = {torch.float32: VMLA_F32, torch.bfloat16: VMLA_BF16}
+
+
+class vmla_dims(ctypes.Structure):
+    _fields_ = [
+        ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("d_nope", ctypes.c_int32),
+        ("d_rope", ctypes.c_int32), ("d_c", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("rope_pairs", ctypes.c_int32 * 3), ("rope_axis_dims", ctypes.c_int32 * 3),
+        ("rope_theta", ctypes.c_float), ("scale", ctypes.c_float),
+    ]
+
+
+class vmla_cache(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("batch", ctypes.c_int32),
+        ("window_frames", ctypes.c_int32), ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+    ]
+
+
+class VmlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {vmla_status_string(status)} (status {status})")
+
+
+_LIB = None
+
+EXPORTED = ("vmla_default_dims", "vmla_cache_append", "vmla_attention_workspace_bytes",
+            "vmla_chunk_attention", "vmla_status_string", "vmla_abi_version")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libvmla.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m latent_kv_attention_cache_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I32 = ctypes.c_int32
+    lib.vmla_default_dims.argtypes = [ctypes.POINTER(vmla_dims)]
+    lib.vmla_default_dims.restype = None
+    lib.vmla_cache_append.argtypes = [ctypes.POINTER(vmla_dims), ctypes.POINTER(vmla_cache), I32,
+                                      P, P, P, I32, I32, P]
+    lib.vmla_cache_append.restype = I32
+    lib.vmla_attention_workspace_bytes.argtypes = [ctypes.POINTER(vmla_dims), I32, I32]
+    lib.vmla_attention_workspace_bytes.restype = ctypes.c_size_t
+    lib.vmla_chunk_attention.argtypes = [ctypes.POINTER(vmla_dims), ctypes.POINTER(vmla_cache), I32,
+                                         P, P, P, P, I32, I32, I32, P, P, ctypes.c_size_t, P]
+    lib.vmla_chunk_attention.restype = I32
+    lib.vmla_status_string.argtypes = [I32]
+    lib.vmla_status_string.restype = ctypes.c_char_p
+    lib.vmla_abi_version.argtypes = []
+    lib.vmla_abi_version.restype = I32
+    _LIB = lib
+    return lib
+
+
+def vmla_status_string(status: int) -> str:
+    return load_library().vmla_status_string(int(status)).decode()
+
+
+def default_dims(**overrides) -> vmla_dims:
+    d = vmla_dims()
+    load_library().vmla_default_dims(ctypes.byref(d))
+    for k, v in overrides.items():
+        if k in ("rope_pairs", "rope_axis_dims"):
+            getattr(d, k)[:] = list(v)
+        else:
+            setattr(d, k, v)
+    return d
+
+
+@dataclass
+class LatentCache:
+    """Ring of latent frames: ``data`` [batch, window_frames * grid_h * grid_w, d_c + d_rope]."""
+    data: torch.Tensor
+    window_frames: int
+    grid_h: int
+    grid_w: int
+
+    @staticmethod
+    def empty(batch: int, window_frames: int, grid_h: int, grid_w: int, dtype=torch.bfloat16,
+              device="cuda", dims: vmla_dims | None = None, fill: float | None = None) -> "LatentCache":
+        d = dims or default_dims()
+        t = torch.empty((batch, window_frames * grid_h * grid_w, d.d_c + d.d_rope), dtype=dtype,
+                        device=device)
+        if fill is not None:
+            t.fill_(fill)
+        return LatentCache(t, window_frames, grid_h, grid_w)
+
+    @property
+    def batch(self) -> int:
+        return self.data.shape[0]
+
+    @property
+    def tokens_per_frame(self) -> int:
+        return self.grid_h * self.grid_w
+
+    def c_struct(self) -> vmla_cache:
+        return vmla_cache(self.data.data_ptr(), _dtype_code(self.data), self.data.shape[0],
+                          self.window_frames, self.grid_h, self.grid_w)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _VMLA_DTYPE[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32") from None
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _expect_shape(t: torch.Tensor, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def vmla_cache_append(cache: LatentCache, x: torch.Tensor, w_down: torch.Tensor, w_kr: torch.Tensor,
+                      t_first: int, n_frames: int, dims: vmla_dims | None = None, stream=None) -> None:
+    """Write frames t_first .. t_first + n_frames - 1 of every batch element into the ring."""
+    lib = load_library()
+    d = dims or default_dims()
+    B, T = cache.batch, cache.tokens_per_frame
+    _expect_shape(x, (B, n_frames * T, d.d_model), "x")
+    _expect_shape(w_down, (d.d_model, d.d_c), "w_down")
+    _expect_shape(w_kr, (d.d_model, d.d_rope), "w_kr")
+    code = _dtype_code(cache.data)
+    for t, n in ((x, "x"), (w_down, "w_down"), (w_kr, "w_kr")):
+        if t.dtype != cache.data.dtype:
+            raise TypeError(f"{n} dtype {t.dtype} differs from the cache's {cache.data.dtype}")
+    _dev(cache.data, "cache")
+    cs = cache.c_struct()
+    st = lib.vmla_cache_append(ctypes.byref(d), ctypes.byref(cs), code, _dev(x, "x"),
+                               _dev(w_down, "w_down"), _dev(w_kr, "w_kr"), int(t_first),
+                               int(n_frames), _stream(stream))
+    if st != VMLA_OK:
+        raise VmlaError(st, "vmla_cache_append")
+
+
+def vmla_attention_workspace_bytes(batch: int, n_q: int, dims: vmla_dims | None = None) -> int:
+    d = dims or default_dims()
+    return int(load_library().vmla_attention_workspace_bytes(ctypes.byref(d), int(batch), int(n_q)))
+
+
+def vmla_chunk_attention(cache: LatentCache, x: torch.Tensor, w_q: torch.Tensor, w_k_up: torch.Tensor,
+                         w_v_up: torch.Tensor, t_first: int, n_frames: int, n_valid_frames: int,
+                         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                         dims: vmla_dims | None = None, stream=None) -> torch.Tensor:
+    """Attention of the chunk's queries over ring slots [0, n_valid_frames * T).
+
+    Returns ``out`` [batch, n_frames * T, n_heads, d_v] in the cache dtype.
+    """
+    lib = load_library()
+    d = dims or default_dims()
+    B, T = cache.batch, cache.tokens_per_frame
+    n_q = n_frames * T
+    _expect_shape(x, (B, n_q, d.d_model), "x")
+    _expect_shape(w_q, (d.d_model, d.n_heads * (d.d_nope + d.d_rope)), "w_q")
+    _expect_shape(w_k_up, (d.n_heads, d.d_c, d.d_nope), "w_k_up")
+    _expect_shape(w_v_up, (d.n_heads, d.d_c, d.d_v), "w_v_up")
+    code = _dtype_code(cache.data)
+    for t, n in ((x, "x"), (w_q, "w_q"), (w_k_up, "w_k_up"), (w_v_up, "w_v_up")):
+        if t.dtype != cache.data.dtype:
+            raise TypeError(f"{n} dtype {t.dtype} differs from the cache's {cache.data.dtype}")
+    if out is None:
+        out = torch.empty((B, n_q, d.n_heads, d.d_v), dtype=cache.data.dtype, device=x.device)
+    _expect_shape(out, (B, n_q, d.n_heads, d.d_v), "out")
+    need = vmla_attention_workspace_bytes(B, n_q, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _dev(cache.data, "cache")
+    cs = cache.c_struct()
+    st = lib.vmla_chunk_attention(ctypes.byref(d), ctypes.byref(cs), code, _dev(x, "x"),
+                                  _dev(w_q, "w_q"), _dev(w_k_up, "w_k_up"), _dev(w_v_up, "w_v_up"),
+                                  int(t_first), int(n_frames), int(n_valid_frames),
+                                  _dev(out, "out"), _dev(workspace, "workspace"),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != VMLA_OK:
+        raise VmlaError(st, "vmla_chunk_attention")
+    return out

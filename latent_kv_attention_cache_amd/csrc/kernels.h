@@ -1,0 +1,59 @@
+// Internal launch interface between the C-ABI host layer (vmla_api.cpp) and the
+// gfx950 kernels. Arguments are validated by the host layer before any launcher
+// is called; launchers only configure grids and launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vmla {
+
+// Fixed widths of this version (VideoMLA defaults: 96/32 NoPE/RoPE split,
+// 192-wide content latent, 128-wide values).
+constexpr int kDNope = 96;
+constexpr int kDRope = 32;
+constexpr int kDC = 192;
+constexpr int kDV = 128;
+constexpr int kDHead = kDNope + kDRope;   // 128
+constexpr int kRow = kDC + kDRope;        // 224 cached scalars per token
+constexpr int kPairs = kDRope / 2;        // 16 complex RoPE pairs
+
+// Angular rate and axis (0 = t, 1 = h, 2 = w) of each RoPE pair.
+struct RopeTable {
+  float omega[kPairs];
+  int axis[kPairs];
+};
+
+struct AppendArgs {
+  const void* x;        // [batch, n_tok, d_model]
+  const void* w_down;   // [d_model, kDC]
+  const void* w_kr;     // [d_model, kDRope]
+  void* cache;          // [batch, window_frames * T, kRow]
+  int batch, n_tok, d_model;
+  int grid_w, tokens_per_frame, window_frames, t_first;
+  RopeTable rope;
+};
+
+struct QArgs {
+  const void* x;        // [batch, n_q, d_model]
+  const void* w_q;      // [d_model, n_heads * kDHead]
+  const void* w_k_up;   // [n_heads, kDC, kDNope]
+  uint16_t* qhat;       // [batch, n_heads, n_q, kRow] bf16 (workspace)
+  int batch, n_q, d_model, n_heads;
+  int grid_w, tokens_per_frame, t_first;
+  float qscale;         // softmax scale * log2(e)
+  RopeTable rope;
+};
+
+struct AttnArgs {
+  const uint16_t* qhat; // [batch, n_heads, n_q, kRow] bf16
+  const void* cache;    // [batch, cache_rows, kRow]
+  const void* w_v_up;   // [n_heads, kDC, kDV]
+  void* out;            // [batch, n_q, n_heads, kDV]
+  int batch, n_q, n_heads, n_k, cache_rows;
+};
+
+hipError_t launch_append(const AppendArgs& a, bool f32, hipStream_t s);
+hipError_t launch_qprologue(const QArgs& a, bool f32, hipStream_t s);
+hipError_t launch_latent_attn(const AttnArgs& a, bool f32, hipStream_t s);
+
+}  // namespace vmla

@@ -1,0 +1,165 @@
+// Host side of the C ABI declared in include/vmla.h: argument validation (no
+// HIP call before it passes), RoPE frequency table, kernel dispatch.
+#include "vmla.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.h"
+
+namespace {
+
+using namespace vmla;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t check_dims(const vmla_dims* d) {
+  if (!d) return VMLA_ERR_NULL;
+  if (d->d_nope != kDNope || d->d_rope != kDRope || d->d_c != kDC || d->d_v != kDV) return VMLA_ERR_SHAPE;
+  if (d->d_model < 64 || d->d_model % 64 != 0 || d->d_model > (1 << 16)) return VMLA_ERR_SHAPE;
+  if (d->n_heads < 1 || d->n_heads > 64) return VMLA_ERR_SHAPE;
+  int pairs = 0;
+  for (int i = 0; i < 3; ++i) {
+    if (d->rope_pairs[i] < 0 || d->rope_axis_dims[i] < 1) return VMLA_ERR_SHAPE;
+    pairs += d->rope_pairs[i];
+  }
+  if (pairs != kPairs) return VMLA_ERR_SHAPE;
+  if (!(d->rope_theta > 0.f) || !std::isfinite(d->rope_theta)) return VMLA_ERR_SHAPE;
+  if (!(d->scale > 0.f) || !std::isfinite(d->scale)) return VMLA_ERR_SHAPE;
+  return VMLA_OK;
+}
+
+int32_t check_cache(const vmla_cache* c, int32_t dtype) {
+  if (!c) return VMLA_ERR_NULL;
+  if (!c->data) return VMLA_ERR_NULL;
+  if (!aligned16(c->data)) return VMLA_ERR_ALIGN;
+  if (dtype != VMLA_F32 && dtype != VMLA_BF16) return VMLA_ERR_DTYPE;
+  if (c->dtype != dtype) return VMLA_ERR_DTYPE;
+  if (c->batch < 1 || c->window_frames < 1 || c->grid_h < 1 || c->grid_w < 1) return VMLA_ERR_SHAPE;
+  const int64_t t = (int64_t)c->grid_h * c->grid_w;
+  const int64_t rows = t * c->window_frames;
+  // every element offset handled by the kernels must fit in int32 per batch element
+  if (rows * kRow > INT32_MAX || t > INT32_MAX / 64) return VMLA_ERR_SHAPE;
+  return VMLA_OK;
+}
+
+// omega_i = theta^(-2 i / D_a) for the pairs of each axis group, in double.
+RopeTable rope_table(const vmla_dims* d) {
+  RopeTable r{};
+  int j = 0;
+  for (int ax = 0; ax < 3; ++ax) {
+    for (int i = 0; i < d->rope_pairs[ax]; ++i, ++j) {
+      r.omega[j] = (float)std::pow((double)d->rope_theta, -2.0 * i / (double)d->rope_axis_dims[ax]);
+      r.axis[j] = ax;
+    }
+  }
+  return r;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? VMLA_OK : VMLA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+void vmla_default_dims(vmla_dims* d) {
+  if (!d) return;
+  d->d_model = 1536;
+  d->n_heads = 12;
+  d->d_nope = kDNope;
+  d->d_rope = kDRope;
+  d->d_c = kDC;
+  d->d_v = kDV;
+  d->rope_pairs[0] = 6; d->rope_pairs[1] = 5; d->rope_pairs[2] = 5;
+  d->rope_axis_dims[0] = 12; d->rope_axis_dims[1] = 10; d->rope_axis_dims[2] = 10;
+  d->rope_theta = 10000.f;
+  d->scale = (float)(1.0 / std::sqrt((double)(kDNope + kDRope)));
+}
+
+int32_t vmla_abi_version(void) { return VMLA_ABI_VERSION; }
+
+const char* vmla_status_string(int32_t s) {
+  switch (s) {
+    case VMLA_OK: return "ok";
+    case VMLA_ERR_NULL: return "null pointer argument";
+    case VMLA_ERR_SHAPE: return "unsupported or inconsistent dimensions";
+    case VMLA_ERR_DTYPE: return "invalid dtype or dtype mismatch with the cache";
+    case VMLA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case VMLA_ERR_RANGE: return "t_first / n_frames / n_valid_frames out of range";
+    case VMLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case VMLA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t vmla_cache_append(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                          const void* x, const void* w_down, const void* w_kr,
+                          int32_t t_first, int32_t n_frames, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st) return st;
+  if (!x || !w_down || !w_kr) return VMLA_ERR_NULL;
+  st = check_cache(cache, dtype);
+  if (st) return st;
+  if (!aligned16(x) || !aligned16(w_down) || !aligned16(w_kr)) return VMLA_ERR_ALIGN;
+  if (t_first < 0 || n_frames < 1 || n_frames > cache->window_frames) return VMLA_ERR_RANGE;
+  if ((int64_t)t_first + n_frames > (int64_t)INT32_MAX / 2) return VMLA_ERR_RANGE;
+  const int64_t T = (int64_t)cache->grid_h * cache->grid_w;
+  const int64_t n_tok = T * n_frames;
+  if (n_tok * dims->d_model > INT32_MAX) return VMLA_ERR_SHAPE;
+
+  AppendArgs a{};
+  a.x = x; a.w_down = w_down; a.w_kr = w_kr; a.cache = cache->data;
+  a.batch = cache->batch; a.n_tok = (int)n_tok; a.d_model = dims->d_model;
+  a.grid_w = cache->grid_w; a.tokens_per_frame = (int)T;
+  a.window_frames = cache->window_frames; a.t_first = t_first;
+  a.rope = rope_table(dims);
+  return hip_status(launch_append(a, dtype == VMLA_F32, static_cast<hipStream_t>(stream)));
+}
+
+size_t vmla_attention_workspace_bytes(const vmla_dims* dims, int32_t batch, int32_t n_q) {
+  if (check_dims(dims) != VMLA_OK || batch < 1 || n_q < 1) return 0;
+  return (size_t)batch * dims->n_heads * (size_t)n_q * kRow * sizeof(uint16_t);
+}
+
+int32_t vmla_chunk_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                             const void* x, const void* w_q, const void* w_k_up,
+                             const void* w_v_up, int32_t t_first, int32_t n_frames,
+                             int32_t n_valid_frames, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st) return st;
+  if (!x || !w_q || !w_k_up || !w_v_up || !out) return VMLA_ERR_NULL;
+  st = check_cache(cache, dtype);
+  if (st) return st;
+  if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_k_up) || !aligned16(w_v_up) || !aligned16(out))
+    return VMLA_ERR_ALIGN;
+  if (t_first < 0 || n_frames < 1 || n_frames > cache->window_frames) return VMLA_ERR_RANGE;
+  if ((int64_t)t_first + n_frames > (int64_t)INT32_MAX / 2) return VMLA_ERR_RANGE;
+  const int64_t t_end = (int64_t)t_first + n_frames;
+  const int64_t expect_valid = t_end < cache->window_frames ? t_end : cache->window_frames;
+  if (n_valid_frames != expect_valid) return VMLA_ERR_RANGE;
+  const int64_t T = (int64_t)cache->grid_h * cache->grid_w;
+  const int64_t n_q = T * n_frames;
+  if (n_q * dims->d_model > INT32_MAX || n_q * dims->n_heads * kDV > INT32_MAX) return VMLA_ERR_SHAPE;
+  const size_t need = vmla_attention_workspace_bytes(dims, cache->batch, (int32_t)n_q);
+  if (!workspace || workspace_bytes < need) return VMLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return VMLA_ERR_ALIGN;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QArgs q{};
+  q.x = x; q.w_q = w_q; q.w_k_up = w_k_up; q.qhat = static_cast<uint16_t*>(workspace);
+  q.batch = cache->batch; q.n_q = (int)n_q; q.d_model = dims->d_model; q.n_heads = dims->n_heads;
+  q.grid_w = cache->grid_w; q.tokens_per_frame = (int)T; q.t_first = t_first;
+  q.qscale = (float)((double)dims->scale * 1.4426950408889634);   // scale * log2(e)
+  q.rope = rope_table(dims);
+  st = hip_status(launch_qprologue(q, dtype == VMLA_F32, s));
+  if (st) return st;
+
+  AttnArgs a{};
+  a.qhat = q.qhat; a.cache = cache->data; a.w_v_up = w_v_up; a.out = out;
+  a.batch = cache->batch; a.n_q = (int)n_q; a.n_heads = dims->n_heads;
+  a.n_k = (int)(T * n_valid_frames); a.cache_rows = (int)(T * cache->window_frames);
+  return hip_status(launch_latent_attn(a, dtype == VMLA_F32, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+"""Helpers for GPU parity tests: build seeded device inputs, drive the HIP path
+through the C ABI binding, and compare with the CPU oracle.
+
+The device side and the oracle side share only the seeded generators of
+``workloads``; no expected value ever comes from the HIP path.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import latent_kv_attention_cache_amd as vm
+import oracle.vmla_oracle as orc
+from workloads import weights, x_frame
+
+REL_FROB = 1e-2     # ||gpu - ref||_F / ||ref||_F
+MAX_ABS = 3e-2      # max |gpu - ref|
+
+
+def tdtype(w):
+    return torch.float32 if w.dtype == "f32" else torch.bfloat16
+
+
+def to_dev(a, w, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device).to(tdtype(w))
+
+
+def dev_weights(w, wts, device="cuda"):
+    return {k: to_dev(v, w, device) for k, v in wts.items()}
+
+
+def compare(gpu, ref, what, rel_frob=REL_FROB, max_abs=MAX_ABS, per_head_axis=None):
+    """Assert the acceptance bar and return the error summary."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite values in GPU output"
+    err = gpu - ref
+    rel = float(np.linalg.norm(err) / np.linalg.norm(ref))
+    mx = float(np.abs(err).max())
+    summary = {"rel_frob": rel, "max_abs": mx, "max_abs_over_max_ref": mx / float(np.abs(ref).max())}
+    if per_head_axis is not None:
+        e = np.moveaxis(err, per_head_axis, 0).reshape(err.shape[per_head_axis], -1)
+        r = np.moveaxis(ref, per_head_axis, 0).reshape(ref.shape[per_head_axis], -1)
+        summary["worst_head_rel_frob"] = float((np.linalg.norm(e, axis=1) / np.linalg.norm(r, axis=1)).max())
+    print(f"[parity] {what}: {summary}", flush=True)
+    assert rel <= rel_frob, f"{what}: rel Frobenius {rel:.3e} > {rel_frob}"
+    assert mx <= max_abs, f"{what}: max abs {mx:.3e} > {max_abs}"
+    return summary
+
+
+class Run:
+    """One batch of seeded inputs driven through the HIP path for workload ``w``."""
+
+    def __init__(self, w, layer=0, step_of_frame=None, device="cuda", fill=None, batch_x=None):
+        self.w = w
+        self.layer = layer
+        self.step_of_frame = step_of_frame or (lambda t: 0)
+        self.wts = weights(w, layer)
+        self.dw = dev_weights(w, self.wts, device)
+        self.dims = vm.default_dims(d_model=w.d_model, n_heads=w.n_heads)
+        self.cache = vm.LatentCache.empty(w.batch, w.window_frames, w.grid_h, w.grid_w,
+                                          dtype=tdtype(w), device=device, dims=self.dims, fill=fill)
+        self.device = device
+        self._xcache = {}
+        self.batch_x = batch_x   # optional fn(t, b) -> device tensor [T, D] (bulk inputs)
+
+    def x_host(self, t, b=0):
+        key = (t, b, self.step_of_frame(t))
+        if key not in self._xcache:
+            self._xcache[key] = x_frame(self.w, t, b=b, step=key[2], layer=self.layer)
+        return self._xcache[key]
+
+    def x_dev(self, frames):
+        rows = []
+        for b in range(self.w.batch):
+            per = []
+            for t in frames:
+                if self.batch_x is not None:
+                    per.append(self.batch_x(t, b))
+                else:
+                    per.append(to_dev(self.x_host(t, b), self.w, self.device))
+            rows.append(torch.cat(per, 0))
+        return torch.stack(rows, 0).contiguous()
+
+    def append(self, t_first, n_frames):
+        x = self.x_dev(range(t_first, t_first + n_frames))
+        vm.vmla_cache_append(self.cache, x, self.dw["w_down"], self.dw["w_kr"], t_first, n_frames,
+                             dims=self.dims)
+        return x
+
+    def fill_window(self):
+        """Append the frames that precede the query chunk, in chunks of at most W frames."""
+        prior = list(self.w.prior_frames)
+        i = 0
+        while i < len(prior):
+            n = min(self.w.window_frames, len(prior) - i)
+            self.append(prior[i], n)
+            i += n
+
+    def attention(self, t_first=None, n_frames=None):
+        w = self.w
+        t_first = w.t_first if t_first is None else t_first
+        n_frames = w.chunk_frames if n_frames is None else n_frames
+        x = self.x_dev(range(t_first, t_first + n_frames))
+        n_valid = min(t_first + n_frames, w.window_frames)
+        return vm.vmla_chunk_attention(self.cache, x, self.dw["w_q"], self.dw["w_k_up"],
+                                       self.dw["w_v_up"], t_first, n_frames, n_valid,
+                                       dims=self.dims)
+
+    def chunk_step(self):
+        """Fill the window, append the chunk, attend. Returns out [B, N_q, H, d_v]."""
+        self.fill_window()
+        self.append(self.w.t_first, self.w.chunk_frames)
+        return self.attention()
+
+    def reference(self, b=0, query_tokens=None, t_first=None, n_frames=None):
+        w = self.w
+        if t_first is not None:
+            w = w.with_(t_first=t_first, chunk_frames=n_frames or w.chunk_frames)
+        return orc.chunk_attention_reference(w, self.wts, lambda t: self.x_host(t, b), query_tokens)
+
+    def append_reference(self, t_first, n_frames, b=0):
+        x = np.concatenate([self.x_host(t, b) for t in range(t_first, t_first + n_frames)])
+        return orc.append_reference(self.w, self.wts, x, t_first, n_frames)
+
+    def cache_rows(self, t_first, n_frames, b=0):
+        T, W = self.w.tokens_per_frame, self.w.window_frames
+        rows = []
+        data = self.cache.data[b].float().cpu().numpy()
+        for t in range(t_first, t_first + n_frames):
+            s = (t % W) * T
+            rows.append(data[s:s + T])
+        return np.concatenate(rows)

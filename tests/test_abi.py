@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/vmla.h declares, and rejects bad arguments on the host, before any HIP
+call, with the documented status codes."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import latent_kv_attention_cache_amd as vm
+from latent_kv_attention_cache_amd import _binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vmla.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vmla_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return vm.load_library()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert set(names) == set(vm.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.vmla_abi_version() == 1
+    for code in range(-7, 1):
+        s = vm.vmla_status_string(code)
+        assert s and s != "unknown status"
+    assert vm.vmla_status_string(-99) == "unknown status"
+
+
+def test_default_dims_are_wan_videomla(lib):
+    d = vm.default_dims()
+    assert (d.d_model, d.n_heads, d.d_nope, d.d_rope, d.d_c, d.d_v) == (1536, 12, 96, 32, 192, 128)
+    assert list(d.rope_pairs) == [6, 5, 5] and list(d.rope_axis_dims) == [12, 10, 10]
+    assert d.rope_theta == 10000.0
+    assert abs(d.scale - 128 ** -0.5) < 1e-7
+
+
+def test_workspace_bytes(lib):
+    d = vm.default_dims()
+    assert vm.vmla_attention_workspace_bytes(1, 4680, d) == 12 * 4680 * 224 * 2
+    assert vm.vmla_attention_workspace_bytes(0, 4680, d) == 0
+    bad = vm.default_dims(d_c=128)
+    assert vm.vmla_attention_workspace_bytes(1, 10, bad) == 0
+
+
+# Fake, never-dereferenced device addresses: validation must fail before any use.
+A = 0x10000
+B = 0x20000
+C = 0x30000
+MIS = 0x30008   # 8-byte aligned only
+
+
+def _cache(**kw):
+    c = dict(data=A, dtype=vm.VMLA_BF16, batch=1, window_frames=3, grid_h=4, grid_w=6)
+    c.update(kw)
+    return bd.vmla_cache(**c)
+
+
+def _append(lib, dims=None, cache=None, dtype=vm.VMLA_BF16, x=B, wd=C, wk=A, t_first=0, n_frames=1):
+    d = dims if dims is not None else vm.default_dims()
+    cs = cache if cache is not None else _cache()
+    return lib.vmla_cache_append(ctypes.byref(d), ctypes.byref(cs), dtype, x, wd, wk, t_first,
+                                 n_frames, None)
+
+
+def _attn(lib, dims=None, cache=None, dtype=vm.VMLA_BF16, t_first=2, n_frames=1, n_valid=3,
+          ws_bytes=None, ws=B, out=C, x=A):
+    d = dims if dims is not None else vm.default_dims()
+    cs = cache if cache is not None else _cache()
+    if ws_bytes is None:
+        ws_bytes = vm.vmla_attention_workspace_bytes(cs.batch, n_frames * cs.grid_h * cs.grid_w, d)
+    return lib.vmla_chunk_attention(ctypes.byref(d), ctypes.byref(cs), dtype, x, B, C, A, t_first,
+                                    n_frames, n_valid, out, ws, ws_bytes, None)
+
+
+def test_append_validation(lib):
+    assert _append(lib, x=None) == vm.VMLA_ERR_NULL
+    assert _append(lib, wd=None) == vm.VMLA_ERR_NULL
+    assert _append(lib, cache=_cache(data=None)) == vm.VMLA_ERR_NULL
+    assert lib.vmla_cache_append(None, None, 1, A, B, C, 0, 1, None) == vm.VMLA_ERR_NULL
+    assert _append(lib, x=MIS) == vm.VMLA_ERR_ALIGN
+    assert _append(lib, cache=_cache(data=MIS)) == vm.VMLA_ERR_ALIGN
+    assert _append(lib, dtype=7) == vm.VMLA_ERR_DTYPE
+    assert _append(lib, dtype=vm.VMLA_F32) == vm.VMLA_ERR_DTYPE          # cache is bf16
+    assert _append(lib, dims=vm.default_dims(d_c=128)) == vm.VMLA_ERR_SHAPE
+    assert _append(lib, dims=vm.default_dims(d_model=100)) == vm.VMLA_ERR_SHAPE
+    assert _append(lib, dims=vm.default_dims(rope_pairs=(6, 5, 4))) == vm.VMLA_ERR_SHAPE
+    assert _append(lib, dims=vm.default_dims(n_heads=0)) == vm.VMLA_ERR_SHAPE
+    assert _append(lib, cache=_cache(grid_w=0)) == vm.VMLA_ERR_SHAPE
+    assert _append(lib, cache=_cache(batch=0)) == vm.VMLA_ERR_SHAPE
+    assert _append(lib, t_first=-1) == vm.VMLA_ERR_RANGE
+    assert _append(lib, n_frames=0) == vm.VMLA_ERR_RANGE
+    assert _append(lib, n_frames=4) == vm.VMLA_ERR_RANGE                 # > window_frames
+
+
+def test_attention_validation(lib):
+    assert _attn(lib, x=None) == vm.VMLA_ERR_NULL
+    assert _attn(lib, out=None) == vm.VMLA_ERR_NULL
+    assert _attn(lib, out=MIS) == vm.VMLA_ERR_ALIGN
+    assert _attn(lib, dtype=vm.VMLA_F32) == vm.VMLA_ERR_DTYPE
+    assert _attn(lib, dims=vm.default_dims(d_v=64)) == vm.VMLA_ERR_SHAPE
+    assert _attn(lib, t_first=-1) == vm.VMLA_ERR_RANGE
+    assert _attn(lib, n_frames=4, n_valid=3) == vm.VMLA_ERR_RANGE
+    assert _attn(lib, n_valid=2) == vm.VMLA_ERR_RANGE                     # must be min(t_end, W) = 3
+    assert _attn(lib, t_first=0, n_frames=1, n_valid=3) == vm.VMLA_ERR_RANGE   # only 1 frame written
+    assert _attn(lib, t_first=10, n_frames=1, n_valid=4) == vm.VMLA_ERR_RANGE  # > window
+    assert _attn(lib, ws=None) == vm.VMLA_ERR_WORKSPACE
+    assert _attn(lib, ws_bytes=10) == vm.VMLA_ERR_WORKSPACE
+    assert _attn(lib, ws=MIS) == vm.VMLA_ERR_ALIGN
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    cache = vm.LatentCache(torch.zeros(1, 72, 224, dtype=torch.bfloat16), 3, 4, 6)
+    x = torch.zeros(1, 24, 1536, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        vm.vmla_cache_append(cache, x, torch.zeros(1536, 192, dtype=torch.bfloat16),
+                             torch.zeros(1536, 32, dtype=torch.bfloat16), 0, 1)

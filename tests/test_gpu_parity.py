@@ -1,0 +1,117 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU fp64 oracle.
+
+Acceptance: relative Frobenius error <= 1e-2 and max abs error <= 3e-2 (bf16
+in, fp32 accumulate). Because |o| is small at large key counts, the sweeps at
+small key counts (where every key matters), NaN poisoning of slots past the
+valid prefix and canaries around appended frames guard against off-by-one
+errors that the Frobenius bound alone would not see.
+"""
+import numpy as np
+import pytest
+import torch
+
+import latent_kv_attention_cache_amd as vm
+from gpu_cases import Run, compare
+from workloads import config, custom
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs an MI355X")
+    vm.load_library()   # raises if the HIP library was not built
+
+
+def _sync_np(t):
+    torch.cuda.synchronize()
+    return t.float().cpu().numpy()
+
+
+def test_config1_fp32_full():
+    w = config(1)
+    r = Run(w)
+    out = _sync_np(r.chunk_step())
+    compare(out[0], r.reference(), "config 1 output", per_head_axis=1)
+    compare(r.cache_rows(0, 3), r.append_reference(0, 3), "config 1 cache rows")
+
+
+def test_ragged_small_bf16_batch2():
+    # 104 tokens per frame: 208 queries (not a multiple of 256), 520 keys (not a multiple of 64)
+    w = custom(8, 13, window_frames=5, chunk_frames=2, t_first=3, batch=2)
+    r = Run(w)
+    out = _sync_np(r.chunk_step())
+    for b in range(2):
+        compare(out[b], r.reference(b=b), f"ragged b={b}", per_head_axis=1)
+        compare(r.cache_rows(0, 5, b=b), r.append_reference(0, 5, b=b), f"ragged cache b={b}")
+
+
+@pytest.mark.parametrize("grid_h,grid_w,window,t_first", [
+    (1, 1, 1, 0),     # N_k = 1
+    (7, 9, 1, 0),     # 63
+    (8, 8, 1, 0),     # 64
+    (5, 13, 1, 0),    # 65
+    (4, 6, 3, 2),     # 72
+    (7, 223, 1, 0),   # 1561
+])
+def test_key_count_sweep(grid_h, grid_w, window, t_first):
+    w = custom(grid_h, grid_w, window_frames=window, chunk_frames=1, t_first=t_first)
+    r = Run(w)
+    out = _sync_np(r.chunk_step())
+    compare(out[0], r.reference(), f"N_k={w.n_k}", per_head_axis=1)
+
+
+def test_ring_wrap_and_nan_poisoned_prefix():
+    # The ring starts as NaN: attention may only read the valid prefix while it fills.
+    w = custom(4, 6, window_frames=3, chunk_frames=1, t_first=0)
+    r = Run(w, fill=float("nan"))
+    for t in range(8):
+        r.append(t, 1)
+        out = _sync_np(r.attention(t, 1))
+        if t in (0, 1, 2, 3, 5, 7):
+            compare(out[0], r.reference(t_first=t, n_frames=1), f"ring t={t}", per_head_axis=1)
+
+
+def test_append_touches_only_its_slots():
+    w = custom(4, 6, window_frames=5, chunk_frames=2, t_first=6)
+    canary = 7.0
+    r = Run(w, fill=canary)
+    r.append(6, 2)      # frames 6, 7 -> ring slots of frames 1 and 2
+    data = _sync_np(r.cache.data)[0]
+    T = w.tokens_per_frame
+    written = np.zeros(5 * T, bool)
+    written[T:3 * T] = True
+    assert np.all(data[~written] == canary)
+    compare(r.cache_rows(6, 2), r.append_reference(6, 2), "append slots")
+
+
+def test_reappend_overwrites_denoising_step():
+    w = custom(4, 6, window_frames=3, chunk_frames=1, t_first=2)
+    steps = {"s": 0}
+    r = Run(w, step_of_frame=lambda t: steps["s"] if t == 2 else 0)
+    r.fill_window()
+    for s in range(3):
+        steps["s"] = s
+        r.append(2, 1)
+        out = _sync_np(r.attention())
+        compare(out[0], r.reference(), f"denoising step {s}", per_head_axis=1)
+
+
+def test_bitwise_determinism():
+    w = custom(8, 13, window_frames=4, chunk_frames=2, t_first=2)
+    r = Run(w)
+    a = _sync_np(r.chunk_step())
+    b = _sync_np(r.attention())
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_config2_full_shape_sampled_rows():
+    w = config(2)
+    r = Run(w)
+    out = _sync_np(r.chunk_step())
+    rng = np.random.default_rng(2)
+    idx = np.unique(np.concatenate([[0, 1, 255, 256, w.n_q - 1],
+                                    rng.choice(w.n_q, 43, replace=False)]))
+    compare(out[0, idx], r.reference(query_tokens=idx), "config 2 sampled rows", per_head_axis=1)
+    compare(r.cache_rows(18, 3), r.append_reference(18, 3), "config 2 chunk cache rows")
