@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the latent-cache chunk-attention hot path on one MI355X.
+
+One step = one chunk-layer at the Wan2.1-1.3B shape (batch 1, 30x52 latent grid,
+3-frame query chunk = 4680 tokens, 21-frame window = 32760 keys, 12 heads,
+d_c = 192, d_rope = 32, bf16 storage, fp32 accumulation):
+  vmla_cache_append     down-projection + 3D-RoPE + ring write of the chunk
+  vmla_query_prologue   absorbed, pre-scaled queries
+  vmla_latent_attention scores vs the latent window, online softmax, P.c, W_V_up
+All inputs are seeded synthetic tensors already resident in HBM when the timed
+region starts. Prints one JSON line on stdout.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "latent-cache MLA chunk attention TFLOP/s + ms/chunk-layer (Wan-1.3B shape)"
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def work(w):
+    """Algorithmic flops and bytes of one step (absorbed method, bf16 storage)."""
+    H, Nq, Nk, D = w.n_heads, w.n_q * w.batch, w.n_k, w.d_model
+    B = w.batch
+    per_qkh = 2 * (w.d_c + w.d_rope) + 2 * w.d_c                # 832
+    core = per_qkh * w.n_q * Nk * H * B
+    prologue = Nq * (2 * D * H * w.d_head + H * 2 * w.d_nope * w.d_c)
+    epilogue = Nq * H * 2 * w.d_c * w.d_v
+    append = Nq * 2 * D * w.cache_row
+    row = 2 * w.cache_row
+    bytes_append = Nq * D * 2 + D * w.cache_row * 2 + Nq * row
+    bytes_prologue = Nq * D * 2 + D * H * w.d_head * 2 + H * w.d_c * w.d_nope * 2 + Nq * H * row
+    bytes_attn = Nq * H * row + B * Nk * row + H * w.d_c * w.d_v * 2 + Nq * H * w.d_v * 2
+    return dict(core=core, prologue=prologue, epilogue=epilogue, append=append,
+                attn_kernel=core + epilogue, step=core + prologue + epilogue + append,
+                bytes_append=bytes_append, bytes_prologue=bytes_prologue, bytes_attn=bytes_attn)
+
+
+def cpu_baseline(w, wts, x_host, step_flops):
+    """Time the CPU fp64 oracle on two query samples of the same step and
+    extrapolate linearly in query tokens (rows are independent)."""
+    import numpy as np
+    import oracle.vmla_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(7)
+    times = {}
+    for s in (64, 512):
+        idx = np.sort(rng.choice(w.n_q, s, replace=False))
+        t0 = time.perf_counter()
+        orc.chunk_attention_reference(w, wts, x_host, idx)
+        times[s] = time.perf_counter() - t0
+        log(f"[cpu_baseline] oracle on {s} query tokens: {times[s]:.2f} s")
+    per_tok = max((times[512] - times[64]) / 448.0, 0.0)
+    fixed = max(times[64] - 64 * per_tok, 0.0)
+    full_s = fixed + w.n_q * per_tok
+    return {
+        "value": step_flops / full_s / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+        "kind": "oracle", "ms_per_step": full_s * 1e3,
+        "sample": (f"numpy fp64 oracle (explicit per-head K/V) on 64 and 512 of the {w.n_q} "
+                   f"query tokens, all {w.n_heads} heads, full {w.n_k}-key window including its "
+                   f"cache build; timed {times[64]:.2f} s and {times[512]:.2f} s, extrapolated "
+                   f"linearly in query tokens to the full step"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the chunk-attention hot path runs on a single "
+              "MI355X; run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import latent_kv_attention_cache_amd as vm
+    from workloads import config, weights, x_frame
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    vm.load_library()
+    dev = torch.device("cuda:0")
+    w = config(2)
+    wts = weights(w)
+    log(f"[bench] workload: {w.name}")
+    xs = {t: x_frame(w, t) for t in range(w.window_frames)}
+    dw = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in wts.items()}
+    dims = vm.default_dims()
+
+    def xdev(frames):
+        return torch.from_numpy(np.concatenate([xs[t] for t in frames]))[None].to(dev).to(torch.bfloat16)
+
+    cache = vm.LatentCache.empty(w.batch, w.window_frames, w.grid_h, w.grid_w, device=dev)
+    vm.vmla_cache_append(cache, xdev(range(0, 18)), dw["w_down"], dw["w_kr"], 0, 18)
+    chunk = list(w.chunk_frame_ids)
+    x = xdev(chunk).contiguous()
+    n_valid = w.n_valid_frames
+    ws = torch.empty(vm.vmla_attention_workspace_bytes(w.batch, w.n_q, dims), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((w.batch, w.n_q, w.n_heads, w.d_v), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        vm.vmla_cache_append(cache, x, dw["w_down"], dw["w_kr"], w.t_first, w.chunk_frames, dims=dims)
+        if ev is not None:
+            ev[1].record(stream)
+        vm.vmla_query_prologue(cache, x, dw["w_q"], dw["w_k_up"], w.t_first, w.chunk_frames, n_valid,
+                               ws, dims=dims)
+        if ev is not None:
+            ev[2].record(stream)
+        vm.vmla_latent_attention(cache, dw["w_v_up"], w.t_first, w.chunk_frames, n_valid, out, ws,
+                                 dims=dims)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    k_ms = {"append": 0.0, "query_prologue": 0.0, "latent_attn": 0.0}
+    for ev in events:
+        k_ms["append"] += ev[0].elapsed_time(ev[1])
+        k_ms["query_prologue"] += ev[1].elapsed_time(ev[2])
+        k_ms["latent_attn"] += ev[2].elapsed_time(ev[3])
+    k_ms = {k: v / args.steps for k, v in k_ms.items()}
+    assert torch.isfinite(out.float()).all().item(), "non-finite output"
+
+    wk = work(w)
+    tflops = wk["step"] / (ms_step * 1e-3) / 1e12
+    attn_tflops = wk["attn_kernel"] / (k_ms["latent_attn"] * 1e-3) / 1e12
+    append_gbs = wk["bytes_append"] / (k_ms["append"] * 1e-3) / 1e9
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "latent_attn_config2_traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha") == _kernel_sha():
+            traffic = tr.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Wan-1.3B-shaped chunk-layer: B=1, 30x52 grid, 3-frame query chunk over a "
+                        "21-frame latent window",
+            "batch": w.batch, "n_q": w.n_q, "n_k": w.n_k, "n_heads": w.n_heads, "d_model": w.d_model,
+            "d_c": w.d_c, "d_rope": w.d_rope, "d_nope": w.d_nope, "d_v": w.d_v,
+            "flops_per_step": wk["step"],
+        },
+        "kernels_ms": {k: round(v, 4) for k, v in k_ms.items()},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "latent_attn",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "flops_per_launch": wk["attn_kernel"],
+        },
+        "append_roofline": {
+            "bound": "hbm", "achieved": round(append_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(append_gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": wk["bytes_append"],
+        },
+    }
+    log(f"[bench] ms/step {ms_step:.4f}  kernels {k_ms}  attention {attn_tflops:.1f} TFLOP/s")
+    if not args.no_cpu_baseline:
+        xh = lambda t: xs[t]  # noqa: E731
+        result["cpu_baseline"] = cpu_baseline(w, wts, xh, wk["step"])
+    print(json.dumps(result), flush=True)
+
+
+def _kernel_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("latent_attn.hip", "device_common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "latent_kv_attention_cache_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

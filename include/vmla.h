@@ -154,6 +154,31 @@ int32_t vmla_chunk_attention(const vmla_dims* dims, const vmla_cache* cache, int
                              int32_t n_valid_frames, void* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/*
+ * The two stages of vmla_chunk_attention, callable separately (same arguments,
+ * same validation and errors; vmla_chunk_attention == the two in sequence).
+ *
+ * vmla_query_prologue -- queries in absorbed latent form ([PL] App. E
+ * "Content-path absorption", "RoPE branch"; [PL] App. D.3): writes the
+ * pre-scaled bf16 rows [q_nope W_K_up[h]^T | RoPE3D(q_rope)] * scale * log2(e)
+ * of every (batch, head, token) into workspace, layout
+ * [batch, n_heads, n_q, d_c + d_rope].
+ *
+ * vmla_latent_attention -- scores of those rows against the cached rows
+ * [c | k_R] of ring slots [0, n_valid_frames * T), online softmax, weighted sum
+ * of the latents c, projection by W_V_up[h] ([PL] App. E "Value-path
+ * absorption"). Reads the query rows from workspace; writes out.
+ */
+int32_t vmla_query_prologue(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                            const void* x, const void* w_q, const void* w_k_up,
+                            int32_t t_first, int32_t n_frames, int32_t n_valid_frames,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+int32_t vmla_latent_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                              const void* w_v_up, int32_t t_first, int32_t n_frames,
+                              int32_t n_valid_frames, void* out, const void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* vmla_status_string(int32_t status);
 

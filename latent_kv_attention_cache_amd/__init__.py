@@ -8,12 +8,13 @@ from ._binding import (VMLA_OK, VMLA_ERR_NULL, VMLA_ERR_SHAPE, VMLA_ERR_DTYPE, V
                        VMLA_ERR_RANGE, VMLA_ERR_WORKSPACE, VMLA_ERR_HIP, VMLA_F32, VMLA_BF16,
                        EXPORTED, LatentCache, VmlaError, default_dims, load_library, vmla_cache,
                        vmla_dims, vmla_attention_workspace_bytes, vmla_cache_append,
-                       vmla_chunk_attention, vmla_status_string)
+                       vmla_chunk_attention, vmla_latent_attention,
+                       vmla_query_prologue, vmla_status_string)
 
 __all__ = [
     "VMLA_OK", "VMLA_ERR_NULL", "VMLA_ERR_SHAPE", "VMLA_ERR_DTYPE", "VMLA_ERR_ALIGN",
     "VMLA_ERR_RANGE", "VMLA_ERR_WORKSPACE", "VMLA_ERR_HIP", "VMLA_F32", "VMLA_BF16", "EXPORTED",
     "LatentCache", "VmlaError", "default_dims", "load_library", "vmla_cache", "vmla_dims",
     "vmla_attention_workspace_bytes", "vmla_cache_append", "vmla_chunk_attention",
-    "vmla_status_string",
+    "vmla_query_prologue", "vmla_latent_attention", "vmla_status_string",
 ]

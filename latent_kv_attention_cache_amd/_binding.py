@@ -56,7 +56,8 @@ class VmlaError(RuntimeError):
 _LIB = None
 
 EXPORTED = ("vmla_default_dims", "vmla_cache_append", "vmla_attention_workspace_bytes",
-            "vmla_chunk_attention", "vmla_status_string", "vmla_abi_version")
+            "vmla_chunk_attention", "vmla_query_prologue", "vmla_latent_attention",
+            "vmla_status_string", "vmla_abi_version")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -80,6 +81,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vmla_chunk_attention.argtypes = [ctypes.POINTER(vmla_dims), ctypes.POINTER(vmla_cache), I32,
                                          P, P, P, P, I32, I32, I32, P, P, ctypes.c_size_t, P]
     lib.vmla_chunk_attention.restype = I32
+    lib.vmla_query_prologue.argtypes = [ctypes.POINTER(vmla_dims), ctypes.POINTER(vmla_cache), I32,
+                                        P, P, P, I32, I32, I32, P, ctypes.c_size_t, P]
+    lib.vmla_query_prologue.restype = I32
+    lib.vmla_latent_attention.argtypes = [ctypes.POINTER(vmla_dims), ctypes.POINTER(vmla_cache), I32,
+                                          P, I32, I32, I32, P, P, ctypes.c_size_t, P]
+    lib.vmla_latent_attention.restype = I32
     lib.vmla_status_string.argtypes = [I32]
     lib.vmla_status_string.restype = ctypes.c_char_p
     lib.vmla_abi_version.argtypes = []
@@ -226,4 +233,58 @@ def vmla_chunk_attention(cache: LatentCache, x: torch.Tensor, w_q: torch.Tensor,
                                   workspace.numel() * workspace.element_size(), _stream(stream))
     if st != VMLA_OK:
         raise VmlaError(st, "vmla_chunk_attention")
+    return out
+
+
+def _attn_common(cache, x, w_q, w_k_up, w_v_up, n_frames, out, workspace, d):
+    B, T = cache.batch, cache.tokens_per_frame
+    n_q = n_frames * T
+    if x is not None:
+        _expect_shape(x, (B, n_q, d.d_model), "x")
+    if w_q is not None:
+        _expect_shape(w_q, (d.d_model, d.n_heads * (d.d_nope + d.d_rope)), "w_q")
+    if w_k_up is not None:
+        _expect_shape(w_k_up, (d.n_heads, d.d_c, d.d_nope), "w_k_up")
+    if w_v_up is not None:
+        _expect_shape(w_v_up, (d.n_heads, d.d_c, d.d_v), "w_v_up")
+    for t, n in ((x, "x"), (w_q, "w_q"), (w_k_up, "w_k_up"), (w_v_up, "w_v_up"), (out, "out")):
+        if t is not None and t.dtype != cache.data.dtype:
+            raise TypeError(f"{n} dtype {t.dtype} differs from the cache's {cache.data.dtype}")
+    if out is not None:
+        _expect_shape(out, (B, n_q, d.n_heads, d.d_v), "out")
+    need = vmla_attention_workspace_bytes(B, n_q, d)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold at least {need} bytes")
+    _dev(cache.data, "cache")
+    return cache.c_struct(), _dtype_code(cache.data)
+
+
+def vmla_query_prologue(cache: LatentCache, x, w_q, w_k_up, t_first: int, n_frames: int,
+                        n_valid_frames: int, workspace: torch.Tensor, dims: vmla_dims | None = None,
+                        stream=None) -> None:
+    """First stage of vmla_chunk_attention: absorbed, pre-scaled queries into ``workspace``."""
+    lib = load_library()
+    d = dims or default_dims()
+    cs, code = _attn_common(cache, x, w_q, w_k_up, None, n_frames, None, workspace, d)
+    st = lib.vmla_query_prologue(ctypes.byref(d), ctypes.byref(cs), code, _dev(x, "x"),
+                                 _dev(w_q, "w_q"), _dev(w_k_up, "w_k_up"), int(t_first),
+                                 int(n_frames), int(n_valid_frames), _dev(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != VMLA_OK:
+        raise VmlaError(st, "vmla_query_prologue")
+
+
+def vmla_latent_attention(cache: LatentCache, w_v_up, t_first: int, n_frames: int,
+                          n_valid_frames: int, out: torch.Tensor, workspace: torch.Tensor,
+                          dims: vmla_dims | None = None, stream=None) -> torch.Tensor:
+    """Second stage of vmla_chunk_attention: attention over the window from ``workspace``."""
+    lib = load_library()
+    d = dims or default_dims()
+    cs, code = _attn_common(cache, None, None, None, w_v_up, n_frames, out, workspace, d)
+    st = lib.vmla_latent_attention(ctypes.byref(d), ctypes.byref(cs), code, _dev(w_v_up, "w_v_up"),
+                                   int(t_first), int(n_frames), int(n_valid_frames),
+                                   _dev(out, "out"), _dev(workspace, "workspace"),
+                                   workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != VMLA_OK:
+        raise VmlaError(st, "vmla_latent_attention")
     return out

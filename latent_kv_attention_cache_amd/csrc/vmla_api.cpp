@@ -121,18 +121,16 @@ size_t vmla_attention_workspace_bytes(const vmla_dims* dims, int32_t batch, int3
   return (size_t)batch * dims->n_heads * (size_t)n_q * kRow * sizeof(uint16_t);
 }
 
-int32_t vmla_chunk_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
-                             const void* x, const void* w_q, const void* w_k_up,
-                             const void* w_v_up, int32_t t_first, int32_t n_frames,
-                             int32_t n_valid_frames, void* out, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+namespace {
+
+// Shared validation of the attention stages; fills the launch arguments.
+int32_t check_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                        int32_t t_first, int32_t n_frames, int32_t n_valid_frames,
+                        const void* workspace, size_t workspace_bytes, QArgs* q, AttnArgs* a) {
   int32_t st = check_dims(dims);
   if (st) return st;
-  if (!x || !w_q || !w_k_up || !w_v_up || !out) return VMLA_ERR_NULL;
   st = check_cache(cache, dtype);
   if (st) return st;
-  if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_k_up) || !aligned16(w_v_up) || !aligned16(out))
-    return VMLA_ERR_ALIGN;
   if (t_first < 0 || n_frames < 1 || n_frames > cache->window_frames) return VMLA_ERR_RANGE;
   if ((int64_t)t_first + n_frames > (int64_t)INT32_MAX / 2) return VMLA_ERR_RANGE;
   const int64_t t_end = (int64_t)t_first + n_frames;
@@ -145,20 +143,70 @@ int32_t vmla_chunk_attention(const vmla_dims* dims, const vmla_cache* cache, int
   if (!workspace || workspace_bytes < need) return VMLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return VMLA_ERR_ALIGN;
 
+  *q = QArgs{};
+  q->qhat = static_cast<uint16_t*>(const_cast<void*>(workspace));
+  q->batch = cache->batch; q->n_q = (int)n_q; q->d_model = dims->d_model; q->n_heads = dims->n_heads;
+  q->grid_w = cache->grid_w; q->tokens_per_frame = (int)T; q->t_first = t_first;
+  q->qscale = (float)((double)dims->scale * 1.4426950408889634);   // scale * log2(e)
+  q->rope = rope_table(dims);
+
+  *a = AttnArgs{};
+  a->qhat = q->qhat; a->cache = cache->data;
+  a->batch = cache->batch; a->n_q = (int)n_q; a->n_heads = dims->n_heads;
+  a->n_k = (int)(T * n_valid_frames); a->cache_rows = (int)(T * cache->window_frames);
+  return VMLA_OK;
+}
+
+}  // namespace
+
+int32_t vmla_query_prologue(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                            const void* x, const void* w_q, const void* w_k_up,
+                            int32_t t_first, int32_t n_frames, int32_t n_valid_frames,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !w_q || !w_k_up) return VMLA_ERR_NULL;
+  QArgs q;
+  AttnArgs a;
+  int32_t st = check_attention(dims, cache, dtype, t_first, n_frames, n_valid_frames, workspace,
+                               workspace_bytes, &q, &a);
+  if (st) return st;
+  if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_k_up)) return VMLA_ERR_ALIGN;
+  q.x = x; q.w_q = w_q; q.w_k_up = w_k_up;
+  return hip_status(launch_qprologue(q, dtype == VMLA_F32, static_cast<hipStream_t>(stream)));
+}
+
+int32_t vmla_latent_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                              const void* w_v_up, int32_t t_first, int32_t n_frames,
+                              int32_t n_valid_frames, void* out, const void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!w_v_up || !out) return VMLA_ERR_NULL;
+  QArgs q;
+  AttnArgs a;
+  int32_t st = check_attention(dims, cache, dtype, t_first, n_frames, n_valid_frames, workspace,
+                               workspace_bytes, &q, &a);
+  if (st) return st;
+  if (!aligned16(w_v_up) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  a.w_v_up = w_v_up; a.out = out;
+  return hip_status(launch_latent_attn(a, dtype == VMLA_F32, static_cast<hipStream_t>(stream)));
+}
+
+int32_t vmla_chunk_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                             const void* x, const void* w_q, const void* w_k_up,
+                             const void* w_v_up, int32_t t_first, int32_t n_frames,
+                             int32_t n_valid_frames, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!x || !w_q || !w_k_up || !w_v_up || !out) return VMLA_ERR_NULL;
+  QArgs q;
+  AttnArgs a;
+  int32_t st = check_attention(dims, cache, dtype, t_first, n_frames, n_valid_frames, workspace,
+                               workspace_bytes, &q, &a);
+  if (st) return st;
+  if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_k_up) || !aligned16(w_v_up) || !aligned16(out))
+    return VMLA_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  QArgs q{};
-  q.x = x; q.w_q = w_q; q.w_k_up = w_k_up; q.qhat = static_cast<uint16_t*>(workspace);
-  q.batch = cache->batch; q.n_q = (int)n_q; q.d_model = dims->d_model; q.n_heads = dims->n_heads;
-  q.grid_w = cache->grid_w; q.tokens_per_frame = (int)T; q.t_first = t_first;
-  q.qscale = (float)((double)dims->scale * 1.4426950408889634);   // scale * log2(e)
-  q.rope = rope_table(dims);
+  q.x = x; q.w_q = w_q; q.w_k_up = w_k_up;
   st = hip_status(launch_qprologue(q, dtype == VMLA_F32, s));
   if (st) return st;
-
-  AttnArgs a{};
-  a.qhat = q.qhat; a.cache = cache->data; a.w_v_up = w_v_up; a.out = out;
-  a.batch = cache->batch; a.n_q = (int)n_q; a.n_heads = dims->n_heads;
-  a.n_k = (int)(T * n_valid_frames); a.cache_rows = (int)(T * cache->window_frames);
+  a.w_v_up = w_v_up; a.out = out;
   return hip_status(launch_latent_attn(a, dtype == VMLA_F32, s));
 }
 
