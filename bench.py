@@ -88,6 +88,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain device-to-device copy of MIB MiB, whose counter "
+                         "readings calibrate FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -106,6 +109,15 @@ def main():
         sys.exit(1)
     vm.load_library()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {nbytes} bytes read and {nbytes} bytes written")
+        del src, dst
     w = config(2)
     wts = weights(w)
     log(f"[bench] workload: {w.name}")

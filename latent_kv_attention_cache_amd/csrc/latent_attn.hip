@@ -24,6 +24,8 @@
 //   order of keys is permuted identically on both operands).
 // Epilogue: out^T[e][q] = W_V_up[h]^T[e][:] . (O^T / l)[:][q], W_V_up[h]
 // staged in LDS and read transposed.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -41,6 +43,7 @@ constexpr int kCpt = (kChunks + kThreads - 1) / kThreads;
 constexpr int kVLd = kDV + 8;               // padded LDS row of W_V_up[h]
 constexpr int kFeatSteps = kRow / 16;       // 14
 constexpr int kLatTiles = kDC / 32;         // 6
+constexpr float kLazy = 8.f;                // lazy-rescale threshold (log2 units)
 static_assert(kDC * kVLd <= 2 * kTileElems, "W_V_up staging must fit in the tile buffers");
 
 template <typename T>
@@ -95,14 +98,14 @@ void latent_attn_kernel(AttnArgs a) {
   f32x16 o[kLatTiles];
 #pragma unroll
   for (int t = 0; t < kLatTiles; ++t) o[t] = f32x16{};
-  float m = -INFINITY;   // running max of this query (log2 units), shared by both halves
-  float l = 0.f;         // running sum over this lane's half of the keys
+  // m: reference max of this query (log2 units), identical in lanes l and l^32;
+  // l: running sum over this lane's half of the keys, relative to m.
+  float m = -INFINITY;
+  float l = 0.f;
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
-    const bf16_t* K = kt + buf * kTileElems;
-
+  // One 64-key tile. Register r of s0 / s1 holds key 8(r/4) + 4*half + r%4 of
+  // the tile's first / second 32-key block.
+  auto tile = [&](const bf16_t* K, int key0, auto masked) {
     f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kFeatSteps; ++ks) {
@@ -111,11 +114,10 @@ void latent_attn_kernel(AttnArgs a) {
       s0 = mfma32(a0, qf[ks], s0);
       s1 = mfma32(a1, qf[ks], s1);
     }
-    // Register r holds key 8(r/4) + 4*half + r%4 of each 32-key block.
-    if ((j + 1) * kKT > a.n_k) {
+    if constexpr (decltype(masked)::value) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = j * kKT + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
         if (key >= a.n_k) s0[r] = -INFINITY;
         if (key + 32 >= a.n_k) s1[r] = -INFINITY;
       }
@@ -124,28 +126,34 @@ void latent_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
     mx = max_across_halves(mx);
-    const float m_new = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    // Lazy rescaling: the reference max only moves when a score exceeds it by
+    // more than 2^kLazy, so exp2(s - m) <= 2^kLazy stays exact in fp32/bf16 and
+    // the O / l rescale runs on few tiles. Wave-uniform branch.
+    const bool grow = mx > m + kLazy;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mx : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int t = 0; t < kLatTiles; ++t) o[t] *= alpha;
+      m = m_new;
+    }
     float ls = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s0[r] = __builtin_amdgcn_exp2f(s0[r] - m_new);
-      s1[r] = __builtin_amdgcn_exp2f(s1[r] - m_new);
+      s0[r] = __builtin_amdgcn_exp2f(s0[r] - m);
+      s1[r] = __builtin_amdgcn_exp2f(s1[r] - m);
       ls += s0[r] + s1[r];
     }
-    l = l * alpha + ls;
-    m = m_new;
-#pragma unroll
-    for (int t = 0; t < kLatTiles; ++t) o[t] *= alpha;
-
+    l += ls;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
-        const f32x16& s = kb ? s1 : s0;
+        const f32x16& sv = kb ? s1 : s0;
         bf16x8 pb;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[8 * jj + e];
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sv[8 * jj + e];
         const int kbase = kb * 32 + jj * 16;
 #pragma unroll
         for (int t = 0; t < kLatTiles; ++t) {
@@ -154,7 +162,19 @@ void latent_attn_kernel(AttnArgs a) {
         }
       }
     }
+  };
+
+  // Full tiles, then the partial tail tile (if any) with key masking.
+  const int nfull = a.n_k / kKT;
+  for (int j = 0; j < nfull; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < ntiles) load_tile(j + 1);
+    tile(kt + buf * kTileElems, j * kKT, std::false_type{});
     if (j + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+  if (nfull < ntiles) {
+    tile(kt + (nfull & 1) * kTileElems, nfull * kKT, std::true_type{});
     __syncthreads();
   }
 
