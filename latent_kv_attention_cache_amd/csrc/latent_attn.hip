@@ -8,20 +8,41 @@
 // Every query of the chunk attends to every valid key of the window, its own
 // chunk included (App. D.4: chunk-causal, so no mask inside the window).
 //
-// Work split. A workgroup of 8 waves owns 256 query tokens of one (batch, head);
-// each wave owns 32 tokens and keeps their Qhat rows in registers. The waves
-// walk the key window in tiles of 64 keys. A tile [64][224] is staged once in
-// LDS (row-major, double-buffered) and read by all 8 waves, i.e. all query
-// tokens of the block share each cache read.
+// Work split. A workgroup of 8 waves (two per SIMD) owns 256 query tokens of
+// one (batch, head); each wave owns 32 tokens and keeps their Qhat rows in
+// registers. The waves walk the key window in tiles of 64 keys. A tile
+// [64][224] is copied once from global memory straight into LDS (16-byte
+// LDS-DMA loads, no VGPR staging) and read by all 8 waves, so every cache read
+// is shared by all 256 query tokens of the block.
 //
-// Per tile and wave (transposed formulation, keys on MFMA rows):
-//   S^T[key][q]  = K[key][:] . Qhat[q][:]     2 key blocks x 14 MFMA 32x32x16
-//   online softmax per query (= per lane): max / sum over the lane's own keys,
-//   the other half of the keys sits in lane l^32 (one permlane32 swap)
-//   O^T[d][q]   += C^T[d][key] . P^T[key][q]  6 latent blocks x 4 MFMA; C^T is
-//   read straight from the row-major tile with the LDS transpose read, and P^T
-//   is the S^T accumulator converted to bf16 in place (the MFMA contraction
-//   order of keys is permuted identically on both operands).
+// Ping-pong schedule. Time is cut into phases separated by workgroup barriers.
+// Waves 0-3 ("X") and 4-7 ("Y", one per SIMD next to an X wave) run the same
+// program, Y one phase behind X. In its matrix phase for tile j a wave runs
+//   O^T += C^T(j-1) P^T(j-1)   and   S^T(j) = K(j) Qhat^T      (52 MFMA 32x32x16)
+// and in its vector phase it runs the online softmax of S^T(j) and packs
+// P^T(j) to bf16. While one wave of a SIMD is in its matrix phase the other is
+// in its vector phase, so matrix cores and VALU overlap by construction. Every
+// wave executes exactly one barrier per phase, outside all branches, with the
+// same trip count. Within a matrix phase the LDS operand reads run two MFMA
+// steps ahead of the MFMAs (scheduling groups below).
+//
+// Tile buffers. Tile t is read in phases 2t .. 2t+3 (X scores, Y scores, X and Y
+// P.C). The X waves fetch tile t+2 at the end of their matrix phase 2t, after
+// their own LDS reads, into the buffer of tile t-2 (four buffers), and wait for
+// it at the start of their next matrix phase, two barriers before its first
+// reader.
+//
+// LDS tile layout: key row r occupies 448 contiguous bytes (28 chunks of 16 B);
+// chunk c of row r sits at chunk position c ^ swz(r), swz(r) = ((r>>1)^(r>>2)) & 3.
+// The swizzle spreads the row-wise 16-byte reads of 32 consecutive keys over
+// all banks; the transpose reads of 8 rows x 64 B are conflict-free unswizzled.
+//
+// MFMA formulation (keys on MFMA rows): S^T[key][q] = K[key][:] . Qhat[q][:];
+// per query (= per lane) max and sum over the lane's own keys, the other half
+// of the keys sitting in lane l^32 (one permlane32 swap); O^T[d][q] +=
+// C^T[d][key] . P^T[key][q] with C^T read straight from the row-major tile by
+// the LDS transpose read and P^T the S^T accumulator packed to bf16 in place
+// (the MFMA contraction order of keys is permuted identically on both sides).
 // Epilogue: out^T[e][q] = W_V_up[h]^T[e][:] . (O^T / l)[:][q], W_V_up[h]
 // staged in LDS and read transposed.
 #include <type_traits>
@@ -36,64 +57,104 @@ constexpr int kKT = 64;                     // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlockQ = 32 * kWaves;        // query tokens per workgroup
-constexpr int kKLd = kRow + 8;              // padded LDS key row (elements)
-constexpr int kTileElems = kKT * kKLd;
-constexpr int kChunks = kKT * kRow / 8;     // 16-byte chunks per tile
-constexpr int kCpt = (kChunks + kThreads - 1) / kThreads;
-constexpr int kVLd = kDV + 8;               // padded LDS row of W_V_up[h]
+constexpr int kChunksPerRow = kRow / 8;     // 28
+constexpr int kTileElems = kKT * kRow;      // unpadded, swizzled
+constexpr int kTileLoads = kKT * kChunksPerRow / 64;   // wave-wide 16-byte loads per tile (28)
+constexpr int kLoaders = kWaves / 2;        // the X waves issue the tile loads
+constexpr int kLoadsPerWave = kTileLoads / kLoaders;
+constexpr int kBufs = 4;
+constexpr int kVLd = kDV + 8;               // padded LDS row of W_V_up[h] (epilogue)
 constexpr int kFeatSteps = kRow / 16;       // 14
 constexpr int kLatTiles = kDC / 32;         // 6
 constexpr float kLazy = 8.f;                // lazy-rescale threshold (log2 units)
-static_assert(kDC * kVLd <= 2 * kTileElems, "W_V_up staging must fit in the tile buffers");
+static_assert(kKT * kChunksPerRow % 64 == 0, "tile must split into wave-wide loads");
+static_assert(kTileLoads % kLoaders == 0, "tile loads must split evenly over the loading waves");
+static_assert(kDC * kVLd <= kBufs * kTileElems, "W_V_up staging must fit in the tile buffers");
+
+// Scheduling-group masks (instruction classes of sched_group_barrier).
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+
+// 16-byte LDS-DMA load: lane i's 16 bytes from base + voff (bytes; base
+// wave-uniform) land at LDS byte address lds_addr + 16 i (lds_addr
+// wave-uniform). Issued as inline assembly so the compiler does not serialize
+// unrelated LDS reads behind it; completion is waited for explicitly with
+// s_waitcnt vmcnt. No register output; M0 is set inside the statement.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory");
+}
 
 template <typename T>
 __global__ __launch_bounds__(kThreads)
 void latent_attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t kt[2 * kTileElems];
+  __shared__ __attribute__((aligned(16))) bf16_t kt[kBufs * kTileElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int half = lane >> 5;
   const int qi = lane & 31;
+  const int lag = wave >= kLoaders ? 1 : 0;   // Y waves run one phase behind
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int qrow = blockIdx.x * kBlockQ + 32 * wave + qi;
   const bool qvalid = qrow < a.n_q;
 
   // Qhat fragments (B operand of S^T): lane holds features ks*16 + 8*half + e of its query.
-  const bf16_t* qp = a.qhat + (((size_t)b * a.n_heads + h) * a.n_q + (qvalid ? qrow : a.n_q - 1)) * kRow;
   bf16x8 qf[kFeatSteps];
+  {
+    const bf16_t* qp = a.qhat + (((size_t)b * a.n_heads + h) * a.n_q + (qvalid ? qrow : a.n_q - 1)) * kRow;
 #pragma unroll
-  for (int ks = 0; ks < kFeatSteps; ++ks)
-    qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + 8 * half);
+    for (int ks = 0; ks < kFeatSteps; ++ks)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + 8 * half);
+  }
 
   const T* cache = static_cast<const T*>(a.cache) + (size_t)b * a.cache_rows * kRow;
   const int ntiles = (a.n_k + kKT - 1) / kKT;
 
-  uint4 pre[kCpt];
-  auto load_tile = [&](int j) {
+  // ---- tile staging (X waves only). Wave-wide load n fills chunk slots
+  // [64n, 64n + 64) of a tile; lane i fills slot 64n + i, which holds chunk
+  // (key, c) with slot = key * 28 + (c ^ swz(key)). Keys past the window are
+  // clamped to the last valid key (finite data; their scores are masked).
+  const uint32_t kt_lds = (uint32_t)(uintptr_t)(VMLA_LDS bf16_t*)kt;
+  auto issue_tile = [&](int j) {
+    const int buf = j % kBufs;
 #pragma unroll
-    for (int i = 0; i < kCpt; ++i) {
-      const int c = tid + i * kThreads;
-      const int key = c / (kRow / 8), cc = c % (kRow / 8);
-      const int kg = j * kKT + key;
-      pre[i] = make_uint4(0, 0, 0, 0);
-      if (c < kChunks && kg < a.n_k) pre[i] = load8_bf16<T>(cache + (size_t)kg * kRow + 8 * cc);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kCpt; ++i) {
-      const int c = tid + i * kThreads;
-      const int key = c / (kRow / 8), cc = c % (kRow / 8);
-      if (c < kChunks) *reinterpret_cast<uint4*>(&kt[buf * kTileElems + key * kKLd + 8 * cc]) = pre[i];
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+      const int n = wave + kLoaders * i;
+      const int slot = 64 * n + lane;
+      const int key = slot / kChunksPerRow;
+      const int col = 8 * ((slot - key * kChunksPerRow) ^ swz(key));
+      const int kg = min(j * kKT + key, a.n_k - 1);
+      if constexpr (std::is_same_v<T, bf16_t>) {
+        dma16(cache, (uint32_t)((kg * kRow + col) * 2),
+              kt_lds + 2u * (uint32_t)(buf * kTileElems + 512 * n));
+      } else {
+        const T* src = cache + (size_t)kg * kRow + col;
+        *reinterpret_cast<uint4*>(kt + buf * kTileElems + 512 * n + 8 * lane) = load8_bf16<T>(src);
+      }
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  // Per-lane LDS element offsets (relative to a tile) of the operand reads.
+  // Score A operand: row qi (+32 for the second key block), features
+  // 16 ks + 8 half, i.e. chunk 2 ks + half; with s = swz(qi) (swz(qi + 32) == s)
+  // the chunk lands at 2 (ks ^ (s >> 1)) + (half ^ (s & 1)).
+  const int s_q = swz(qi);
+  const int a_base = qi * kRow + 8 * (half ^ (s_q & 1));
+  const int a_flip = 16 * (s_q >> 1);
+  // Transpose reads of C^T: lane j of a 16-lane group reads row
+  // kbase + rb + j/4 (rb = 4*half or 8 + 4*half), elements 32 t + nsub + 4 (j%4);
+  // kbase is a multiple of 16, so the swizzle depends only on rb + j/4.
+  const int jl = lane & 15;
+  const int x4 = ((lane & 16) >> 3) + ((jl & 3) >> 1);   // chunk within the 4-chunk group
+  const int sub = 4 * (jl & 1);
+  const int r1 = 4 * half + (jl >> 2), r2 = 8 + 4 * half + (jl >> 2);
+  const int v_off1 = r1 * kRow + 8 * (x4 ^ swz(r1)) + sub;
+  const int v_off2 = r2 * kRow + 8 * (x4 ^ swz(r2)) + sub;
 
   f32x16 o[kLatTiles];
 #pragma unroll
@@ -102,19 +163,56 @@ void latent_attn_kernel(AttnArgs a) {
   // l: running sum over this lane's half of the keys, relative to m.
   float m = -INFINITY;
   float l = 0.f;
+  f32x16 s0, s1;          // S^T of the current tile: register r holds key 32 kb + 8(r/4) + 4 half + r%4
+  bf16x8 pb[2][2];        // P^T of the previous tile, bf16, per (key block, 16-key step)
 
-  // One 64-key tile. Register r of s0 / s1 holds key 8(r/4) + 4*half + r%4 of
-  // the tile's first / second 32-key block.
-  auto tile = [&](const bf16_t* K, int key0, auto masked) {
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+  // O^T += C^T(tile) P^T: 24 MFMAs, 48 transpose reads issued two MFMAs ahead.
+  auto accumulate = [&](const bf16_t* K) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const bf16_t* Kb = K + (kb * 32 + jj * 16) * kRow;
+#pragma unroll
+        for (int t = 0; t < kLatTiles; ++t) {
+          const bf16x4 lo = lds_tr4(Kb + v_off1 + 32 * t);
+          const bf16x4 hi = lds_tr4(Kb + v_off2 + 32 * t);
+          const bf16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[t] = mfma32(av, pb[kb][jj], o[t]);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 22; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+  };
+  // S^T of one tile: 28 MFMAs, 28 row reads issued two steps ahead.
+  auto scores = [&](const bf16_t* K) {
+    s0 = f32x16{};
+    s1 = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kFeatSteps; ++ks) {
-      const bf16x8 a0 = lds_row8(&K[qi * kKLd + ks * 16 + 8 * half]);
-      const bf16x8 a1 = lds_row8(&K[(32 + qi) * kKLd + ks * 16 + 8 * half]);
+      const int off = a_base + ((16 * ks) ^ a_flip);
+      const bf16x8 a0 = lds_row8(K + off);
+      const bf16x8 a1 = lds_row8(K + off + 32 * kRow);
       s0 = mfma32(a0, qf[ks], s0);
       s1 = mfma32(a1, qf[ks], s1);
     }
-    if constexpr (decltype(masked)::value) {
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 1);
+  };
+  // Online softmax of the current tile; leaves P^T (bf16) in pb.
+  auto softmax = [&](int key0) {
+    if (key0 + kKT > a.n_k) {    // the window ends inside this tile (wave-uniform)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -147,36 +245,41 @@ void latent_attn_kernel(AttnArgs a) {
     }
     l += ls;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const f32x16& sv = kb ? s1 : s0;
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sv[8 * jj + e];
-        const int kbase = kb * 32 + jj * 16;
-#pragma unroll
-        for (int t = 0; t < kLatTiles; ++t) {
-          const bf16x8 av = lds_tr8(K, kKLd, kbase + 4 * half, kbase + 8 + 4 * half, 32 * t, lane);
-          o[t] = mfma32(av, pb, o[t]);
-        }
+      for (int e = 0; e < 8; ++e) {
+        pb[0][jj][e] = (__bf16)s0[8 * jj + e];
+        pb[1][jj][e] = (__bf16)s1[8 * jj + e];
       }
-    }
   };
 
-  // Full tiles, then the partial tail tile (if any) with key masking.
-  const int nfull = a.n_k / kKT;
-  for (int j = 0; j < nfull; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
-    tile(kt + buf * kTileElems, j * kKT, std::false_type{});
-    if (j + 1 < ntiles) store_tile(buf ^ 1);
+  if (!lag) {
+    issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+
+  // Phases p = 0 .. 2 ntiles + 1; wave-local phase q = p - lag.
+  const int nphases = 2 * ntiles + 2;
+  for (int p = 0; p < nphases; ++p) {
+    const int q = p - lag;
+    if (q >= 0) {
+      const int jt = q >> 1;
+      if ((q & 1) == 0) {          // matrix phase for tile jt
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile jt+1 (fetched two phases ago)
+        __builtin_amdgcn_s_setprio(1);
+        if (jt >= 1) accumulate(kt + ((jt - 1) % kBufs) * kTileElems);
+        if (jt < ntiles) scores(kt + (jt % kBufs) * kTileElems);
+        __builtin_amdgcn_s_setprio(0);
+        if (!lag && jt + 2 < ntiles) issue_tile(jt + 2);
+      } else if (jt < ntiles) {    // vector phase for tile jt
+        softmax(jt * kKT);
+      }
+    }
     __syncthreads();
   }
-  if (nfull < ntiles) {
-    tile(kt + (nfull & 1) * kTileElems, nfull * kKT, std::true_type{});
-    __syncthreads();
-  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: out = (O / l) @ W_V_up[h]
   const float inv = 1.f / sum_across_halves(l);
