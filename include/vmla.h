@@ -108,8 +108,9 @@ void vmla_default_dims(vmla_dims* dims);
  *
  * Errors: VMLA_ERR_NULL (any pointer NULL), VMLA_ERR_ALIGN, VMLA_ERR_DTYPE
  * (dtype invalid or != cache->dtype), VMLA_ERR_SHAPE (unsupported dims,
- * non-positive grid/batch/window), VMLA_ERR_RANGE (t_first < 0, n_frames < 1,
- * n_frames > window_frames), VMLA_ERR_HIP.
+ * non-positive grid/batch/window, window_frames * T >= 2^24 slots),
+ * VMLA_ERR_RANGE (t_first < 0, n_frames < 1, n_frames > window_frames,
+ * t_first + n_frames > 2^20), VMLA_ERR_HIP.
  */
 int32_t vmla_cache_append(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
                           const void* x, const void* w_down, const void* w_kr,

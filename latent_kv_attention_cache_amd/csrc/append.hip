@@ -8,28 +8,39 @@
 // (App. D.3); the cache is a fixed-size window of latent frames with FIFO
 // eviction (App. D.4).
 //
-// One workgroup (4 waves) computes a 128-token x 224-column tile; wave w owns
-// tokens [32w, 32w+32) of the tile and all seven 32-column output blocks. The
-// K loop stages a 64-deep slice of x and of [W_down | W_KR] in LDS, row-major;
-// x fragments are read row-wise, weight fragments with the LDS transpose read.
+// One workgroup (7 waves) computes a 64-token x 224-column tile; wave w owns
+// the 32-column block w (blocks 0-5: c from W_down, block 6: k_R from W_KR)
+// for all 64 tokens. The d_model contraction runs as a pipeline of 64-deep
+// stages (kStages buffers fetched by LDS-DMA kStages-1 stages ahead, one
+// barrier per stage); x, W_down and W_KR slices sit in separate LDS regions.
 #include "device_common.h"
 #include "kernels.h"
+#include "staging.h"
 
 namespace vmla {
 namespace {
 
-constexpr int kTok = 128;            // tokens per workgroup
-constexpr int kKc = 64;              // K slice per stage
-constexpr int kXLd = kKc + 8;        // padded LDS row of the x slice
-constexpr int kWLd = kRow + 8;       // padded LDS row of the weight slice
-constexpr int kThreads = 256;
-constexpr int kColTiles = kRow / 32; // 7
+constexpr int kTok = 64;               // tokens per workgroup
+constexpr int kWaves = kRow / 32;      // 7: one per 32-column block
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStages = 4;
+constexpr int kAElems = kTok * kStageK;          // x slice        (8 KB)
+constexpr int kB1Elems = kStageK * kDC;          // W_down slice   (24 KB)
+constexpr int kB2Elems = kStageK * kDRope;       // W_KR slice     (4 KB)
+constexpr int kStageElems = kAElems + kB1Elems + kB2Elems;
+constexpr int kALoads = kAElems * 2 / 1024;      // 8
+constexpr int kB1Loads = kB1Elems * 2 / 1024;    // 24
+constexpr int kB2Loads = kB2Elems * 2 / 1024;    // 4
+constexpr int kLoads = kALoads + kB1Loads + kB2Loads;   // 36
+// wave w issues loads w, w + 7, ...: wave 0 issues 6 per stage, waves 1-6 issue 5
+constexpr int kLoadsWave0 = (kLoads + kWaves - 1) / kWaves;
+constexpr int kLoadsOther = kLoads / kWaves;
+static_assert(kLoads % kWaves == 1, "load split assumed: wave 0 takes one extra load");
 
 template <typename T>
 __global__ __launch_bounds__(kThreads)
 void append_kernel(AppendArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t xs[kTok * kXLd];
-  __shared__ __attribute__((aligned(16))) bf16_t ws[kKc * kWLd];
+  __shared__ __attribute__((aligned(16))) bf16_t smem[kStages * kStageElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -40,78 +51,80 @@ void append_kernel(AppendArgs a) {
   const T* x = static_cast<const T*>(a.x) + (size_t)b * a.n_tok * a.d_model;
   const T* wd = static_cast<const T*>(a.w_down);
   const T* wr = static_cast<const T*>(a.w_kr);
+  const int nst = a.d_model / kStageK;
 
-  f32x16 acc[kColTiles];
-#pragma unroll
-  for (int c = 0; c < kColTiles; ++c) acc[c] = f32x16{};
-
-  for (int k0 = 0; k0 < a.d_model; k0 += kKc) {
-    // stage x[tok0 .. tok0+127][k0 .. k0+63]: 1024 chunks of 8
-#pragma unroll
-    for (int i = 0; i < (kTok * kKc / 8) / kThreads; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c >> 3, kc = c & 7;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (tok0 + row < a.n_tok) v = load8_bf16<T>(x + (size_t)(tok0 + row) * a.d_model + k0 + 8 * kc);
-      *reinterpret_cast<uint4*>(&xs[row * kXLd + 8 * kc]) = v;
+  auto issue = [&](int s) {
+    bf16_t* st = smem + (s % kStages) * kStageElems;
+    for (int n = wave; n < kLoads; n += kWaves) {
+      if (n < kALoads) stage_a_load<T>(st, x, a.d_model, tok0, a.n_tok, s * kStageK, n, lane);
+      else if (n < kALoads + kB1Loads)
+        stage_b_load<T, kDC>(st + kAElems, wd, kDC, 0, s * kStageK, n - kALoads, lane);
+      else
+        stage_b_load<T, kDRope>(st + kAElems + kB1Elems, wr, kDRope, 0, s * kStageK,
+                                n - kALoads - kB1Loads, lane);
     }
-    // stage [W_down | W_KR][k0 .. k0+63][0 .. 223]: 1792 chunks of 8
+  };
+  auto wait = [&](int stages) {
+    if (wave == 0) wait_stages<kLoadsWave0>(stages);
+    else wait_stages<kLoadsOther>(stages);
+  };
+
+  for (int s = 0; s < kStages - 1 && s < nst; ++s) issue(s);
+
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  for (int s = 0; s < nst; ++s) {
+    wait(min(kStages - 2, nst - 1 - s));                  // stage s has landed
+    __syncthreads();
+    if (s + kStages - 1 < nst) issue(s + kStages - 1);    // into the buffer of stage s-1
+    const bf16_t* A = smem + (s % kStages) * kStageElems;
 #pragma unroll
-    for (int i = 0; i < (kKc * kRow / 8 + kThreads - 1) / kThreads; ++i) {
-      const int c = tid + i * kThreads;
-      if (c < kKc * kRow / 8) {
-        const int kr = c / (kRow / 8), cc = c % (kRow / 8);
-        const T* src = cc < kDC / 8 ? wd + (size_t)(k0 + kr) * kDC + 8 * cc
-                                    : wr + (size_t)(k0 + kr) * kDRope + 8 * (cc - kDC / 8);
-        *reinterpret_cast<uint4*>(&ws[kr * kWLd + 8 * cc]) = load8_bf16<T>(src);
+    for (int ks = 0; ks < kStageK / 16; ++ks) {
+      bf16x8 bv;
+      if (wave < kWaves - 1) bv = b_frag<kDC>(A + kAElems, ks, 32 * wave, lane);
+      else bv = b_frag<kDRope>(A + kAElems + kB1Elems, ks, 0, lane);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const bf16x8 av = a_frag(A, 32 * tt + (lane & 31), ks, half);
+        acc[tt] = mfma32(av, bv, acc[tt]);
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < kKc / 16; ++ks) {
-      const bf16x8 av = lds_row8(&xs[(32 * wave + (lane & 31)) * kXLd + ks * 16 + 8 * half]);
-      const int ka = ks * 16 + 8 * half;
-#pragma unroll
-      for (int c = 0; c < kColTiles; ++c) {
-        const bf16x8 bv = lds_tr8(ws, kWLd, ka, ka + 4, 32 * c, lane);
-        acc[c] = mfma32(av, bv, acc[c]);
-      }
-    }
-    __syncthreads();
   }
 
-  // Epilogue. Register r of lane l holds token row 8(r/4) + 4*half + r%4 of the
-  // wave's 32 tokens and column 32c + l%32.
+  // Epilogue. Register r of lane l holds token row 32 tt + 8(r/4) + 4 half + r%4
+  // and column 32 wave + l%32; wave 6 holds the k_R columns and rotates them.
   const int col = lane & 31;
   const int pair = col >> 1;
   const bool odd = col & 1;
-  const float omega = a.rope.omega[pair];
+  const bool rope = wave == kWaves - 1;
+  const float rev = a.rope.rev[pair];
   const int axis = a.rope.axis[pair];
   T* cache = static_cast<T*>(a.cache);
   const size_t ring_rows = (size_t)a.window_frames * a.tokens_per_frame;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = 32 * wave + 8 * (r >> 2) + 4 * half + (r & 3);
-    const int n = tok0 + row;
-    // the RoPE lane exchange runs in every lane so that partners are always live
-    const float v = acc[kColTiles - 1][r];
-    const float partner = swap_adjacent(v);
-    if (n >= a.n_tok) continue;
-    const int f = n / a.tokens_per_frame;
-    const int n_in = n - f * a.tokens_per_frame;
-    const int t = a.t_first + f;
-    const int hh = n_in / a.grid_w;
-    const int ww = n_in - hh * a.grid_w;
-    const int pos = axis == 0 ? t : (axis == 1 ? hh : ww);
-    float sn, cs;
-    sincosf((float)pos * omega, &sn, &cs);
-    // pair (a0, a1) -> (a0 cos - a1 sin, a0 sin + a1 cos)
-    const float rot = odd ? partner * sn + v * cs : v * cs - partner * sn;
-    const size_t slot = (size_t)(t % a.window_frames) * a.tokens_per_frame + n_in;
-    T* dst = cache + ((size_t)b * ring_rows + slot) * kRow;
+  for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-    for (int c = 0; c < kColTiles - 1; ++c) dst[32 * c + col] = from_f32<T>(acc[c][r]);
-    dst[32 * (kColTiles - 1) + col] = from_f32<T>(rot);
+    for (int r = 0; r < 16; ++r) {
+      const int row = 32 * tt + 8 * (r >> 2) + 4 * half + (r & 3);
+      const int n = tok0 + row;
+      float v = acc[tt][r];
+      // the RoPE lane exchange runs in every lane so that partners are always live
+      const float partner = swap_adjacent(v);
+      if (n >= a.n_tok) continue;
+      int n_in, ww, tw;
+      const int f = div_small(n, a.tokens_per_frame, a.inv_tokens_per_frame, &n_in);
+      const int t = a.t_first + f;
+      if (rope) {
+        const int hh = div_small(n_in, a.grid_w, a.inv_grid_w, &ww);
+        const int pos = axis == 0 ? t : (axis == 1 ? hh : ww);
+        float sn, cs;
+        sincos_rev(pos, rev, &sn, &cs);
+        // pair (a0, a1) -> (a0 cos - a1 sin, a0 sin + a1 cos)
+        v = odd ? partner * sn + v * cs : v * cs - partner * sn;
+      }
+      div_small(t, a.window_frames, a.inv_window_frames, &tw);
+      const size_t slot = (size_t)tw * a.tokens_per_frame + n_in;
+      cache[((size_t)b * ring_rows + slot) * kRow + 32 * wave + col] = from_f32<T>(v);
+    }
   }
 }
 

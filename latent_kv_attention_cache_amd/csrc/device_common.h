@@ -84,6 +84,32 @@ __device__ __forceinline__ float swap_adjacent(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
 
+// q = n / d and *rem = n % d for 0 <= n < 2^24 and 1 <= d < 2^24, with
+// inv_d = 1 / d rounded to float: the float estimate is within 2 of the
+// quotient, and two correction steps each way make the result exact. Replaces
+// the long integer-division sequence in per-row position arithmetic.
+__device__ __forceinline__ int div_small(int n, int d, float inv_d, int* rem) {
+  int q = (int)((float)n * inv_d);
+  int r = n - q * d;
+  if (r < 0) { --q; r += d; }
+  if (r < 0) { --q; r += d; }
+  if (r >= d) { ++q; r -= d; }
+  if (r >= d) { ++q; r -= d; }
+  *rem = r;
+  return q;
+}
+
+// sin and cos of the angle pos * rev revolutions. The fractional part of the
+// revolution count is taken first (exact for an integer pos times a float rate
+// up to rounding of the product: |error| <= |pos * rev| * 2^-24 revolutions),
+// then v_sin_f32 / v_cos_f32, which take their input in revolutions.
+__device__ __forceinline__ void sincos_rev(int pos, float rev, float* s, float* c) {
+  float r = (float)pos * rev;
+  r -= floorf(r);
+  *s = __builtin_amdgcn_sinf(r);
+  *c = __builtin_amdgcn_cosf(r);
+}
+
 __device__ __forceinline__ float max_across_halves(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

@@ -17,9 +17,10 @@ constexpr int kDHead = kDNope + kDRope;   // 128
 constexpr int kRow = kDC + kDRope;        // 224 cached scalars per token
 constexpr int kPairs = kDRope / 2;        // 16 complex RoPE pairs
 
-// Angular rate and axis (0 = t, 1 = h, 2 = w) of each RoPE pair.
+// Rate of each RoPE pair in revolutions per position step (omega / 2 pi) and
+// its axis (0 = t, 1 = h, 2 = w).
 struct RopeTable {
-  float omega[kPairs];
+  float rev[kPairs];
   int axis[kPairs];
 };
 
@@ -30,6 +31,7 @@ struct AppendArgs {
   void* cache;          // [batch, window_frames * T, kRow]
   int batch, n_tok, d_model;
   int grid_w, tokens_per_frame, window_frames, t_first;
+  float inv_grid_w, inv_tokens_per_frame, inv_window_frames;   // 1/x as float
   RopeTable rope;
 };
 
@@ -40,6 +42,7 @@ struct QArgs {
   uint16_t* qhat;       // [batch, n_heads, n_q, kRow] bf16 (workspace)
   int batch, n_q, d_model, n_heads;
   int grid_w, tokens_per_frame, t_first;
+  float inv_grid_w, inv_tokens_per_frame;   // 1/x as float
   float qscale;         // softmax scale * log2(e)
   RopeTable rope;
 };

@@ -11,85 +11,101 @@
 // with the token's (t, h, w) (App. D.3). Folding log2 e into the scale lets the
 // attention kernel use exp2 directly.
 //
-// One workgroup (4 waves) handles 64 tokens of one head. Wave w computes output
-// columns [32w, 32w+32) of q_h for all 64 tokens; wave 3 therefore holds the
-// rope channels. The absorption GEMM then splits its 2 x 6 output blocks
-// three per wave. The [64 x 224] result is assembled in LDS and written with
-// 16-byte row stores.
+// One workgroup (4 waves) handles 64 tokens of one head (XCD-aware order, see
+// the kernel). The d_model
+// contraction runs as a pipeline of 64-deep stages (kStages buffers, fetched
+// by LDS-DMA kStages-1 stages ahead, one barrier per stage). Wave w computes
+// output columns [32w, 32w+32) of q_h for all 64 tokens; wave 3 therefore holds
+// the rope channels. The absorption GEMM then splits its 2 x 6 output blocks
+// three per wave, and the [64 x 224] result is assembled in LDS and written
+// with 16-byte row stores.
 #include "device_common.h"
 #include "kernels.h"
+#include "staging.h"
 
 namespace vmla {
 namespace {
 
 constexpr int kTok = 64;
-constexpr int kKc = 64;
-constexpr int kThreads = 256;
-constexpr int kXLd = kKc + 8;          // x slice row (elements)
-constexpr int kWLd = kDHead + 8;       // W_Q slice row
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStages = 3;
+constexpr int kAElems = kTok * kStageK;                 // 4096
+constexpr int kBElems = kStageK * kDHead;               // 8192
+constexpr int kStageElems = kAElems + kBElems;
+constexpr int kALoads = kAElems * 2 / 1024;             // 8
+constexpr int kBLoads = kBElems * 2 / 1024;             // 16
+constexpr int kLoadsPerWave = (kALoads + kBLoads) / kWaves;   // 6
 constexpr int kQnLd = kDNope + 8;      // q_nope staging row
 constexpr int kOutLd = kRow + 8;       // output tile row
-constexpr int kLoopElems = kTok * kXLd + kKc * kWLd;
 constexpr int kEpiElems = kTok * kQnLd + kTok * kOutLd;
-constexpr int kSmemElems = kLoopElems > kEpiElems ? kLoopElems : kEpiElems;
+constexpr int kSmemElems = kStages * kStageElems > kEpiElems ? kStages * kStageElems : kEpiElems;
+static_assert((kALoads + kBLoads) % kWaves == 0, "stage loads must split evenly");
 
 template <typename T>
 __global__ __launch_bounds__(kThreads)
 void qprologue_kernel(QArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t smem[kSmemElems];
-  bf16_t* xs = smem;                       // [kTok][kXLd]
-  bf16_t* ws = smem + kTok * kXLd;         // [kKc][kWLd]
   bf16_t* qn = smem;                       // [kTok][kQnLd]   (after the K loop)
   bf16_t* ot = smem + kTok * kQnLd;        // [kTok][kOutLd]
 
+  // Workgroups are dispatched round-robin over the 8 XCDs; id = 8 (H q + h) + x8
+  // keeps all heads of token block 8 q + x8 on XCD x8, so that block's x rows
+  // are fetched into that XCD's L2 once and shared by its heads.
+  const int ntb = (a.n_q + kTok - 1) / kTok;
+  const int x8 = blockIdx.x & 7;
+  const int rest = blockIdx.x >> 3;
+  const int h = rest % a.n_heads;
+  const int tb = 8 * (rest / a.n_heads) + x8;
+  if (tb >= ntb) return;                   // whole workgroup: no barrier is skipped
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int half = lane >> 5;
-  const int h = blockIdx.y;
   const int b = blockIdx.z;
-  const int tok0 = blockIdx.x * kTok;
+  const int tok0 = tb * kTok;
   const int wq_ld = a.n_heads * kDHead;
   const T* x = static_cast<const T*>(a.x) + (size_t)b * a.n_q * a.d_model;
   const T* wq = static_cast<const T*>(a.w_q) + (size_t)h * kDHead;
+  const int nst = a.d_model / kStageK;
+
+  auto issue = [&](int s) {
+    bf16_t* st = smem + (s % kStages) * kStageElems;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+      const int n = wave + kWaves * i;
+      if (n < kALoads) stage_a_load<T>(st, x, a.d_model, tok0, a.n_q, s * kStageK, n, lane);
+      else stage_b_load<T, kDHead>(st + kAElems, wq, wq_ld, 0, s * kStageK, n - kALoads, lane);
+    }
+  };
+
+  for (int s = 0; s < kStages - 1 && s < nst; ++s) issue(s);
 
   f32x16 acc[2] = {f32x16{}, f32x16{}};
-  for (int k0 = 0; k0 < a.d_model; k0 += kKc) {
-#pragma unroll
-    for (int i = 0; i < kTok * kKc / 8 / kThreads; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c >> 3, kc = c & 7;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (tok0 + row < a.n_q) v = load8_bf16<T>(x + (size_t)(tok0 + row) * a.d_model + k0 + 8 * kc);
-      *reinterpret_cast<uint4*>(&xs[row * kXLd + 8 * kc]) = v;
-    }
-#pragma unroll
-    for (int i = 0; i < kKc * kDHead / 8 / kThreads; ++i) {
-      const int c = tid + i * kThreads;
-      const int kr = c >> 4, cc = c & 15;
-      *reinterpret_cast<uint4*>(&ws[kr * kWLd + 8 * cc]) =
-          load8_bf16<T>(wq + (size_t)(k0 + kr) * wq_ld + 8 * cc);
-    }
+  for (int s = 0; s < nst; ++s) {
+    wait_stages<kLoadsPerWave>(min(kStages - 2, nst - 1 - s));   // stage s has landed
     __syncthreads();
+    if (s + kStages - 1 < nst) issue(s + kStages - 1);            // into the buffer of stage s-1
+    const bf16_t* A = smem + (s % kStages) * kStageElems;
+    const bf16_t* B = A + kAElems;
 #pragma unroll
-    for (int ks = 0; ks < kKc / 16; ++ks) {
-      const int ka = ks * 16 + 8 * half;
-      const bf16x8 bv = lds_tr8(ws, kWLd, ka, ka + 4, 32 * wave, lane);
+    for (int ks = 0; ks < kStageK / 16; ++ks) {
+      const bf16x8 bv = b_frag<kDHead>(B, ks, 32 * wave, lane);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const bf16x8 av = lds_row8(&xs[(32 * tt + (lane & 31)) * kXLd + ka]);
+        const bf16x8 av = a_frag(A, 32 * tt + (lane & 31), ks, half);
         acc[tt] = mfma32(av, bv, acc[tt]);
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   // Register r of lane l: token row 32*tt + 8(r/4) + 4*half + r%4, column 32*wave + l%32.
   const int col = lane & 31;
   if (wave == 3) {
     const int pair = col >> 1;
     const bool odd = col & 1;
-    const float omega = a.rope.omega[pair];
+    const float rev = a.rope.rev[pair];
     const int axis = a.rope.axis[pair];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -99,12 +115,12 @@ void qprologue_kernel(QArgs a) {
         const float v = acc[tt][r];
         const float partner = swap_adjacent(v);
         const int n = min(tok0 + row, a.n_q - 1);
-        const int f = n / a.tokens_per_frame;
-        const int n_in = n - f * a.tokens_per_frame;
-        const int hh = n_in / a.grid_w;
-        const int pos = axis == 0 ? a.t_first + f : (axis == 1 ? hh : n_in - hh * a.grid_w);
+        int n_in, ww;
+        const int f = div_small(n, a.tokens_per_frame, a.inv_tokens_per_frame, &n_in);
+        const int hh = div_small(n_in, a.grid_w, a.inv_grid_w, &ww);
+        const int pos = axis == 0 ? a.t_first + f : (axis == 1 ? hh : ww);
         float sn, cs;
-        sincosf((float)pos * omega, &sn, &cs);
+        sincos_rev(pos, rev, &sn, &cs);
         const float rot = odd ? partner * sn + v * cs : v * cs - partner * sn;
         ot[row * kOutLd + kDC + col] = f2bf(rot * a.qscale);
       }
@@ -158,7 +174,8 @@ void qprologue_kernel(QArgs a) {
 }  // namespace
 
 hipError_t launch_qprologue(const QArgs& a, bool f32, hipStream_t s) {
-  dim3 grid((a.n_q + kTok - 1) / kTok, a.n_heads, a.batch);
+  const int ntb = (a.n_q + kTok - 1) / kTok;
+  dim3 grid(8 * a.n_heads * ((ntb + 7) / 8), 1, a.batch);
   if (f32) hipLaunchKernelGGL(qprologue_kernel<float>, grid, dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL(qprologue_kernel<bf16_t>, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();

@@ -13,6 +13,10 @@ using namespace vmla;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Largest t_first + n_frames accepted: keeps every position below 2^24 for the
+// exact float-reciprocal division and the RoPE angle error below 1e-4 rev.
+constexpr int64_t kMaxFrameIndex = 1 << 20;
+
 int32_t check_dims(const vmla_dims* d) {
   if (!d) return VMLA_ERR_NULL;
   if (d->d_nope != kDNope || d->d_rope != kDRope || d->d_c != kDC || d->d_v != kDV) return VMLA_ERR_SHAPE;
@@ -39,17 +43,20 @@ int32_t check_cache(const vmla_cache* c, int32_t dtype) {
   const int64_t t = (int64_t)c->grid_h * c->grid_w;
   const int64_t rows = t * c->window_frames;
   // every element offset handled by the kernels must fit in int32 per batch element
-  if (rows * kRow > INT32_MAX || t > INT32_MAX / 64) return VMLA_ERR_SHAPE;
+  if (rows * kRow > INT32_MAX || rows >= (1 << 24)) return VMLA_ERR_SHAPE;
   return VMLA_OK;
 }
 
-// omega_i = theta^(-2 i / D_a) for the pairs of each axis group, in double.
+// omega_i = theta^(-2 i / D_a) for the pairs of each axis group, computed in
+// double and passed as revolutions per position step (omega_i / 2 pi).
 RopeTable rope_table(const vmla_dims* d) {
   RopeTable r{};
+  const double two_pi = 6.283185307179586476925286766559;
   int j = 0;
   for (int ax = 0; ax < 3; ++ax) {
     for (int i = 0; i < d->rope_pairs[ax]; ++i, ++j) {
-      r.omega[j] = (float)std::pow((double)d->rope_theta, -2.0 * i / (double)d->rope_axis_dims[ax]);
+      const double omega = std::pow((double)d->rope_theta, -2.0 * i / (double)d->rope_axis_dims[ax]);
+      r.rev[j] = (float)(omega / two_pi);
       r.axis[j] = ax;
     }
   }
@@ -102,7 +109,7 @@ int32_t vmla_cache_append(const vmla_dims* dims, const vmla_cache* cache, int32_
   if (st) return st;
   if (!aligned16(x) || !aligned16(w_down) || !aligned16(w_kr)) return VMLA_ERR_ALIGN;
   if (t_first < 0 || n_frames < 1 || n_frames > cache->window_frames) return VMLA_ERR_RANGE;
-  if ((int64_t)t_first + n_frames > (int64_t)INT32_MAX / 2) return VMLA_ERR_RANGE;
+  if ((int64_t)t_first + n_frames > kMaxFrameIndex) return VMLA_ERR_RANGE;
   const int64_t T = (int64_t)cache->grid_h * cache->grid_w;
   const int64_t n_tok = T * n_frames;
   if (n_tok * dims->d_model > INT32_MAX) return VMLA_ERR_SHAPE;
@@ -112,6 +119,9 @@ int32_t vmla_cache_append(const vmla_dims* dims, const vmla_cache* cache, int32_
   a.batch = cache->batch; a.n_tok = (int)n_tok; a.d_model = dims->d_model;
   a.grid_w = cache->grid_w; a.tokens_per_frame = (int)T;
   a.window_frames = cache->window_frames; a.t_first = t_first;
+  a.inv_grid_w = 1.f / (float)cache->grid_w;
+  a.inv_tokens_per_frame = 1.f / (float)T;
+  a.inv_window_frames = 1.f / (float)cache->window_frames;
   a.rope = rope_table(dims);
   return hip_status(launch_append(a, dtype == VMLA_F32, static_cast<hipStream_t>(stream)));
 }
@@ -132,7 +142,7 @@ int32_t check_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t 
   st = check_cache(cache, dtype);
   if (st) return st;
   if (t_first < 0 || n_frames < 1 || n_frames > cache->window_frames) return VMLA_ERR_RANGE;
-  if ((int64_t)t_first + n_frames > (int64_t)INT32_MAX / 2) return VMLA_ERR_RANGE;
+  if ((int64_t)t_first + n_frames > kMaxFrameIndex) return VMLA_ERR_RANGE;
   const int64_t t_end = (int64_t)t_first + n_frames;
   const int64_t expect_valid = t_end < cache->window_frames ? t_end : cache->window_frames;
   if (n_valid_frames != expect_valid) return VMLA_ERR_RANGE;
@@ -147,6 +157,8 @@ int32_t check_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t 
   q->qhat = static_cast<uint16_t*>(const_cast<void*>(workspace));
   q->batch = cache->batch; q->n_q = (int)n_q; q->d_model = dims->d_model; q->n_heads = dims->n_heads;
   q->grid_w = cache->grid_w; q->tokens_per_frame = (int)T; q->t_first = t_first;
+  q->inv_grid_w = 1.f / (float)cache->grid_w;
+  q->inv_tokens_per_frame = 1.f / (float)T;
   q->qscale = (float)((double)dims->scale * 1.4426950408889634);   // scale * log2(e)
   q->rope = rope_table(dims);
 
