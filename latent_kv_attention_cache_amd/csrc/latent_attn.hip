@@ -27,10 +27,9 @@
 // steps ahead of the MFMAs (scheduling groups below).
 //
 // Tile buffers. Tile t is read in phases 2t .. 2t+3 (X scores, Y scores, X and Y
-// P.C). The X waves fetch tile t+2 at the end of their matrix phase 2t, after
-// their own LDS reads, into the buffer of tile t-2 (four buffers), and wait for
-// it at the start of their next matrix phase, two barriers before its first
-// reader.
+// P.C). The X waves fetch tile t+2 during their vector phase 2t+1 into the
+// buffer of tile t-2 (four buffers) and make sure it has landed before the
+// barrier that precedes its first reader (phase 2t+4).
 //
 // LDS tile layout: key row r occupies 448 contiguous bytes (28 chunks of 16 B);
 // chunk c of row r sits at chunk position c ^ swz(r), swz(r) = ((r>>1)^(r>>2)) & 3.
@@ -260,20 +259,28 @@ void latent_attn_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // Phases p = 0 .. 2 ntiles + 1; wave-local phase q = p - lag.
+  // Phases p = 0 .. 2 ntiles + 1; wave-local phase q = p - lag. In its vector
+  // phase for tile jt (phase 2 jt + 1) an X wave first waits for all of its
+  // loads, i.e. its part of tile jt + 1 (requested in phase 2 jt - 1), so that
+  // the barrier closing this phase publishes tile jt + 1 to its first readers
+  // (phase 2 jt + 2); it then requests tile jt + 2 into the buffer of tile
+  // jt - 2, whose last readers ran in phase 2 jt - 1. The requests stay off the
+  // matrix phases.
   const int nphases = 2 * ntiles + 2;
   for (int p = 0; p < nphases; ++p) {
     const int q = p - lag;
     if (q >= 0) {
       const int jt = q >> 1;
       if ((q & 1) == 0) {          // matrix phase for tile jt
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile jt+1 (fetched two phases ago)
         __builtin_amdgcn_s_setprio(1);
         if (jt >= 1) accumulate(kt + ((jt - 1) % kBufs) * kTileElems);
         if (jt < ntiles) scores(kt + (jt % kBufs) * kTileElems);
         __builtin_amdgcn_s_setprio(0);
-        if (!lag && jt + 2 < ntiles) issue_tile(jt + 2);
       } else if (jt < ntiles) {    // vector phase for tile jt
+        if (!lag) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          if (jt + 2 < ntiles) issue_tile(jt + 2);
+        }
         softmax(jt * kKT);
       }
     }
