@@ -31,10 +31,13 @@
 // buffer of tile t-2 (four buffers) and make sure it has landed before the
 // barrier that precedes its first reader (phase 2t+4).
 //
-// LDS tile layout: key row r occupies 448 contiguous bytes (28 chunks of 16 B);
-// chunk c of row r sits at chunk position c ^ swz(r), swz(r) = ((r>>1)^(r>>2)) & 3.
-// The swizzle spreads the row-wise 16-byte reads of 32 consecutive keys over
-// all banks; the transpose reads of 8 rows x 64 B are conflict-free unswizzled.
+// LDS tile layout, chunk-major: the 16-byte chunk c (features 8c .. 8c+7) of
+// key row r sits at slot c * 68 + r. One wave-wide LDS-DMA load moves chunk c of
+// all 64 rows (lane = row), so a lane's source address is its row plus a
+// scalar column offset. A score operand read (chunk c of 32 consecutive rows)
+// is contiguous; the 4-slot pad per chunk column places chunk c+1 of a row 16
+// banks after chunk c, so the transpose reads of 4 rows x 2 chunks that a
+// 16-lane group issues cover distinct banks.
 //
 // MFMA formulation (keys on MFMA rows): S^T[key][q] = K[key][:] . Qhat[q][:];
 // per query (= per lane) max and sum over the lane's own keys, the other half
@@ -56,9 +59,10 @@ constexpr int kKT = 64;                     // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlockQ = 32 * kWaves;        // query tokens per workgroup
-constexpr int kChunksPerRow = kRow / 8;     // 28
-constexpr int kTileElems = kKT * kRow;      // unpadded, swizzled
-constexpr int kTileLoads = kKT * kChunksPerRow / 64;   // wave-wide 16-byte loads per tile (28)
+constexpr int kChunks = kRow / 8;           // 16-byte chunks per key row (28)
+constexpr int kSlots = kKT + 4;             // slots per chunk column (padded)
+constexpr int kTileElems = kChunks * kSlots * 8;
+constexpr int kTileLoads = kChunks;         // wave-wide 16-byte loads per tile (one per chunk column)
 constexpr int kLoaders = kWaves / 2;        // the X waves issue the tile loads
 constexpr int kLoadsPerWave = kTileLoads / kLoaders;
 constexpr int kBufs = 4;
@@ -66,15 +70,13 @@ constexpr int kVLd = kDV + 8;               // padded LDS row of W_V_up[h] (epil
 constexpr int kFeatSteps = kRow / 16;       // 14
 constexpr int kLatTiles = kDC / 32;         // 6
 constexpr float kLazy = 8.f;                // lazy-rescale threshold (log2 units)
-static_assert(kKT * kChunksPerRow % 64 == 0, "tile must split into wave-wide loads");
+
 static_assert(kTileLoads % kLoaders == 0, "tile loads must split evenly over the loading waves");
 static_assert(kDC * kVLd <= kBufs * kTileElems, "W_V_up staging must fit in the tile buffers");
 
 // Scheduling-group masks (instruction classes of sched_group_barrier).
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
-
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
 // 16-byte LDS-DMA load: lane i's 16 bytes from base + voff (bytes; base
 // wave-uniform) land at LDS byte address lds_addr + 16 i (lds_addr
@@ -109,51 +111,52 @@ void latent_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < kFeatSteps; ++ks)
       qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + 8 * half);
+    // Re-define the fragments by an (empty) register statement: the memory
+    // wait for the loads is then placed here, once. Otherwise the compiler
+    // keeps vmcnt waits for them in front of every score MFMA of the loop,
+    // where they would also wait for the tile prefetches in flight.
+#pragma unroll
+    for (int ks = 0; ks < kFeatSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
   }
 
   const T* cache = static_cast<const T*>(a.cache) + (size_t)b * a.cache_rows * kRow;
   const int ntiles = (a.n_k + kKT - 1) / kKT;
 
-  // ---- tile staging (X waves only). Wave-wide load n fills chunk slots
-  // [64n, 64n + 64) of a tile; lane i fills slot 64n + i, which holds chunk
-  // (key, c) with slot = key * 28 + (c ^ swz(key)). Keys past the window are
-  // clamped to the last valid key (finite data; their scores are masked).
+  // ---- tile staging (X waves only). Wave-wide load n moves chunk column n:
+  // lane r reads features 8n .. 8n+7 of key 64 j + r into slot n * kSlots + r.
+  // Keys past the window are clamped to the last valid key (finite data; their
+  // scores are masked).
   const uint32_t kt_lds = (uint32_t)(uintptr_t)(VMLA_LDS bf16_t*)kt;
   auto issue_tile = [&](int j) {
     const int buf = j % kBufs;
+    const int kg = min(j * kKT + lane, a.n_k - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);   // scalar load index and LDS address
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
-      const int n = wave + kLoaders * i;
-      const int slot = 64 * n + lane;
-      const int key = slot / kChunksPerRow;
-      const int col = 8 * ((slot - key * kChunksPerRow) ^ swz(key));
-      const int kg = min(j * kKT + key, a.n_k - 1);
+      const int n = wv + kLoaders * i;
       if constexpr (std::is_same_v<T, bf16_t>) {
-        dma16(cache, (uint32_t)((kg * kRow + col) * 2),
-              kt_lds + 2u * (uint32_t)(buf * kTileElems + 512 * n));
+        dma16(cache, (uint32_t)(kg * (kRow * 2)) + (uint32_t)(16 * n),
+              kt_lds + 2u * (uint32_t)(buf * kTileElems + n * kSlots * 8));
       } else {
-        const T* src = cache + (size_t)kg * kRow + col;
-        *reinterpret_cast<uint4*>(kt + buf * kTileElems + 512 * n + 8 * lane) = load8_bf16<T>(src);
+        const T* src = cache + (size_t)kg * kRow + 8 * n;
+        *reinterpret_cast<uint4*>(kt + buf * kTileElems + (n * kSlots + lane) * 8) = load8_bf16<T>(src);
       }
     }
   };
 
-  // Per-lane LDS element offsets (relative to a tile) of the operand reads.
-  // Score A operand: row qi (+32 for the second key block), features
-  // 16 ks + 8 half, i.e. chunk 2 ks + half; with s = swz(qi) (swz(qi + 32) == s)
-  // the chunk lands at 2 (ks ^ (s >> 1)) + (half ^ (s & 1)).
-  const int s_q = swz(qi);
-  const int a_base = qi * kRow + 8 * (half ^ (s_q & 1));
-  const int a_flip = 16 * (s_q >> 1);
-  // Transpose reads of C^T: lane j of a 16-lane group reads row
-  // kbase + rb + j/4 (rb = 4*half or 8 + 4*half), elements 32 t + nsub + 4 (j%4);
-  // kbase is a multiple of 16, so the swizzle depends only on rb + j/4.
+  // Per-lane LDS element offsets (relative to a tile) of the operand reads; a
+  // key row advances by 8 elements. Score A operand: row qi (+32 for the second
+  // key block), features 16 ks + 8 half, i.e. chunk 2 ks + half.
+  const int a_base = (half * kSlots + qi) * 8;
+  // Transpose reads of C^T: lane j of a 16-lane group points at row
+  // kbase + rb + j/4 (rb = 4*half, or 8 + 4*half for the second read), elements
+  // 32 t + nsub + 4 (j%4) .. +3 with nsub = 16 ((lane / 16) % 2), i.e. chunk
+  // 4 t + x4 at element offset sub inside the chunk.
   const int jl = lane & 15;
   const int x4 = ((lane & 16) >> 3) + ((jl & 3) >> 1);   // chunk within the 4-chunk group
   const int sub = 4 * (jl & 1);
-  const int r1 = 4 * half + (jl >> 2), r2 = 8 + 4 * half + (jl >> 2);
-  const int v_off1 = r1 * kRow + 8 * (x4 ^ swz(r1)) + sub;
-  const int v_off2 = r2 * kRow + 8 * (x4 ^ swz(r2)) + sub;
+  const int v_off1 = (x4 * kSlots + 4 * half + (jl >> 2)) * 8 + sub;
+  const int v_off2 = v_off1 + 8 * 8;
 
   f32x16 o[kLatTiles];
 #pragma unroll
@@ -171,11 +174,11 @@ void latent_attn_kernel(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
-        const bf16_t* Kb = K + (kb * 32 + jj * 16) * kRow;
+        const bf16_t* Kb = K + (kb * 32 + jj * 16) * 8;
 #pragma unroll
         for (int t = 0; t < kLatTiles; ++t) {
-          const bf16x4 lo = lds_tr4(Kb + v_off1 + 32 * t);
-          const bf16x4 hi = lds_tr4(Kb + v_off2 + 32 * t);
+          const bf16x4 lo = lds_tr4(Kb + v_off1 + 4 * kSlots * 8 * t);
+          const bf16x4 hi = lds_tr4(Kb + v_off2 + 4 * kSlots * 8 * t);
           const bf16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           o[t] = mfma32(av, pb[kb][jj], o[t]);
         }
@@ -195,9 +198,9 @@ void latent_attn_kernel(AttnArgs a) {
     s1 = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kFeatSteps; ++ks) {
-      const int off = a_base + ((16 * ks) ^ a_flip);
+      const int off = a_base + 2 * kSlots * 8 * ks;
       const bf16x8 a0 = lds_row8(K + off);
-      const bf16x8 a1 = lds_row8(K + off + 32 * kRow);
+      const bf16x8 a1 = lds_row8(K + off + 32 * 8);
       s0 = mfma32(a0, qf[ks], s0);
       s1 = mfma32(a1, qf[ks], s1);
     }
@@ -212,11 +215,13 @@ void latent_attn_kernel(AttnArgs a) {
   // Online softmax of the current tile; leaves P^T (bf16) in pb.
   auto softmax = [&](int key0) {
     if (key0 + kKT > a.n_k) {    // the window ends inside this tile (wave-uniform)
+      // register r of key block kb holds key key0 + 32 kb + 8(r/4) + 4 half + r%4
+      const int lim = a.n_k - key0 - 4 * half;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (key >= a.n_k) s0[r] = -INFINITY;
-        if (key + 32 >= a.n_k) s1[r] = -INFINITY;
+        const int k = 8 * (r >> 2) + (r & 3);
+        if (k >= lim) s0[r] = -INFINITY;
+        if (k + 32 >= lim) s1[r] = -INFINITY;
       }
     }
     float mx = fmaxf(s0[0], s1[0]);
