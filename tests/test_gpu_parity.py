@@ -115,3 +115,90 @@ def test_config2_full_shape_sampled_rows():
                                     rng.choice(w.n_q, 43, replace=False)]))
     compare(out[0, idx], r.reference(query_tokens=idx), "config 2 sampled rows", per_head_axis=1)
     compare(r.cache_rows(18, 3), r.append_reference(18, 3), "config 2 chunk cache rows")
+
+
+def _device_noise(w, seed):
+    """Bulk inputs whose values are never checked (other batch elements, frames
+    that leave the window before any check): device N(0,1), seeded."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    T, D = w.tokens_per_frame, w.d_model
+    return lambda: torch.randn((T, D), generator=g, device="cuda").to(torch.bfloat16)
+
+
+def _sample_rows(n_q, k, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 255, 256, n_q - 1], rng.choice(n_q, k, replace=False)]))
+
+
+def test_config3_layers_and_batches_sampled():
+    # B=8 at the Wan-1.3B shape; layers {0, 29} x batch elements {0, 7} x 512 rows
+    # checked. Batch elements are independent, so the others run on device noise.
+    w = config(3)
+    checked = (0, 7)
+    for layer in (0, 29):
+        noise = _device_noise(w, 1000 + layer)
+        r = Run(w, layer=layer)
+        r.batch_x = lambda t, b, r=r: (torch.from_numpy(r.x_host(t, b)).cuda().to(torch.bfloat16)
+                                       if b in checked else noise())
+        out = _sync_np(r.chunk_step())
+        for b in checked:
+            idx = _sample_rows(w.n_q, 508, seed=10 * layer + b)
+            compare(out[b, idx], r.reference(b=b, query_tokens=idx),
+                    f"config 3 layer {layer} b={b}", per_head_axis=1)
+            compare(r.cache_rows(18, 3, b=b), r.append_reference(18, 3, b=b),
+                    f"config 3 layer {layer} b={b} cache rows")
+
+
+def test_config4_batch16_single_frame_sampled():
+    # B=16, one 1560-token frame against the full 21-frame window
+    w = config(4)
+    checked = (0, 9, 15)
+    noise = _device_noise(w, 4000)
+    r = Run(w)
+    r.batch_x = lambda t, b: (torch.from_numpy(r.x_host(t, b)).cuda().to(torch.bfloat16)
+                              if b in checked else noise())
+    out = _sync_np(r.chunk_step())
+    for b in checked:
+        idx = _sample_rows(w.n_q, 252, seed=40 + b)
+        compare(out[b, idx], r.reference(b=b, query_tokens=idx), f"config 4 b={b}", per_head_axis=1)
+    compare(r.cache_rows(20, 1, b=15), r.append_reference(20, 1, b=15), "config 4 cache rows")
+
+
+def test_config5_reduced_rollout():
+    # The rollout at B=1, one layer: 80 chunks of 3 frames, 4 denoising steps
+    # each (every step re-appends the chunk), window of 21 frames, t up to 239.
+    # Checked at chunks 0 (pre-fill), 5, 6 (first full window), 7 (first wrap),
+    # 13 and 79 (t = 237..239), at the first and last denoising step. Frames
+    # that are inside a checked window carry seeded host inputs; the others
+    # leave the window before any check and run on device noise.
+    w = config(5).with_(batch=1, n_layers=1)
+    cw = w.window_frames // w.chunk_frames          # chunks per window
+    last = w.n_steps - 1
+    checked = (0, 5, 6, 7, 13, w.n_chunks - 1)
+    seeded = {c for k in checked for c in range(max(0, k - cw + 1), k + 1)}
+    state = {"chunk": 0, "step": 0}
+
+    def step_of_frame(t):
+        return state["step"] if t // w.chunk_frames == state["chunk"] else last
+
+    noise = _device_noise(w, 5000)
+    r = Run(w, step_of_frame=step_of_frame)
+
+    def x_of(t, b):
+        c = t // w.chunk_frames
+        host = c in seeded and (step_of_frame(t) == last or c in checked)
+        return torch.from_numpy(r.x_host(t, b)).cuda().to(torch.bfloat16) if host else noise()
+
+    r.batch_x = x_of
+    idx = _sample_rows(w.n_q, 60, seed=5)
+    for c in range(w.n_chunks):
+        state["chunk"] = c
+        t_first = c * w.chunk_frames
+        for s in range(w.n_steps):
+            state["step"] = s
+            r.append(t_first, w.chunk_frames)
+            out = r.attention(t_first, w.chunk_frames)
+            if c in checked and s in (0, last):
+                ref = r.reference(query_tokens=idx, t_first=t_first, n_frames=w.chunk_frames)
+                compare(_sync_np(out)[0, idx], ref, f"rollout chunk {c} step {s}", per_head_axis=1)
