@@ -10,7 +10,13 @@ d_c = 192, d_rope = 32, bf16 storage, fp32 accumulation):
 All inputs are seeded synthetic tensors already resident in HBM when the timed
 region starts. Prints one JSON line on stdout.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+`--config 3` and `--config 4` time the batch-8 (30 layers, one buffer set per
+layer) and batch-16 single-frame workloads instead; their buffers rotate so the
+append and the query prologue read HBM, not the 256 MB Infinity Cache, and
+their bulk inputs are device-generated N(0,1) tensors (values do not change the
+work).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--config 2|3|4]
 """
 from __future__ import annotations
 
@@ -83,6 +89,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed steps first; the shader clock needs tens of ms of load to settle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4),
+                    help="2: Wan-1.3B chunk-layer at B=1 (the reported workload); 3: B=8, 30 "
+                         "layers; 4: B=16, one-frame chunk")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device-to-device copy of MIB MiB, whose counter "
                          "readings calibrate FETCH_SIZE / WRITE_SIZE")
@@ -113,20 +122,40 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy: {nbytes} bytes read and {nbytes} bytes written")
         del src, dst
-    w = config(2)
-    wts = weights(w)
+    w = config(args.config)
     log(f"[bench] workload: {w.name}")
-    xs = {t: x_frame(w, t) for t in range(w.window_frames)}
-    dw = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in wts.items()}
     dims = vm.default_dims()
+    xs = None
+    if args.config == 2:
+        # seeded host inputs, the same as the parity tests use
+        wts = weights(w)
+        xs = {t: x_frame(w, t) for t in range(w.window_frames)}
+        dw = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in wts.items()}
 
-    def xdev(frames):
-        return torch.from_numpy(np.concatenate([xs[t] for t in frames]))[None].to(dev).to(torch.bfloat16)
+        def xdev(frames):
+            return torch.from_numpy(np.concatenate([xs[t] for t in frames]))[None].to(dev).to(torch.bfloat16)
 
-    cache = vm.LatentCache.empty(w.batch, w.window_frames, w.grid_h, w.grid_w, device=dev)
-    vm.vmla_cache_append(cache, xdev(range(0, 18)), dw["w_down"], dw["w_kr"], 0, 18)
-    chunk = list(w.chunk_frame_ids)
-    x = xdev(chunk).contiguous()
+        cache = vm.LatentCache.empty(w.batch, w.window_frames, w.grid_h, w.grid_w, device=dev)
+        vm.vmla_cache_append(cache, xdev(range(0, w.t_first)), dw["w_down"], dw["w_kr"], 0, w.t_first)
+        sets = [(xdev(list(w.chunk_frame_ids)).contiguous(), dw, cache)]
+    else:
+        # one buffer set per layer (config 3) or eight rotating sets (config 4)
+        n_sets = w.n_layers if w.n_layers > 1 else 8
+        g = torch.Generator(device=dev)
+        g.manual_seed(w.cfg_id)
+        shapes = {"w_q": (w.d_model, w.n_heads * w.d_head), "w_down": (w.d_model, w.d_c),
+                  "w_kr": (w.d_model, w.d_rope), "w_k_up": (w.n_heads, w.d_c, w.d_nope),
+                  "w_v_up": (w.n_heads, w.d_c, w.d_v)}
+        sets = []
+        for _ in range(n_sets):
+            dw = {k: (torch.randn(shp, generator=g, device=dev) * shp[-2] ** -0.5).to(torch.bfloat16)
+                  for k, shp in shapes.items()}
+            cache = vm.LatentCache.empty(w.batch, w.window_frames, w.grid_h, w.grid_w, device=dev)
+            cache.data.normal_(generator=g)
+            x = torch.randn((w.batch, w.n_q, w.d_model), generator=g, device=dev).to(torch.bfloat16)
+            sets.append((x, dw, cache))
+        log(f"[bench] {n_sets} buffer sets of "
+            f"{(sets[0][0].numel() + sets[0][2].data.numel()) * 2 / 1e6:.0f} MB")
     n_valid = w.n_valid_frames
     ws = torch.empty(vm.vmla_attention_workspace_bytes(w.batch, w.n_q, dims), dtype=torch.uint8,
                      device=dev)
@@ -135,7 +164,8 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step(ev=None, i=0):
+        x, dw, cache = sets[i % len(sets)]
         if ev is not None:
             ev[0].record(stream)
         vm.vmla_cache_append(cache, x, dw["w_down"], dw["w_kr"], w.t_first, w.chunk_frames, dims=dims)
@@ -150,15 +180,15 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i=i)
     torch.cuda.synchronize()
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step(events[i], i=i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -176,7 +206,7 @@ def main():
     append_gbs = wk["bytes_append"] / (k_ms["append"] * 1e-3) / 1e9
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "latent_attn_config2_traffic.json")
-    if os.path.exists(tfile):
+    if args.config == 2 and os.path.exists(tfile):
         with open(tfile) as f:
             tr = json.load(f)
         if tr.get("kernel_source_sha") == _kernel_sha():
@@ -196,8 +226,12 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "Wan-1.3B-shaped chunk-layer: B=1, 30x52 grid, 3-frame query chunk over a "
-                        "21-frame latent window",
+            "workload": {2: "Wan-1.3B-shaped chunk-layer: B=1, 30x52 grid, 3-frame query chunk over "
+                            "a 21-frame latent window",
+                         3: "Wan-1.3B-shaped chunk-layer at B=8, 30 layers with their own weights, "
+                            "inputs and caches, one layer per step",
+                         4: "single-frame chunk at B=16: 1560 query tokens per element over a "
+                            "21-frame latent window"}[args.config],
             "batch": w.batch, "n_q": w.n_q, "n_k": w.n_k, "n_heads": w.n_heads, "d_model": w.d_model,
             "d_c": w.d_c, "d_rope": w.d_rope, "d_nope": w.d_nope, "d_v": w.d_v,
             "flops_per_step": wk["step"],
@@ -219,7 +253,7 @@ def main():
         },
     }
     log(f"[bench] ms/step {ms_step:.4f}  kernels {k_ms}  attention {attn_tflops:.1f} TFLOP/s")
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.config == 2:
         xh = lambda t: xs[t]  # noqa: E731
         result["cpu_baseline"] = cpu_baseline(w, wts, xh, wk["step"])
     print(json.dumps(result), flush=True)

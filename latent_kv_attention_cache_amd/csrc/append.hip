@@ -8,11 +8,20 @@
 // (App. D.3); the cache is a fixed-size window of latent frames with FIFO
 // eviction (App. D.4).
 //
-// One workgroup (7 waves) computes a 64-token x 224-column tile; wave w owns
-// the 32-column block w (blocks 0-5: c from W_down, block 6: k_R from W_KR)
-// for all 64 tokens. The d_model contraction runs as a pipeline of 64-deep
-// stages (kStages buffers fetched by LDS-DMA kStages-1 stages ahead, one
-// barrier per stage); x, W_down and W_KR slices sit in separate LDS regions.
+// A skinny GEMM (N = 224, K = d_model) over all tokens of the chunk. One
+// workgroup (7 waves) computes a TM-token x 224-column tile; wave w owns the
+// 32-column block w (blocks 0-5: c from W_down, block 6: k_R from W_KR) for all
+// TM tokens. The d_model contraction runs as a pipeline of 64-deep stages
+// (kStages buffers fetched by LDS-DMA kStages-1 stages ahead, one barrier per
+// stage); x, W_down and W_KR slices sit in separate LDS regions. All 7 waves
+// issue a share of each stage's loads: the issue rate of LDS-DMA loads grows
+// with the number of issuing waves.
+//
+// Tile height. Every workgroup streams all of W_down / W_KR (688 KB at
+// d_model = 1536) from L2 next to its TM x d_model slice of x from HBM, so a
+// tall tile amortises the weight stream, while a short tile spreads a small
+// chunk over more compute units. The launcher picks TM in {32, ..., 160} from
+// the token count (one workgroup per compute unit at a time, see below).
 #include "device_common.h"
 #include "kernels.h"
 #include "staging.h"
@@ -20,70 +29,83 @@
 namespace vmla {
 namespace {
 
-constexpr int kTok = 64;               // tokens per workgroup
 constexpr int kWaves = kRow / 32;      // 7: one per 32-column block
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStages = 4;
-constexpr int kAElems = kTok * kStageK;          // x slice        (8 KB)
 constexpr int kB1Elems = kStageK * kDC;          // W_down slice   (24 KB)
 constexpr int kB2Elems = kStageK * kDRope;       // W_KR slice     (4 KB)
-constexpr int kStageElems = kAElems + kB1Elems + kB2Elems;
-constexpr int kALoads = kAElems * 2 / 1024;      // 8
 constexpr int kB1Loads = kB1Elems * 2 / 1024;    // 24
 constexpr int kB2Loads = kB2Elems * 2 / 1024;    // 4
-constexpr int kLoads = kALoads + kB1Loads + kB2Loads;   // 36
-// wave w issues loads w, w + 7, ...: wave 0 issues 6 per stage, waves 1-6 issue 5
-constexpr int kLoadsWave0 = (kLoads + kWaves - 1) / kWaves;
-constexpr int kLoadsOther = kLoads / kWaves;
-static_assert(kLoads % kWaves == 1, "load split assumed: wave 0 takes one extra load");
 
-template <typename T>
+template <int TM>
+struct Tile {
+  static constexpr int kTB = TM / 32;                        // 32-token blocks per wave
+  static constexpr int kAElems = TM * kStageK;               // x slice
+  static constexpr int kALoads = kAElems * 2 / 1024;         // TM / 8
+  static constexpr int kStageElems = kAElems + kB1Elems + kB2Elems;
+  static constexpr int kStages = TM >= 96 ? 3 : 4;           // <= 144 KB of LDS
+  static constexpr int kLoads = kALoads + kB1Loads + kB2Loads;
+  // wave w issues loads w, w + 7, ...: the first kLoads % 7 waves issue one more
+  static constexpr int kLoadsHi = (kLoads + kWaves - 1) / kWaves;
+  static constexpr int kLoadsLo = kLoads / kWaves;
+  static constexpr int kHiWaves = kLoads % kWaves;
+  static_assert(TM % 32 == 0 && TM >= 32 && TM <= 160, "tile height");
+  static_assert(kStages * kStageElems * 2 <= 160 * 1024, "LDS budget");
+};
+
+template <typename T, int TM>
 __global__ __launch_bounds__(kThreads)
 void append_kernel(AppendArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t smem[kStages * kStageElems];
+  using Tl = Tile<TM>;
+  __shared__ __attribute__((aligned(16))) bf16_t smem[Tl::kStages * Tl::kStageElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int half = lane >> 5;
   const int b = blockIdx.y;
-  const int tok0 = blockIdx.x * kTok;
+  const int tok0 = blockIdx.x * TM;
   const T* x = static_cast<const T*>(a.x) + (size_t)b * a.n_tok * a.d_model;
   const T* wd = static_cast<const T*>(a.w_down);
   const T* wr = static_cast<const T*>(a.w_kr);
   const int nst = a.d_model / kStageK;
 
   auto issue = [&](int s) {
-    bf16_t* st = smem + (s % kStages) * kStageElems;
-    for (int n = wave; n < kLoads; n += kWaves) {
-      if (n < kALoads) stage_a_load<T>(st, x, a.d_model, tok0, a.n_tok, s * kStageK, n, lane);
-      else if (n < kALoads + kB1Loads)
-        stage_b_load<T, kDC>(st + kAElems, wd, kDC, 0, s * kStageK, n - kALoads, lane);
+    bf16_t* st = smem + (s % Tl::kStages) * Tl::kStageElems;
+    for (int n = wave; n < Tl::kLoads; n += kWaves) {
+      if (n < Tl::kALoads) stage_a_load<T>(st, x, a.d_model, tok0, a.n_tok, s * kStageK, n, lane);
+      else if (n < Tl::kALoads + kB1Loads)
+        stage_b_load<T, kDC>(st + Tl::kAElems, wd, kDC, 0, s * kStageK, n - Tl::kALoads, lane);
       else
-        stage_b_load<T, kDRope>(st + kAElems + kB1Elems, wr, kDRope, 0, s * kStageK,
-                                n - kALoads - kB1Loads, lane);
+        stage_b_load<T, kDRope>(st + Tl::kAElems + kB1Elems, wr, kDRope, 0, s * kStageK,
+                                n - Tl::kALoads - kB1Loads, lane);
     }
   };
-  auto wait = [&](int stages) {
-    if (wave == 0) wait_stages<kLoadsWave0>(stages);
-    else wait_stages<kLoadsOther>(stages);
+  auto wait = [&](int stages) {      // own loads of all but the newest `stages` stages landed
+    if constexpr (Tl::kHiWaves == 0) {
+      wait_stages<Tl::kLoadsLo>(stages);
+    } else {
+      if (wave < Tl::kHiWaves) wait_stages<Tl::kLoadsHi>(stages);
+      else wait_stages<Tl::kLoadsLo>(stages);
+    }
   };
 
-  for (int s = 0; s < kStages - 1 && s < nst; ++s) issue(s);
+  for (int s = 0; s < Tl::kStages - 1 && s < nst; ++s) issue(s);
 
-  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  f32x16 acc[Tl::kTB];
+#pragma unroll
+  for (int tt = 0; tt < Tl::kTB; ++tt) acc[tt] = f32x16{};
   for (int s = 0; s < nst; ++s) {
-    wait(min(kStages - 2, nst - 1 - s));                  // stage s has landed
+    wait(min(Tl::kStages - 2, nst - 1 - s));                   // stage s has landed
     __syncthreads();
-    if (s + kStages - 1 < nst) issue(s + kStages - 1);    // into the buffer of stage s-1
-    const bf16_t* A = smem + (s % kStages) * kStageElems;
+    if (s + Tl::kStages - 1 < nst) issue(s + Tl::kStages - 1); // into the buffer of stage s-1
+    const bf16_t* A = smem + (s % Tl::kStages) * Tl::kStageElems;
 #pragma unroll
     for (int ks = 0; ks < kStageK / 16; ++ks) {
       bf16x8 bv;
-      if (wave < kWaves - 1) bv = b_frag<kDC>(A + kAElems, ks, 32 * wave, lane);
-      else bv = b_frag<kDRope>(A + kAElems + kB1Elems, ks, 0, lane);
+      if (wave < kWaves - 1) bv = b_frag<kDC>(A + Tl::kAElems, ks, 32 * wave, lane);
+      else bv = b_frag<kDRope>(A + Tl::kAElems + kB1Elems, ks, 0, lane);
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+      for (int tt = 0; tt < Tl::kTB; ++tt) {
         const bf16x8 av = a_frag(A, 32 * tt + (lane & 31), ks, half);
         acc[tt] = mfma32(av, bv, acc[tt]);
       }
@@ -101,7 +123,7 @@ void append_kernel(AppendArgs a) {
   T* cache = static_cast<T*>(a.cache);
   const size_t ring_rows = (size_t)a.window_frames * a.tokens_per_frame;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < Tl::kTB; ++tt) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 32 * tt + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -128,12 +150,50 @@ void append_kernel(AppendArgs a) {
   }
 }
 
+template <typename T, int TM>
+void launch_tm(const AppendArgs& a, hipStream_t s) {
+  dim3 grid((a.n_tok + TM - 1) / TM, a.batch);
+  hipLaunchKernelGGL((append_kernel<T, TM>), grid, dim3(kThreads), 0, s, a);
+}
+
+template <typename T>
+void launch_t(const AppendArgs& a, int tm, hipStream_t s) {
+  switch (tm) {
+    case 160: launch_tm<T, 160>(a, s); break;
+    case 128: launch_tm<T, 128>(a, s); break;
+    case 96: launch_tm<T, 96>(a, s); break;
+    case 64: launch_tm<T, 64>(a, s); break;
+    default: launch_tm<T, 32>(a, s); break;
+  }
+}
+
 }  // namespace
 
+// Tile height: one workgroup fits a compute unit (LDS), so a launch runs in
+// ceil(workgroups / CUs) rounds of one tile each; a tile costs about TM + 32
+// token-rows of work (the weight stream is the fixed part). Pick the TM with
+// the least rounds x (TM + 32).
+int append_tile_rows(int n_tok, int batch, int cus) {
+  int best = 32;
+  int64_t best_cost = -1;
+  for (int tm : {160, 128, 96, 64, 32}) {
+    const int64_t wgs = (int64_t)((n_tok + tm - 1) / tm) * batch;
+    const int64_t rounds = (wgs + cus - 1) / cus;
+    const int64_t cost = rounds * (tm + 32);
+    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = tm; }
+  }
+  return best;
+}
+
 hipError_t launch_append(const AppendArgs& a, bool f32, hipStream_t s) {
-  dim3 grid((a.n_tok + kTok - 1) / kTok, a.batch);
-  if (f32) hipLaunchKernelGGL(append_kernel<float>, grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(append_kernel<bf16_t>, grid, dim3(kThreads), 0, s, a);
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int tm = append_tile_rows(a.n_tok, a.batch, cus > 0 ? cus : 1);
+  if (f32) launch_t<float>(a, tm, s);
+  else launch_t<bf16_t>(a, tm, s);
   return hipGetLastError();
 }
 

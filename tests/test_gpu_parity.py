@@ -202,3 +202,15 @@ def test_config5_reduced_rollout():
             if c in checked and s in (0, last):
                 ref = r.reference(query_tokens=idx, t_first=t_first, n_frames=w.chunk_frames)
                 compare(_sync_np(out)[0, idx], ref, f"rollout chunk {c} step {s}", per_head_axis=1)
+
+
+@pytest.mark.parametrize("batch", [2, 4])
+def test_append_tile_heights(batch):
+    # a 3-frame chunk of 4680 tokens at batch 1, 2, 4, 8 selects append tiles of
+    # 32, 64, 96 and 160 rows (16 one-frame elements: 128); the other tests cover
+    # 32, 128 and 160
+    w = custom(30, 52, window_frames=3, chunk_frames=3, t_first=0, batch=batch)
+    r = Run(w)
+    r.append(0, 3)
+    for b in (0, batch - 1):
+        compare(r.cache_rows(0, 3, b=b), r.append_reference(0, 3, b=b), f"append B={batch} b={b}")
