@@ -103,6 +103,10 @@ void latent_attn_kernel(AttnArgs a) {
   const int b = blockIdx.z;
   const int qrow = blockIdx.x * kBlockQ + 32 * wave + qi;
   const bool qvalid = qrow < a.n_q;
+  // A wave whose 32 query rows all lie past n_q (the padded last block of a
+  // head) keeps the barriers and its share of the tile loads but skips the
+  // math: on a power-limited chip idle matrix cores raise the others' clock.
+  const bool live = (int)blockIdx.x * kBlockQ + 32 * wave < a.n_q;
 
   // Qhat fragments (B operand of S^T): lane holds features ks*16 + 8*half + e of its query.
   bf16x8 qf[kFeatSteps];
@@ -278,15 +282,17 @@ void latent_attn_kernel(AttnArgs a) {
       const int jt = q >> 1;
       if ((q & 1) == 0) {          // matrix phase for tile jt
         __builtin_amdgcn_s_setprio(1);
-        if (jt >= 1) accumulate(kt + ((jt - 1) % kBufs) * kTileElems);
-        if (jt < ntiles) scores(kt + (jt % kBufs) * kTileElems);
+        if (live) {
+          if (jt >= 1) accumulate(kt + ((jt - 1) % kBufs) * kTileElems);
+          if (jt < ntiles) scores(kt + (jt % kBufs) * kTileElems);
+        }
         __builtin_amdgcn_s_setprio(0);
       } else if (jt < ntiles) {    // vector phase for tile jt
         if (!lag) {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           if (jt + 2 < ntiles) issue_tile(jt + 2);
         }
-        softmax(jt * kKT);
+        if (live) softmax(jt * kKT);
       }
     }
     __syncthreads();
@@ -305,6 +311,7 @@ void latent_attn_kernel(AttnArgs a) {
   }
   __syncthreads();
 
+  if (!live) return;   // no barrier follows
   bf16x8 ob[kLatTiles][2];
 #pragma unroll
   for (int t = 0; t < kLatTiles; ++t)
