@@ -108,7 +108,8 @@ void vmla_default_dims(vmla_dims* dims);
  *
  * Errors: VMLA_ERR_NULL (any pointer NULL), VMLA_ERR_ALIGN, VMLA_ERR_DTYPE
  * (dtype invalid or != cache->dtype), VMLA_ERR_SHAPE (unsupported dims,
- * non-positive grid/batch/window, window_frames * T >= 2^24 slots),
+ * non-positive grid/batch/window, window_frames * T >= 2^24 slots,
+ * n_frames * T * d_model > 2^31 - 1 elements per batch element),
  * VMLA_ERR_RANGE (t_first < 0, n_frames < 1, n_frames > window_frames,
  * t_first + n_frames > 2^20), VMLA_ERR_HIP.
  */

@@ -14,8 +14,9 @@
 // TM tokens. The d_model contraction runs as a pipeline of 64-deep stages
 // (kStages buffers fetched by LDS-DMA kStages-1 stages ahead, one barrier per
 // stage); x, W_down and W_KR slices sit in separate LDS regions. All 7 waves
-// issue a share of each stage's loads: the issue rate of LDS-DMA loads grows
-// with the number of issuing waves.
+// issue a share of each stage's loads (the LDS-DMA issue rate grows with the
+// number of issuing waves), spread between the MFMAs of the current stage, and
+// each load costs only a scalar base update: the lane offsets are fixed.
 //
 // Tile height. Every workgroup streams all of W_down / W_KR (688 KB at
 // d_model = 1536) from L2 next to its TM x d_model slice of x from HBM, so a
@@ -69,15 +70,38 @@ void append_kernel(AppendArgs a) {
   const T* wr = static_cast<const T*>(a.w_kr);
   const int nst = a.d_model / kStageK;
 
-  auto issue = [&](int s) {
+  // Wave w issues loads n = w, w + 7, ... of every stage. For bf16 sources the
+  // lane offsets of those loads are computed once; a stage only moves the
+  // scalar source pointer and the LDS destination.
+  uint32_t voff[Tl::kLoadsHi];
+  if constexpr (std::is_same_v<T, bf16_t>) {
+#pragma unroll
+    for (int i = 0; i < Tl::kLoadsHi; ++i) {
+      const int n = wave + kWaves * i;
+      if (n < Tl::kALoads) voff[i] = stage_a_voff(a.d_model, tok0, a.n_tok, n, lane);
+      else if (n < Tl::kALoads + kB1Loads) voff[i] = stage_b_voff<kDC>(kDC, n - Tl::kALoads, lane);
+      else voff[i] = stage_b_voff<kDRope>(kDRope, n - Tl::kALoads - kB1Loads, lane);
+    }
+  }
+  auto issue = [&](int s, int i0 = 0, int i1 = Tl::kLoadsHi) {   // this wave's loads i0 <= i < i1 of stage s
     bf16_t* st = smem + (s % Tl::kStages) * Tl::kStageElems;
-    for (int n = wave; n < Tl::kLoads; n += kWaves) {
-      if (n < Tl::kALoads) stage_a_load<T>(st, x, a.d_model, tok0, a.n_tok, s * kStageK, n, lane);
-      else if (n < Tl::kALoads + kB1Loads)
-        stage_b_load<T, kDC>(st + Tl::kAElems, wd, kDC, 0, s * kStageK, n - Tl::kALoads, lane);
-      else
-        stage_b_load<T, kDRope>(st + Tl::kAElems + kB1Elems, wr, kDRope, 0, s * kStageK,
-                                n - Tl::kALoads - kB1Loads, lane);
+    const int k0 = s * kStageK;
+#pragma unroll
+    for (int i = 0; i < Tl::kLoadsHi; ++i) {
+      const int n = wave + kWaves * i;
+      if (i < i0 || i >= i1 || n >= Tl::kLoads) continue;
+      if constexpr (std::is_same_v<T, bf16_t>) {
+        if (n < Tl::kALoads) dma16_lds(x + k0, voff[i], lds_u32(st + 512 * n));
+        else if (n < Tl::kALoads + kB1Loads) dma16_lds(wd + (size_t)k0 * kDC, voff[i], lds_u32(st + 512 * n));
+        else dma16_lds(wr + (size_t)k0 * kDRope, voff[i], lds_u32(st + 512 * n));
+      } else {
+        if (n < Tl::kALoads) stage_a_load<T>(st, x, a.d_model, tok0, a.n_tok, k0, n, lane);
+        else if (n < Tl::kALoads + kB1Loads)
+          stage_b_load<T, kDC>(st + Tl::kAElems, wd, kDC, 0, k0, n - Tl::kALoads, lane);
+        else
+          stage_b_load<T, kDRope>(st + Tl::kAElems + kB1Elems, wr, kDRope, 0, k0,
+                                  n - Tl::kALoads - kB1Loads, lane);
+      }
     }
   };
   auto wait = [&](int stages) {      // own loads of all but the newest `stages` stages landed
@@ -97,7 +121,7 @@ void append_kernel(AppendArgs a) {
   for (int s = 0; s < nst; ++s) {
     wait(min(Tl::kStages - 2, nst - 1 - s));                   // stage s has landed
     __syncthreads();
-    if (s + Tl::kStages - 1 < nst) issue(s + Tl::kStages - 1); // into the buffer of stage s-1
+    const bool more = s + Tl::kStages - 1 < nst;               // loads into the buffer of stage s-1
     const bf16_t* A = smem + (s % Tl::kStages) * Tl::kStageElems;
 #pragma unroll
     for (int ks = 0; ks < kStageK / 16; ++ks) {
@@ -109,43 +133,103 @@ void append_kernel(AppendArgs a) {
         const bf16x8 av = a_frag(A, 32 * tt + (lane & 31), ks, half);
         acc[tt] = mfma32(av, bv, acc[tt]);
       }
+      // the wave's next-stage loads, spread over the k-steps so that their
+      // issue overlaps the MFMAs already in flight
+      if (more) issue(s + Tl::kStages - 1, 2 * ks, ks == 3 ? Tl::kLoadsHi : 2 * ks + 2);
     }
   }
 
   // Epilogue. Register r of lane l holds token row 32 tt + 8(r/4) + 4 half + r%4
-  // and column 32 wave + l%32; wave 6 holds the k_R columns and rotates them.
+  // and column 32 wave + l%32; wave 6 holds the k_R columns.
   const int col = lane & 31;
-  const int pair = col >> 1;
-  const bool odd = col & 1;
-  const bool rope = wave == kWaves - 1;
-  const float rev = a.rope.rev[pair];
-  const int axis = a.rope.axis[pair];
-  T* cache = static_cast<T*>(a.cache);
-  const size_t ring_rows = (size_t)a.window_frames * a.tokens_per_frame;
-#pragma unroll
-  for (int tt = 0; tt < Tl::kTB; ++tt) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 32 * tt + 8 * (r >> 2) + 4 * half + (r & 3);
+  T* cache = static_cast<T*>(a.cache) + (size_t)b * a.window_frames * a.tokens_per_frame * kRow;
+  if constexpr (std::is_same_v<T, bf16_t>) {
+    // The tile is assembled in LDS: c as bf16 rows of 224 + 8, k_R unrotated in
+    // fp32; per row the ring slot and (t, h, w) are computed once. The store
+    // pass rotates k_R (each (row, pair) once, spread over all threads) and
+    // writes whole 448-byte cache rows as 16-byte stores.
+    constexpr int kOutLd = kRow + 8;
+    constexpr int kKrLd = kDRope + 1;
+    static_assert(TM * kOutLd * 2 + TM * kKrLd * 4 + TM * 16 <= Tl::kStages * Tl::kStageElems * 2,
+                  "epilogue tile fits");
+    __syncthreads();                            // all stage reads done; the buffers are free
+    bf16_t* ot = smem;                                                     // [TM][kOutLd]
+    float* kr = reinterpret_cast<float*>(smem + TM * kOutLd);             // [TM][kKrLd]
+    int* rowinfo = reinterpret_cast<int*>(kr + TM * kKrLd);               // [TM][4]: slot, t, h, w
+    for (int row = tid; row < TM; row += kThreads) {
       const int n = tok0 + row;
-      float v = acc[tt][r];
-      // the RoPE lane exchange runs in every lane so that partners are always live
-      const float partner = swap_adjacent(v);
-      if (n >= a.n_tok) continue;
       int n_in, ww, tw;
-      const int f = div_small(n, a.tokens_per_frame, a.inv_tokens_per_frame, &n_in);
-      const int t = a.t_first + f;
-      if (rope) {
-        const int hh = div_small(n_in, a.grid_w, a.inv_grid_w, &ww);
-        const int pos = axis == 0 ? t : (axis == 1 ? hh : ww);
-        float sn, cs;
-        sincos_rev(pos, rev, &sn, &cs);
-        // pair (a0, a1) -> (a0 cos - a1 sin, a0 sin + a1 cos)
-        v = odd ? partner * sn + v * cs : v * cs - partner * sn;
+      const int f = div_small(min(n, a.n_tok - 1), a.tokens_per_frame, a.inv_tokens_per_frame, &n_in);
+      const int hh = div_small(n_in, a.grid_w, a.inv_grid_w, &ww);
+      div_small(a.t_first + f, a.window_frames, a.inv_window_frames, &tw);
+      rowinfo[4 * row] = n < a.n_tok ? tw * a.tokens_per_frame + n_in : -1;
+      rowinfo[4 * row + 1] = a.t_first + f;
+      rowinfo[4 * row + 2] = hh;
+      rowinfo[4 * row + 3] = ww;
+    }
+#pragma unroll
+    for (int tt = 0; tt < Tl::kTB; ++tt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * tt + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (wave < kWaves - 1) ot[row * kOutLd + 32 * wave + col] = f2bf(acc[tt][r]);
+        else kr[row * kKrLd + col] = acc[tt][r];
       }
-      div_small(t, a.window_frames, a.inv_window_frames, &tw);
-      const size_t slot = (size_t)tw * a.tokens_per_frame + n_in;
-      cache[((size_t)b * ring_rows + slot) * kRow + 32 * wave + col] = from_f32<T>(v);
+    }
+    __syncthreads();
+    for (int c = tid; c < TM * (kRow / 8); c += kThreads) {
+      const int row = c / (kRow / 8), cc = c - row * (kRow / 8);
+      const int slot = rowinfo[4 * row];
+      if (slot < 0) continue;
+      uint4 v;
+      if (cc < kDC / 8) {
+        v = *reinterpret_cast<const uint4*>(&ot[row * kOutLd + 8 * cc]);
+      } else {                                  // k_R pairs 4 j .. 4 j + 3
+        const int j = cc - kDC / 8;
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int pr = 4 * j + q;
+          const float a0 = kr[row * kKrLd + 2 * pr], a1 = kr[row * kKrLd + 2 * pr + 1];
+          float sn, cs;
+          sincos_rev(rowinfo[4 * row + 1 + a.rope.axis[pr]], a.rope.rev[pr], &sn, &cs);
+          // pair (a0, a1) -> (a0 cos - a1 sin, a0 sin + a1 cos)
+          w[q] = pack2(a0 * cs - a1 * sn, a0 * sn + a1 * cs);
+        }
+        v = uint4{w[0], w[1], w[2], w[3]};
+      }
+      *reinterpret_cast<uint4*>(cache + (size_t)slot * kRow + 8 * cc) = v;
+    }
+  } else {
+    // fp32 storage keeps the fp32 result: per-element stores, RoPE in wave 6
+    const int pair = col >> 1;
+    const bool odd = col & 1;
+    const bool rope = wave == kWaves - 1;
+    const float rev = a.rope.rev[pair];
+    const int axis = a.rope.axis[pair];
+#pragma unroll
+    for (int tt = 0; tt < Tl::kTB; ++tt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * tt + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int n = tok0 + row;
+        float v = acc[tt][r];
+        // the RoPE lane exchange runs in every lane so that partners are always live
+        const float partner = swap_adjacent(v);
+        if (n >= a.n_tok) continue;
+        int n_in, ww, tw;
+        const int f = div_small(n, a.tokens_per_frame, a.inv_tokens_per_frame, &n_in);
+        const int t = a.t_first + f;
+        if (rope) {
+          const int hh = div_small(n_in, a.grid_w, a.inv_grid_w, &ww);
+          const int pos = axis == 0 ? t : (axis == 1 ? hh : ww);
+          float sn, cs;
+          sincos_rev(pos, rev, &sn, &cs);
+          v = odd ? partner * sn + v * cs : v * cs - partner * sn;
+        }
+        div_small(t, a.window_frames, a.inv_window_frames, &tw);
+        cache[((size_t)tw * a.tokens_per_frame + n_in) * kRow + 32 * wave + col] = v;
+      }
     }
   }
 }

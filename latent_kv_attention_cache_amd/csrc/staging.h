@@ -76,6 +76,28 @@ __device__ __forceinline__ void stage_b_load(bf16_t* dst, const T* src, int ld, 
   }
 }
 
+// Byte offsets of one lane's 16 bytes in load n, relative to the stage's first
+// element (A tile: &src[0][k0] with rows from m0; B tile: &src[k0][n0]). They do
+// not depend on the stage, so a pipeline computes them once and only moves a
+// scalar base pointer from stage to stage (bf16 sources).
+__device__ __forceinline__ uint32_t stage_a_voff(int ld, int m0, int n_rows, int n, int lane) {
+  const int slot = 64 * n + lane;
+  const int r = slot >> 3;
+  const int c = (slot & 7) ^ swz_a(r);
+  const int row = min(m0 + r, n_rows - 1);
+  return (uint32_t)(row * ld + 8 * c) * 2u;
+}
+
+template <int NT>
+__device__ __forceinline__ uint32_t stage_b_voff(int ld, int n, int lane) {
+  constexpr int kChunksRow = NT / 8;
+  const int slot = 64 * n + lane;
+  const int k = slot / kChunksRow;
+  const int cpos = slot - k * kChunksRow;
+  const int col = ((((cpos >> 2) ^ swz_b<NT>(k)) << 2) | (cpos & 3)) * 8;
+  return (uint32_t)(k * ld + col) * 2u;
+}
+
 // Row-wise A operand (8 bf16) of MFMA 32x32x16: row r, K step ks of the stage.
 __device__ __forceinline__ bf16x8 a_frag(const bf16_t* tile, int r, int ks, int half) {
   return lds_row8(tile + 64 * r + 8 * ((2 * ks + half) ^ swz_a(r)));
