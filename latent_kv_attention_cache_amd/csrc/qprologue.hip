@@ -69,13 +69,32 @@ void qprologue_kernel(QArgs a) {
   const T* wq = static_cast<const T*>(a.w_q) + (size_t)h * kDHead;
   const int nst = a.d_model / kStageK;
 
-  auto issue = [&](int s) {
-    bf16_t* st = smem + (s % kStages) * kStageElems;
+  // Wave w issues loads n = w, w + 4, ... of every stage. For bf16 sources the
+  // lane offsets of those loads are computed once; a stage only moves the
+  // scalar source pointer and the LDS destination.
+  uint32_t voff[kLoadsPerWave];
+  if constexpr (std::is_same_v<T, bf16_t>) {
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
       const int n = wave + kWaves * i;
-      if (n < kALoads) stage_a_load<T>(st, x, a.d_model, tok0, a.n_q, s * kStageK, n, lane);
-      else stage_b_load<T, kDHead>(st + kAElems, wq, wq_ld, 0, s * kStageK, n - kALoads, lane);
+      voff[i] = n < kALoads ? stage_a_voff(a.d_model, tok0, a.n_q, n, lane)
+                            : stage_b_voff<kDHead>(wq_ld, n - kALoads, lane);
+    }
+  }
+  auto issue = [&](int s, int i0 = 0, int i1 = kLoadsPerWave) {   // this wave's loads i0 <= i < i1
+    bf16_t* st = smem + (s % kStages) * kStageElems;
+    const int k0 = s * kStageK;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+      if (i < i0 || i >= i1) continue;
+      const int n = wave + kWaves * i;
+      if constexpr (std::is_same_v<T, bf16_t>) {
+        if (n < kALoads) dma16_lds(x + k0, voff[i], lds_u32(st + 512 * n));
+        else dma16_lds(wq + (size_t)k0 * wq_ld, voff[i], lds_u32(st + 512 * n));
+      } else {
+        if (n < kALoads) stage_a_load<T>(st, x, a.d_model, tok0, a.n_q, k0, n, lane);
+        else stage_b_load<T, kDHead>(st + kAElems, wq, wq_ld, 0, k0, n - kALoads, lane);
+      }
     }
   };
 
@@ -85,7 +104,7 @@ void qprologue_kernel(QArgs a) {
   for (int s = 0; s < nst; ++s) {
     wait_stages<kLoadsPerWave>(min(kStages - 2, nst - 1 - s));   // stage s has landed
     __syncthreads();
-    if (s + kStages - 1 < nst) issue(s + kStages - 1);            // into the buffer of stage s-1
+    const bool more = s + kStages - 1 < nst;                      // loads into the buffer of stage s-1
     const bf16_t* A = smem + (s % kStages) * kStageElems;
     const bf16_t* B = A + kAElems;
 #pragma unroll
@@ -96,6 +115,9 @@ void qprologue_kernel(QArgs a) {
         const bf16x8 av = a_frag(A, 32 * tt + (lane & 31), ks, half);
         acc[tt] = mfma32(av, bv, acc[tt]);
       }
+      // the wave's next-stage loads, spread over the k-steps so that their
+      // issue overlaps the MFMAs already in flight
+      if (more) issue(s + kStages - 1, (kLoadsPerWave * ks) / 4, (kLoadsPerWave * (ks + 1)) / 4);
     }
   }
   __syncthreads();

@@ -36,8 +36,13 @@ __device__ __forceinline__ int swz_b(int k) {
 // wave-uniform). Inline assembly so the compiler does not serialize unrelated
 // LDS reads behind it; callers wait with s_waitcnt vmcnt. No register output.
 __device__ __forceinline__ void dma16_lds(const void* base, uint32_t voff, uint32_t lds_addr) {
+  // the base is wave-uniform; take it through readfirstlane so it is an SGPR pair
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint64_t sp = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory");
+               :: "v"(voff), "s"(reinterpret_cast<const void*>(sp)),
+                  "s"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_u32(const bf16_t* p) {
