@@ -8,12 +8,15 @@
 // Every query of the chunk attends to every valid key of the window, its own
 // chunk included (App. D.4: chunk-causal, so no mask inside the window).
 //
-// Work split. A workgroup of 8 waves (two per SIMD) owns 256 query tokens of
-// one (batch, head); each wave owns 32 tokens and keeps their Qhat rows in
-// registers. The waves walk the key window in tiles of 64 keys. A tile
-// [64][224] is copied once from global memory straight into LDS (16-byte
-// LDS-DMA loads, no VGPR staging) and read by all 8 waves, so every cache read
-// is shared by all 256 query tokens of the block.
+// Work split. The queries of a batch element are cut into units of 32 tokens
+// of one head, numbered head-major (U = ceil(n_q / 32) units per head, at
+// least 8). A workgroup of 8 waves (two per SIMD) takes 8 consecutive units,
+// one per wave; since the cache rows are shared by all heads, a workgroup may
+// span two heads, and only the last unit of a head can be partial. Each wave
+// keeps its 32 queries' Qhat rows in registers. The waves walk the key window
+// in tiles of 64 keys. A tile [64][224] is copied once from global memory
+// straight into LDS (16-byte LDS-DMA loads, no VGPR staging) and read by all 8
+// waves, so every cache read is shared by all 256 queries of the block.
 //
 // Ping-pong schedule. Time is cut into phases separated by workgroup barriers.
 // Waves 0-3 ("X") and 4-7 ("Y", one per SIMD next to an X wave) run the same
@@ -58,7 +61,6 @@ namespace {
 constexpr int kKT = 64;                     // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBlockQ = 32 * kWaves;        // query tokens per workgroup
 constexpr int kChunks = kRow / 8;           // 16-byte chunks per key row (28)
 constexpr int kSlots = kKT + 4;             // slots per chunk column (padded)
 constexpr int kTileElems = kChunks * kSlots * 8;
@@ -72,7 +74,7 @@ constexpr int kLatTiles = kDC / 32;         // 6
 constexpr float kLazy = 8.f;                // lazy-rescale threshold (log2 units)
 
 static_assert(kTileLoads % kLoaders == 0, "tile loads must split evenly over the loading waves");
-static_assert(kDC * kVLd <= kBufs * kTileElems, "W_V_up staging must fit in the tile buffers");
+static_assert(2 * kDC * kVLd <= kBufs * kTileElems, "W_V_up of two heads must fit in the tile buffers");
 
 // Scheduling-group masks (instruction classes of sched_group_barrier).
 constexpr int kSchedMfma = 0x008;
@@ -99,14 +101,22 @@ void latent_attn_kernel(AttnArgs a) {
   const int half = lane >> 5;
   const int qi = lane & 31;
   const int lag = wave >= kLoaders ? 1 : 0;   // Y waves run one phase behind
-  const int h = blockIdx.y;
   const int b = blockIdx.z;
-  const int qrow = blockIdx.x * kBlockQ + 32 * wave + qi;
-  const bool qvalid = qrow < a.n_q;
-  // A wave whose 32 query rows all lie past n_q (the padded last block of a
-  // head) keeps the barriers and its share of the tile loads but skips the
-  // math: on a power-limited chip idle matrix cores raise the others' clock.
-  const bool live = (int)blockIdx.x * kBlockQ + 32 * wave < a.n_q;
+  // This wave's unit: head h, query rows 32 qb .. 32 qb + 31.
+  const int units = (a.n_q + 31) / 32;
+  const int upad = units > kWaves ? units : kWaves;      // units per head, padded to >= 8
+  const int u0 = blockIdx.x * kWaves;
+  const int u = u0 + wave;
+  const int h_lo = u0 / upad;                             // heads of this workgroup: h_lo, h_lo + 1
+  const int h = min(u / upad, a.n_heads - 1);
+  const int qb = u - (u / upad) * upad;
+  const int qrow = 32 * qb + qi;
+  // A wave without queries (past the last head, or a pad unit of a head with
+  // fewer than 8 units) keeps the barriers and its share of the tile loads but
+  // skips the math: on a power-limited chip idle matrix cores raise the
+  // others' clock.
+  const bool live = u / upad < a.n_heads && qb < units;
+  const bool qvalid = live && qrow < a.n_q;
 
   // Qhat fragments (B operand of S^T): lane holds features ks*16 + 8*half + e of its query.
   bf16x8 qf[kFeatSteps];
@@ -299,17 +309,22 @@ void latent_attn_kernel(AttnArgs a) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- epilogue: out = (O / l) @ W_V_up[h]
+  // ---- epilogue: out = (O / l) @ W_V_up[h]; W_V_up of the workgroup's one or
+  // two heads staged in LDS, [kDC][kVLd] each.
   const float inv = 1.f / sum_across_halves(l);
-  bf16_t* wv = kt;   // [kDC][kVLd]
-  const T* wsrc = static_cast<const T*>(a.w_v_up) + (size_t)h * kDC * kDV;
+  const int nh = min((u0 + kWaves - 1) / upad, a.n_heads - 1) - h_lo + 1;   // 1 or 2 (upad >= 8)
+  const T* wsrc = static_cast<const T*>(a.w_v_up) + (size_t)h_lo * kDC * kDV;
+  for (int hh = 0; hh < nh; ++hh) {
 #pragma unroll
-  for (int i = 0; i < kDC * kDV / 8 / kThreads; ++i) {
-    const int c = tid + i * kThreads;
-    const int row = c / (kDV / 8), cc = c % (kDV / 8);
-    *reinterpret_cast<uint4*>(&wv[row * kVLd + 8 * cc]) = load8_bf16<T>(wsrc + (size_t)row * kDV + 8 * cc);
+    for (int i = 0; i < kDC * kDV / 8 / kThreads; ++i) {
+      const int c = tid + i * kThreads;
+      const int row = c / (kDV / 8), cc = c % (kDV / 8);
+      *reinterpret_cast<uint4*>(&kt[(hh * kDC + row) * kVLd + 8 * cc]) =
+          load8_bf16<T>(wsrc + ((size_t)hh * kDC + row) * kDV + 8 * cc);
+    }
   }
   __syncthreads();
+  const bf16_t* wv = kt + (h - h_lo) * kDC * kVLd;
 
   if (!live) return;   // no barrier follows
   bf16x8 ob[kLatTiles][2];
@@ -347,7 +362,9 @@ void latent_attn_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_latent_attn(const AttnArgs& a, bool f32, hipStream_t s) {
-  dim3 grid((a.n_q + kBlockQ - 1) / kBlockQ, a.n_heads, a.batch);
+  const int units = (a.n_q + 31) / 32;
+  const int upad = units > kWaves ? units : kWaves;
+  dim3 grid((a.n_heads * upad + kWaves - 1) / kWaves, 1, a.batch);
   if (f32) hipLaunchKernelGGL(latent_attn_kernel<float>, grid, dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL(latent_attn_kernel<bf16_t>, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();

@@ -62,6 +62,20 @@ def test_key_count_sweep(grid_h, grid_w, window, t_first):
     compare(out[0], r.reference(), f"N_k={w.n_k}", per_head_axis=1)
 
 
+@pytest.mark.parametrize("grid_h,grid_w", [
+    (8, 32),      # 256 queries: 8 units of 32 per head, one head per workgroup
+    (1, 257),     # 257: 9 units, the last with one row; workgroups span two heads
+    (10, 29),     # 290: 10 units, the last with two rows
+])
+def test_heads_sharing_a_workgroup(grid_h, grid_w):
+    # Query units (32 tokens of one head) are packed 8 to a workgroup across
+    # head boundaries; every head's output is checked in full.
+    w = custom(grid_h, grid_w, window_frames=2, chunk_frames=1, t_first=1)
+    r = Run(w)
+    out = _sync_np(r.chunk_step())
+    compare(out[0], r.reference(), f"n_q={w.n_q}", per_head_axis=1)
+
+
 def test_ring_wrap_and_nan_poisoned_prefix():
     # The ring starts as NaN: attention may only read the valid prefix while it fills.
     w = custom(4, 6, window_frames=3, chunk_frames=1, t_first=0)
