@@ -8,21 +8,37 @@
 // (App. D.3); the cache is a fixed-size window of latent frames with FIFO
 // eviction (App. D.4).
 //
-// A skinny GEMM (N = 224, K = d_model) over all tokens of the chunk. One
-// workgroup (7 waves) computes a TM-token x 224-column tile; wave w owns the
-// 32-column block w (blocks 0-5: c from W_down, block 6: k_R from W_KR) for all
-// TM tokens. The d_model contraction runs as a pipeline of 64-deep stages
-// (kStages buffers fetched by LDS-DMA kStages-1 stages ahead, one barrier per
-// stage); x, W_down and W_KR slices sit in separate LDS regions. All 7 waves
-// issue a share of each stage's loads (the LDS-DMA issue rate grows with the
-// number of issuing waves), spread between the MFMAs of the current stage, and
-// each load costs only a scalar base update: the lane offsets are fixed.
+// A skinny GEMM: M = batch x tokens rows (the batch elements are contiguous in
+// x, so they form one row range), N = 224, K = d_model. The M rows are split
+// into one contiguous range per workgroup, at most 160 rows, as evenly as the
+// device's compute units allow (a workgroup fills one compute unit's LDS).
+// Every workgroup streams all of W_down / W_KR (688 KB at d_model = 1536) from
+// L2 next to its slice of x from HBM.
 //
-// Tile height. Every workgroup streams all of W_down / W_KR (688 KB at
-// d_model = 1536) from L2 next to its TM x d_model slice of x from HBM, so a
-// tall tile amortises the weight stream, while a short tile spreads a small
-// chunk over more compute units. The launcher picks TM in {32, ..., 160} from
-// the token count (one workgroup per compute unit at a time, see below).
+// Four waves, one per SIMD, split the tile 2 x 2: wave (rh, ch) owns row half
+// rh (up to 5 blocks of 16 rows) and column half ch (7 blocks of 16 columns;
+// half 1 holds c columns 112-191 and the 32 k_R columns), with
+// v_mfma_f32_16x16x32_bf16 computing the transposed block out^T = W^T x^T, so
+// that a lane ends up with four consecutive columns of one token row. Per
+// 32-deep step a wave reads 5 x and 7 W fragments from LDS for 35 MFMAs, so
+// LDS traffic per MFMA is low and the four SIMDs carry equal work.
+//
+// The d_model contraction runs as a pipeline of 64-deep stages (3-4 buffers,
+// fetched by 16-byte LDS-DMA loads kStages-1 stages ahead, one barrier per
+// stage); each wave issues its share of the next stage's loads between its
+// MFMAs, and each load costs a scalar base update only (fixed lane offsets).
+// LDS layouts of a stage:
+//   x tile: row-major, 64 bf16 (8 chunks of 16 B) per row, chunk c of row r at
+//           position c ^ swz_a(r): the row-wise operand reads of 16 consecutive
+//           rows hit distinct banks;
+//   W tiles: W_down [64][192] and W_KR [64][32], row-major, so that a DMA load
+//           reads 1 KB of contiguous weight. The 16-byte chunks of row k are
+//           XOR-permuted, chunk c at position c ^ 2 t(k) with
+//           t(k) = bit1(k) | bit3(k) << 1 for W_down and t(k) = bit3(k) for
+//           W_KR: a transposed B read of 32 lanes (rows k0 .. k0+3 and
+//           k0+8 .. k0+11, two chunks each) then covers all 64 banks once.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "staging.h"
@@ -30,243 +46,316 @@
 namespace vmla {
 namespace {
 
-constexpr int kWaves = kRow / 32;      // 7: one per 32-column block
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kB1Elems = kStageK * kDC;          // W_down slice   (24 KB)
-constexpr int kB2Elems = kStageK * kDRope;       // W_KR slice     (4 KB)
-constexpr int kB1Loads = kB1Elems * 2 / 1024;    // 24
-constexpr int kB2Loads = kB2Elems * 2 / 1024;    // 4
+constexpr int kWChunks = kRow / 8;              // 28 chunks per weight row: 24 W_down + 4 W_KR
+constexpr int kWdElems = kStageK * kDC;         // W_down tile
+constexpr int kWElems = kStageK * kRow;         // W_down + W_KR tiles
+constexpr int kWdLoads = kWdElems * 2 / 1024;   // 24 wave-wide loads
+constexpr int kColBlocks = 7;                   // 16-wide column blocks per wave
+constexpr int kMaxRows = 160;
 
-template <int TM>
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// chunk permutation masks of W_down / W_KR row k (an involution per row)
+__device__ __forceinline__ int swz_wd(int k) { return 2 * (((k >> 1) & 1) | (((k >> 3) & 1) << 1)); }
+__device__ __forceinline__ int swz_wr(int k) { return 2 * ((k >> 3) & 1); }
+
+template <typename T, int NRB>
 struct Tile {
-  static constexpr int kTB = TM / 32;                        // 32-token blocks per wave
-  static constexpr int kAElems = TM * kStageK;               // x slice
-  static constexpr int kALoads = kAElems * 2 / 1024;         // TM / 8
-  static constexpr int kStageElems = kAElems + kB1Elems + kB2Elems;
-  static constexpr int kStages = TM >= 96 ? 3 : 4;           // <= 144 KB of LDS
-  static constexpr int kLoads = kALoads + kB1Loads + kB2Loads;
-  // wave w issues loads w, w + 7, ...: the first kLoads % 7 waves issue one more
-  static constexpr int kLoadsHi = (kLoads + kWaves - 1) / kWaves;
-  static constexpr int kLoadsLo = kLoads / kWaves;
-  static constexpr int kHiWaves = kLoads % kWaves;
-  static_assert(TM % 32 == 0 && TM >= 32 && TM <= 160, "tile height");
-  static_assert(kStages * kStageElems * 2 <= 160 * 1024, "LDS budget");
+  static constexpr int kRows = 32 * NRB;                   // rows of a workgroup at most
+  static constexpr int kXElems = kRows * kStageK;
+  static constexpr int kXLoads = kXElems * 2 / 1024;       // 4 NRB
+  static constexpr int kStageElems = kXElems + kWElems;
+  static constexpr int kStages = 4 * kStageElems * 2 <= 160 * 1024 ? 4 : 3;
+  static constexpr int kLoadsPerWave = (kXLoads + kWChunks) / kWaves;   // NRB x loads + 7 W chunks
+  // epilogue: bf16 storage keeps c as bf16 rows of 224 + 8 and k_R in fp32;
+  // fp32 storage keeps all 224 columns in fp32 rows of 228; 5 ints of row info
+  static constexpr int kOutLd = std::is_same_v<T, bf16_t> ? kRow + 8 : kRow + 4;
+  static constexpr int kKrLd = kDRope + 4;
+  static constexpr int kEpiBytes = std::is_same_v<T, bf16_t>
+      ? kRows * (kOutLd * 2 + kKrLd * 4 + 20) : kRows * (kOutLd * 4 + 20);
+  static constexpr int kSmemElems = std::max(kStages * kStageElems, (kEpiBytes + 1) / 2);
+  static_assert(NRB >= 1 && NRB <= 5, "row blocks per wave");
+  static_assert((kXLoads + kWChunks) % kWaves == 0 && kXLoads == kWaves * NRB, "load split");
+  static_assert(kSmemElems * 2 <= 160 * 1024, "LDS budget");
 };
 
-template <typename T, int TM>
+template <typename T, int NRB>
 __global__ __launch_bounds__(kThreads)
 void append_kernel(AppendArgs a) {
-  using Tl = Tile<TM>;
-  __shared__ __attribute__((aligned(16))) bf16_t smem[Tl::kStages * Tl::kStageElems];
+  using Tl = Tile<T, NRB>;
+  constexpr bool kBf16 = std::is_same_v<T, bf16_t>;
+  __shared__ __attribute__((aligned(16))) bf16_t smem[Tl::kSmemElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int half = lane >> 5;
-  const int b = blockIdx.y;
-  const int tok0 = blockIdx.x * TM;
-  const T* x = static_cast<const T*>(a.x) + (size_t)b * a.n_tok * a.d_model;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int g = lane >> 4;                  // 16-lane group: k sub-range of an MFMA operand
+  const int rh = wv >> 1, ch = wv & 1;      // wave-uniform
+
+  // This workgroup's rows [m0, m0 + rows) of the flattened batch x tokens.
+  const int64_t M = (int64_t)a.batch * a.n_tok;
+  const int64_t m0 = (int64_t)blockIdx.x * M / gridDim.x;
+  const int rows = (int)((int64_t)(blockIdx.x + 1) * M / gridDim.x - m0);
+  const int nb = (rows + 15) / 16;          // 16-row blocks of the tile
+  const int nb0 = (nb + 1) / 2;             // blocks of row half 0 (<= NRB)
+  const int rbase = rh ? 16 * nb0 : 0;
+
+  const T* xw = static_cast<const T*>(a.x) + m0 * a.d_model;
   const T* wd = static_cast<const T*>(a.w_down);
   const T* wr = static_cast<const T*>(a.w_kr);
   const int nst = a.d_model / kStageK;
 
-  // Wave w issues loads n = w, w + 7, ... of every stage. For bf16 sources the
-  // lane offsets of those loads are computed once; a stage only moves the
-  // scalar source pointer and the LDS destination.
-  uint32_t voff[Tl::kLoadsHi];
-  if constexpr (std::is_same_v<T, bf16_t>) {
+  // Loads of a stage: x loads n = NRB wv + i (i < NRB), W chunks c = 7 wv + j
+  // (j < 7). For bf16 sources the lane offsets are fixed; a stage moves only
+  // the scalar source pointers and the LDS destinations.
+  uint32_t voff[Tl::kLoadsPerWave];
+  if constexpr (kBf16) {
 #pragma unroll
-    for (int i = 0; i < Tl::kLoadsHi; ++i) {
-      const int n = wave + kWaves * i;
-      if (n < Tl::kALoads) voff[i] = stage_a_voff(a.d_model, tok0, a.n_tok, n, lane);
-      else if (n < Tl::kALoads + kB1Loads) voff[i] = stage_b_voff<kDC>(kDC, n - Tl::kALoads, lane);
-      else voff[i] = stage_b_voff<kDRope>(kDRope, n - Tl::kALoads - kB1Loads, lane);
-    }
-  }
-  auto issue = [&](int s, int i0 = 0, int i1 = Tl::kLoadsHi) {   // this wave's loads i0 <= i < i1 of stage s
-    bf16_t* st = smem + (s % Tl::kStages) * Tl::kStageElems;
-    const int k0 = s * kStageK;
-#pragma unroll
-    for (int i = 0; i < Tl::kLoadsHi; ++i) {
-      const int n = wave + kWaves * i;
-      if (i < i0 || i >= i1 || n >= Tl::kLoads) continue;
-      if constexpr (std::is_same_v<T, bf16_t>) {
-        if (n < Tl::kALoads) dma16_lds(x + k0, voff[i], lds_u32(st + 512 * n));
-        else if (n < Tl::kALoads + kB1Loads) dma16_lds(wd + (size_t)k0 * kDC, voff[i], lds_u32(st + 512 * n));
-        else dma16_lds(wr + (size_t)k0 * kDRope, voff[i], lds_u32(st + 512 * n));
+    for (int i = 0; i < Tl::kLoadsPerWave; ++i) {
+      if (i < NRB) {
+        voff[i] = stage_a_voff(a.d_model, 0, rows, NRB * wv + i, lane);
       } else {
-        if (n < Tl::kALoads) stage_a_load<T>(st, x, a.d_model, tok0, a.n_tok, k0, n, lane);
-        else if (n < Tl::kALoads + kB1Loads)
-          stage_b_load<T, kDC>(st + Tl::kAElems, wd, kDC, 0, k0, n - Tl::kALoads, lane);
-        else
-          stage_b_load<T, kDRope>(st + Tl::kAElems + kB1Elems, wr, kDRope, 0, k0,
-                                  n - Tl::kALoads - kB1Loads, lane);
+        // W load n: 1 KB of the W_down tile (n < 24) or of the W_KR tile; LDS
+        // slot q holds chunk position q % rowchunks of row q / rowchunks
+        const int n = kColBlocks * wv + (i - NRB);
+        if (n < kWdLoads) {
+          const int q = 64 * n + lane, k = q / (kDC / 8), cp = q - k * (kDC / 8);
+          voff[i] = (uint32_t)(k * (kDC / 8) + (cp ^ swz_wd(k))) * 16u;
+        } else {
+          const int q = 64 * (n - kWdLoads) + lane, k = q / (kDRope / 8), cp = q - k * (kDRope / 8);
+          voff[i] = (uint32_t)(k * (kDRope / 8) + (cp ^ swz_wr(k))) * 16u;
+        }
+      }
+    }
+  }
+  // this wave's loads i0 <= i < i1: data of stage sd into the buffer of stage sb
+  auto issue = [&](int sb, int sd, int i0, int i1) {
+    bf16_t* st = smem + (sb % Tl::kStages) * Tl::kStageElems;
+    const int k0 = sd * kStageK;
+#pragma unroll
+    for (int i = 0; i < Tl::kLoadsPerWave; ++i) {
+      if (i < i0 || i >= i1) continue;
+      if (i < NRB) {
+        const int n = NRB * wv + i;
+        if constexpr (kBf16) dma16_lds(xw + k0, voff[i], lds_u32(st + 512 * n));
+        else stage_a_load<T>(st, xw, a.d_model, 0, rows, k0, n, lane);
+      } else {
+        const int n = kColBlocks * wv + (i - NRB);
+        bf16_t* dst = st + Tl::kXElems + 512 * n;
+        if constexpr (kBf16) {
+          const bf16_t* src = n < kWdLoads ? wd + (size_t)k0 * kDC : wr + (size_t)k0 * kDRope;
+          dma16_lds(src, voff[i], lds_u32(dst));
+        } else {
+          const T* src;
+          if (n < kWdLoads) {
+            const int q = 64 * n + lane, k = q / (kDC / 8), cp = q - k * (kDC / 8);
+            src = wd + (size_t)(k0 + k) * kDC + 8 * (cp ^ swz_wd(k));
+          } else {
+            const int q = 64 * (n - kWdLoads) + lane, k = q / (kDRope / 8), cp = q - k * (kDRope / 8);
+            src = wr + (size_t)(k0 + k) * kDRope + 8 * (cp ^ swz_wr(k));
+          }
+          *reinterpret_cast<uint4*>(dst + 8 * lane) = load8_bf16<T>(src);
+        }
       }
     }
   };
-  auto wait = [&](int stages) {      // own loads of all but the newest `stages` stages landed
-    if constexpr (Tl::kHiWaves == 0) {
-      wait_stages<Tl::kLoadsLo>(stages);
-    } else {
-      if (wave < Tl::kHiWaves) wait_stages<Tl::kLoadsHi>(stages);
-      else wait_stages<Tl::kLoadsLo>(stages);
-    }
-  };
 
-  for (int s = 0; s < Tl::kStages - 1 && s < nst; ++s) issue(s);
-
-  f32x16 acc[Tl::kTB];
+  // Per-lane operand offsets (elements, relative to a stage's tile).
+  // A (x, row-major swizzled): lane = row (lane % 16) of block rb, chunk 4 kk + g.
+  int a_off[NRB][2];
 #pragma unroll
-  for (int tt = 0; tt < Tl::kTB; ++tt) acc[tt] = f32x16{};
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int row = rbase + 16 * rb + (lane & 15);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) a_off[rb][kk] = 64 * row + 8 * ((4 * kk + g) ^ swz_a(row));
+  }
+  // B (W) by ds_read_b64_tr_b16: lane j of 16-lane group g points at k row
+  // 32 kk + 8 g + j/4 (+4 for the upper half of the fragment) and columns
+  // col0 + 4 (j%4) .. +3, i.e. logical chunk col0/8 + (j%4)/2, element 4 (j%2).
+  // Bits 1 and 3 of that row (the swizzle bits) depend on the lane only, so one
+  // offset per column block serves every (kk, half).
+  const int j = lane & 15;
+  int b_off[kColBlocks];
+  {
+    const int k = 8 * g + (j >> 2);
+#pragma unroll
+    for (int cb = 0; cb < kColBlocks; ++cb) {
+      const int gcb = kColBlocks * ch + cb;            // 16-column block of [c | k_R]
+      const int c = (gcb < kDC / 16 ? 2 * gcb : 2 * (gcb - kDC / 16)) + ((j & 3) >> 1);
+      b_off[cb] = gcb < kDC / 16 ? k * kDC + 8 * (c ^ swz_wd(k)) + 4 * (j & 1)
+                                 : kWdElems + k * kDRope + 8 * (c ^ swz_wr(k)) + 4 * (j & 1);
+    }
+  }
+
+  for (int s = 0; s < Tl::kStages - 1 && s < nst; ++s) issue(s, s, 0, Tl::kLoadsPerWave);
+
+  f32x4 acc[NRB][kColBlocks];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < kColBlocks; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int kL = Tl::kLoadsPerWave;
+  // Stage s: two 32-deep steps of NRB x 7 MFMAs. The A fragment of the next
+  // row block and the B fragments of the second step are read while the
+  // current MFMAs run, and the wave's share of the loads of stage
+  // s + kStages - 1 goes out after every row block. Past the last stage those
+  // loads repeat the last stage's (cached) data into the buffer of stage s-1,
+  // which is not read again, so the stage body has no branch.
+  // Every iteration issues one stage, so min(kStages - 2, nst - 1) stages are in
+  // flight behind stage s at the top of each iteration.
+  const int behind = min(Tl::kStages - 2, nst - 1);
   for (int s = 0; s < nst; ++s) {
-    wait(min(Tl::kStages - 2, nst - 1 - s));                   // stage s has landed
+    wait_stages<kL>(behind);                                     // stage s has landed
     __syncthreads();
-    const bool more = s + Tl::kStages - 1 < nst;               // loads into the buffer of stage s-1
-    const bf16_t* A = smem + (s % Tl::kStages) * Tl::kStageElems;
+    const int sn = min(s + Tl::kStages - 1, nst - 1);           // source stage of the loads
+    const bf16_t* X = smem + (s % Tl::kStages) * Tl::kStageElems;
+    const bf16_t* W = X + Tl::kXElems;
+    auto read_b = [&](int kk, bf16x8* bf) {
 #pragma unroll
-    for (int ks = 0; ks < kStageK / 16; ++ks) {
-      bf16x8 bv;
-      if (wave < kWaves - 1) bv = b_frag<kDC>(A + Tl::kAElems, ks, 32 * wave, lane);
-      else bv = b_frag<kDRope>(A + Tl::kAElems + kB1Elems, ks, 0, lane);
-#pragma unroll
-      for (int tt = 0; tt < Tl::kTB; ++tt) {
-        const bf16x8 av = a_frag(A, 32 * tt + (lane & 31), ks, half);
-        acc[tt] = mfma32(av, bv, acc[tt]);
+      for (int cb = 0; cb < kColBlocks; ++cb) {
+        const bf16_t* p = W + b_off[cb] + 32 * kk * (cb + kColBlocks * ch < kDC / 16 ? kDC : kDRope);
+        const int up = 4 * (cb + kColBlocks * ch < kDC / 16 ? kDC : kDRope);
+        const bf16x4 lo = lds_tr4(p);
+        const bf16x4 hi = lds_tr4(p + up);
+        bf[cb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
-      // the wave's next-stage loads, spread over the k-steps so that their
-      // issue overlaps the MFMAs already in flight
-      if (more) issue(s + Tl::kStages - 1, 2 * ks, ks == 3 ? Tl::kLoadsHi : 2 * ks + 2);
-    }
-  }
-
-  // Epilogue. Register r of lane l holds token row 32 tt + 8(r/4) + 4 half + r%4
-  // and column 32 wave + l%32; wave 6 holds the k_R columns.
-  const int col = lane & 31;
-  T* cache = static_cast<T*>(a.cache) + (size_t)b * a.window_frames * a.tokens_per_frame * kRow;
-  if constexpr (std::is_same_v<T, bf16_t>) {
-    // The tile is assembled in LDS: c as bf16 rows of 224 + 8, k_R unrotated in
-    // fp32; per row the ring slot and (t, h, w) are computed once. The store
-    // pass rotates k_R (each (row, pair) once, spread over all threads) and
-    // writes whole 448-byte cache rows as 16-byte stores.
-    constexpr int kOutLd = kRow + 8;
-    constexpr int kKrLd = kDRope + 1;
-    static_assert(TM * kOutLd * 2 + TM * kKrLd * 4 + TM * 16 <= Tl::kStages * Tl::kStageElems * 2,
-                  "epilogue tile fits");
-    __syncthreads();                            // all stage reads done; the buffers are free
-    bf16_t* ot = smem;                                                     // [TM][kOutLd]
-    float* kr = reinterpret_cast<float*>(smem + TM * kOutLd);             // [TM][kKrLd]
-    int* rowinfo = reinterpret_cast<int*>(kr + TM * kKrLd);               // [TM][4]: slot, t, h, w
-    for (int row = tid; row < TM; row += kThreads) {
-      const int n = tok0 + row;
-      int n_in, ww, tw;
-      const int f = div_small(min(n, a.n_tok - 1), a.tokens_per_frame, a.inv_tokens_per_frame, &n_in);
-      const int hh = div_small(n_in, a.grid_w, a.inv_grid_w, &ww);
-      div_small(a.t_first + f, a.window_frames, a.inv_window_frames, &tw);
-      rowinfo[4 * row] = n < a.n_tok ? tw * a.tokens_per_frame + n_in : -1;
-      rowinfo[4 * row + 1] = a.t_first + f;
-      rowinfo[4 * row + 2] = hh;
-      rowinfo[4 * row + 3] = ww;
-    }
+    };
+    bf16x8 b0[kColBlocks], b1[kColBlocks];
+    read_b(0, b0);
+    bf16x8 av = lds_row8(X + a_off[0][0]);
 #pragma unroll
-    for (int tt = 0; tt < Tl::kTB; ++tt) {
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * tt + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (wave < kWaves - 1) ot[row * kOutLd + 32 * wave + col] = f2bf(acc[tt][r]);
-        else kr[row * kKrLd + col] = acc[tt][r];
-      }
-    }
-    __syncthreads();
-    for (int c = tid; c < TM * (kRow / 8); c += kThreads) {
-      const int row = c / (kRow / 8), cc = c - row * (kRow / 8);
-      const int slot = rowinfo[4 * row];
-      if (slot < 0) continue;
-      uint4 v;
-      if (cc < kDC / 8) {
-        v = *reinterpret_cast<const uint4*>(&ot[row * kOutLd + 8 * cc]);
-      } else {                                  // k_R pairs 4 j .. 4 j + 3
-        const int j = cc - kDC / 8;
-        uint32_t w[4];
+      for (int rb = 0; rb < NRB; ++rb) {
+        const int q = kk * NRB + rb;
+        bf16x8 an = av;
+        if (q + 1 < 2 * NRB) an = lds_row8(X + a_off[(q + 1) % NRB][(q + 1) / NRB]);
+        if (kk == 0 && rb == NRB - 1) read_b(1, b1);
+        issue(s + Tl::kStages - 1, sn, q * kL / (2 * NRB), (q + 1) * kL / (2 * NRB));
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int pr = 4 * j + q;
-          const float a0 = kr[row * kKrLd + 2 * pr], a1 = kr[row * kKrLd + 2 * pr + 1];
-          float sn, cs;
-          sincos_rev(rowinfo[4 * row + 1 + a.rope.axis[pr]], a.rope.rev[pr], &sn, &cs);
-          // pair (a0, a1) -> (a0 cos - a1 sin, a0 sin + a1 cos)
-          w[q] = pack2(a0 * cs - a1 * sn, a0 * sn + a1 * cs);
-        }
-        v = uint4{w[0], w[1], w[2], w[3]};
-      }
-      *reinterpret_cast<uint4*>(cache + (size_t)slot * kRow + 8 * cc) = v;
-    }
-  } else {
-    // fp32 storage keeps the fp32 result: per-element stores, RoPE in wave 6
-    const int pair = col >> 1;
-    const bool odd = col & 1;
-    const bool rope = wave == kWaves - 1;
-    const float rev = a.rope.rev[pair];
-    const int axis = a.rope.axis[pair];
-#pragma unroll
-    for (int tt = 0; tt < Tl::kTB; ++tt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * tt + 8 * (r >> 2) + 4 * half + (r & 3);
-        const int n = tok0 + row;
-        float v = acc[tt][r];
-        // the RoPE lane exchange runs in every lane so that partners are always live
-        const float partner = swap_adjacent(v);
-        if (n >= a.n_tok) continue;
-        int n_in, ww, tw;
-        const int f = div_small(n, a.tokens_per_frame, a.inv_tokens_per_frame, &n_in);
-        const int t = a.t_first + f;
-        if (rope) {
-          const int hh = div_small(n_in, a.grid_w, a.inv_grid_w, &ww);
-          const int pos = axis == 0 ? t : (axis == 1 ? hh : ww);
-          float sn, cs;
-          sincos_rev(pos, rev, &sn, &cs);
-          v = odd ? partner * sn + v * cs : v * cs - partner * sn;
-        }
-        div_small(t, a.window_frames, a.inv_window_frames, &tw);
-        cache[((size_t)tw * a.tokens_per_frame + n_in) * kRow + 32 * wave + col] = v;
+        for (int cb = 0; cb < kColBlocks; ++cb)
+          acc[rb][cb] = mfma16(kk == 0 ? b0[cb] : b1[cb], av, acc[rb][cb]);
+        av = an;
       }
     }
   }
-}
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // the trailing loads have landed
 
-template <typename T, int TM>
-void launch_tm(const AppendArgs& a, hipStream_t s) {
-  dim3 grid((a.n_tok + TM - 1) / TM, a.batch);
-  hipLaunchKernelGGL((append_kernel<T, TM>), grid, dim3(kThreads), 0, s, a);
+  // ---- epilogue. Register r of acc[rb][cb] in lane l: token row
+  // rbase + 16 rb + l%16, column 112 ch + 16 cb + 4 g + r. Per row the batch element, the ring slot and
+  // (t, h, w) are computed once; the store pass rotates each (row, k_R pair)
+  // once, spread over all threads, and writes whole cache rows in 16-byte stores.
+  __syncthreads();                          // all stage reads done; the buffers are free
+  constexpr int kOutLd = Tl::kOutLd;
+  constexpr int kKrLd = Tl::kKrLd;
+  using OutT = std::conditional_t<kBf16, bf16_t, float>;
+  OutT* ot = reinterpret_cast<OutT*>(smem);                                 // [kRows][kOutLd]
+  float* kr = reinterpret_cast<float*>(ot + Tl::kRows * kOutLd);            // bf16: [kRows][kKrLd]
+  int* ri = kBf16 ? reinterpret_cast<int*>(kr + Tl::kRows * kKrLd)
+                  : reinterpret_cast<int*>(ot + Tl::kRows * kOutLd);        // [kRows][5]
+  const int64_t cache_rows = (int64_t)a.window_frames * a.tokens_per_frame;
+  for (int row = tid; row < rows; row += kThreads) {
+    const int64_t m = m0 + row;
+    const int bb = (int)(m / a.n_tok);
+    const int n = (int)(m - (int64_t)bb * a.n_tok);
+    int n_in, ww, tw;
+    const int f = div_small(n, a.tokens_per_frame, a.inv_tokens_per_frame, &n_in);
+    const int hh = div_small(n_in, a.grid_w, a.inv_grid_w, &ww);
+    div_small(a.t_first + f, a.window_frames, a.inv_window_frames, &tw);
+    ri[5 * row] = bb;
+    ri[5 * row + 1] = tw * a.tokens_per_frame + n_in;
+    ri[5 * row + 2] = a.t_first + f;
+    ri[5 * row + 3] = hh;
+    ri[5 * row + 4] = ww;
+  }
+  {
+    const int row0 = rbase + (lane & 15);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int row = row0 + 16 * rb;
+#pragma unroll
+      for (int cb = 0; cb < kColBlocks; ++cb) {
+        const int col = 112 * ch + 16 * cb + 4 * g;
+        const f32x4 v = acc[rb][cb];
+        if constexpr (kBf16) {
+          if (ch == 0 || cb < 5)
+            *reinterpret_cast<uint2*>(&ot[row * kOutLd + col]) = uint2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+          else
+            *reinterpret_cast<f32x4*>(&kr[row * kKrLd + col - kDC]) = v;
+        } else {
+          *reinterpret_cast<f32x4*>(&ot[row * kOutLd + col]) = v;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  T* cache = static_cast<T*>(a.cache);
+  constexpr int kPer = 16 / sizeof(T);      // elements per 16-byte store
+  constexpr int kChunksRow = kRow / kPer;
+  constexpr int kCChunks = kDC / kPer;
+  for (int c = tid; c < rows * kChunksRow; c += kThreads) {
+    const int row = c / kChunksRow, cc = c - row * kChunksRow;
+    T* dst = cache + ((size_t)ri[5 * row] * cache_rows + ri[5 * row + 1]) * kRow + kPer * cc;
+    uint4 v;
+    if (cc < kCChunks) {
+      v = *reinterpret_cast<const uint4*>(&ot[row * kOutLd + kPer * cc]);
+    } else {                                // k_R pairs kPer/2 (cc - kCChunks) ...
+      const int p0 = kPer / 2 * (cc - kCChunks);
+      const float* src = kBf16 ? kr + row * kKrLd + kPer * (cc - kCChunks)
+                               : reinterpret_cast<const float*>(ot) + row * kOutLd + kPer * cc;
+      float o[kPer];
+#pragma unroll
+      for (int q = 0; q < kPer / 2; ++q) {
+        const int pr = p0 + q;
+        const float a0 = src[2 * q], a1 = src[2 * q + 1];
+        float sn, cs;
+        sincos_rev(ri[5 * row + 2 + a.rope.axis[pr]], a.rope.rev[pr], &sn, &cs);
+        // pair (a0, a1) -> (a0 cos - a1 sin, a0 sin + a1 cos)
+        o[2 * q] = a0 * cs - a1 * sn;
+        o[2 * q + 1] = a0 * sn + a1 * cs;
+      }
+      if constexpr (kBf16) {
+        v = uint4{pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
+      } else {
+        v = uint4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                  __float_as_uint(o[3])};
+      }
+    }
+    *reinterpret_cast<uint4*>(dst) = v;
+  }
 }
 
 template <typename T>
-void launch_t(const AppendArgs& a, int tm, hipStream_t s) {
-  switch (tm) {
-    case 160: launch_tm<T, 160>(a, s); break;
-    case 128: launch_tm<T, 128>(a, s); break;
-    case 96: launch_tm<T, 96>(a, s); break;
-    case 64: launch_tm<T, 64>(a, s); break;
-    default: launch_tm<T, 32>(a, s); break;
+void launch_t(const AppendArgs& a, int groups, int nrb, hipStream_t s) {
+  const dim3 grid(groups), block(kThreads);
+  switch (nrb) {
+    case 5: hipLaunchKernelGGL((append_kernel<T, 5>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((append_kernel<T, 4>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((append_kernel<T, 3>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((append_kernel<T, 2>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((append_kernel<T, 1>), grid, block, 0, s, a); break;
   }
 }
 
 }  // namespace
 
-// Tile height: one workgroup fits a compute unit (LDS), so a launch runs in
-// ceil(workgroups / CUs) rounds of one tile each; a tile costs about TM + 32
-// token-rows of work (the weight stream is the fixed part). Pick the TM with
-// the least rounds x (TM + 32).
-int append_tile_rows(int n_tok, int batch, int cus) {
-  int best = 32;
-  int64_t best_cost = -1;
-  for (int tm : {160, 128, 96, 64, 32}) {
-    const int64_t wgs = (int64_t)((n_tok + tm - 1) / tm) * batch;
-    const int64_t rounds = (wgs + cus - 1) / cus;
-    const int64_t cost = rounds * (tm + 32);
-    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = tm; }
-  }
-  return best;
+// Workgroups and row blocks per wave for m rows on `cus` compute units: one
+// workgroup per compute unit while the ranges stay within 160 rows (more
+// workgroups, in rounds, beyond that), but no range below 32 rows, since each
+// workgroup streams the whole weight. A range of r rows is 16-row blocks split
+// over the two row halves: ceil(ceil(r / 16) / 2) blocks per wave.
+int append_plan(int64_t m, int cus, int* nrb) {
+  const int64_t lo = (m + kMaxRows - 1) / kMaxRows;
+  const int64_t groups = std::max<int64_t>(lo, std::min<int64_t>(cus, (m + 31) / 32));
+  const int64_t rows = (m + groups - 1) / groups;
+  *nrb = (int)(((rows + 15) / 16 + 1) / 2);
+  return (int)groups;
 }
 
 hipError_t launch_append(const AppendArgs& a, bool f32, hipStream_t s) {
@@ -275,9 +364,10 @@ hipError_t launch_append(const AppendArgs& a, bool f32, hipStream_t s) {
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  const int tm = append_tile_rows(a.n_tok, a.batch, cus > 0 ? cus : 1);
-  if (f32) launch_t<float>(a, tm, s);
-  else launch_t<bf16_t>(a, tm, s);
+  int nrb = 1;
+  const int groups = append_plan((int64_t)a.batch * a.n_tok, cus > 0 ? cus : 1, &nrb);
+  if (f32) launch_t<float>(a, groups, nrb, s);
+  else launch_t<bf16_t>(a, groups, nrb, s);
   return hipGetLastError();
 }
 

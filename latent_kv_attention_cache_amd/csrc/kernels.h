@@ -56,7 +56,7 @@ struct AttnArgs {
 };
 
 hipError_t launch_append(const AppendArgs& a, bool f32, hipStream_t s);
-int append_tile_rows(int n_tok, int batch, int cus);   // token rows per append workgroup
+int append_plan(int64_t m, int cus, int* nrb);   // append workgroups for m rows; row blocks per wave
 hipError_t launch_qprologue(const QArgs& a, bool f32, hipStream_t s);
 hipError_t launch_latent_attn(const AttnArgs& a, bool f32, hipStream_t s);
 

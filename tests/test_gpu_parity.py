@@ -220,9 +220,11 @@ def test_config5_reduced_rollout():
 
 @pytest.mark.parametrize("batch", [2, 4])
 def test_append_tile_heights(batch):
-    # a 3-frame chunk of 4680 tokens at batch 1, 2, 4, 8 selects append tiles of
-    # 32, 64, 96 and 160 rows (16 one-frame elements: 128); the other tests cover
-    # 32, 128 and 160
+    # The append splits batch x tokens rows into one range per compute unit (at
+    # least 32, at most 160 rows). A 3-frame chunk of 4680 tokens at batch 1, 2,
+    # 4, 8 gives ranges of 32, 37, 73 and 146 rows, i.e. 1, 2, 3 and 5 blocks of
+    # 16 rows per wave (16 one-frame elements: 98 rows, 4 blocks); the other
+    # tests cover 1, 4 and 5
     w = custom(30, 52, window_frames=3, chunk_frames=3, t_first=0, batch=batch)
     r = Run(w)
     r.append(0, 3)
