@@ -11,14 +11,23 @@
 // with the token's (t, h, w) (App. D.3). Folding log2 e into the scale lets the
 // attention kernel use exp2 directly.
 //
-// One workgroup (4 waves) handles 64 tokens of one head (XCD-aware order, see
-// the kernel). The d_model
-// contraction runs as a pipeline of 64-deep stages (kStages buffers, fetched
-// by LDS-DMA kStages-1 stages ahead, one barrier per stage). Wave w computes
-// output columns [32w, 32w+32) of q_h for all 64 tokens; wave 3 therefore holds
-// the rope channels. The absorption GEMM then splits its 2 x 6 output blocks
-// three per wave, and the [64 x 224] result is assembled in LDS and written
-// with 16-byte row stores.
+// Tile: 128 query rows (batch x tokens flattened, so a tile may span two batch
+// elements) x two heads (256 columns of W_Q). Per output the L2 traffic of the
+// projection is (1/128 + 1/256) of the operand bytes. Four waves, one per
+// SIMD: wave (rh, hh) computes rows 64 rh .. 64 rh + 63 and the 128 columns of
+// head hh of the pair with v_mfma_f32_16x16x32_bf16 as out^T = W^T x^T, so that
+// a lane holds four consecutive columns of one row (a RoPE pair sits in one
+// lane). The d_model contraction runs as a 3-stage pipeline of 64-deep slices
+// of x (row-major, chunk-swizzled) and W_Q (row-major, 512-byte rows, chunk c
+// of row k at position c ^ 2 t(k), t(k) = (k & 3) | bit3(k) << 2, so that a
+// transposed operand read of 32 lanes, rows k0 .. k0+3 and k0+8 .. k0+11,
+// covers all 64 banks once), fetched by LDS-DMA two stages ahead; each wave
+// issues its share of the next loads between its MFMAs.
+//
+// Epilogue, per wave and in registers: RoPE on the 32 rope columns and their
+// store; q_nope goes to LDS as bf16, and q_lat^T = W_K_up[h] q_nope^T by MFMA
+// with the W_K_up rows (contiguous in the contraction index) read straight
+// from global memory; results are stored 8 bytes per lane.
 #include "device_common.h"
 #include "kernels.h"
 #include "staging.h"
@@ -26,178 +35,282 @@
 namespace vmla {
 namespace {
 
-constexpr int kTok = 64;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsT = 128;                       // query rows per workgroup
+constexpr int kNRB = 4;                           // 16-row blocks per wave
+constexpr int kHeadsT = 2;                        // heads per workgroup
+constexpr int kColsT = kHeadsT * kDHead;          // 256 columns of W_Q
+constexpr int kCB = kDHead / 16;                  // 8 column blocks per wave
+constexpr int kXElems = kRowsT * kStageK;         // x slice of a stage
+constexpr int kXLoads = kXElems * 2 / 1024;       // 16 wave-wide 1 KB loads
+constexpr int kWElems = kStageK * kColsT;         // W_Q slice of a stage
+constexpr int kWLoads = kWElems * 2 / 1024;       // 32
+constexpr int kStageElems = kXElems + kWElems;
 constexpr int kStages = 3;
-constexpr int kAElems = kTok * kStageK;                 // 4096
-constexpr int kBElems = kStageK * kDHead;               // 8192
-constexpr int kStageElems = kAElems + kBElems;
-constexpr int kALoads = kAElems * 2 / 1024;             // 8
-constexpr int kBLoads = kBElems * 2 / 1024;             // 16
-constexpr int kLoadsPerWave = (kALoads + kBLoads) / kWaves;   // 6
-constexpr int kQnLd = kDNope + 8;      // q_nope staging row
-constexpr int kOutLd = kRow + 8;       // output tile row
-constexpr int kEpiElems = kTok * kQnLd + kTok * kOutLd;
-constexpr int kSmemElems = kStages * kStageElems > kEpiElems ? kStages * kStageElems : kEpiElems;
-static_assert((kALoads + kBLoads) % kWaves == 0, "stage loads must split evenly");
+constexpr int kXPerWave = kXLoads / kWaves;       // 4
+constexpr int kWPerWave = kWLoads / kWaves;       // 8
+constexpr int kL = kXPerWave + kWPerWave;         // loads per wave per stage
+constexpr int kWChunks = kColsT / 8;              // 32 chunks per W_Q tile row
+constexpr int kQnLd = kDNope + 8;                 // q_nope staging row (bf16)
+static_assert(kXLoads % kWaves == 0 && kWLoads % kWaves == 0, "loads split evenly");
+static_assert(kStages * kStageElems * 2 <= 160 * 1024, "LDS budget");
+static_assert(kWaves * 64 * kQnLd <= kStages * kStageElems, "epilogue staging fits");
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// chunk permutation mask of W_Q tile row k (an involution on the chunks of a row)
+__device__ __forceinline__ int swz_q(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
 
 template <typename T>
 __global__ __launch_bounds__(kThreads)
 void qprologue_kernel(QArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t smem[kSmemElems];
-  bf16_t* qn = smem;                       // [kTok][kQnLd]   (after the K loop)
-  bf16_t* ot = smem + kTok * kQnLd;        // [kTok][kOutLd]
+  __shared__ __attribute__((aligned(16))) bf16_t smem[kStages * kStageElems];
 
-  // Workgroups are dispatched round-robin over the 8 XCDs; id = 8 (H q + h) + x8
-  // keeps all heads of token block 8 q + x8 on XCD x8, so that block's x rows
-  // are fetched into that XCD's L2 once and shared by its heads.
-  const int ntb = (a.n_q + kTok - 1) / kTok;
+  // Workgroups are dispatched round-robin over the 8 XCDs; id = 8 (HP q + hp) + x8
+  // keeps every head pair of row tile 8 q + x8 on XCD x8, so that tile's x rows
+  // are fetched into that XCD's L2 once and shared by its head pairs.
+  const int64_t M = (int64_t)a.batch * a.n_q;
+  const int n_rt = (int)((M + kRowsT - 1) / kRowsT);
+  const int n_hp = (a.n_heads + kHeadsT - 1) / kHeadsT;
   const int x8 = blockIdx.x & 7;
   const int rest = blockIdx.x >> 3;
-  const int h = rest % a.n_heads;
-  const int tb = 8 * (rest / a.n_heads) + x8;
-  if (tb >= ntb) return;                   // whole workgroup: no barrier is skipped
+  const int hp = rest % n_hp;
+  const int rt = 8 * (rest / n_hp) + x8;
+  if (rt >= n_rt) return;                   // whole workgroup: no barrier is skipped
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int half = lane >> 5;
-  const int b = blockIdx.z;
-  const int tok0 = tb * kTok;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  const int rh = wv >> 1, hh = wv & 1;      // wave-uniform
+  const int64_t m0 = (int64_t)rt * kRowsT;
+  const int rows = (int)min<int64_t>(kRowsT, M - m0);
   const int wq_ld = a.n_heads * kDHead;
-  const T* x = static_cast<const T*>(a.x) + (size_t)b * a.n_q * a.d_model;
-  const T* wq = static_cast<const T*>(a.w_q) + (size_t)h * kDHead;
+  const int col0 = kColsT * hp;             // first W_Q column of the pair
+  const T* xw = static_cast<const T*>(a.x) + m0 * a.d_model;
+  const T* wq = static_cast<const T*>(a.w_q) + col0;
   const int nst = a.d_model / kStageK;
 
-  // Wave w issues loads n = w, w + 4, ... of every stage. For bf16 sources the
-  // lane offsets of those loads are computed once; a stage only moves the
-  // scalar source pointer and the LDS destination.
-  uint32_t voff[kLoadsPerWave];
+  // Load offsets (bytes; bf16 sources). x load n = 4 wv + i moves rows
+  // 8n .. 8n+7 of the tile (clamped to the last row); W load n = 8 wv + i moves
+  // rows 2n, 2n+1 of the W_Q slice. A head pair with one head (odd head count)
+  // reads the existing head's columns in place of the missing one.
+  uint32_t voff[kL];
   if constexpr (std::is_same_v<T, bf16_t>) {
 #pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i) {
-      const int n = wave + kWaves * i;
-      voff[i] = n < kALoads ? stage_a_voff(a.d_model, tok0, a.n_q, n, lane)
-                            : stage_b_voff<kDHead>(wq_ld, n - kALoads, lane);
+    for (int i = 0; i < kXPerWave; ++i) voff[i] = stage_a_voff(a.d_model, 0, rows, kXPerWave * wv + i, lane);
+#pragma unroll
+    for (int i = 0; i < kWPerWave; ++i) {
+      const int q = 64 * (kWPerWave * wv + i) + lane, k = q / kWChunks, cp = q - k * kWChunks;
+      int c = cp ^ swz_q(k);
+      if (col0 + 8 * c >= wq_ld) c -= kDHead / 8;
+      voff[kXPerWave + i] = (uint32_t)(k * wq_ld + 8 * c) * 2u;
     }
   }
-  auto issue = [&](int s, int i0 = 0, int i1 = kLoadsPerWave) {   // this wave's loads i0 <= i < i1
-    bf16_t* st = smem + (s % kStages) * kStageElems;
-    const int k0 = s * kStageK;
+  auto issue = [&](int sb, int sd, int i0, int i1) {   // loads i0 <= i < i1: data of stage sd, buffer of sb
+    bf16_t* st = smem + (sb % kStages) * kStageElems;
+    const int k0 = sd * kStageK;
 #pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i) {
+    for (int i = 0; i < kL; ++i) {
       if (i < i0 || i >= i1) continue;
-      const int n = wave + kWaves * i;
-      if constexpr (std::is_same_v<T, bf16_t>) {
-        if (n < kALoads) dma16_lds(x + k0, voff[i], lds_u32(st + 512 * n));
-        else dma16_lds(wq + (size_t)k0 * wq_ld, voff[i], lds_u32(st + 512 * n));
+      if (i < kXPerWave) {
+        const int n = kXPerWave * wv + i;
+        if constexpr (std::is_same_v<T, bf16_t>) dma16_lds(xw + k0, voff[i], lds_u32(st + 512 * n));
+        else stage_a_load<T>(st, xw, a.d_model, 0, rows, k0, n, lane);
       } else {
-        if (n < kALoads) stage_a_load<T>(st, x, a.d_model, tok0, a.n_q, k0, n, lane);
-        else stage_b_load<T, kDHead>(st + kAElems, wq, wq_ld, 0, k0, n - kALoads, lane);
+        const int n = kWPerWave * wv + (i - kXPerWave);
+        bf16_t* dst = st + kXElems + 512 * n;
+        if constexpr (std::is_same_v<T, bf16_t>) {
+          dma16_lds(wq + (size_t)k0 * wq_ld, voff[i], lds_u32(dst));
+        } else {
+          const int q = 64 * n + lane, k = q / kWChunks, cp = q - k * kWChunks;
+          int c = cp ^ swz_q(k);
+          if (col0 + 8 * c >= wq_ld) c -= kDHead / 8;
+          *reinterpret_cast<uint4*>(dst + 8 * lane) = load8_bf16<T>(wq + (size_t)(k0 + k) * wq_ld + 8 * c);
+        }
       }
     }
   };
 
-  for (int s = 0; s < kStages - 1 && s < nst; ++s) issue(s);
+  // Operand offsets (elements, relative to a stage's tiles).
+  // x (B operand): lane (j, g) of block rb = row 64 rh + 16 rb + j, chunk 4 kk + g.
+  int a_off[kNRB][2];
+#pragma unroll
+  for (int rb = 0; rb < kNRB; ++rb) {
+    const int row = 64 * rh + 16 * rb + j;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) a_off[rb][kk] = 64 * row + 8 * ((4 * kk + g) ^ swz_a(row));
+  }
+  // W_Q (A operand) by ds_read_b64_tr_b16: lane j of group g points at row
+  // 32 kk + 8 g + j/4 (+4 for the upper half) and columns col + 4 (j%4) .. +3
+  // of column block cb of head hh. The swizzle bits of that row (bits 0, 1, 3)
+  // depend on the lane only.
+  int b_off[kCB];
+  {
+    const int k = 8 * g + (j >> 2);
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      const int c = 2 * (kCB * hh + cb) + ((j & 3) >> 1);
+      b_off[cb] = k * kColsT + 8 * (c ^ swz_q(k)) + 4 * (j & 1);
+    }
+  }
 
-  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  for (int s = 0; s < kStages - 1 && s < nst; ++s) issue(s, s, 0, kL);
+
+  f32x4 acc[kNRB][kCB];
+#pragma unroll
+  for (int rb = 0; rb < kNRB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Stage s: two 32-deep steps of 4 x 8 MFMAs; the next x fragment and the W
+  // fragments of the second step are read while the current MFMAs run. Past
+  // the last stage the loads repeat the last stage into a buffer that is not
+  // read again, so the stage body has no branch; every iteration issues one
+  // stage, so min(kStages - 2, nst - 1) stages are in flight behind stage s.
+  const int behind = min(kStages - 2, nst - 1);
   for (int s = 0; s < nst; ++s) {
-    wait_stages<kLoadsPerWave>(min(kStages - 2, nst - 1 - s));   // stage s has landed
+    wait_stages<kL>(behind);                                    // stage s has landed
     __syncthreads();
-    const bool more = s + kStages - 1 < nst;                      // loads into the buffer of stage s-1
-    const bf16_t* A = smem + (s % kStages) * kStageElems;
-    const bf16_t* B = A + kAElems;
+    const int sn = min(s + kStages - 1, nst - 1);
+    const bf16_t* X = smem + (s % kStages) * kStageElems;
+    const bf16_t* W = X + kXElems;
+    auto read_w = [&](int kk, bf16x8* bw) {
 #pragma unroll
-    for (int ks = 0; ks < kStageK / 16; ++ks) {
-      const bf16x8 bv = b_frag<kDHead>(B, ks, 32 * wave, lane);
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const bf16x8 av = a_frag(A, 32 * tt + (lane & 31), ks, half);
-        acc[tt] = mfma32(av, bv, acc[tt]);
+      for (int cb = 0; cb < kCB; ++cb) {
+        const bf16_t* p = W + b_off[cb] + 32 * kk * kColsT;
+        const bf16x4 lo = lds_tr4(p);
+        const bf16x4 hi = lds_tr4(p + 4 * kColsT);
+        bw[cb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
-      // the wave's next-stage loads, spread over the k-steps so that their
-      // issue overlaps the MFMAs already in flight
-      if (more) issue(s + kStages - 1, (kLoadsPerWave * ks) / 4, (kLoadsPerWave * (ks + 1)) / 4);
-    }
-  }
-  __syncthreads();
-
-  // Register r of lane l: token row 32*tt + 8(r/4) + 4*half + r%4, column 32*wave + l%32.
-  const int col = lane & 31;
-  if (wave == 3) {
-    const int pair = col >> 1;
-    const bool odd = col & 1;
-    const float rev = a.rope.rev[pair];
-    const int axis = a.rope.axis[pair];
+    };
+    bf16x8 b0[kCB], b1[kCB];
+    read_w(0, b0);
+    bf16x8 av = lds_row8(X + a_off[0][0]);
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * tt + 8 * (r >> 2) + 4 * half + (r & 3);
-        const float v = acc[tt][r];
-        const float partner = swap_adjacent(v);
-        const int n = min(tok0 + row, a.n_q - 1);
-        int n_in, ww;
-        const int f = div_small(n, a.tokens_per_frame, a.inv_tokens_per_frame, &n_in);
-        const int hh = div_small(n_in, a.grid_w, a.inv_grid_w, &ww);
-        const int pos = axis == 0 ? a.t_first + f : (axis == 1 ? hh : ww);
-        float sn, cs;
-        sincos_rev(pos, rev, &sn, &cs);
-        const float rot = odd ? partner * sn + v * cs : v * cs - partner * sn;
-        ot[row * kOutLd + kDC + col] = f2bf(rot * a.qscale);
-      }
-    }
-  } else {
+      for (int rb = 0; rb < kNRB; ++rb) {
+        const int q = kk * kNRB + rb;
+        bf16x8 an = av;
+        if (q + 1 < 2 * kNRB) an = lds_row8(X + a_off[(q + 1) % kNRB][(q + 1) / kNRB]);
+        if (kk == 0 && rb == kNRB - 1) read_w(1, b1);
+        issue(s + kStages - 1, sn, q * kL / (2 * kNRB), (q + 1) * kL / (2 * kNRB));
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * tt + 8 * (r >> 2) + 4 * half + (r & 3);
-        qn[row * kQnLd + 32 * wave + col] = f2bf(acc[tt][r]);
+        for (int cb = 0; cb < kCB; ++cb)
+          acc[rb][cb] = mfma16(kk == 0 ? b0[cb] : b1[cb], av, acc[rb][cb]);
+        av = an;
       }
     }
   }
-  __syncthreads();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // the trailing loads have landed
+  __syncthreads();                                     // the stage buffers are free
 
-  // q_lat[64][192] = q_nope[64][96] @ W_K_up[h]^T: B[k = n][col = c] = W_K_up[h][c][n]
+  // ---- epilogue. Register r of acc[rb][cb] in lane (j, g): row 64 rh + 16 rb + j
+  // of the tile, column 16 cb + 4 g + r of head h.
+  const int h = kHeadsT * hp + hh;
+  if (h >= a.n_heads) return;                         // no barrier follows
+  // W_K_up[h] fragments of the absorption, A operand: lane (j, g) of column
+  // tile ct holds row 16 ct + j, n = 32 ks + 8 g .. +7. The first six tiles are
+  // requested now and land during the RoPE and q_nope work; each register set
+  // is refilled with tile ct + 6 once tile ct has been consumed.
+  constexpr int kCT = kDC / 16;                        // 12 column tiles of q_lat
+  constexpr int kKS = kDNope / 32;                     // 3 steps
   const T* wku = static_cast<const T*>(a.w_k_up) + (size_t)h * kDC * kDNope;
+  auto load_wk = [&](int ct, bf16x8 (&w)[kKS]) {
 #pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int tile = wave + 4 * i;         // 0..11
-    const int tt = tile / 6, ct = tile % 6;
-    f32x16 q = f32x16{};
+    for (int ks = 0; ks < kKS; ++ks)
+      w[ks] = __builtin_bit_cast(bf16x8, load8_bf16<T>(wku + (size_t)(16 * ct + j) * kDNope + 32 * ks + 8 * g));
+  };
+  bf16x8 wk[kCT / 2][kKS];
 #pragma unroll
-    for (int ks = 0; ks < kDNope / 16; ++ks) {
-      const bf16x8 av = lds_row8(&qn[(32 * tt + (lane & 31)) * kQnLd + ks * 16 + 8 * half]);
-      const uint4 braw = load8_bf16<T>(wku + (size_t)(32 * ct + (lane & 31)) * kDNope + ks * 16 + 8 * half);
-      q = mfma32(av, __builtin_bit_cast(bf16x8, braw), q);
-    }
+  for (int c = 0; c < kCT / 2; ++c) load_wk(c, wk[c]);
+  int64_t qrow[kNRB];                                  // Qhat row index, -1 past the last row
+  int pos[kNRB][3];                                    // (t, h, w) of each row
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 32 * tt + 8 * (r >> 2) + 4 * half + (r & 3);
-      ot[row * kOutLd + 32 * ct + col] = f2bf(q[r] * a.qscale);
+  for (int rb = 0; rb < kNRB; ++rb) {
+    const int64_t m = m0 + 64 * rh + 16 * rb + j;
+    const int64_t mc = m < M ? m : M - 1;
+    const int b = (int)(mc / a.n_q);
+    const int n = (int)(mc - (int64_t)b * a.n_q);
+    int n_in, ww;
+    const int f = div_small(n, a.tokens_per_frame, a.inv_tokens_per_frame, &n_in);
+    const int hpos = div_small(n_in, a.grid_w, a.inv_grid_w, &ww);
+    pos[rb][0] = a.t_first + f;
+    pos[rb][1] = hpos;
+    pos[rb][2] = ww;
+    qrow[rb] = m < M ? ((int64_t)b * a.n_heads + h) * a.n_q + n : -1;
+  }
+  uint16_t* qhat = a.qhat;
+  // RoPE: columns 96 + 16 (cb - 6) + 4 g + r, pairs 8 (cb - 6) + 2 g + {0, 1}
+#pragma unroll
+  for (int cb = kDNope / 16; cb < kCB; ++cb) {
+#pragma unroll
+    for (int rb = 0; rb < kNRB; ++rb) {
+      const f32x4 v = acc[rb][cb];
+      float o[4];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int pr = 8 * (cb - kDNope / 16) + 2 * g + q;
+        float sn, cs;
+        sincos_rev(pos[rb][a.rope.axis[pr]], a.rope.rev[pr], &sn, &cs);
+        o[2 * q] = v[2 * q] * cs - v[2 * q + 1] * sn;
+        o[2 * q + 1] = v[2 * q] * sn + v[2 * q + 1] * cs;
+      }
+      if (qrow[rb] >= 0) {
+        const int col = kDC + 16 * (cb - kDNope / 16) + 4 * g;
+        *reinterpret_cast<uint2*>(qhat + qrow[rb] * kRow + col) =
+            uint2{pack2(o[0] * a.qscale, o[1] * a.qscale), pack2(o[2] * a.qscale, o[3] * a.qscale)};
+      }
     }
   }
-  __syncthreads();
-
-  uint16_t* dst = a.qhat + (((size_t)b * a.n_heads + h) * a.n_q + tok0) * kRow;
+  // q_nope of this wave's 64 rows to LDS: qn[row][0..95] (bf16)
+  bf16_t* qn = smem + wv * 64 * kQnLd;
 #pragma unroll
-  for (int i = 0; i < (kTok * kRow / 8 + kThreads - 1) / kThreads; ++i) {
-    const int c = tid + i * kThreads;
-    if (c < kTok * kRow / 8) {
-      const int row = c / (kRow / 8), cc = c % (kRow / 8);
-      if (tok0 + row < a.n_q)
-        *reinterpret_cast<uint4*>(dst + (size_t)row * kRow + 8 * cc) =
-            *reinterpret_cast<const uint4*>(&ot[row * kOutLd + 8 * cc]);
+  for (int rb = 0; rb < kNRB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < kDNope / 16; ++cb) {
+      const f32x4 v = acc[rb][cb];
+      *reinterpret_cast<uint2*>(&qn[(16 * rb + j) * kQnLd + 16 * cb + 4 * g]) =
+          uint2{pack2(v[0], v[1]), pack2(v[2], v[3])};
     }
+  // q_lat^T[c][row] = sum_n W_K_up[h][c][n] q_nope[row][n]: A = W_K_up rows,
+  // B = q_nope rows from LDS (lane (j, g): row 16 rb + j, n = 32 ks + 8 g .. +7).
+  bf16x8 qb[kNRB][kKS];
+#pragma unroll
+  for (int rb = 0; rb < kNRB; ++rb)
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks)
+      qb[rb][ks] = lds_row8(&qn[(16 * rb + j) * kQnLd + 32 * ks + 8 * g]);
+#pragma unroll
+  for (int ct = 0; ct < kCT; ++ct) {
+    bf16x8 (&w)[kKS] = wk[ct % (kCT / 2)];
+#pragma unroll
+    for (int rb = 0; rb < kNRB; ++rb) {
+      f32x4 ql = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) ql = mfma16(w[ks], qb[rb][ks], ql);
+      // register r: c = 16 ct + 4 g + r of row 16 rb + j
+      if (qrow[rb] >= 0)
+        *reinterpret_cast<uint2*>(qhat + qrow[rb] * kRow + 16 * ct + 4 * g) =
+            uint2{pack2(ql[0] * a.qscale, ql[1] * a.qscale), pack2(ql[2] * a.qscale, ql[3] * a.qscale)};
+    }
+    if (ct + kCT / 2 < kCT) load_wk(ct + kCT / 2, w);
   }
 }
 
 }  // namespace
 
 hipError_t launch_qprologue(const QArgs& a, bool f32, hipStream_t s) {
-  const int ntb = (a.n_q + kTok - 1) / kTok;
-  dim3 grid(8 * a.n_heads * ((ntb + 7) / 8), 1, a.batch);
+  const int64_t M = (int64_t)a.batch * a.n_q;
+  const int64_t n_rt = (M + kRowsT - 1) / kRowsT;
+  const int n_hp = (a.n_heads + kHeadsT - 1) / kHeadsT;
+  const dim3 grid((unsigned)(8 * n_hp * ((n_rt + 7) / 8)));
   if (f32) hipLaunchKernelGGL(qprologue_kernel<float>, grid, dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL(qprologue_kernel<bf16_t>, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
