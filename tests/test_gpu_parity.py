@@ -76,6 +76,21 @@ def test_heads_sharing_a_workgroup(grid_h, grid_w):
     compare(out[0], r.reference(), f"n_q={w.n_q}", per_head_axis=1)
 
 
+@pytest.mark.parametrize("grid_h,grid_w,n_heads,d_model,batch", [
+    (5, 13, 3, 640, 1),     # 65 queries, odd head count: a query-prologue head pair with one head
+    (10, 29, 5, 1024, 2),   # 290 queries per element, row tiles across the batch boundary
+    (4, 6, 1, 64, 3),       # one head, a single 64-deep stage of the contraction
+])
+def test_other_head_counts_and_model_widths(grid_h, grid_w, n_heads, d_model, batch):
+    w = custom(grid_h, grid_w, window_frames=3, chunk_frames=1, t_first=2,
+               batch=batch).with_(n_heads=n_heads, d_model=d_model)
+    r = Run(w)
+    out = _sync_np(r.chunk_step())
+    for b in range(batch):
+        compare(out[b], r.reference(b=b), f"H={n_heads} D={d_model} b={b}", per_head_axis=1)
+        compare(r.cache_rows(0, 3, b=b), r.append_reference(0, 3, b=b), f"H={n_heads} D={d_model} cache b={b}")
+
+
 def test_ring_wrap_and_nan_poisoned_prefix():
     # The ring starts as NaN: attention may only read the valid prefix while it fills.
     w = custom(4, 6, window_frames=3, chunk_frames=1, t_first=0)
