@@ -46,6 +46,11 @@ Readings of points the pages leave open (each is also listed in the design doc):
   * Token n of a frame is at (h, w) = (n // grid_w, n % grid_w); t is the
     absolute latent-frame index from 0.
   * Ring slot of token n of frame t: (t mod W) * T + n.
+  * Long-horizon context ([PL] App. D.4-D.5): the sink frames are the first
+    ones (frame 0 for one sink frame); the active context is the sink frames
+    followed by the most recent window frames, numbered 0, 1, 2, ... oldest
+    first, and those local numbers are the temporal RoPE coordinate of keys
+    and queries (``chunk_attention_reindexed_reference``).
 PARITY UNPINNED: final output values at the benchmark shapes (the pages print
 no worked example); they are pinned only through the identities checked in
 tests/test_oracle_pins.py.
@@ -276,6 +281,66 @@ def chunk_attention_reference(w, wts, x_of_frame, query_tokens=None):
                              w.rope_pairs)
     scale = 1.0 / np.sqrt(w.d_nope + w.d_rope)
     return attention_explicit(q_nope, q_rope, k_nope, k_r, v, scale)
+
+
+# ---------------------------------------------------------------------------
+# Long-horizon context: sink frame + sliding window, RoPE at read time
+# ([PL] App. D.4 "Chunk-Causal Sliding-Window Attention", App. D.5 "Long-Horizon
+# RoPE Re-indexing", App. E "RoPE branch")
+# ---------------------------------------------------------------------------
+
+def active_context(t_first: int, chunk_frames: int, window: int, sink: int):
+    """(absolute t, local t) of every frame of the active context once the chunk
+    is appended, oldest first. The first ``sink`` frames stay for good; of the
+    others the ``window`` most recent stay (FIFO eviction, [PL] App. D.4). The
+    context is numbered 0, 1, 2, ... in that order: the frames get local
+    temporal coordinates inside the sink-plus-window context ([PL] App. D.5)."""
+    t_end = t_first + chunk_frames
+    frames = list(range(min(sink, t_end))) + list(range(max(sink, t_end - window), t_end))
+    return [(t, i) for i, t in enumerate(frames)]
+
+
+def chunk_attention_reindexed_reference(w, wts, x_of_frame, query_tokens=None):
+    """Reference output of one chunk step with read-time RoPE re-indexing.
+
+    The cached positional keys are kept before RoPE (x W_KR); at attention time
+    every frame of the active context (``active_context``) gets its local
+    temporal coordinate, and the cached keys and the query chunk are rotated
+    with it ([PL] App. D.5; App. E "RoPE branch"). Everything else is the
+    definition of ``chunk_attention_reference``: explicit per-head K/V, softmax
+    over every key of the context, no mask. Same arguments and result layout.
+    """
+    omega = rope_frequencies(w.rope_pairs, w.rope_axis_dims, w.rope_theta)
+    ctx = active_context(w.t_first, w.chunk_frames, w.window_frames, w.sink_frames)
+    local = dict(ctx)
+    cs, krs = [], []
+    for t, tl in ctx:
+        x = np.asarray(x_of_frame(t), dtype=F64)
+        cs.append(x @ np.asarray(wts["w_down"], dtype=F64))
+        k_raw = x @ np.asarray(wts["w_kr"], dtype=F64)            # stored before RoPE
+        krs.append(rope3d(k_raw, frame_positions(tl, w.grid_h, w.grid_w), omega, w.rope_pairs))
+    c = np.concatenate(cs, axis=0)
+    k_r = np.concatenate(krs, axis=0)
+    k_nope, v = reconstruct_heads(c, wts["w_k_up"], wts["w_v_up"])
+
+    chunk = list(range(w.t_first, w.t_first + w.chunk_frames))
+    xq = np.concatenate([np.asarray(x_of_frame(t), dtype=F64) for t in chunk], axis=0)
+    pos_q = np.concatenate([frame_positions(local[t], w.grid_h, w.grid_w) for t in chunk], axis=0)
+    if query_tokens is not None:
+        query_tokens = np.asarray(query_tokens)
+        xq, pos_q = xq[query_tokens], pos_q[query_tokens]
+    q_nope, q_rope = queries(xq, wts["w_q"], pos_q, omega, w.n_heads, w.d_nope, w.d_rope,
+                             w.rope_pairs)
+    scale = 1.0 / np.sqrt(w.d_nope + w.d_rope)
+    return attention_explicit(q_nope, q_rope, k_nope, k_r, v, scale)
+
+
+def append_reference_raw(w, wts, x_chunk):
+    """Cache rows [n_frames * T, d_c + d_rope] = [c | x W_KR] when the
+    positional keys are cached before RoPE ([PL] App. D.5)."""
+    x = np.asarray(x_chunk, dtype=F64)
+    return np.concatenate([x @ np.asarray(wts["w_down"], dtype=F64),
+                           x @ np.asarray(wts["w_kr"], dtype=F64)], axis=1)
 
 
 def append_reference(w, wts, x_chunk, t_first, n_frames):

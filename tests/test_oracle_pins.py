@@ -347,6 +347,116 @@ def test_absolute_rotation_equals_window_local_rotation():
     assert rel(local, absolute) < 1e-12
 
 
+# ---------------------------------------------------------------------------
+# Long-horizon context: sink frame + window, RoPE at read time ([PL] App. D.4-D.5)
+# ---------------------------------------------------------------------------
+
+def test_reindexed_context_without_eviction_is_the_whole_history():
+    # Before any frame is evicted the context is frames 0 .. t_end - 1 and their
+    # local coordinates are the absolute ones: plain attention over all frames.
+    w = custom(2, 3, window_frames=6, chunk_frames=3, t_first=2,
+               dtype="f32").with_(sink_frames=1, rope_at_read=True)
+    wt = weights(w)
+    xs = {t: x_frame(w, t) for t in range(0, 5)}
+    re = orc.chunk_attention_reindexed_reference(w, wt, lambda t: xs[t])
+    plain = orc.chunk_attention_reference(
+        w.with_(window_frames=5, sink_frames=0, rope_at_read=False), wt, lambda t: xs[t])
+    assert rel(re, plain) < 1e-12
+
+
+def test_reindexed_window_without_sink_equals_append_time_rotation():
+    # Without a sink the local coordinates are a uniform shift of the absolute
+    # ones, so the scores equal those of keys rotated when they were cached.
+    w = custom(2, 3, window_frames=4, chunk_frames=2, t_first=7, dtype="f32")
+    wt = weights(w)
+    xs = {t: x_frame(w, t) for t in range(5, 9)}
+    plain = orc.chunk_attention_reference(w, wt, lambda t: xs[t])
+    re = orc.chunk_attention_reindexed_reference(w.with_(rope_at_read=True), wt, lambda t: xs[t])
+    assert rel(re, plain) < 1e-12
+
+
+def test_reindexed_sink_context_brute_force_tiny():
+    # One sink frame (frame 0), a window of 2 frames, chunk = frame 4: the
+    # context is frames 0, 3, 4 at local t 0, 1, 2. Every sum a scalar loop.
+    D, H, dn, dr, dc, dv = 3, 2, 2, 4, 3, 2
+    pairs, dims = (1, 1, 0), (2, 2, 2)
+    w = custom(1, 2, window_frames=2, chunk_frames=1, t_first=4, dtype="f32").with_(
+        d_model=D, n_heads=H, d_nope=dn, d_rope=dr, d_c=dc, d_v=dv, rope_pairs=pairs,
+        rope_axis_dims=dims, sink_frames=1, rope_at_read=True)
+    wt = {"w_q": RNG.standard_normal((D, H * (dn + dr))), "w_down": RNG.standard_normal((D, dc)),
+          "w_kr": RNG.standard_normal((D, dr)), "w_k_up": RNG.standard_normal((H, dc, dn)),
+          "w_v_up": RNG.standard_normal((H, dc, dv))}
+    xs = {t: RNG.standard_normal((2, D)) for t in range(5)}
+    om = orc.rope_frequencies(pairs, dims)
+    scale = 1 / math.sqrt(dn + dr)
+
+    def mv(x, W, j):
+        return sum(x[i] * W[i][j] for i in range(len(x)))
+
+    def rot(vec, t, h):
+        ang = [t * om[0], h * om[1]]
+        o = list(vec)
+        for j in range(2):
+            a, b = vec[2 * j], vec[2 * j + 1]
+            o[2 * j] = a * math.cos(ang[j]) - b * math.sin(ang[j])
+            o[2 * j + 1] = a * math.sin(ang[j]) + b * math.cos(ang[j])
+        return o
+
+    keys = [(xs[t][n], tl, n // 2) for t, tl in ((0, 0), (3, 1), (4, 2)) for n in range(2)]
+    ref = np.zeros((2, H, dv))
+    for qi in range(2):
+        qfull = [mv(xs[4][qi], wt["w_q"], j) for j in range(H * (dn + dr))]
+        for h in range(H):
+            qn = qfull[h * (dn + dr):h * (dn + dr) + dn]
+            qr = rot(qfull[h * (dn + dr) + dn:(h + 1) * (dn + dr)], 2, qi // 2)
+            s, vals = [], []
+            for xk, tl, hk in keys:
+                c = [mv(xk, wt["w_down"], j) for j in range(dc)]
+                kr = rot([mv(xk, wt["w_kr"], j) for j in range(dr)], tl, hk)
+                kn = [sum(c[i] * wt["w_k_up"][h][i][j] for i in range(dc)) for j in range(dn)]
+                vv = [sum(c[i] * wt["w_v_up"][h][i][j] for i in range(dc)) for j in range(dv)]
+                s.append(scale * (sum(qn[j] * kn[j] for j in range(dn)) +
+                                  sum(qr[j] * kr[j] for j in range(dr))))
+                vals.append(vv)
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            z = sum(e)
+            for j in range(dv):
+                ref[qi, h, j] = sum(e[k] / z * vals[k][j] for k in range(len(keys)))
+    out = orc.chunk_attention_reindexed_reference(w, wt, lambda t: xs[t])
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_reindexing_sees_relative_coordinates_only(monkeypatch):
+    # After eviction: adding a constant to every local coordinate leaves the
+    # output unchanged (RoPE's relative invariance), while keeping the window
+    # frames at their absolute t next to the sink at 0 changes it.
+    w = custom(2, 3, window_frames=3, chunk_frames=2, t_first=9,
+               dtype="f32").with_(sink_frames=1, rope_at_read=True)
+    wt = weights(w)
+    xs = {t: x_frame(w, t) for t in range(0, 11)}
+    base = orc.chunk_attention_reindexed_reference(w, wt, lambda t: xs[t])
+    orig = orc.active_context
+    monkeypatch.setattr(orc, "active_context", lambda *a: [(t, tl + 5) for t, tl in orig(*a)])
+    shifted = orc.chunk_attention_reindexed_reference(w, wt, lambda t: xs[t])
+    monkeypatch.setattr(orc, "active_context", lambda *a: [(t, t) for t, _ in orig(*a)])
+    absolute = orc.chunk_attention_reindexed_reference(w, wt, lambda t: xs[t])
+    assert rel(shifted, base) < 1e-12
+    assert rel(absolute, base) > 1e-3
+
+
+def test_append_reference_raw_rows():
+    w = custom(2, 3, window_frames=4, chunk_frames=2, t_first=7, dtype="f32")
+    wt = weights(w)
+    x = np.concatenate([x_frame(w, t) for t in (7, 8)])
+    raw = orc.append_reference_raw(w, wt, x)
+    rot = orc.append_reference(w, wt, x, 7, 2)
+    assert rel(raw[:, :w.d_c], rot[:, :w.d_c]) < 1e-15
+    pos = np.concatenate([orc.frame_positions(t, 2, 3) for t in (7, 8)])
+    om = orc.rope_frequencies(w.rope_pairs, w.rope_axis_dims, w.rope_theta)
+    assert rel(orc.rope3d(raw[:, w.d_c:], pos, om, w.rope_pairs), rot[:, w.d_c:]) < 1e-13
+
+
 def test_ring_after_wrap_equals_linear_window_and_slot_order_is_irrelevant():
     w = custom(2, 2, window_frames=3, chunk_frames=1, t_first=0, dtype="f32")
     wt = weights(w)
@@ -444,6 +554,16 @@ def _positions_hw_swapped(t, grid_h, grid_w):
     return p[:, [0, 2, 1]]
 
 
+def _context_absolute(t_first, chunk_frames, window, sink):
+    return [(t, t) for t, _ in _ORIG_CTX(t_first, chunk_frames, window, sink)]
+
+
+def _context_without_sink(t_first, chunk_frames, window, sink):
+    return [(t, i) for i, (t, _) in enumerate(
+        [c for c in _ORIG_CTX(t_first, chunk_frames, window, sink) if c[0] >= sink])]
+
+
+_ORIG_CTX = orc.active_context
 _ORIG_ATT = orc.attention_explicit
 _ORIG_REC = orc.reconstruct_heads
 _ORIG_POS = orc.frame_positions
@@ -452,7 +572,8 @@ PINS = [test_rope_is_complex_rotation, test_attention_matches_torch_sdpa_fp64,
         test_mla_reduces_to_dense_mha_with_selection_up_projections,
         test_mla_equals_dense_mha_with_composed_weights_real_dims,
         test_brute_force_scalar_loops_tiny, test_append_reference_rows_layout,
-        test_frame_positions_token_order, test_absorbed_equals_explicit]
+        test_frame_positions_token_order, test_absorbed_equals_explicit,
+        test_reindexed_sink_context_brute_force_tiny]
 
 
 @pytest.mark.parametrize("name,patch", [
@@ -461,6 +582,8 @@ PINS = [test_rope_is_complex_rotation, test_attention_matches_torch_sdpa_fp64,
     ("wrong softmax scale", ("attention_explicit", _attention_wrong_scale)),
     ("values of the wrong head", ("reconstruct_heads", _reconstruct_transposed_value)),
     ("h and w swapped in positions", ("frame_positions", _positions_hw_swapped)),
+    ("window frames not re-indexed", ("active_context", _context_absolute)),
+    ("sink evicted with the window", ("active_context", _context_without_sink)),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, patch):
     attr, fn = patch

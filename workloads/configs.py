@@ -38,6 +38,8 @@ class Workload:
     rope_pairs: tuple = (6, 5, 5)     # complex pairs on the t, h, w axes
     rope_axis_dims: tuple = (12, 10, 10)
     rope_theta: float = 10000.0
+    sink_frames: int = 0              # latent frames kept for good at the front of the context
+    rope_at_read: bool = False        # k_R cached before RoPE, rotated in the active context
 
     @property
     def tokens_per_frame(self) -> int:
