@@ -30,8 +30,10 @@
  *
  * Token and position convention: token n of a latent frame sits at grid
  * position (h, w) = (n / grid_w, n % grid_w); t is the absolute latent-frame
- * index counted from 0. Ring slot of token n of frame t: (t mod W) * T + n,
- * with T = grid_h * grid_w tokens per frame and W = window_frames.
+ * index counted from 0. T = grid_h * grid_w tokens per frame, W =
+ * window_frames, S = sink_frames (0 or 1). Slot of token n of frame t:
+ * t * T + n for t < S (the sink frame, kept for good), otherwise
+ * (S + (t - S) mod W) * T + n (the ring of the most recent W frames).
  */
 #ifndef VMLA_H
 #define VMLA_H
@@ -43,7 +45,7 @@
 extern "C" {
 #endif
 
-#define VMLA_ABI_VERSION 1
+#define VMLA_ABI_VERSION 2
 
 typedef enum vmla_status {
   VMLA_OK = 0,
@@ -73,9 +75,21 @@ typedef struct vmla_dims {
   float scale;              /* softmax scale applied to the full score, 1/sqrt(d_nope + d_rope) */
 } vmla_dims;
 
-/* Sliding-window ring of cached latent frames ([PL] App. C.1, App. D.4).
- * data: [batch, window_frames * grid_h * grid_w, d_c + d_rope]; row of a slot =
- * [c (d_c) | k_R rotated by 3D-RoPE at its absolute (t, h, w) (d_rope)]. */
+/* Cache of latent frames ([PL] App. C.1, App. D.4-D.5): an optional sink
+ * frame followed by a sliding-window ring with FIFO eviction.
+ * data: [batch, (sink_frames + window_frames) * grid_h * grid_w, d_c + d_rope];
+ * row of a slot = [c (d_c) | k_R (d_rope)].
+ *  - rope_at_read = 0: k_R is stored rotated by 3D-RoPE at its absolute
+ *    (t, h, w); queries use absolute t ([PL] App. C.1 clip-length window).
+ *  - rope_at_read = 1: k_R is stored before RoPE (x W_KR) and rotated when the
+ *    window is assembled: the frames of the active context (sink frames, then
+ *    the window frames oldest first) are numbered 0, 1, 2, ... and that local
+ *    number is the temporal coordinate of their keys and of the query chunk
+ *    ([PL] App. D.5 "Long-Horizon RoPE Re-indexing"; App. E "RoPE branch").
+ *    Equivalently a window frame t sits at t - shift with
+ *    shift = max(0, t_first + n_frames - S - W), and the sink frame at 0.
+ * sink_frames = 1 requires rope_at_read = 1 (the pages' long-horizon scheme:
+ * one sink frame and a 6-frame window). */
 typedef struct vmla_cache {
   void* data;
   int32_t dtype;            /* vmla_dtype */
@@ -83,6 +97,8 @@ typedef struct vmla_cache {
   int32_t window_frames;    /* W */
   int32_t grid_h;
   int32_t grid_w;
+  int32_t sink_frames;      /* S: 0, or 1 (frame 0 is kept for good) */
+  int32_t rope_at_read;     /* 0: k_R rotated at append (absolute t); 1: rotated at read */
 } vmla_cache;
 
 /* Fills *dims with the Wan2.1-T2V-1.3B VideoMLA defaults listed above. */
@@ -102,13 +118,17 @@ void vmla_default_dims(vmla_dims* dims);
  *                                           t_first .. t_first + n_frames - 1
  *   w_down  [d_model, d_c]
  *   w_kr    [d_model, d_rope]
- *   cache   ring written in place: exactly the slots of the chunk's frames,
- *           (t mod W) * T + n, are (over)written; no other slot is touched.
- *           Appending a frame again (a later denoising step) overwrites it.
+ *   cache   written in place: exactly the slots of the chunk's frames (see
+ *           the slot convention above) are (over)written; no other slot is
+ *           touched. Appending a frame again (a later denoising step)
+ *           overwrites it. With rope_at_read = 1 the k_R columns receive
+ *           x W_KR unrotated ([PL] App. D.5).
  *
  * Errors: VMLA_ERR_NULL (any pointer NULL), VMLA_ERR_ALIGN, VMLA_ERR_DTYPE
  * (dtype invalid or != cache->dtype), VMLA_ERR_SHAPE (unsupported dims,
- * non-positive grid/batch/window, window_frames * T >= 2^24 slots,
+ * non-positive grid/batch/window, sink_frames not 0 or 1, rope_at_read not
+ * 0 or 1, sink_frames = 1 with rope_at_read = 0,
+ * (sink_frames + window_frames) * T >= 2^24 slots,
  * n_frames * T * d_model > 2^31 - 1 elements per batch element),
  * VMLA_ERR_RANGE (t_first < 0, n_frames < 1, n_frames > window_frames,
  * t_first + n_frames > 2^20), VMLA_ERR_HIP.
@@ -141,14 +161,18 @@ size_t vmla_attention_workspace_bytes(const vmla_dims* dims, int32_t batch, int3
  *            each head [nope (d_nope) | rope (d_rope)]
  *   w_k_up   [n_heads, d_c, d_nope]
  *   w_v_up   [n_heads, d_c, d_v]
- *   n_valid_frames  must equal min(t_first + n_frames, window_frames): keys are
- *            the ring slots [0, n_valid_frames * T) of each batch element
+ *   n_valid_frames  must equal min(t_first + n_frames, sink_frames +
+ *            window_frames): keys are the slots [0, n_valid_frames * T) of
+ *            each batch element (the sink frame, then the ring)
  *   out      [batch, n_q, n_heads, d_v] (dtype of the call)
  *   workspace >= vmla_attention_workspace_bytes(dims, batch, n_q) bytes; its
  *            contents are scratch owned by the call until it completes on stream.
  *
+ * With rope_at_read = 1 the queries and the cached k_R are rotated with the
+ * local temporal coordinates of the active context (see vmla_cache).
+ *
  * Errors: as vmla_cache_append, plus VMLA_ERR_RANGE when n_valid_frames is not
- * min(t_first + n_frames, window_frames), VMLA_ERR_WORKSPACE.
+ * min(t_first + n_frames, sink_frames + window_frames), VMLA_ERR_WORKSPACE.
  */
 int32_t vmla_chunk_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
                              const void* x, const void* w_q, const void* w_k_up,
@@ -167,7 +191,8 @@ int32_t vmla_chunk_attention(const vmla_dims* dims, const vmla_cache* cache, int
  * [batch, n_heads, n_q, d_c + d_rope].
  *
  * vmla_latent_attention -- scores of those rows against the cached rows
- * [c | k_R] of ring slots [0, n_valid_frames * T), online softmax, weighted sum
+ * [c | k_R] of slots [0, n_valid_frames * T) (k_R rotated as it is read when
+ * rope_at_read = 1), online softmax, weighted sum
  * of the latents c, projection by W_V_up[h] ([PL] App. E "Value-path
  * absorption"). Reads the query rows from workspace; writes out.
  */

@@ -44,6 +44,7 @@ class vmla_cache(ctypes.Structure):
     _fields_ = [
         ("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("batch", ctypes.c_int32),
         ("window_frames", ctypes.c_int32), ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+        ("sink_frames", ctypes.c_int32), ("rope_at_read", ctypes.c_int32),
     ]
 
 
@@ -112,21 +113,37 @@ def default_dims(**overrides) -> vmla_dims:
 
 @dataclass
 class LatentCache:
-    """Ring of latent frames: ``data`` [batch, window_frames * grid_h * grid_w, d_c + d_rope]."""
+    """Cache of latent frames: ``data`` [batch, (sink_frames + window_frames) *
+    grid_h * grid_w, d_c + d_rope]: the sink frame (if any), then the ring of the
+    most recent ``window_frames`` frames. ``rope_at_read``: k_R is kept before
+    RoPE and rotated in the active context at attention time."""
     data: torch.Tensor
     window_frames: int
     grid_h: int
     grid_w: int
+    sink_frames: int = 0
+    rope_at_read: bool = False
 
     @staticmethod
     def empty(batch: int, window_frames: int, grid_h: int, grid_w: int, dtype=torch.bfloat16,
-              device="cuda", dims: vmla_dims | None = None, fill: float | None = None) -> "LatentCache":
+              device="cuda", dims: vmla_dims | None = None, fill: float | None = None,
+              sink_frames: int = 0, rope_at_read: bool = False) -> "LatentCache":
         d = dims or default_dims()
-        t = torch.empty((batch, window_frames * grid_h * grid_w, d.d_c + d.d_rope), dtype=dtype,
-                        device=device)
+        t = torch.empty((batch, (sink_frames + window_frames) * grid_h * grid_w, d.d_c + d.d_rope),
+                        dtype=dtype, device=device)
         if fill is not None:
             t.fill_(fill)
-        return LatentCache(t, window_frames, grid_h, grid_w)
+        return LatentCache(t, window_frames, grid_h, grid_w, sink_frames, rope_at_read)
+
+    def n_valid_frames(self, t_first: int, n_frames: int) -> int:
+        """Frames of the active context once frames t_first .. t_first + n_frames - 1 are in."""
+        return min(t_first + n_frames, self.sink_frames + self.window_frames)
+
+    def slot_frame(self, t: int) -> int:
+        """Slot frame (slots [s * T, (s + 1) * T)) that latent frame t is stored in."""
+        if t < self.sink_frames:
+            return t
+        return self.sink_frames + (t - self.sink_frames) % self.window_frames
 
     @property
     def batch(self) -> int:
@@ -138,7 +155,8 @@ class LatentCache:
 
     def c_struct(self) -> vmla_cache:
         return vmla_cache(self.data.data_ptr(), _dtype_code(self.data), self.data.shape[0],
-                          self.window_frames, self.grid_h, self.grid_w)
+                          self.window_frames, self.grid_h, self.grid_w, int(self.sink_frames),
+                          int(bool(self.rope_at_read)))
 
 
 def _dtype_code(t: torch.Tensor) -> int:

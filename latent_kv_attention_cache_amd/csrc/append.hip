@@ -8,6 +8,10 @@
 // (App. D.3); the cache is a fixed-size window of latent frames with FIFO
 // eviction (App. D.4).
 //
+// With a cache that keeps k_R before RoPE (read-time rotation, App. D.5) the
+// k_R columns are stored as computed; with a sink frame, frame 0 keeps slots
+// [0, T) and the ring of the most recent frames follows it.
+//
 // A skinny GEMM: M = batch x tokens rows (the batch elements are contiguous in
 // x, so they form one row range), N = 224, K = d_model. The M rows are split
 // into one contiguous range per workgroup, at most 160 rows, as evenly as the
@@ -259,7 +263,7 @@ void append_kernel(AppendArgs a) {
   float* kr = reinterpret_cast<float*>(ot + Tl::kRows * kOutLd);            // bf16: [kRows][kKrLd]
   int* ri = kBf16 ? reinterpret_cast<int*>(kr + Tl::kRows * kKrLd)
                   : reinterpret_cast<int*>(ot + Tl::kRows * kOutLd);        // [kRows][5]
-  const int64_t cache_rows = (int64_t)a.window_frames * a.tokens_per_frame;
+  const int64_t cache_rows = ((int64_t)a.sink_frames + a.window_frames) * a.tokens_per_frame;
   for (int row = tid; row < rows; row += kThreads) {
     const int64_t m = m0 + row;
     const int bb = (int)(m / a.n_tok);
@@ -267,7 +271,13 @@ void append_kernel(AppendArgs a) {
     int n_in, ww, tw;
     const int f = div_small(n, a.tokens_per_frame, a.inv_tokens_per_frame, &n_in);
     const int hh = div_small(n_in, a.grid_w, a.inv_grid_w, &ww);
-    div_small(a.t_first + f, a.window_frames, a.inv_window_frames, &tw);
+    const int t = a.t_first + f;
+    if (t < a.sink_frames) {                // the sink frame keeps slots [0, T)
+      tw = t;
+    } else {                                // ring of the most recent frames after it
+      div_small(t - a.sink_frames, a.window_frames, a.inv_window_frames, &tw);
+      tw += a.sink_frames;
+    }
     ri[5 * row] = bb;
     ri[5 * row + 1] = tw * a.tokens_per_frame + n_in;
     ri[5 * row + 2] = a.t_first + f;
@@ -314,8 +324,8 @@ void append_kernel(AppendArgs a) {
       for (int q = 0; q < kPer / 2; ++q) {
         const int pr = p0 + q;
         const float a0 = src[2 * q], a1 = src[2 * q + 1];
-        float sn, cs;
-        sincos_rev(ri[5 * row + 2 + a.rope.axis[pr]], a.rope.rev[pr], &sn, &cs);
+        float sn = 0.f, cs = 1.f;           // keys kept before RoPE: stored as computed
+        if (!a.rope_at_read) sincos_rev(ri[5 * row + 2 + a.rope.axis[pr]], a.rope.rev[pr], &sn, &cs);
         // pair (a0, a1) -> (a0 cos - a1 sin, a0 sin + a1 cos)
         o[2 * q] = a0 * cs - a1 * sn;
         o[2 * q + 1] = a0 * sn + a1 * cs;

@@ -32,6 +32,8 @@ struct AppendArgs {
   int batch, n_tok, d_model;
   int grid_w, tokens_per_frame, window_frames, t_first;
   float inv_grid_w, inv_tokens_per_frame, inv_window_frames;   // 1/x as float
+  int sink_frames;      // 0 or 1: frame 0 kept in slots [0, T)
+  int rope_at_read;     // 1: k_R stored unrotated
   RopeTable rope;
 };
 
@@ -53,6 +55,12 @@ struct AttnArgs {
   const void* w_v_up;   // [n_heads, kDC, kDV]
   void* out;            // [batch, n_q, n_heads, kDV]
   int batch, n_q, n_heads, n_k, cache_rows;
+  // Read-time RoPE of k_R (rope_at_read = 1): the key in slot frame fs sits at
+  // temporal coordinate fs when fs < sink_frames, otherwise at
+  // sink_frames + ((fs - sink_frames - shift_mod_w) mod window_frames).
+  int rope_at_read, sink_frames, window_frames, shift_mod_w, tokens_per_frame, grid_w;
+  float inv_tokens_per_frame, inv_grid_w;
+  RopeTable rope;
 };
 
 hipError_t launch_append(const AppendArgs& a, bool f32, hipStream_t s);

@@ -50,6 +50,13 @@
 // (the MFMA contraction order of keys is permuted identically on both sides).
 // Epilogue: out^T[e][q] = W_V_up[h]^T[e][:] . (O^T / l)[:][q], W_V_up[h]
 // staged in LDS and read transposed.
+//
+// Read-time RoPE (caches that keep k_R before rotation, [PL] App. D.5 and
+// App. E "RoPE branch"; template flag kRot): loading wave w moves chunk column
+// 24 + w of every tile, i.e. RoPE pairs 4w .. 4w+3 of k_R. Once its own loads
+// of a tile have landed it rotates that column in LDS, in place (lane = key
+// row), with the key's local coordinate in the active context, before the
+// barrier that publishes the tile.
 #include <type_traits>
 
 #include "device_common.h"
@@ -90,7 +97,7 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
                :: "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory");
 }
 
-template <typename T>
+template <typename T, bool kRot>
 __global__ __launch_bounds__(kThreads)
 void latent_attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t kt[kBufs * kTileElems];
@@ -156,6 +163,35 @@ void latent_attn_kernel(AttnArgs a) {
         *reinterpret_cast<uint4*>(kt + buf * kTileElems + (n * kSlots + lane) * 8) = load8_bf16<T>(src);
       }
     }
+  };
+
+  // Read-time RoPE of this loading wave's k_R column of tile j (kRot only).
+  auto rotate_tile = [&](int j) {
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    bf16_t* p = kt + (j % kBufs) * kTileElems + ((kDC / 8 + wv) * kSlots + lane) * 8;
+    const int kg = min(j * kKT + lane, a.n_k - 1);
+    int n_in, ww;
+    const int fs = div_small(kg, a.tokens_per_frame, a.inv_tokens_per_frame, &n_in);
+    const int hh = div_small(n_in, a.grid_w, a.inv_grid_w, &ww);
+    int tl = fs;                                  // sink frame: its own index
+    if (fs >= a.sink_frames) {
+      int r = fs - a.sink_frames - a.shift_mod_w;
+      if (r < 0) r += a.window_frames;
+      tl = a.sink_frames + r;
+    }
+    const uint4 raw = *reinterpret_cast<const uint4*>(p);
+    const uint32_t in[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pr = 4 * wv + q;
+      const int ax = a.rope.axis[pr];
+      const float a0 = __uint_as_float(in[q] << 16), a1 = __uint_as_float(in[q] & 0xffff0000u);
+      float sn, cs;
+      sincos_rev(ax == 0 ? tl : (ax == 1 ? hh : ww), a.rope.rev[pr], &sn, &cs);
+      o[q] = pack2(a0 * cs - a1 * sn, a0 * sn + a1 * cs);
+    }
+    *reinterpret_cast<uint4*>(p) = uint4{o[0], o[1], o[2], o[3]};
   };
 
   // Per-lane LDS element offsets (relative to a tile) of the operand reads; a
@@ -275,6 +311,8 @@ void latent_attn_kernel(AttnArgs a) {
     issue_tile(0);
     if (ntiles > 1) issue_tile(1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // tile 1 is rotated in the vector phase of tile 0, like every later tile
+    if constexpr (kRot) rotate_tile(0);
   }
   __syncthreads();
 
@@ -300,6 +338,9 @@ void latent_attn_kernel(AttnArgs a) {
       } else if (jt < ntiles) {    // vector phase for tile jt
         if (!lag) {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          if constexpr (kRot) {
+            if (jt + 1 < ntiles) rotate_tile(jt + 1);
+          }
           if (jt + 2 < ntiles) issue_tile(jt + 2);
         }
         if (live) softmax(jt * kKT);
@@ -365,8 +406,13 @@ hipError_t launch_latent_attn(const AttnArgs& a, bool f32, hipStream_t s) {
   const int units = (a.n_q + 31) / 32;
   const int upad = units > kWaves ? units : kWaves;
   dim3 grid((a.n_heads * upad + kWaves - 1) / kWaves, 1, a.batch);
-  if (f32) hipLaunchKernelGGL(latent_attn_kernel<float>, grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(latent_attn_kernel<bf16_t>, grid, dim3(kThreads), 0, s, a);
+  if (a.rope_at_read) {
+    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, true>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false>), grid, dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

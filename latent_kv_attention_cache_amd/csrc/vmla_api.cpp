@@ -40,8 +40,11 @@ int32_t check_cache(const vmla_cache* c, int32_t dtype) {
   if (dtype != VMLA_F32 && dtype != VMLA_BF16) return VMLA_ERR_DTYPE;
   if (c->dtype != dtype) return VMLA_ERR_DTYPE;
   if (c->batch < 1 || c->window_frames < 1 || c->grid_h < 1 || c->grid_w < 1) return VMLA_ERR_SHAPE;
+  if ((c->sink_frames != 0 && c->sink_frames != 1) || (c->rope_at_read != 0 && c->rope_at_read != 1))
+    return VMLA_ERR_SHAPE;
+  if (c->sink_frames && !c->rope_at_read) return VMLA_ERR_SHAPE;
   const int64_t t = (int64_t)c->grid_h * c->grid_w;
-  const int64_t rows = t * c->window_frames;
+  const int64_t rows = t * ((int64_t)c->sink_frames + c->window_frames);
   // every element offset handled by the kernels must fit in int32 per batch element
   if (rows * kRow > INT32_MAX || rows >= (1 << 24)) return VMLA_ERR_SHAPE;
   return VMLA_OK;
@@ -122,6 +125,8 @@ int32_t vmla_cache_append(const vmla_dims* dims, const vmla_cache* cache, int32_
   a.inv_grid_w = 1.f / (float)cache->grid_w;
   a.inv_tokens_per_frame = 1.f / (float)T;
   a.inv_window_frames = 1.f / (float)cache->window_frames;
+  a.sink_frames = cache->sink_frames;
+  a.rope_at_read = cache->rope_at_read;
   a.rope = rope_table(dims);
   return hip_status(launch_append(a, dtype == VMLA_F32, static_cast<hipStream_t>(stream)));
 }
@@ -144,8 +149,12 @@ int32_t check_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t 
   if (t_first < 0 || n_frames < 1 || n_frames > cache->window_frames) return VMLA_ERR_RANGE;
   if ((int64_t)t_first + n_frames > kMaxFrameIndex) return VMLA_ERR_RANGE;
   const int64_t t_end = (int64_t)t_first + n_frames;
-  const int64_t expect_valid = t_end < cache->window_frames ? t_end : cache->window_frames;
+  const int64_t span = (int64_t)cache->sink_frames + cache->window_frames;   // frames the cache holds
+  const int64_t expect_valid = t_end < span ? t_end : span;
   if (n_valid_frames != expect_valid) return VMLA_ERR_RANGE;
+  // Read-time RoPE: frames of the active context are renumbered from 0; a window
+  // frame t sits at t - shift, the sink frame at 0.
+  const int64_t shift = cache->rope_at_read && t_end > span ? t_end - span : 0;
   const int64_t T = (int64_t)cache->grid_h * cache->grid_w;
   const int64_t n_q = T * n_frames;
   if (n_q * dims->d_model > INT32_MAX || n_q * dims->n_heads * kDV > INT32_MAX) return VMLA_ERR_SHAPE;
@@ -156,7 +165,7 @@ int32_t check_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t 
   *q = QArgs{};
   q->qhat = static_cast<uint16_t*>(const_cast<void*>(workspace));
   q->batch = cache->batch; q->n_q = (int)n_q; q->d_model = dims->d_model; q->n_heads = dims->n_heads;
-  q->grid_w = cache->grid_w; q->tokens_per_frame = (int)T; q->t_first = t_first;
+  q->grid_w = cache->grid_w; q->tokens_per_frame = (int)T; q->t_first = (int)(t_first - shift);
   q->inv_grid_w = 1.f / (float)cache->grid_w;
   q->inv_tokens_per_frame = 1.f / (float)T;
   q->qscale = (float)((double)dims->scale * 1.4426950408889634);   // scale * log2(e)
@@ -165,7 +174,16 @@ int32_t check_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t 
   *a = AttnArgs{};
   a->qhat = q->qhat; a->cache = cache->data;
   a->batch = cache->batch; a->n_q = (int)n_q; a->n_heads = dims->n_heads;
-  a->n_k = (int)(T * n_valid_frames); a->cache_rows = (int)(T * cache->window_frames);
+  a->n_k = (int)(T * n_valid_frames); a->cache_rows = (int)(T * span);
+  a->rope_at_read = cache->rope_at_read;
+  a->sink_frames = cache->sink_frames;
+  a->window_frames = cache->window_frames;
+  a->shift_mod_w = (int)(shift % cache->window_frames);
+  a->tokens_per_frame = (int)T;
+  a->grid_w = cache->grid_w;
+  a->inv_tokens_per_frame = 1.f / (float)T;
+  a->inv_grid_w = 1.f / (float)cache->grid_w;
+  a->rope = q->rope;
   return VMLA_OK;
 }
 

@@ -60,7 +60,8 @@ class Run:
         self.dw = dev_weights(w, self.wts, device)
         self.dims = vm.default_dims(d_model=w.d_model, n_heads=w.n_heads)
         self.cache = vm.LatentCache.empty(w.batch, w.window_frames, w.grid_h, w.grid_w,
-                                          dtype=tdtype(w), device=device, dims=self.dims, fill=fill)
+                                          dtype=tdtype(w), device=device, dims=self.dims, fill=fill,
+                                          sink_frames=w.sink_frames, rope_at_read=w.rope_at_read)
         self.device = device
         self._xcache = {}
         self.batch_x = batch_x   # optional fn(t, b) -> device tensor [T, D] (bulk inputs)
@@ -90,11 +91,15 @@ class Run:
         return x
 
     def fill_window(self):
-        """Append the frames that precede the query chunk, in chunks of at most W frames."""
+        """Append the frames that precede the query chunk: each run of consecutive
+        frames in pieces of at most W frames."""
         prior = list(self.w.prior_frames)
         i = 0
         while i < len(prior):
-            n = min(self.w.window_frames, len(prior) - i)
+            n = 1
+            while (i + n < len(prior) and prior[i + n] == prior[i] + n
+                   and n < self.w.window_frames):
+                n += 1
             self.append(prior[i], n)
             i += n
 
@@ -103,7 +108,7 @@ class Run:
         t_first = w.t_first if t_first is None else t_first
         n_frames = w.chunk_frames if n_frames is None else n_frames
         x = self.x_dev(range(t_first, t_first + n_frames))
-        n_valid = min(t_first + n_frames, w.window_frames)
+        n_valid = self.cache.n_valid_frames(t_first, n_frames)
         return vm.vmla_chunk_attention(self.cache, x, self.dw["w_q"], self.dw["w_k_up"],
                                        self.dw["w_v_up"], t_first, n_frames, n_valid,
                                        dims=self.dims)
@@ -118,17 +123,20 @@ class Run:
         w = self.w
         if t_first is not None:
             w = w.with_(t_first=t_first, chunk_frames=n_frames or w.chunk_frames)
-        return orc.chunk_attention_reference(w, self.wts, lambda t: self.x_host(t, b), query_tokens)
+        ref = orc.chunk_attention_reindexed_reference if w.rope_at_read else orc.chunk_attention_reference
+        return ref(w, self.wts, lambda t: self.x_host(t, b), query_tokens)
 
     def append_reference(self, t_first, n_frames, b=0):
         x = np.concatenate([self.x_host(t, b) for t in range(t_first, t_first + n_frames)])
+        if self.w.rope_at_read:
+            return orc.append_reference_raw(self.w, self.wts, x)
         return orc.append_reference(self.w, self.wts, x, t_first, n_frames)
 
     def cache_rows(self, t_first, n_frames, b=0):
-        T, W = self.w.tokens_per_frame, self.w.window_frames
+        T = self.w.tokens_per_frame
         rows = []
         data = self.cache.data[b].float().cpu().numpy()
         for t in range(t_first, t_first + n_frames):
-            s = (t % W) * T
+            s = self.cache.slot_frame(t) * T
             rows.append(data[s:s + T])
         return np.concatenate(rows)

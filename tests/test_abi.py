@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.vmla_abi_version() == 1
+    assert lib.vmla_abi_version() == 2
     for code in range(-7, 1):
         s = vm.vmla_status_string(code)
         assert s and s != "unknown status"
@@ -120,6 +120,32 @@ def test_attention_validation(lib):
     assert _attn(lib, ws=None) == vm.VMLA_ERR_WORKSPACE
     assert _attn(lib, ws_bytes=10) == vm.VMLA_ERR_WORKSPACE
     assert _attn(lib, ws=MIS) == vm.VMLA_ERR_ALIGN
+
+
+def test_cache_mode_validation(lib):
+    # sink_frames in {0, 1}, rope_at_read in {0, 1}, and a sink only with read-time RoPE
+    assert _append(lib, cache=_cache(sink_frames=2, rope_at_read=1)) == vm.VMLA_ERR_SHAPE
+    assert _append(lib, cache=_cache(rope_at_read=2)) == vm.VMLA_ERR_SHAPE
+    assert _append(lib, cache=_cache(sink_frames=1, rope_at_read=0)) == vm.VMLA_ERR_SHAPE
+    assert _attn(lib, cache=_cache(sink_frames=1, rope_at_read=0)) == vm.VMLA_ERR_SHAPE
+    sink = _cache(sink_frames=1, rope_at_read=1)
+    # valid frames = min(t_first + n_frames, sink + W): 4 once the ring is full
+    assert _attn(lib, cache=sink, t_first=10, n_frames=1, n_valid=3) == vm.VMLA_ERR_RANGE
+    assert _attn(lib, cache=sink, t_first=10, n_frames=1, n_valid=5) == vm.VMLA_ERR_RANGE
+    assert _attn(lib, cache=sink, t_first=0, n_frames=2, n_valid=3) == vm.VMLA_ERR_RANGE
+    assert _append(lib, cache=sink, n_frames=4) == vm.VMLA_ERR_RANGE   # > window_frames
+
+
+def test_binding_cache_geometry():
+    import torch
+    c = vm.LatentCache(torch.zeros(1, 7 * 24, 224), 6, 4, 6, sink_frames=1, rope_at_read=True)
+    assert [c.slot_frame(t) for t in (0, 1, 6, 7, 12, 13)] == [0, 1, 6, 1, 6, 1]
+    assert c.n_valid_frames(0, 3) == 3 and c.n_valid_frames(18, 3) == 7
+    plain = vm.LatentCache(torch.zeros(1, 3 * 24, 224), 3, 4, 6)
+    assert [plain.slot_frame(t) for t in (0, 2, 3, 7)] == [0, 2, 0, 1]
+    assert plain.n_valid_frames(7, 1) == 3
+    cs = c.c_struct()
+    assert (cs.sink_frames, cs.rope_at_read) == (1, 1)
 
 
 def test_binding_rejects_cpu_tensors():

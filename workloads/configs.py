@@ -67,9 +67,10 @@ class Workload:
 
     @property
     def prior_frames(self) -> tuple:
-        """Frames that sit in the window before the query chunk is appended."""
-        lo = max(0, self.t_first + self.chunk_frames - self.window_frames)
-        return tuple(range(lo, self.t_first))
+        """Frames that sit in the cache before the query chunk is appended: the
+        sink frames, then the window's earlier frames."""
+        lo = max(self.sink_frames, self.t_first + self.chunk_frames - self.window_frames)
+        return tuple(range(min(self.sink_frames, self.t_first))) + tuple(range(lo, self.t_first))
 
     @property
     def chunk_frame_ids(self) -> tuple:
