@@ -69,7 +69,8 @@ def cpu_baseline(w, wts, x_host, step_flops):
     except Exception:  # pragma: no cover - threadpoolctl is optional
         threads = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
-    orc.chunk_attention_reference(w, wts, x_host, np.arange(w.n_q))
+    ref = orc.chunk_attention_reindexed_reference if w.rope_at_read else orc.chunk_attention_reference
+    ref(w, wts, x_host, np.arange(w.n_q))
     full_s = time.perf_counter() - t0
     log(f"[cpu_baseline] oracle on the full step: {full_s:.2f} s")
     return {
@@ -92,6 +93,10 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4),
                     help="2: Wan-1.3B chunk-layer at B=1 (the reported workload); 3: B=8, 30 "
                          "layers; 4: B=16, one-frame chunk")
+    ap.add_argument("--long-horizon", action="store_true",
+                    help="with --config 2: the long-rollout cache instead of the 21-frame window -- "
+                         "one sink frame plus a 6-frame window, k_R cached before RoPE and "
+                         "rotated in the active context, chunk at t = 18..20 after evictions")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device-to-device copy of MIB MiB, whose counter "
                          "readings calibrate FETCH_SIZE / WRITE_SIZE")
@@ -123,20 +128,35 @@ def main():
         log(f"[bench] calibration copy: {nbytes} bytes read and {nbytes} bytes written")
         del src, dst
     w = config(args.config)
+    if args.long_horizon:
+        if args.config != 2:
+            print("--long-horizon applies to --config 2", file=sys.stderr)
+            sys.exit(2)
+        w = w.with_(window_frames=6, sink_frames=1, rope_at_read=True,
+                    name=w.name + ", sink 1 + window 6, read-time RoPE")
     log(f"[bench] workload: {w.name}")
     dims = vm.default_dims()
     xs = None
     if args.config == 2:
         # seeded host inputs, the same as the parity tests use
         wts = weights(w)
-        xs = {t: x_frame(w, t) for t in range(w.window_frames)}
+        xs = {t: x_frame(w, t) for t in w.prior_frames + w.chunk_frame_ids}
         dw = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in wts.items()}
 
         def xdev(frames):
             return torch.from_numpy(np.concatenate([xs[t] for t in frames]))[None].to(dev).to(torch.bfloat16)
 
-        cache = vm.LatentCache.empty(w.batch, w.window_frames, w.grid_h, w.grid_w, device=dev)
-        vm.vmla_cache_append(cache, xdev(range(0, w.t_first)), dw["w_down"], dw["w_kr"], 0, w.t_first)
+        cache = vm.LatentCache.empty(w.batch, w.window_frames, w.grid_h, w.grid_w, device=dev,
+                                     sink_frames=w.sink_frames, rope_at_read=w.rope_at_read)
+        prior = w.prior_frames
+        i = 0
+        while i < len(prior):       # contiguous runs of earlier frames
+            j = i
+            while j + 1 < len(prior) and prior[j + 1] == prior[j] + 1:
+                j += 1
+            vm.vmla_cache_append(cache, xdev(prior[i:j + 1]), dw["w_down"], dw["w_kr"], prior[i],
+                                 j + 1 - i)
+            i = j + 1
         sets = [(xdev(list(w.chunk_frame_ids)).contiguous(), dw, cache)]
     else:
         # one buffer set per layer (config 3) or eight rotating sets (config 4)
@@ -206,7 +226,7 @@ def main():
     append_gbs = wk["bytes_append"] / (k_ms["append"] * 1e-3) / 1e9
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "latent_attn_config2_traffic.json")
-    if args.config == 2 and os.path.exists(tfile):
+    if args.config == 2 and not args.long_horizon and os.path.exists(tfile):
         with open(tfile) as f:
             tr = json.load(f)
         if tr.get("kernel_source_sha") == _kernel_sha():
@@ -256,6 +276,12 @@ def main():
     if not args.no_cpu_baseline and args.config == 2:
         xh = lambda t: xs[t]  # noqa: E731
         result["cpu_baseline"] = cpu_baseline(w, wts, xh, wk["step"])
+    if args.long_horizon:
+        result["config"]["workload"] = ("Wan-1.3B-shaped chunk-layer, long rollout: B=1, 30x52 "
+                                        "grid, 3-frame query chunk at t=18..20 over one sink frame "
+                                        "plus a 6-frame window, RoPE applied at read time")
+        result["config"]["sink_frames"] = w.sink_frames
+        result["config"]["window_frames"] = w.window_frames
     print(json.dumps(result), flush=True)
 
 

@@ -51,7 +51,9 @@ class Workload:
 
     @property
     def n_valid_frames(self) -> int:
-        return min(self.t_first + self.chunk_frames, self.window_frames)
+        """Frames in the active context once the chunk is appended: the sink
+        frames plus the window, or the whole history while it is shorter."""
+        return min(self.t_first + self.chunk_frames, self.sink_frames + self.window_frames)
 
     @property
     def n_k(self) -> int:
