@@ -51,6 +51,11 @@ Readings of points the pages leave open (each is also listed in the design doc):
     followed by the most recent window frames, numbered 0, 1, 2, ... oldest
     first, and those local numbers are the temporal RoPE coordinate of keys
     and queries (``chunk_attention_reindexed_reference``).
+  * Whole layer (``chunk_layer_reference``): queries through a query latent
+    c_q = x W_DQ (d_q = 768, [PL] §4) and q = c_q W_UQ, no normalisation of
+    c_q (the pages name none); the head outputs are concatenated head-major
+    and mixed by W_O [H d_v, d_model]; A_h and B_h W_O[h] are the folded
+    weights of [PL] App. E.
 PARITY UNPINNED: final output values at the benchmark shapes (the pages print
 no worked example); they are pinned only through the identities checked in
 tests/test_oracle_pins.py.
@@ -333,6 +338,116 @@ def chunk_attention_reindexed_reference(w, wts, x_of_frame, query_tokens=None):
                              w.rope_pairs)
     scale = 1.0 / np.sqrt(w.d_nope + w.d_rope)
     return attention_explicit(q_nope, q_rope, k_nope, k_r, v, scale)
+
+
+# ---------------------------------------------------------------------------
+# The whole attention layer: query latent and output mixer
+# ([PL] §4 "Implementation Details": d_q = 768; App. E "Content-path
+# absorption", "Value-path absorption")
+# ---------------------------------------------------------------------------
+
+def query_latent_queries(x, w_dq, w_uq, pos, omega, n_heads, d_nope, d_rope, pairs=(6, 5, 5)):
+    """Queries through the query latent: c_q = x W_DQ (d_q wide), then
+    q = c_q W_UQ, split per head and rotated exactly as ``queries`` does."""
+    c_q = np.asarray(x, dtype=F64) @ np.asarray(w_dq, dtype=F64)
+    return queries(c_q, w_uq, pos, omega, n_heads, d_nope, d_rope, pairs)
+
+
+def output_mixer(o, w_o):
+    """Layer output y = [o_0 | o_1 | ... | o_{H-1}] W_O of the head outputs
+    o [Nq, H, d_v] -> [Nq, d_model]."""
+    o = np.asarray(o, dtype=F64)
+    return o.reshape(o.shape[0], -1) @ np.asarray(w_o, dtype=F64)
+
+
+def context_keys(w, wts, x_of_frame):
+    """Keys of the attended context once the chunk is appended, and the
+    temporal RoPE coordinate of every frame in it.
+
+    Plain window (``w.rope_at_read`` false): the window's frames at their
+    absolute t. Long-horizon mode: the sink-plus-window context of
+    ``active_context`` at local coordinates. Returns (c [Nk, d_c],
+    k_R [Nk, d_rope] rotated at those coordinates, {t: coordinate})."""
+    omega = rope_frequencies(w.rope_pairs, w.rope_axis_dims, w.rope_theta)
+    if w.rope_at_read:
+        ctx = active_context(w.t_first, w.chunk_frames, w.window_frames, w.sink_frames)
+    else:
+        ctx = [(t, t) for t in window_frames(w.t_first, w.chunk_frames, w.window_frames)]
+    cs, krs = [], []
+    for t, tc in ctx:
+        x = np.asarray(x_of_frame(t), dtype=F64)
+        cs.append(x @ np.asarray(wts["w_down"], dtype=F64))
+        krs.append(rope3d(x @ np.asarray(wts["w_kr"], dtype=F64),
+                          frame_positions(tc, w.grid_h, w.grid_w), omega, w.rope_pairs))
+    return np.concatenate(cs, axis=0), np.concatenate(krs, axis=0), dict(ctx)
+
+
+def chunk_layer_reference(w, wts, mix, x_of_frame, query_tokens=None):
+    """Reference output of one chunk step through the whole attention layer.
+
+    Queries come from the query latent (``query_latent_queries`` with
+    ``mix["w_dq"]``, ``mix["w_uq"]``); keys and values are reconstructed per
+    head from the context of ``context_keys``; softmax over every key of it
+    (no mask); the head outputs are mixed by ``mix["w_o"]``. ``wts`` holds the
+    cache weights (``w_down``, ``w_kr``, ``w_k_up``, ``w_v_up``). Returns
+    [len(query_tokens), d_model]."""
+    omega = rope_frequencies(w.rope_pairs, w.rope_axis_dims, w.rope_theta)
+    c, k_r, coord = context_keys(w, wts, x_of_frame)
+    k_nope, v = reconstruct_heads(c, wts["w_k_up"], wts["w_v_up"])
+    chunk = list(range(w.t_first, w.t_first + w.chunk_frames))
+    xq = np.concatenate([np.asarray(x_of_frame(t), dtype=F64) for t in chunk], axis=0)
+    pos_q = np.concatenate([frame_positions(coord[t], w.grid_h, w.grid_w) for t in chunk], axis=0)
+    if query_tokens is not None:
+        query_tokens = np.asarray(query_tokens)
+        xq, pos_q = xq[query_tokens], pos_q[query_tokens]
+    q_nope, q_rope = query_latent_queries(xq, mix["w_dq"], mix["w_uq"], pos_q, omega, w.n_heads,
+                                          w.d_nope, w.d_rope, w.rope_pairs)
+    scale = 1.0 / np.sqrt(w.d_nope + w.d_rope)
+    return output_mixer(attention_explicit(q_nope, q_rope, k_nope, k_r, v, scale), mix["w_o"])
+
+
+def fold_query_weights(w_uq, w_k_up, n_heads, d_nope, d_rope):
+    """Per head [A_h | W_UQ^R[h]], head-major -> [d_q, H (d_c + d_rope)].
+
+    A_h = W_UQ^nope[h] W_K_up[h]^T takes the query latent straight to the
+    content score against c; it depends on no token, time step or position,
+    so it is formed once ([PL] App. E "Content-path absorption"). The rope
+    columns W_UQ^R[h] stay as they are: RoPE cannot be folded ("RoPE branch")."""
+    w_uq = np.asarray(w_uq, dtype=F64).reshape(-1, n_heads, d_nope + d_rope)
+    w_k_up = np.asarray(w_k_up, dtype=F64)
+    blocks = [np.concatenate([w_uq[:, h, :d_nope] @ w_k_up[h].T, w_uq[:, h, d_nope:]], axis=1)
+              for h in range(n_heads)]
+    return np.concatenate(blocks, axis=1)
+
+
+def fold_output_weights(w_v_up, w_o):
+    """Per head B_h W_O[h], stacked head-major -> [H d_c, d_model]: the value
+    up-projection folded into the output mixer, W_O[h] being the d_v rows of
+    W_O that mix head h ([PL] App. E "Value-path absorption")."""
+    w_v_up = np.asarray(w_v_up, dtype=F64)
+    w_o = np.asarray(w_o, dtype=F64)
+    d_v = w_v_up.shape[2]
+    return np.concatenate([w_v_up[h] @ w_o[h * d_v:(h + 1) * d_v] for h in range(w_v_up.shape[0])],
+                          axis=0)
+
+
+def layer_latent_folded(c_q, pos_q, c, k_r, w_qa, w_vo, omega, n_heads, d_c, d_rope, scale,
+                        pairs=(6, 5, 5)):
+    """The layer in latent form, used to cross-check ``chunk_layer_reference``
+    ([PL] App. E): per head, content score (c_q A_h) . c, positional score
+    RoPE(c_q W_UQ^R[h]) . k_R, softmax, weighted latents p c, then
+    y += (p c) (B_h W_O[h]). No per-head key or value is formed."""
+    c_q = np.asarray(c_q, dtype=F64)
+    c = np.asarray(c, dtype=F64)
+    k_r = np.asarray(k_r, dtype=F64)
+    row = d_c + d_rope
+    y = np.zeros((c_q.shape[0], w_vo.shape[1]), dtype=F64)
+    for h in range(n_heads):
+        qa = c_q @ w_qa[:, h * row:h * row + d_c]
+        qr = rope3d(c_q @ w_qa[:, h * row + d_c:(h + 1) * row], pos_q, omega, pairs)
+        p = softmax_rows((qa @ c.T + qr @ k_r.T) * scale)
+        y += (p @ c) @ w_vo[h * d_c:(h + 1) * d_c]
+    return y
 
 
 def append_reference_raw(w, wts, x_chunk):

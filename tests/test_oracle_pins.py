@@ -445,6 +445,117 @@ def test_reindexing_sees_relative_coordinates_only(monkeypatch):
     assert rel(absolute, base) > 1e-3
 
 
+# ---------------------------------------------------------------------------
+# The whole layer: query latent and output mixer ([PL] §4, App. E)
+# ---------------------------------------------------------------------------
+
+def test_layer_with_identity_query_latent_and_mixer_is_the_attention_reference():
+    # d_q = d_model with W_DQ = I and W_UQ = W_Q, and W_O = I: the layer is the
+    # pinned single-projection reference with the heads concatenated in order,
+    # for the plain window and for the re-indexed sink-plus-window context.
+    for kw, ref_fn in (({}, orc.chunk_attention_reference),
+                       (dict(sink_frames=1, rope_at_read=True),
+                        orc.chunk_attention_reindexed_reference)):
+        w = custom(2, 3, window_frames=3, chunk_frames=2, t_first=5, dtype="f32").with_(
+            d_q=1536, **kw)
+        wt = weights(w)
+        xs = {t: x_frame(w, t) for t in range(0, 7)}
+        eye = np.eye(w.d_model)
+        mix = {"w_dq": eye, "w_uq": wt["w_q"], "w_o": eye}
+        y = orc.chunk_layer_reference(w, wt, mix, lambda t: xs[t])
+        ref = ref_fn(w, wt, lambda t: xs[t])
+        assert rel(y, ref.reshape(ref.shape[0], -1)) < 1e-12
+
+
+def _tiny_layer(D=7, dq=5, H=3, dn=4, dr=4, dc=6, dv=5):
+    pairs, dims = (1, 1, 0), (2, 2, 2)
+    return dict(D=D, dq=dq, H=H, dn=dn, dr=dr, dc=dc, dv=dv, pairs=pairs,
+                om=orc.rope_frequencies(pairs, dims),
+                w_dq=RNG.standard_normal((D, dq)), w_uq=RNG.standard_normal((dq, H * (dn + dr))),
+                w_down=RNG.standard_normal((D, dc)), w_kr=RNG.standard_normal((D, dr)),
+                w_k_up=RNG.standard_normal((H, dc, dn)), w_v_up=RNG.standard_normal((H, dc, dv)),
+                w_o=RNG.standard_normal((H * dv, D)))
+
+
+def test_layer_folded_latent_form_equals_explicit():
+    # [PL] App. E: with A_h on the query latent and B_h folded into W_O, the
+    # layer needs no per-head key or value and changes nothing but rounding.
+    L = _tiny_layer()
+    xk, xq = RNG.standard_normal((9, L["D"])), RNG.standard_normal((4, L["D"]))
+    pk, pq = RNG.integers(0, 9, size=(9, 3)), RNG.integers(0, 9, size=(4, 3))
+    scale = 1 / math.sqrt(L["dn"] + L["dr"])
+    c, k_r = orc.latent_entry(xk, L["w_down"], L["w_kr"], pk, L["om"], L["pairs"])
+    k_nope, v = orc.reconstruct_heads(c, L["w_k_up"], L["w_v_up"])
+    q_nope, q_rope = orc.query_latent_queries(xq, L["w_dq"], L["w_uq"], pq, L["om"], L["H"],
+                                              L["dn"], L["dr"], L["pairs"])
+    explicit = orc.output_mixer(orc.attention_explicit(q_nope, q_rope, k_nope, k_r, v, scale),
+                                L["w_o"])
+    w_qa = orc.fold_query_weights(L["w_uq"], L["w_k_up"], L["H"], L["dn"], L["dr"])
+    w_vo = orc.fold_output_weights(L["w_v_up"], L["w_o"])
+    assert w_qa.shape == (L["dq"], L["H"] * (L["dc"] + L["dr"]))
+    assert w_vo.shape == (L["H"] * L["dc"], L["D"])
+    folded = orc.layer_latent_folded(xq @ L["w_dq"], pq, c, k_r, w_qa, w_vo, L["om"], L["H"],
+                                     L["dc"], L["dr"], scale, L["pairs"])
+    assert rel(folded, explicit) < 1e-12
+
+
+def test_layer_brute_force_scalar_loops_tiny():
+    # Grid 1x2, window of 2 frames, chunk = frame 3: keys of frames 2 and 3 at
+    # their absolute t, queries of frame 3. Every sum a scalar loop. W_O is
+    # square (H d_v = d_model), as in the real layer.
+    D, dq, H, dn, dr, dc, dv = 4, 3, 2, 2, 4, 3, 2
+    pairs, dims = (1, 1, 0), (2, 2, 2)
+    w = custom(1, 2, window_frames=2, chunk_frames=1, t_first=3, dtype="f32").with_(
+        d_model=D, d_q=dq, n_heads=H, d_nope=dn, d_rope=dr, d_c=dc, d_v=dv, rope_pairs=pairs,
+        rope_axis_dims=dims)
+    wt = {"w_down": RNG.standard_normal((D, dc)), "w_kr": RNG.standard_normal((D, dr)),
+          "w_k_up": RNG.standard_normal((H, dc, dn)), "w_v_up": RNG.standard_normal((H, dc, dv))}
+    mix = {"w_dq": RNG.standard_normal((D, dq)), "w_uq": RNG.standard_normal((dq, H * (dn + dr))),
+           "w_o": RNG.standard_normal((H * dv, D))}
+    xs = {t: RNG.standard_normal((2, D)) for t in range(4)}
+    om = orc.rope_frequencies(pairs, dims)
+    scale = 1 / math.sqrt(dn + dr)
+
+    def mv(x, W, j):
+        return sum(x[i] * W[i][j] for i in range(len(x)))
+
+    def rot(vec, t, h):
+        ang = [t * om[0], h * om[1]]
+        o = list(vec)
+        for j in range(2):
+            a, b = vec[2 * j], vec[2 * j + 1]
+            o[2 * j] = a * math.cos(ang[j]) - b * math.sin(ang[j])
+            o[2 * j + 1] = a * math.sin(ang[j]) + b * math.cos(ang[j])
+        return o
+
+    keys = [(xs[t][n], t, n // 2) for t in (2, 3) for n in range(2)]
+    ref = np.zeros((2, D))
+    for qi in range(2):
+        cq = [mv(xs[3][qi], mix["w_dq"], j) for j in range(dq)]
+        qfull = [mv(cq, mix["w_uq"], j) for j in range(H * (dn + dr))]
+        heads = []
+        for h in range(H):
+            qn = qfull[h * (dn + dr):h * (dn + dr) + dn]
+            qr = rot(qfull[h * (dn + dr) + dn:(h + 1) * (dn + dr)], 3, qi // 2)
+            s, vals = [], []
+            for xk, tk, hk in keys:
+                c = [mv(xk, wt["w_down"], j) for j in range(dc)]
+                kr = rot([mv(xk, wt["w_kr"], j) for j in range(dr)], tk, hk)
+                kn = [sum(c[i] * wt["w_k_up"][h][i][j] for i in range(dc)) for j in range(dn)]
+                vv = [sum(c[i] * wt["w_v_up"][h][i][j] for i in range(dc)) for j in range(dv)]
+                s.append(scale * (sum(qn[j] * kn[j] for j in range(dn)) +
+                                  sum(qr[j] * kr[j] for j in range(dr))))
+                vals.append(vv)
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            z = sum(e)
+            heads += [sum(e[k] / z * vals[k][j] for k in range(len(keys))) for j in range(dv)]
+        for j in range(D):
+            ref[qi, j] = mv(heads, mix["w_o"], j)
+    out = orc.chunk_layer_reference(w, wt, mix, lambda t: xs[t])
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
 def test_append_reference_raw_rows():
     w = custom(2, 3, window_frames=4, chunk_frames=2, t_first=7, dtype="f32")
     wt = weights(w)
@@ -563,6 +674,31 @@ def _context_without_sink(t_first, chunk_frames, window, sink):
         [c for c in _ORIG_CTX(t_first, chunk_frames, window, sink) if c[0] >= sink])]
 
 
+def _mixer_head_minor(o, w_o):
+    o = np.asarray(o, dtype=np.float64)
+    return o.transpose(0, 2, 1).reshape(o.shape[0], -1) @ np.asarray(w_o, dtype=np.float64)
+
+
+def _mixer_transposed(o, w_o):
+    # a square W_O (H d_v = d_model, as in the real layer) read transposed
+    o = np.asarray(o, dtype=np.float64)
+    w_o = np.asarray(w_o, dtype=np.float64)
+    return o.reshape(o.shape[0], -1) @ (w_o.T if w_o.shape[0] == w_o.shape[1] else w_o)
+
+
+def _fold_query_rope_from_nope(w_uq, w_k_up, n_heads, d_nope, d_rope):
+    w3 = np.asarray(w_uq, dtype=np.float64).reshape(-1, n_heads, d_nope + d_rope)
+    return np.concatenate([np.concatenate([w3[:, h, :d_nope] @ np.asarray(w_k_up[h]).T,
+                                           w3[:, h, :d_rope]], axis=1)
+                           for h in range(n_heads)], axis=1)
+
+
+def _fold_output_wrong_head(w_v_up, w_o):
+    d_v, H = w_v_up.shape[2], w_v_up.shape[0]
+    return np.concatenate([np.asarray(w_v_up[h]) @ np.asarray(w_o)[(H - 1 - h) * d_v:(H - h) * d_v]
+                           for h in range(H)], axis=0)
+
+
 _ORIG_CTX = orc.active_context
 _ORIG_ATT = orc.attention_explicit
 _ORIG_REC = orc.reconstruct_heads
@@ -573,7 +709,9 @@ PINS = [test_rope_is_complex_rotation, test_attention_matches_torch_sdpa_fp64,
         test_mla_equals_dense_mha_with_composed_weights_real_dims,
         test_brute_force_scalar_loops_tiny, test_append_reference_rows_layout,
         test_frame_positions_token_order, test_absorbed_equals_explicit,
-        test_reindexed_sink_context_brute_force_tiny]
+        test_reindexed_sink_context_brute_force_tiny,
+        test_layer_with_identity_query_latent_and_mixer_is_the_attention_reference,
+        test_layer_folded_latent_form_equals_explicit, test_layer_brute_force_scalar_loops_tiny]
 
 
 @pytest.mark.parametrize("name,patch", [
@@ -584,6 +722,10 @@ PINS = [test_rope_is_complex_rotation, test_attention_matches_torch_sdpa_fp64,
     ("h and w swapped in positions", ("frame_positions", _positions_hw_swapped)),
     ("window frames not re-indexed", ("active_context", _context_absolute)),
     ("sink evicted with the window", ("active_context", _context_without_sink)),
+    ("head outputs mixed head-minor", ("output_mixer", _mixer_head_minor)),
+    ("output mixer transposed", ("output_mixer", _mixer_transposed)),
+    ("A_h fold takes rope columns from the nope block", ("fold_query_weights", _fold_query_rope_from_nope)),
+    ("B_h folded with another head's W_O rows", ("fold_output_weights", _fold_output_wrong_head)),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, patch):
     attr, fn = patch

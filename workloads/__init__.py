@@ -6,10 +6,12 @@ HIP path's tests and benchmark can use it without sharing any computation.
 """
 from .configs import Workload, CONFIGS, config, custom
 from .seeded import (ROLE_WQ, ROLE_WDOWN, ROLE_WKR, ROLE_WKUP, ROLE_WVUP, ROLE_X,
-                     round_bf16, bf16_bits, weights, x_frame, x_frames)
+                     ROLE_WDQ, ROLE_WUQ, ROLE_WO, round_bf16, bf16_bits, weights, mixer_weights,
+                     x_frame, x_frames)
 
 __all__ = [
     "Workload", "CONFIGS", "config", "custom",
     "ROLE_WQ", "ROLE_WDOWN", "ROLE_WKR", "ROLE_WKUP", "ROLE_WVUP", "ROLE_X",
-    "round_bf16", "bf16_bits", "weights", "x_frame", "x_frames",
+    "ROLE_WDQ", "ROLE_WUQ", "ROLE_WO", "round_bf16", "bf16_bits", "weights", "mixer_weights",
+    "x_frame", "x_frames",
 ]

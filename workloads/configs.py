@@ -35,6 +35,7 @@ class Workload:
     d_rope: int = 32
     d_c: int = 192
     d_v: int = 128
+    d_q: int = 768                    # query latent width ([PL] §4 Implementation Details)
     rope_pairs: tuple = (6, 5, 5)     # complex pairs on the t, h, w axes
     rope_axis_dims: tuple = (12, 10, 10)
     rope_theta: float = 10000.0

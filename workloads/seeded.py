@@ -21,12 +21,19 @@ Weight layouts (y = x @ W, row-major):
   w_kr   [d_model, d_rope]
   w_k_up [n_heads, d_c, d_nope]
   w_v_up [n_heads, d_c, d_v]
+
+``mixer_weights`` adds the query-latent and output-mixer weights of the full
+attention layer:
+
+  w_dq   [d_model, d_q]                    query down-projection
+  w_uq   [d_q, n_heads * (d_nope + d_rope)] query up-projection, head-major
+  w_o    [n_heads * d_v, d_model]           output mixer
 """
 from __future__ import annotations
 
 import numpy as np
 
-ROLE_WQ, ROLE_WDOWN, ROLE_WKR, ROLE_WKUP, ROLE_WVUP, ROLE_X = range(6)
+ROLE_WQ, ROLE_WDOWN, ROLE_WKR, ROLE_WKUP, ROLE_WVUP, ROLE_X, ROLE_WDQ, ROLE_WUQ, ROLE_WO = range(9)
 
 
 def _rng(key) -> np.random.Generator:
@@ -68,6 +75,20 @@ def weights(w, layer: int = 0) -> dict:
         "w_kr": _normal([w.cfg_id, layer, ROLE_WKR, 0, 0, 0], (D, w.d_rope), sd, w.dtype),
         "w_k_up": _normal([w.cfg_id, layer, ROLE_WKUP, 0, 0, 0], (H, dc, w.d_nope), su, w.dtype),
         "w_v_up": _normal([w.cfg_id, layer, ROLE_WVUP, 0, 0, 0], (H, dc, w.d_v), su, w.dtype),
+    }
+
+
+def mixer_weights(w, layer: int = 0) -> dict:
+    """Seeded query-latent and output-mixer weights of one layer (fp32 arrays).
+    Scaled so that the query latent, the queries and the layer output keep unit
+    variance per entry for unit-variance inputs."""
+    D, H = w.d_model, w.n_heads
+    return {
+        "w_dq": _normal([w.cfg_id, layer, ROLE_WDQ, 0, 0, 0], (D, w.d_q), 1.0 / np.sqrt(D), w.dtype),
+        "w_uq": _normal([w.cfg_id, layer, ROLE_WUQ, 0, 0, 0], (w.d_q, H * w.d_head),
+                        1.0 / np.sqrt(w.d_q), w.dtype),
+        "w_o": _normal([w.cfg_id, layer, ROLE_WO, 0, 0, 0], (H * w.d_v, D),
+                       1.0 / np.sqrt(H * w.d_v), w.dtype),
     }
 
 
