@@ -16,7 +16,13 @@ append and the query prologue read HBM, not the 256 MB Infinity Cache, and
 their bulk inputs are device-generated N(0,1) tensors (values do not change the
 work).
 
+`--long-horizon` (config 2 only) keeps one sink frame plus a 6-frame window
+with k_R rotated at read time; `--layer` runs the whole attention layer instead
+of the attention core: the d_q = 768 query latent, the latent attention, and
+the output mixer W_O with B_h folded in (out [B, N_q, d_model]).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--config 2|3|4]
+                       [--long-horizon] [--layer]
 """
 from __future__ import annotations
 
@@ -39,8 +45,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def work(w):
-    """Algorithmic flops and bytes of one step (absorbed method, bf16 storage)."""
+def work(w, layer=False):
+    """Algorithmic flops and bytes of one step (absorbed method, bf16 storage).
+    ``layer``: the whole layer instead, with the d_q query latent (x W_DQ, then
+    the folded [A_h | W_UQ^rope[h]]) and B_h folded into the output mixer."""
     H, Nq, Nk, D = w.n_heads, w.n_q * w.batch, w.n_k, w.d_model
     B = w.batch
     per_qkh = 2 * (w.d_c + w.d_rope) + 2 * w.d_c                # 832
@@ -52,12 +60,15 @@ def work(w):
     bytes_append = Nq * D * 2 + D * w.cache_row * 2 + Nq * row
     bytes_prologue = Nq * D * 2 + D * H * w.d_head * 2 + H * w.d_c * w.d_nope * 2 + Nq * H * row
     bytes_attn = Nq * H * row + B * Nk * row + H * w.d_c * w.d_v * 2 + Nq * H * w.d_v * 2
+    if layer:
+        prologue = Nq * (2 * D * w.d_q + 2 * w.d_q * H * w.cache_row)
+        epilogue = Nq * 2 * H * w.d_c * D                            # [O_lat / l] x W_VO
     return dict(core=core, prologue=prologue, epilogue=epilogue, append=append,
                 attn_kernel=core + epilogue, step=core + prologue + epilogue + append,
                 bytes_append=bytes_append, bytes_prologue=bytes_prologue, bytes_attn=bytes_attn)
 
 
-def cpu_baseline(w, wts, x_host, step_flops):
+def cpu_baseline(w, wts, x_host, step_flops, mix=None):
     """Time the CPU fp64 oracle on the whole step: every query token of the
     chunk, all heads, the full key window (its explicit per-head K/V build
     included). About 10-30 s on a 16-core host."""
@@ -69,8 +80,11 @@ def cpu_baseline(w, wts, x_host, step_flops):
     except Exception:  # pragma: no cover - threadpoolctl is optional
         threads = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
-    ref = orc.chunk_attention_reindexed_reference if w.rope_at_read else orc.chunk_attention_reference
-    ref(w, wts, x_host, np.arange(w.n_q))
+    if mix is not None:
+        orc.chunk_layer_reference(w, wts, mix, x_host, np.arange(w.n_q))
+    else:
+        ref = orc.chunk_attention_reindexed_reference if w.rope_at_read else orc.chunk_attention_reference
+        ref(w, wts, x_host, np.arange(w.n_q))
     full_s = time.perf_counter() - t0
     log(f"[cpu_baseline] oracle on the full step: {full_s:.2f} s")
     return {
@@ -97,6 +111,9 @@ def main():
                     help="with --config 2: the long-rollout cache instead of the 21-frame window -- "
                          "one sink frame plus a 6-frame window, k_R cached before RoPE and "
                          "rotated in the active context, chunk at t = 18..20 after evictions")
+    ap.add_argument("--layer", action="store_true",
+                    help="the whole attention layer: d_q = 768 query latent, latent attention, "
+                         "B_h folded into the W_O output mixer (out [B, N_q, d_model])")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device-to-device copy of MIB MiB, whose counter "
                          "readings calibrate FETCH_SIZE / WRITE_SIZE")
@@ -111,7 +128,7 @@ def main():
     import torch
 
     import latent_kv_attention_cache_amd as vm
-    from workloads import config, weights, x_frame
+    from workloads import config, mixer_weights, weights, x_frame
 
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
@@ -142,6 +159,9 @@ def main():
         wts = weights(w)
         xs = {t: x_frame(w, t) for t in w.prior_frames + w.chunk_frame_ids}
         dw = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in wts.items()}
+        mix = mixer_weights(w) if args.layer else None
+        if args.layer:
+            dw.update({k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in mix.items()})
 
         def xdev(frames):
             return torch.from_numpy(np.concatenate([xs[t] for t in frames]))[None].to(dev).to(torch.bfloat16)
@@ -166,6 +186,9 @@ def main():
         shapes = {"w_q": (w.d_model, w.n_heads * w.d_head), "w_down": (w.d_model, w.d_c),
                   "w_kr": (w.d_model, w.d_rope), "w_k_up": (w.n_heads, w.d_c, w.d_nope),
                   "w_v_up": (w.n_heads, w.d_c, w.d_v)}
+        if args.layer:
+            shapes.update({"w_dq": (w.d_model, w.d_q), "w_uq": (w.d_q, w.n_heads * w.d_head),
+                           "w_o": (w.n_heads * w.d_v, w.d_model)})
         sets = []
         for _ in range(n_sets):
             dw = {k: (torch.randn(shp, generator=g, device=dev) * shp[-2] ** -0.5).to(torch.bfloat16)
@@ -177,9 +200,18 @@ def main():
         log(f"[bench] {n_sets} buffer sets of "
             f"{(sets[0][0].numel() + sets[0][2].data.numel()) * 2 / 1e6:.0f} MB")
     n_valid = w.n_valid_frames
-    ws = torch.empty(vm.vmla_attention_workspace_bytes(w.batch, w.n_q, dims), dtype=torch.uint8,
-                     device=dev)
-    out = torch.empty((w.batch, w.n_q, w.n_heads, w.d_v), dtype=torch.bfloat16, device=dev)
+    if args.layer:
+        # the one-time weight folds of the layer (not part of a step)
+        for _, dw, _ in sets:
+            dw["w_qa"] = vm.vmla_fold_query_weights(dw["w_uq"], dw["w_k_up"], w.d_q, dims=dims)
+            dw["w_vo"] = vm.vmla_fold_output_weights(dw["w_v_up"], dw["w_o"], dims=dims)
+        ws = torch.empty(vm.vmla_layer_workspace_bytes(w.batch, w.n_q, w.d_q, dims), dtype=torch.uint8,
+                         device=dev)
+        out = torch.empty((w.batch, w.n_q, w.d_model), dtype=torch.bfloat16, device=dev)
+    else:
+        ws = torch.empty(vm.vmla_attention_workspace_bytes(w.batch, w.n_q, dims), dtype=torch.uint8,
+                         device=dev)
+        out = torch.empty((w.batch, w.n_q, w.n_heads, w.d_v), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -191,12 +223,20 @@ def main():
         vm.vmla_cache_append(cache, x, dw["w_down"], dw["w_kr"], w.t_first, w.chunk_frames, dims=dims)
         if ev is not None:
             ev[1].record(stream)
-        vm.vmla_query_prologue(cache, x, dw["w_q"], dw["w_k_up"], w.t_first, w.chunk_frames, n_valid,
-                               ws, dims=dims)
+        if args.layer:
+            vm.vmla_layer_query_prologue(cache, x, dw["w_dq"], dw["w_qa"], w.t_first, w.chunk_frames,
+                                         n_valid, ws, dims=dims)
+        else:
+            vm.vmla_query_prologue(cache, x, dw["w_q"], dw["w_k_up"], w.t_first, w.chunk_frames,
+                                   n_valid, ws, dims=dims)
         if ev is not None:
             ev[2].record(stream)
-        vm.vmla_latent_attention(cache, dw["w_v_up"], w.t_first, w.chunk_frames, n_valid, out, ws,
-                                 dims=dims)
+        if args.layer:
+            vm.vmla_layer_attention(cache, w.d_q, dw["w_vo"], w.t_first, w.chunk_frames, n_valid, out,
+                                    ws, dims=dims)
+        else:
+            vm.vmla_latent_attention(cache, dw["w_v_up"], w.t_first, w.chunk_frames, n_valid, out, ws,
+                                     dims=dims)
         if ev is not None:
             ev[3].record(stream)
 
@@ -220,13 +260,13 @@ def main():
     k_ms = {k: v / args.steps for k, v in k_ms.items()}
     assert torch.isfinite(out.float()).all().item(), "non-finite output"
 
-    wk = work(w)
+    wk = work(w, layer=args.layer)
     tflops = wk["step"] / (ms_step * 1e-3) / 1e12
     attn_tflops = wk["attn_kernel"] / (k_ms["latent_attn"] * 1e-3) / 1e12
     append_gbs = wk["bytes_append"] / (k_ms["append"] * 1e-3) / 1e9
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "latent_attn_config2_traffic.json")
-    if args.config == 2 and not args.long_horizon and os.path.exists(tfile):
+    if args.config == 2 and not args.long_horizon and not args.layer and os.path.exists(tfile):
         with open(tfile) as f:
             tr = json.load(f)
         if tr.get("kernel_source_sha") == _kernel_sha():
@@ -275,11 +315,17 @@ def main():
     log(f"[bench] ms/step {ms_step:.4f}  kernels {k_ms}  attention {attn_tflops:.1f} TFLOP/s")
     if not args.no_cpu_baseline and args.config == 2:
         xh = lambda t: xs[t]  # noqa: E731
-        result["cpu_baseline"] = cpu_baseline(w, wts, xh, wk["step"])
+        result["cpu_baseline"] = cpu_baseline(w, wts, xh, wk["step"], mix)
     if args.long_horizon:
         result["config"]["workload"] = ("Wan-1.3B-shaped chunk-layer, long rollout: B=1, 30x52 "
                                         "grid, 3-frame query chunk at t=18..20 over one sink frame "
                                         "plus a 6-frame window, RoPE applied at read time")
+    if args.layer:
+        result["config"]["workload"] += ("; whole attention layer: d_q=768 query latent, latent "
+                                         "attention, B_h folded into the W_O output mixer")
+        result["config"]["d_q"] = w.d_q
+        result["kernels_ms"]["layer_attention"] = result["kernels_ms"].pop("latent_attn")
+        result["roofline"]["kernel"] = "latent_attn (folded epilogue) + output-mixer GEMM"
         result["config"]["sink_frames"] = w.sink_frames
         result["config"]["window_frames"] = w.window_frames
     print(json.dumps(result), flush=True)

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define VMLA_ABI_VERSION 2
+#define VMLA_ABI_VERSION 3
 
 typedef enum vmla_status {
   VMLA_OK = 0,
@@ -205,6 +205,88 @@ int32_t vmla_latent_attention(const vmla_dims* dims, const vmla_cache* cache, in
                               const void* w_v_up, int32_t t_first, int32_t n_frames,
                               int32_t n_valid_frames, void* out, const void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/*
+ * The whole attention layer: query latent and output mixer.
+ * ---------------------------------------------------------
+ * Defined by: queries from a d_q-wide query latent, c_q = x W_DQ, q = c_q W_UQ
+ * ([PL] §4 "Implementation Details": d_q = 768 by default); the content score
+ * applies a fixed per-head matrix A_h = W_UQ^nope[h] W_K_up[h]^T to the query
+ * latent ([PL] App. E "Content-path absorption"); the softmax-weighted latents
+ * are projected with B_h = W_V_up[h] folded into the output mixer W_O
+ * ([PL] App. E "Value-path absorption"); the positional branch is not folded
+ * ("RoPE branch"). The layer output is
+ *   y = sum_h softmax_h(...) c W_V_up[h] W_O[h],
+ * W_O[h] the d_v rows of W_O that mix head h, i.e. the concatenated head
+ * outputs of vmla_chunk_attention (queries from c_q W_UQ) times W_O.
+ *
+ * Weight layouts (dtype of the call unless stated):
+ *   w_dq  [d_model, d_q]
+ *   w_uq  [d_q, n_heads * (d_nope + d_rope)]  head-major, each head [nope | rope]
+ *   w_o   [n_heads * d_v, d_model]
+ *   w_qa  [d_q, n_heads * (d_c + d_rope)]     bf16 always: per head [A_h | W_UQ^rope[h]]
+ *   w_vo  [n_heads * d_c, d_model]            bf16 always: per head B_h W_O[h]
+ * d_q: a multiple of 64 in [64, 8192].
+ */
+
+/* w_qa from w_uq and w_k_up (formed once per set of weights; fp32 accumulation,
+ * bf16 result). Errors: VMLA_ERR_NULL, VMLA_ERR_DTYPE, VMLA_ERR_SHAPE (dims,
+ * d_q), VMLA_ERR_ALIGN, VMLA_ERR_HIP. */
+int32_t vmla_fold_query_weights(const vmla_dims* dims, int32_t dtype, int32_t d_q,
+                                const void* w_uq, const void* w_k_up, void* w_qa, void* stream);
+
+/* w_vo from w_v_up and w_o (formed once per set of weights; fp32 accumulation,
+ * bf16 result). Errors as vmla_fold_query_weights. */
+int32_t vmla_fold_output_weights(const vmla_dims* dims, int32_t dtype, const void* w_v_up,
+                                 const void* w_o, void* w_vo, void* stream);
+
+/* Bytes of device workspace the layer entry points need: the Qhat rows of
+ * vmla_attention_workspace_bytes, then one bf16 region of
+ * batch * n_q * max(d_q, n_heads * d_c) elements (its size rounded up to 256
+ * bytes) that holds the query latent during the prologue and the normalized
+ * latent outputs O_lat / l during the attention. Returns 0 for invalid
+ * arguments. */
+size_t vmla_layer_workspace_bytes(const vmla_dims* dims, int32_t d_q, int32_t batch, int32_t n_q);
+
+/*
+ * vmla_chunk_attention_layer -- one chunk step of the whole layer:
+ *   vmla_layer_query_prologue: c_q = x W_DQ (bf16, workspace), then
+ *     Qhat = [c_q A_h | RoPE3D(c_q W_UQ^rope[h])] * scale * log2(e) for every
+ *     head (same Qhat rows and coordinates as vmla_query_prologue);
+ *   vmla_layer_attention: scores, online softmax and weighted latents exactly as
+ *     vmla_latent_attention, then O_lat / l of every head (bf16, workspace) and
+ *     y = [O_lat,0 / l | ... | O_lat,H-1 / l] w_vo.
+ *   x    [batch, n_q, d_model], n_q = n_frames * T
+ *   out  [batch, n_q, d_model] (dtype of the call)
+ * Cache, t_first, n_frames, n_valid_frames: as vmla_chunk_attention.
+ * Errors: as vmla_chunk_attention (workspace checked against
+ * vmla_layer_workspace_bytes), plus VMLA_ERR_SHAPE for d_q or more than 2^28
+ * query rows. The two stages are callable separately with the same arguments;
+ * vmla_layer_attention reads the Qhat rows the prologue left in workspace.
+ */
+int32_t vmla_chunk_attention_layer(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                                   const void* x, const void* w_dq, int32_t d_q, const void* w_qa,
+                                   const void* w_vo, int32_t t_first, int32_t n_frames,
+                                   int32_t n_valid_frames, void* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+int32_t vmla_layer_query_prologue(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                                  const void* x, const void* w_dq, int32_t d_q, const void* w_qa,
+                                  int32_t t_first, int32_t n_frames, int32_t n_valid_frames,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+int32_t vmla_layer_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                             int32_t d_q, const void* w_vo, int32_t t_first, int32_t n_frames,
+                             int32_t n_valid_frames, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* out [m, d_model] = in [m, n_heads * d_v] w_o [n_heads * d_v, d_model]: the
+ * output mixer applied to vmla_chunk_attention's head outputs (viewed as
+ * [batch * n_q, n_heads * d_v]) without folding; the same product as the folded
+ * path up to rounding. Errors: VMLA_ERR_NULL, VMLA_ERR_DTYPE, VMLA_ERR_SHAPE
+ * (dims, m < 1 or m > 2^24), VMLA_ERR_ALIGN, VMLA_ERR_HIP. */
+int32_t vmla_output_projection(const vmla_dims* dims, int32_t dtype, int64_t m, const void* in,
+                               const void* w_o, void* out, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* vmla_status_string(int32_t status);

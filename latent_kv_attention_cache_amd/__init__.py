@@ -9,7 +9,10 @@ from ._binding import (VMLA_OK, VMLA_ERR_NULL, VMLA_ERR_SHAPE, VMLA_ERR_DTYPE, V
                        EXPORTED, LatentCache, VmlaError, default_dims, load_library, vmla_cache,
                        vmla_dims, vmla_attention_workspace_bytes, vmla_cache_append,
                        vmla_chunk_attention, vmla_latent_attention,
-                       vmla_query_prologue, vmla_status_string)
+                       vmla_query_prologue, vmla_status_string, vmla_fold_query_weights,
+                       vmla_fold_output_weights, vmla_layer_workspace_bytes,
+                       vmla_chunk_attention_layer, vmla_layer_query_prologue, vmla_layer_attention,
+                       vmla_output_projection)
 
 __all__ = [
     "VMLA_OK", "VMLA_ERR_NULL", "VMLA_ERR_SHAPE", "VMLA_ERR_DTYPE", "VMLA_ERR_ALIGN",
@@ -17,4 +20,7 @@ __all__ = [
     "LatentCache", "VmlaError", "default_dims", "load_library", "vmla_cache", "vmla_dims",
     "vmla_attention_workspace_bytes", "vmla_cache_append", "vmla_chunk_attention",
     "vmla_query_prologue", "vmla_latent_attention", "vmla_status_string",
+    "vmla_fold_query_weights", "vmla_fold_output_weights", "vmla_layer_workspace_bytes",
+    "vmla_chunk_attention_layer", "vmla_layer_query_prologue", "vmla_layer_attention",
+    "vmla_output_projection",
 ]

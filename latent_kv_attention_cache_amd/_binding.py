@@ -58,7 +58,9 @@ _LIB = None
 
 EXPORTED = ("vmla_default_dims", "vmla_cache_append", "vmla_attention_workspace_bytes",
             "vmla_chunk_attention", "vmla_query_prologue", "vmla_latent_attention",
-            "vmla_status_string", "vmla_abi_version")
+            "vmla_fold_query_weights", "vmla_fold_output_weights", "vmla_layer_workspace_bytes",
+            "vmla_chunk_attention_layer", "vmla_layer_query_prologue", "vmla_layer_attention",
+            "vmla_output_projection", "vmla_status_string", "vmla_abi_version")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -88,6 +90,21 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vmla_latent_attention.argtypes = [ctypes.POINTER(vmla_dims), ctypes.POINTER(vmla_cache), I32,
                                           P, I32, I32, I32, P, P, ctypes.c_size_t, P]
     lib.vmla_latent_attention.restype = I32
+    D, C, SZ = ctypes.POINTER(vmla_dims), ctypes.POINTER(vmla_cache), ctypes.c_size_t
+    lib.vmla_fold_query_weights.argtypes = [D, I32, I32, P, P, P, P]
+    lib.vmla_fold_query_weights.restype = I32
+    lib.vmla_fold_output_weights.argtypes = [D, I32, P, P, P, P]
+    lib.vmla_fold_output_weights.restype = I32
+    lib.vmla_layer_workspace_bytes.argtypes = [D, I32, I32, I32]
+    lib.vmla_layer_workspace_bytes.restype = SZ
+    lib.vmla_chunk_attention_layer.argtypes = [D, C, I32, P, P, I32, P, P, I32, I32, I32, P, P, SZ, P]
+    lib.vmla_chunk_attention_layer.restype = I32
+    lib.vmla_layer_query_prologue.argtypes = [D, C, I32, P, P, I32, P, I32, I32, I32, P, SZ, P]
+    lib.vmla_layer_query_prologue.restype = I32
+    lib.vmla_layer_attention.argtypes = [D, C, I32, I32, P, I32, I32, I32, P, P, SZ, P]
+    lib.vmla_layer_attention.restype = I32
+    lib.vmla_output_projection.argtypes = [D, I32, ctypes.c_int64, P, P, P, P]
+    lib.vmla_output_projection.restype = I32
     lib.vmla_status_string.argtypes = [I32]
     lib.vmla_status_string.restype = ctypes.c_char_p
     lib.vmla_abi_version.argtypes = []
@@ -305,4 +322,170 @@ def vmla_latent_attention(cache: LatentCache, w_v_up, t_first: int, n_frames: in
                                    workspace.numel() * workspace.element_size(), _stream(stream))
     if st != VMLA_OK:
         raise VmlaError(st, "vmla_latent_attention")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# The whole attention layer: query latent and folded output mixer
+# ---------------------------------------------------------------------------
+
+def _same_dtype(ref: torch.Tensor, **tensors):
+    for n, t in tensors.items():
+        if t.dtype != ref.dtype:
+            raise TypeError(f"{n} dtype {t.dtype} differs from {ref.dtype}")
+
+
+def vmla_fold_query_weights(w_uq: torch.Tensor, w_k_up: torch.Tensor, d_q: int,
+                            out: torch.Tensor | None = None, dims: vmla_dims | None = None,
+                            stream=None) -> torch.Tensor:
+    """bf16 [d_q, n_heads * (d_c + d_rope)]: per head [A_h | W_UQ^rope[h]]."""
+    lib = load_library()
+    d = dims or default_dims()
+    _expect_shape(w_uq, (d_q, d.n_heads * (d.d_nope + d.d_rope)), "w_uq")
+    _expect_shape(w_k_up, (d.n_heads, d.d_c, d.d_nope), "w_k_up")
+    _same_dtype(w_uq, w_k_up=w_k_up)
+    if out is None:
+        out = torch.empty((d_q, d.n_heads * (d.d_c + d.d_rope)), dtype=torch.bfloat16,
+                          device=w_uq.device)
+    _expect_shape(out, (d_q, d.n_heads * (d.d_c + d.d_rope)), "w_qa")
+    if out.dtype != torch.bfloat16:
+        raise TypeError("w_qa must be bfloat16")
+    st = lib.vmla_fold_query_weights(ctypes.byref(d), _dtype_code(w_uq), int(d_q), _dev(w_uq, "w_uq"),
+                                     _dev(w_k_up, "w_k_up"), _dev(out, "w_qa"), _stream(stream))
+    if st != VMLA_OK:
+        raise VmlaError(st, "vmla_fold_query_weights")
+    return out
+
+
+def vmla_fold_output_weights(w_v_up: torch.Tensor, w_o: torch.Tensor, out: torch.Tensor | None = None,
+                             dims: vmla_dims | None = None, stream=None) -> torch.Tensor:
+    """bf16 [n_heads * d_c, d_model]: per head B_h W_O[h]."""
+    lib = load_library()
+    d = dims or default_dims()
+    _expect_shape(w_v_up, (d.n_heads, d.d_c, d.d_v), "w_v_up")
+    _expect_shape(w_o, (d.n_heads * d.d_v, d.d_model), "w_o")
+    _same_dtype(w_v_up, w_o=w_o)
+    if out is None:
+        out = torch.empty((d.n_heads * d.d_c, d.d_model), dtype=torch.bfloat16, device=w_o.device)
+    _expect_shape(out, (d.n_heads * d.d_c, d.d_model), "w_vo")
+    if out.dtype != torch.bfloat16:
+        raise TypeError("w_vo must be bfloat16")
+    st = lib.vmla_fold_output_weights(ctypes.byref(d), _dtype_code(w_o), _dev(w_v_up, "w_v_up"),
+                                      _dev(w_o, "w_o"), _dev(out, "w_vo"), _stream(stream))
+    if st != VMLA_OK:
+        raise VmlaError(st, "vmla_fold_output_weights")
+    return out
+
+
+def vmla_layer_workspace_bytes(batch: int, n_q: int, d_q: int, dims: vmla_dims | None = None) -> int:
+    d = dims or default_dims()
+    return int(load_library().vmla_layer_workspace_bytes(ctypes.byref(d), int(d_q), int(batch),
+                                                         int(n_q)))
+
+
+def _layer_common(cache, x, w_dq, d_q, w_qa, w_vo, n_frames, out, workspace, d):
+    B, T = cache.batch, cache.tokens_per_frame
+    n_q = n_frames * T
+    if x is not None:
+        _expect_shape(x, (B, n_q, d.d_model), "x")
+        _same_dtype(cache.data, x=x)
+    if w_dq is not None:
+        _expect_shape(w_dq, (d.d_model, d_q), "w_dq")
+        _same_dtype(cache.data, w_dq=w_dq)
+    if w_qa is not None:
+        _expect_shape(w_qa, (d_q, d.n_heads * (d.d_c + d.d_rope)), "w_qa")
+        if w_qa.dtype != torch.bfloat16:
+            raise TypeError("w_qa must be bfloat16")
+    if w_vo is not None:
+        _expect_shape(w_vo, (d.n_heads * d.d_c, d.d_model), "w_vo")
+        if w_vo.dtype != torch.bfloat16:
+            raise TypeError("w_vo must be bfloat16")
+    if out is not None:
+        _expect_shape(out, (B, n_q, d.d_model), "out")
+        _same_dtype(cache.data, out=out)
+    need = vmla_layer_workspace_bytes(B, n_q, d_q, d)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold at least {need} bytes")
+    _dev(cache.data, "cache")
+    return cache.c_struct(), _dtype_code(cache.data)
+
+
+def vmla_chunk_attention_layer(cache: LatentCache, x: torch.Tensor, w_dq: torch.Tensor,
+                               w_qa: torch.Tensor, w_vo: torch.Tensor, t_first: int, n_frames: int,
+                               n_valid_frames: int, out: torch.Tensor | None = None,
+                               workspace: torch.Tensor | None = None, dims: vmla_dims | None = None,
+                               stream=None) -> torch.Tensor:
+    """One chunk step of the whole layer; returns ``out`` [batch, n_q, d_model]."""
+    lib = load_library()
+    d = dims or default_dims()
+    d_q = w_dq.shape[1]
+    B, n_q = cache.batch, n_frames * cache.tokens_per_frame
+    if out is None:
+        out = torch.empty((B, n_q, d.d_model), dtype=cache.data.dtype, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(vmla_layer_workspace_bytes(B, n_q, d_q, d), dtype=torch.uint8,
+                                device=x.device)
+    cs, code = _layer_common(cache, x, w_dq, d_q, w_qa, w_vo, n_frames, out, workspace, d)
+    st = lib.vmla_chunk_attention_layer(ctypes.byref(d), ctypes.byref(cs), code, _dev(x, "x"),
+                                        _dev(w_dq, "w_dq"), int(d_q), _dev(w_qa, "w_qa"),
+                                        _dev(w_vo, "w_vo"), int(t_first), int(n_frames),
+                                        int(n_valid_frames), _dev(out, "out"),
+                                        _dev(workspace, "workspace"),
+                                        workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != VMLA_OK:
+        raise VmlaError(st, "vmla_chunk_attention_layer")
+    return out
+
+
+def vmla_layer_query_prologue(cache: LatentCache, x, w_dq, w_qa, t_first: int, n_frames: int,
+                              n_valid_frames: int, workspace: torch.Tensor,
+                              dims: vmla_dims | None = None, stream=None) -> None:
+    """First stage of vmla_chunk_attention_layer: query latent and Qhat rows into ``workspace``."""
+    lib = load_library()
+    d = dims or default_dims()
+    d_q = w_dq.shape[1]
+    cs, code = _layer_common(cache, x, w_dq, d_q, w_qa, None, n_frames, None, workspace, d)
+    st = lib.vmla_layer_query_prologue(ctypes.byref(d), ctypes.byref(cs), code, _dev(x, "x"),
+                                       _dev(w_dq, "w_dq"), int(d_q), _dev(w_qa, "w_qa"), int(t_first),
+                                       int(n_frames), int(n_valid_frames), _dev(workspace, "workspace"),
+                                       workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != VMLA_OK:
+        raise VmlaError(st, "vmla_layer_query_prologue")
+
+
+def vmla_layer_attention(cache: LatentCache, d_q: int, w_vo, t_first: int, n_frames: int,
+                         n_valid_frames: int, out: torch.Tensor, workspace: torch.Tensor,
+                         dims: vmla_dims | None = None, stream=None) -> torch.Tensor:
+    """Second stage of vmla_chunk_attention_layer: attention and folded output mixer."""
+    lib = load_library()
+    d = dims or default_dims()
+    cs, code = _layer_common(cache, None, None, d_q, None, w_vo, n_frames, out, workspace, d)
+    st = lib.vmla_layer_attention(ctypes.byref(d), ctypes.byref(cs), code, int(d_q), _dev(w_vo, "w_vo"),
+                                  int(t_first), int(n_frames), int(n_valid_frames), _dev(out, "out"),
+                                  _dev(workspace, "workspace"),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != VMLA_OK:
+        raise VmlaError(st, "vmla_layer_attention")
+    return out
+
+
+def vmla_output_projection(heads: torch.Tensor, w_o: torch.Tensor, out: torch.Tensor | None = None,
+                           dims: vmla_dims | None = None, stream=None) -> torch.Tensor:
+    """Unfolded output mixer: ``heads`` [..., n_heads, d_v] (vmla_chunk_attention's
+    output) times w_o [n_heads * d_v, d_model] -> [..., d_model]."""
+    lib = load_library()
+    d = dims or default_dims()
+    if tuple(heads.shape[-2:]) != (d.n_heads, d.d_v):
+        raise ValueError(f"heads has shape {tuple(heads.shape)}, expected [..., {d.n_heads}, {d.d_v}]")
+    _expect_shape(w_o, (d.n_heads * d.d_v, d.d_model), "w_o")
+    _same_dtype(heads, w_o=w_o)
+    m = heads.numel() // (d.n_heads * d.d_v)
+    if out is None:
+        out = torch.empty(tuple(heads.shape[:-2]) + (d.d_model,), dtype=heads.dtype, device=heads.device)
+    _expect_shape(out, tuple(heads.shape[:-2]) + (d.d_model,), "out")
+    _same_dtype(heads, out=out)
+    st = lib.vmla_output_projection(ctypes.byref(d), _dtype_code(heads), int(m), _dev(heads, "heads"),
+                                    _dev(w_o, "w_o"), _dev(out, "out"), _stream(stream))
+    if st != VMLA_OK:
+        raise VmlaError(st, "vmla_output_projection")
     return out

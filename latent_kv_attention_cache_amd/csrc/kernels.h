@@ -54,6 +54,7 @@ struct AttnArgs {
   const void* cache;    // [batch, cache_rows, kRow]
   const void* w_v_up;   // [n_heads, kDC, kDV]
   void* out;            // [batch, n_q, n_heads, kDV]
+  uint16_t* olat;       // null, or [batch * n_q, n_heads * kDC] bf16: O_lat / l instead of out
   int batch, n_q, n_heads, n_k, cache_rows;
   // Read-time RoPE of k_R (rope_at_read = 1): the key in slot frame fs sits at
   // temporal coordinate fs when fs < sink_frames, otherwise at
@@ -63,9 +64,37 @@ struct AttnArgs {
   RopeTable rope;
 };
 
+// out = A W over row-major operands; A [m][lda >= k], W [k][n]. mode 0:
+// out [m][n]; mode 1: the Qhat epilogue (n = n_heads * kRow, A and W bf16).
+struct GemmArgs {
+  const void* a;
+  const void* w;
+  void* out;
+  int64_t m;
+  int k, n, lda, mode;
+  // Qhat epilogue only
+  int n_q, n_heads, grid_w, tokens_per_frame, t_first;
+  float inv_grid_w, inv_tokens_per_frame, qscale;
+  RopeTable rope;
+};
+
+// One-time weight folds (bf16 results). Query: w_first = W_UQ [d_in][n_heads
+// kDHead], w_second = W_K_up [n_heads][kDC][kDNope], out [d_in][n_heads kRow].
+// Output: w_first = W_V_up [n_heads][kDC][kDV], w_second = W_O [n_heads kDV][d_out],
+// out [n_heads kDC][d_out].
+struct FoldArgs {
+  const void* w_first;
+  const void* w_second;
+  void* out;
+  int d_in, d_out, n_heads;
+};
+
 hipError_t launch_append(const AppendArgs& a, bool f32, hipStream_t s);
 int append_plan(int64_t m, int cus, int* nrb);   // append workgroups for m rows; row blocks per wave
 hipError_t launch_qprologue(const QArgs& a, bool f32, hipStream_t s);
 hipError_t launch_latent_attn(const AttnArgs& a, bool f32, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& a, int a_f32, int out_f32, hipStream_t s);
+hipError_t launch_fold_query(const FoldArgs& a, bool f32, hipStream_t s);
+hipError_t launch_fold_output(const FoldArgs& a, bool f32, hipStream_t s);
 
 }  // namespace vmla

@@ -51,6 +51,11 @@
 // Epilogue: out^T[e][q] = W_V_up[h]^T[e][:] . (O^T / l)[:][q], W_V_up[h]
 // staged in LDS and read transposed.
 //
+// Folded output (template flag kFold; App. E "Value-path absorption" with B_h
+// folded into the output mixer): the epilogue writes the normalized latent
+// O_lat / l of each (token, head) as bf16 to olat[b n_q + n][h d_c ..] and the
+// folded mixer weights are applied by a separate GEMM over all heads.
+//
 // Read-time RoPE (caches that keep k_R before rotation, [PL] App. D.5 and
 // App. E "RoPE branch"; template flag kRot): loading wave w moves chunk column
 // 24 + w of every tile, i.e. RoPE pairs 4w .. 4w+3 of k_R. Once its own loads
@@ -97,7 +102,7 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
                :: "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory");
 }
 
-template <typename T, bool kRot>
+template <typename T, bool kRot, bool kFold>
 __global__ __launch_bounds__(kThreads)
 void latent_attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t kt[kBufs * kTileElems];
@@ -350,9 +355,27 @@ void latent_attn_kernel(AttnArgs a) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+  const float inv = 1.f / sum_across_halves(l);
+  if constexpr (kFold) {
+    // ---- epilogue: olat = O / l. Register 8 jj + e of latent tile t holds
+    // latent dim 32 t + 16 jj + 8 (e / 4) + 4 half + e % 4 of query qrow.
+    if (!qvalid) return;   // no barrier follows
+    uint16_t* dst = a.olat + ((size_t)b * a.n_q + qrow) * ((size_t)a.n_heads * kDC) + (size_t)h * kDC;
+#pragma unroll
+    for (int t = 0; t < kLatTiles; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int e4 = 0; e4 < 2; ++e4) {
+          const int r = 8 * jj + 4 * e4;
+          *reinterpret_cast<uint2*>(dst + 32 * t + 16 * jj + 8 * e4 + 4 * half) =
+              uint2{pack2(o[t][r] * inv, o[t][r + 1] * inv), pack2(o[t][r + 2] * inv, o[t][r + 3] * inv)};
+        }
+    return;
+  }
+
   // ---- epilogue: out = (O / l) @ W_V_up[h]; W_V_up of the workgroup's one or
   // two heads staged in LDS, [kDC][kVLd] each.
-  const float inv = 1.f / sum_across_halves(l);
   const int nh = min((u0 + kWaves - 1) / upad, a.n_heads - 1) - h_lo + 1;   // 1 or 2 (upad >= 8)
   const T* wsrc = static_cast<const T*>(a.w_v_up) + (size_t)h_lo * kDC * kDV;
   for (int hh = 0; hh < nh; ++hh) {
@@ -406,12 +429,20 @@ hipError_t launch_latent_attn(const AttnArgs& a, bool f32, hipStream_t s) {
   const int units = (a.n_q + 31) / 32;
   const int upad = units > kWaves ? units : kWaves;
   dim3 grid((a.n_heads * upad + kWaves - 1) / kWaves, 1, a.batch);
-  if (a.rope_at_read) {
-    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, true>), grid, dim3(kThreads), 0, s, a);
+  if (a.olat) {
+    if (a.rope_at_read) {
+      if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, true, true>), grid, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, true, true>), grid, dim3(kThreads), 0, s, a);
+    } else {
+      if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, true>), grid, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, true>), grid, dim3(kThreads), 0, s, a);
+    }
+  } else if (a.rope_at_read) {
+    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, true, false>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, true, false>), grid, dim3(kThreads), 0, s, a);
   } else {
-    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false>), grid, dim3(kThreads), 0, s, a);
+    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, false>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, false>), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -240,4 +240,171 @@ int32_t vmla_chunk_attention(const vmla_dims* dims, const vmla_cache* cache, int
   return hip_status(launch_latent_attn(a, dtype == VMLA_F32, s));
 }
 
+// ---- the whole attention layer: query latent and folded output mixer
+
+static int32_t check_d_q(int32_t d_q) {
+  return (d_q >= 64 && d_q <= 8192 && d_q % 64 == 0) ? VMLA_OK : VMLA_ERR_SHAPE;
+}
+
+int32_t vmla_fold_query_weights(const vmla_dims* dims, int32_t dtype, int32_t d_q,
+                                const void* w_uq, const void* w_k_up, void* w_qa, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st) return st;
+  if (!w_uq || !w_k_up || !w_qa) return VMLA_ERR_NULL;
+  if (dtype != VMLA_F32 && dtype != VMLA_BF16) return VMLA_ERR_DTYPE;
+  st = check_d_q(d_q);
+  if (st) return st;
+  if (!aligned16(w_uq) || !aligned16(w_k_up) || !aligned16(w_qa)) return VMLA_ERR_ALIGN;
+  FoldArgs f{};
+  f.w_first = w_uq; f.w_second = w_k_up; f.out = w_qa;
+  f.d_in = d_q; f.n_heads = dims->n_heads;
+  return hip_status(launch_fold_query(f, dtype == VMLA_F32, static_cast<hipStream_t>(stream)));
+}
+
+int32_t vmla_fold_output_weights(const vmla_dims* dims, int32_t dtype, const void* w_v_up,
+                                 const void* w_o, void* w_vo, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st) return st;
+  if (!w_v_up || !w_o || !w_vo) return VMLA_ERR_NULL;
+  if (dtype != VMLA_F32 && dtype != VMLA_BF16) return VMLA_ERR_DTYPE;
+  if (!aligned16(w_v_up) || !aligned16(w_o) || !aligned16(w_vo)) return VMLA_ERR_ALIGN;
+  FoldArgs f{};
+  f.w_first = w_v_up; f.w_second = w_o; f.out = w_vo;
+  f.d_out = dims->d_model; f.n_heads = dims->n_heads;
+  return hip_status(launch_fold_output(f, dtype == VMLA_F32, static_cast<hipStream_t>(stream)));
+}
+
+size_t vmla_layer_workspace_bytes(const vmla_dims* dims, int32_t d_q, int32_t batch, int32_t n_q) {
+  if (check_d_q(d_q) != VMLA_OK) return 0;
+  const size_t qhat = vmla_attention_workspace_bytes(dims, batch, n_q);
+  if (!qhat) return 0;
+  const size_t m = (size_t)batch * n_q;
+  const size_t lat = (size_t)dims->n_heads * kDC;
+  const size_t inner = m * ((size_t)d_q > lat ? (size_t)d_q : lat) * sizeof(uint16_t);
+  return qhat + ((inner + 255) / 256) * 256;
+}
+
+namespace {
+
+// Validation shared by the layer stages: the attention checks plus d_q and the
+// layer workspace; *inner points just past the Qhat rows (a multiple of 448 bytes).
+int32_t check_layer(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype, int32_t d_q,
+                    int32_t t_first, int32_t n_frames, int32_t n_valid_frames,
+                    const void* workspace, size_t workspace_bytes, QArgs* q, AttnArgs* a,
+                    uint16_t** inner) {
+  int32_t st = check_d_q(d_q);
+  if (st) return st;
+  st = check_attention(dims, cache, dtype, t_first, n_frames, n_valid_frames, workspace,
+                       workspace_bytes, q, a);
+  if (st) return st;
+  const int64_t m = (int64_t)cache->batch * q->n_q;
+  if (m > ((int64_t)1 << 28)) return VMLA_ERR_SHAPE;
+  if (workspace_bytes < vmla_layer_workspace_bytes(dims, d_q, cache->batch, q->n_q))
+    return VMLA_ERR_WORKSPACE;
+  const size_t qhat = vmla_attention_workspace_bytes(dims, cache->batch, q->n_q);
+  *inner = reinterpret_cast<uint16_t*>(static_cast<char*>(const_cast<void*>(workspace)) + qhat);
+  return VMLA_OK;
+}
+
+int32_t launch_layer_prologue(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                              const void* x, const void* w_dq, int32_t d_q, const void* w_qa,
+                              const QArgs& q, uint16_t* c_q, hipStream_t s) {
+  // c_q = x W_DQ (bf16 rows of the workspace)
+  GemmArgs g1{};
+  g1.a = x; g1.w = w_dq; g1.out = c_q;
+  g1.m = (int64_t)cache->batch * q.n_q; g1.k = dims->d_model; g1.n = d_q; g1.lda = dims->d_model;
+  g1.mode = 0;
+  int32_t st = hip_status(launch_gemm(g1, dtype == VMLA_F32, 0, s));
+  if (st) return st;
+  // Qhat = [c_q A_h | RoPE3D(c_q W_UQ^R[h])] * scale * log2(e), every head
+  GemmArgs g2{};
+  g2.a = c_q; g2.w = w_qa; g2.out = q.qhat;
+  g2.m = g1.m; g2.k = d_q; g2.n = dims->n_heads * kRow; g2.lda = d_q; g2.mode = 1;
+  g2.n_q = q.n_q; g2.n_heads = q.n_heads; g2.grid_w = q.grid_w; g2.tokens_per_frame = q.tokens_per_frame;
+  g2.t_first = q.t_first; g2.inv_grid_w = q.inv_grid_w; g2.inv_tokens_per_frame = q.inv_tokens_per_frame;
+  g2.qscale = q.qscale; g2.rope = q.rope;
+  return hip_status(launch_gemm(g2, 0, 0, s));
+}
+
+int32_t launch_layer_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                               const void* w_vo, void* out, AttnArgs a, uint16_t* olat, hipStream_t s) {
+  a.olat = olat;
+  int32_t st = hip_status(launch_latent_attn(a, dtype == VMLA_F32, s));
+  if (st) return st;
+  // out = [O_lat,0 / l | ... | O_lat,H-1 / l] W_VO over all heads
+  GemmArgs g{};
+  g.a = olat; g.w = w_vo; g.out = out;
+  g.m = (int64_t)cache->batch * a.n_q; g.k = dims->n_heads * kDC; g.n = dims->d_model;
+  g.lda = g.k; g.mode = 0;
+  return hip_status(launch_gemm(g, 0, dtype == VMLA_F32, s));
+}
+
+}  // namespace
+
+int32_t vmla_layer_query_prologue(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                                  const void* x, const void* w_dq, int32_t d_q, const void* w_qa,
+                                  int32_t t_first, int32_t n_frames, int32_t n_valid_frames,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !w_dq || !w_qa) return VMLA_ERR_NULL;
+  QArgs q;
+  AttnArgs a;
+  uint16_t* inner;
+  int32_t st = check_layer(dims, cache, dtype, d_q, t_first, n_frames, n_valid_frames, workspace,
+                           workspace_bytes, &q, &a, &inner);
+  if (st) return st;
+  if (!aligned16(x) || !aligned16(w_dq) || !aligned16(w_qa)) return VMLA_ERR_ALIGN;
+  return launch_layer_prologue(dims, cache, dtype, x, w_dq, d_q, w_qa, q, inner,
+                               static_cast<hipStream_t>(stream));
+}
+
+int32_t vmla_layer_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                             int32_t d_q, const void* w_vo, int32_t t_first, int32_t n_frames,
+                             int32_t n_valid_frames, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!w_vo || !out) return VMLA_ERR_NULL;
+  QArgs q;
+  AttnArgs a;
+  uint16_t* inner;
+  int32_t st = check_layer(dims, cache, dtype, d_q, t_first, n_frames, n_valid_frames, workspace,
+                           workspace_bytes, &q, &a, &inner);
+  if (st) return st;
+  if (!aligned16(w_vo) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  return launch_layer_attention(dims, cache, dtype, w_vo, out, a, inner, static_cast<hipStream_t>(stream));
+}
+
+int32_t vmla_chunk_attention_layer(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                                   const void* x, const void* w_dq, int32_t d_q, const void* w_qa,
+                                   const void* w_vo, int32_t t_first, int32_t n_frames,
+                                   int32_t n_valid_frames, void* out, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (!x || !w_dq || !w_qa || !w_vo || !out) return VMLA_ERR_NULL;
+  QArgs q;
+  AttnArgs a;
+  uint16_t* inner;
+  int32_t st = check_layer(dims, cache, dtype, d_q, t_first, n_frames, n_valid_frames, workspace,
+                           workspace_bytes, &q, &a, &inner);
+  if (st) return st;
+  if (!aligned16(x) || !aligned16(w_dq) || !aligned16(w_qa) || !aligned16(w_vo) || !aligned16(out))
+    return VMLA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch_layer_prologue(dims, cache, dtype, x, w_dq, d_q, w_qa, q, inner, s);
+  if (st) return st;
+  return launch_layer_attention(dims, cache, dtype, w_vo, out, a, inner, s);
+}
+
+int32_t vmla_output_projection(const vmla_dims* dims, int32_t dtype, int64_t m, const void* in,
+                               const void* w_o, void* out, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st) return st;
+  if (!in || !w_o || !out) return VMLA_ERR_NULL;
+  if (dtype != VMLA_F32 && dtype != VMLA_BF16) return VMLA_ERR_DTYPE;
+  if (m < 1 || m > ((int64_t)1 << 31) / 128) return VMLA_ERR_SHAPE;
+  if (!aligned16(in) || !aligned16(w_o) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  GemmArgs g{};
+  g.a = in; g.w = w_o; g.out = out;
+  g.m = m; g.k = dims->n_heads * kDV; g.n = dims->d_model; g.lda = g.k; g.mode = 0;
+  const int f32 = dtype == VMLA_F32;
+  return hip_status(launch_gemm(g, f32, f32, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

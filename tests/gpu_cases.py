@@ -11,7 +11,7 @@ import torch
 
 import latent_kv_attention_cache_amd as vm
 import oracle.vmla_oracle as orc
-from workloads import weights, x_frame
+from workloads import mixer_weights, weights, x_frame
 
 REL_FROB = 1e-2     # ||gpu - ref||_F / ||ref||_F
 MAX_ABS = 3e-2      # max |gpu - ref|
@@ -118,6 +118,41 @@ class Run:
         self.fill_window()
         self.append(self.w.t_first, self.w.chunk_frames)
         return self.attention()
+
+    # ---- the whole layer: query latent and folded output mixer
+
+    def _mixer(self):
+        if not hasattr(self, "mix"):
+            self.mix = mixer_weights(self.w, self.layer)
+            self.dmix = dev_weights(self.w, self.mix, self.device)
+            self.w_qa = vm.vmla_fold_query_weights(self.dmix["w_uq"], self.dw["w_k_up"], self.w.d_q,
+                                                   dims=self.dims)
+            self.w_vo = vm.vmla_fold_output_weights(self.dw["w_v_up"], self.dmix["w_o"], dims=self.dims)
+
+    def layer_call(self, t_first=None, n_frames=None):
+        """vmla_chunk_attention_layer for the chunk; returns out [B, N_q, d_model]."""
+        self._mixer()
+        w = self.w
+        t_first = w.t_first if t_first is None else t_first
+        n_frames = w.chunk_frames if n_frames is None else n_frames
+        x = self.x_dev(range(t_first, t_first + n_frames))
+        n_valid = self.cache.n_valid_frames(t_first, n_frames)
+        return vm.vmla_chunk_attention_layer(self.cache, x, self.dmix["w_dq"], self.w_qa, self.w_vo,
+                                             t_first, n_frames, n_valid, dims=self.dims)
+
+    def layer_step(self):
+        """Fill the window, append the chunk, run the whole layer."""
+        self.fill_window()
+        self.append(self.w.t_first, self.w.chunk_frames)
+        return self.layer_call()
+
+    def layer_reference(self, b=0, query_tokens=None, t_first=None, n_frames=None):
+        self._mixer()
+        w = self.w
+        if t_first is not None:
+            w = w.with_(t_first=t_first, chunk_frames=n_frames or w.chunk_frames)
+        return orc.chunk_layer_reference(w, self.wts, self.mix, lambda t: self.x_host(t, b),
+                                         query_tokens)
 
     def reference(self, b=0, query_tokens=None, t_first=None, n_frames=None):
         w = self.w

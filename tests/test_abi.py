@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.vmla_abi_version() == 2
+    assert lib.vmla_abi_version() == 3
     for code in range(-7, 1):
         s = vm.vmla_status_string(code)
         assert s and s != "unknown status"
@@ -134,6 +134,59 @@ def test_cache_mode_validation(lib):
     assert _attn(lib, cache=sink, t_first=10, n_frames=1, n_valid=5) == vm.VMLA_ERR_RANGE
     assert _attn(lib, cache=sink, t_first=0, n_frames=2, n_valid=3) == vm.VMLA_ERR_RANGE
     assert _append(lib, cache=sink, n_frames=4) == vm.VMLA_ERR_RANGE   # > window_frames
+
+
+def _layer(lib, dims=None, cache=None, dtype=vm.VMLA_BF16, d_q=768, t_first=2, n_frames=1, n_valid=3,
+           ws_bytes=None, ws=B, out=C, x=A, w_dq=B, w_qa=C, w_vo=A):
+    d = dims if dims is not None else vm.default_dims()
+    cs = cache if cache is not None else _cache()
+    if ws_bytes is None:
+        ws_bytes = lib.vmla_layer_workspace_bytes(ctypes.byref(d), 768, cs.batch,
+                                                  n_frames * cs.grid_h * cs.grid_w)
+    return lib.vmla_chunk_attention_layer(ctypes.byref(d), ctypes.byref(cs), dtype, x, w_dq, d_q, w_qa,
+                                          w_vo, t_first, n_frames, n_valid, out, ws, ws_bytes, None)
+
+
+def test_layer_workspace_bytes(lib):
+    d = vm.default_dims()
+    qhat = 12 * 4680 * 224 * 2
+    inner = 4680 * max(768, 12 * 192) * 2
+    assert vm.vmla_layer_workspace_bytes(1, 4680, 768, d) == qhat + (inner + 255) // 256 * 256
+    assert vm.vmla_layer_workspace_bytes(2, 24, 4096, d) == 2 * 12 * 24 * 224 * 2 + 2 * 24 * 4096 * 2
+    assert vm.vmla_layer_workspace_bytes(1, 4680, 700, d) == 0        # d_q not a multiple of 64
+    assert vm.vmla_layer_workspace_bytes(1, 4680, 0, d) == 0
+    assert vm.vmla_layer_workspace_bytes(0, 4680, 768, d) == 0
+
+
+def test_layer_validation(lib):
+    d = vm.default_dims()
+    assert _layer(lib, x=None) == vm.VMLA_ERR_NULL
+    assert _layer(lib, w_qa=None) == vm.VMLA_ERR_NULL
+    assert _layer(lib, w_vo=None) == vm.VMLA_ERR_NULL
+    assert _layer(lib, w_vo=MIS) == vm.VMLA_ERR_ALIGN
+    assert _layer(lib, d_q=100) == vm.VMLA_ERR_SHAPE
+    assert _layer(lib, d_q=16384) == vm.VMLA_ERR_SHAPE
+    assert _layer(lib, dtype=vm.VMLA_F32) == vm.VMLA_ERR_DTYPE
+    assert _layer(lib, n_valid=2) == vm.VMLA_ERR_RANGE
+    assert _layer(lib, ws=None) == vm.VMLA_ERR_WORKSPACE
+    # the attention-only workspace is too small for the layer
+    small = vm.vmla_attention_workspace_bytes(1, 24, d)
+    assert _layer(lib, ws_bytes=small) == vm.VMLA_ERR_WORKSPACE
+    cs = _cache()
+    assert lib.vmla_layer_attention(ctypes.byref(d), ctypes.byref(cs), vm.VMLA_BF16, 768, None, 2, 1, 3,
+                                    C, B, 1 << 20, None) == vm.VMLA_ERR_NULL
+    assert lib.vmla_layer_query_prologue(ctypes.byref(d), ctypes.byref(cs), vm.VMLA_BF16, A, B, 768, C,
+                                         2, 1, 3, B, 16, None) == vm.VMLA_ERR_WORKSPACE
+    assert lib.vmla_fold_query_weights(ctypes.byref(d), vm.VMLA_BF16, 100, A, B, C, None) == vm.VMLA_ERR_SHAPE
+    assert lib.vmla_fold_query_weights(ctypes.byref(d), 5, 768, A, B, C, None) == vm.VMLA_ERR_DTYPE
+    assert lib.vmla_fold_query_weights(ctypes.byref(d), vm.VMLA_BF16, 768, None, B, C, None) == vm.VMLA_ERR_NULL
+    assert lib.vmla_fold_output_weights(ctypes.byref(d), vm.VMLA_BF16, A, MIS, C, None) == vm.VMLA_ERR_ALIGN
+    assert lib.vmla_fold_output_weights(ctypes.byref(vm.default_dims(d_v=64)), vm.VMLA_BF16, A, B, C,
+                                        None) == vm.VMLA_ERR_SHAPE
+    assert lib.vmla_output_projection(ctypes.byref(d), vm.VMLA_BF16, 0, A, B, C, None) == vm.VMLA_ERR_SHAPE
+    assert lib.vmla_output_projection(ctypes.byref(d), vm.VMLA_BF16, 1 << 25, A, B, C, None) == vm.VMLA_ERR_SHAPE
+    assert lib.vmla_output_projection(ctypes.byref(d), vm.VMLA_BF16, 8, None, B, C, None) == vm.VMLA_ERR_NULL
+    assert lib.vmla_output_projection(ctypes.byref(d), 3, 8, A, B, C, None) == vm.VMLA_ERR_DTYPE
 
 
 def test_binding_cache_geometry():
