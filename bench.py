@@ -45,7 +45,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def work(w, layer=False):
+def work(w, layer=False, explicit=False):
     """Algorithmic flops and bytes of one step (absorbed method, bf16 storage).
     ``layer``: the whole layer instead, with the d_q query latent (x W_DQ, then
     the folded [A_h | W_UQ^rope[h]]) and B_h folded into the output mixer."""
@@ -63,6 +63,12 @@ def work(w, layer=False):
     if layer:
         prologue = Nq * (2 * D * w.d_q + 2 * w.d_q * H * w.cache_row)
         epilogue = Nq * 2 * H * w.d_c * D                            # [O_lat / l] x W_VO
+    if explicit:
+        # queries x W_Q; per-head K/V rebuilt from every valid slot; 2 (128 + 128)
+        # flops per (query, key, head)
+        prologue = Nq * 2 * D * H * w.d_head + B * Nk * 2 * w.d_c * H * (w.d_nope + w.d_v)
+        core = 2 * (w.d_head + w.d_v) * w.n_q * Nk * H * B
+        epilogue = 0
     return dict(core=core, prologue=prologue, epilogue=epilogue, append=append,
                 attn_kernel=core + epilogue, step=core + prologue + epilogue + append,
                 bytes_append=bytes_append, bytes_prologue=bytes_prologue, bytes_attn=bytes_attn)
@@ -114,6 +120,9 @@ def main():
     ap.add_argument("--layer", action="store_true",
                     help="the whole attention layer: d_q = 768 query latent, latent attention, "
                          "B_h folded into the W_O output mixer (out [B, N_q, d_model])")
+    ap.add_argument("--explicit", action="store_true",
+                    help="the explicit-reconstruction route instead of the latent form: per-head "
+                         "K/V rebuilt from the cache each step, then 128-dim attention")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device-to-device copy of MIB MiB, whose counter "
                          "readings calibrate FETCH_SIZE / WRITE_SIZE")
@@ -200,6 +209,12 @@ def main():
         log(f"[bench] {n_sets} buffer sets of "
             f"{(sets[0][0].numel() + sets[0][2].data.numel()) * 2 / 1e6:.0f} MB")
     n_valid = w.n_valid_frames
+    if args.explicit:
+        if args.layer or args.long_horizon:
+            print("--explicit runs the attention core with k_R rotated at append", file=sys.stderr)
+            sys.exit(2)
+        for _, dw, _ in sets:
+            dw["w_kv"] = vm.vmla_pack_kv_weights(dw["w_k_up"], dw["w_v_up"], dims=dims)
     if args.layer:
         # the one-time weight folds of the layer (not part of a step)
         for _, dw, _ in sets:
@@ -208,6 +223,10 @@ def main():
         ws = torch.empty(vm.vmla_layer_workspace_bytes(w.batch, w.n_q, w.d_q, dims), dtype=torch.uint8,
                          device=dev)
         out = torch.empty((w.batch, w.n_q, w.d_model), dtype=torch.bfloat16, device=dev)
+    elif args.explicit:
+        ws = torch.empty(vm.vmla_explicit_workspace_bytes(w.batch, w.n_q, w.n_k, dims),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty((w.batch, w.n_q, w.n_heads, w.d_v), dtype=torch.bfloat16, device=dev)
     else:
         ws = torch.empty(vm.vmla_attention_workspace_bytes(w.batch, w.n_q, dims), dtype=torch.uint8,
                          device=dev)
@@ -226,6 +245,8 @@ def main():
         if args.layer:
             vm.vmla_layer_query_prologue(cache, x, dw["w_dq"], dw["w_qa"], w.t_first, w.chunk_frames,
                                          n_valid, ws, dims=dims)
+        elif args.explicit:
+            pass                      # the explicit call below builds its own queries
         else:
             vm.vmla_query_prologue(cache, x, dw["w_q"], dw["w_k_up"], w.t_first, w.chunk_frames,
                                    n_valid, ws, dims=dims)
@@ -234,6 +255,9 @@ def main():
         if args.layer:
             vm.vmla_layer_attention(cache, w.d_q, dw["w_vo"], w.t_first, w.chunk_frames, n_valid, out,
                                     ws, dims=dims)
+        elif args.explicit:
+            vm.vmla_chunk_attention_explicit(cache, x, dw["w_q"], dw["w_kv"], w.t_first, w.chunk_frames,
+                                             n_valid, out, ws, dims=dims)
         else:
             vm.vmla_latent_attention(cache, dw["w_v_up"], w.t_first, w.chunk_frames, n_valid, out, ws,
                                      dims=dims)
@@ -260,13 +284,14 @@ def main():
     k_ms = {k: v / args.steps for k, v in k_ms.items()}
     assert torch.isfinite(out.float()).all().item(), "non-finite output"
 
-    wk = work(w, layer=args.layer)
+    wk = work(w, layer=args.layer, explicit=args.explicit)
     tflops = wk["step"] / (ms_step * 1e-3) / 1e12
     attn_tflops = wk["attn_kernel"] / (k_ms["latent_attn"] * 1e-3) / 1e12
     append_gbs = wk["bytes_append"] / (k_ms["append"] * 1e-3) / 1e9
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "latent_attn_config2_traffic.json")
-    if args.config == 2 and not args.long_horizon and not args.layer and os.path.exists(tfile):
+    if (args.config == 2 and not (args.long_horizon or args.layer or args.explicit)
+            and os.path.exists(tfile)):
         with open(tfile) as f:
             tr = json.load(f)
         if tr.get("kernel_source_sha") == _kernel_sha():
@@ -320,6 +345,17 @@ def main():
         result["config"]["workload"] = ("Wan-1.3B-shaped chunk-layer, long rollout: B=1, 30x52 "
                                         "grid, 3-frame query chunk at t=18..20 over one sink frame "
                                         "plus a 6-frame window, RoPE applied at read time")
+    if args.explicit:
+        result["config"]["workload"] += ("; explicit route: per-head K/V rebuilt from the latent "
+                                         "cache each step (201 MB at B=1), then 128-dim attention")
+        result["kernels_ms"] = {"append": round(k_ms["append"], 4),
+                                "explicit_route": round(k_ms["latent_attn"], 4)}
+        result["roofline"]["kernel"] = "explicit route (query GEMM + K/V rebuild GEMM + attention)"
+        result["roofline"]["flops_per_launch"] = wk["prologue"] + wk["core"]
+        et = (wk["prologue"] + wk["core"]) / (k_ms["latent_attn"] * 1e-3) / 1e12
+        result["roofline"]["achieved"] = round(et, 2)
+        result["roofline"]["frac"] = round(et / PEAK_BF16_TFLOPS, 4)
+        result["absorbed_flops_per_step"] = work(w)["step"]
     if args.layer:
         result["config"]["workload"] += ("; whole attention layer: d_q=768 query latent, latent "
                                          "attention, B_h folded into the W_O output mixer")

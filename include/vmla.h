@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define VMLA_ABI_VERSION 3
+#define VMLA_ABI_VERSION 4
 
 typedef enum vmla_status {
   VMLA_OK = 0,
@@ -287,6 +287,36 @@ int32_t vmla_layer_attention(const vmla_dims* dims, const vmla_cache* cache, int
  * (dims, m < 1 or m > 2^24), VMLA_ERR_ALIGN, VMLA_ERR_HIP. */
 int32_t vmla_output_projection(const vmla_dims* dims, int32_t dtype, int64_t m, const void* in,
                                const void* w_o, void* out, void* stream);
+
+/*
+ * Explicit reconstruction: the comparison point of the latent form.
+ * -----------------------------------------------------------------
+ * Defined by: on-demand reconstruction of per-head keys k_h = [c W_K_up[h] |
+ * k_R] and values v_h = c W_V_up[h] from the cached pair ([PL] §3 "On-demand
+ * reconstruction"), then ordinary 128-dimensional multi-head attention over
+ * them; App. E's latent form computes the same result without the rebuilt
+ * rows. The output equals vmla_chunk_attention's up to rounding.
+ *
+ * w_kv [d_c, n_heads * (d_nope + d_v)] (dtype of the call): per head
+ * [W_K_up[h] | W_V_up[h]], packed once by vmla_pack_kv_weights.
+ * Workspace: the pre-scaled bf16 queries [batch, n_heads, n_q, d_nope + d_rope]
+ * then the rebuilt bf16 rows [batch, n_heads, n_k, 2 (d_nope + d_rope)] with
+ * row = [k_nope | k_R | v], n_k = n_valid_frames * T.
+ * Only caches with rope_at_read = 0 (k_R rotated at append).
+ * Errors: as vmla_chunk_attention (workspace against
+ * vmla_explicit_workspace_bytes), plus VMLA_ERR_SHAPE for rope_at_read = 1 or
+ * more than 2^31 rebuilt elements per batch element.
+ */
+int32_t vmla_pack_kv_weights(const vmla_dims* dims, int32_t dtype, const void* w_k_up,
+                             const void* w_v_up, void* w_kv, void* stream);
+
+size_t vmla_explicit_workspace_bytes(const vmla_dims* dims, int32_t batch, int32_t n_q, int32_t n_k);
+
+int32_t vmla_chunk_attention_explicit(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                                      const void* x, const void* w_q, const void* w_kv,
+                                      int32_t t_first, int32_t n_frames, int32_t n_valid_frames,
+                                      void* out, void* workspace, size_t workspace_bytes,
+                                      void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* vmla_status_string(int32_t status);

@@ -60,7 +60,8 @@ EXPORTED = ("vmla_default_dims", "vmla_cache_append", "vmla_attention_workspace_
             "vmla_chunk_attention", "vmla_query_prologue", "vmla_latent_attention",
             "vmla_fold_query_weights", "vmla_fold_output_weights", "vmla_layer_workspace_bytes",
             "vmla_chunk_attention_layer", "vmla_layer_query_prologue", "vmla_layer_attention",
-            "vmla_output_projection", "vmla_status_string", "vmla_abi_version")
+            "vmla_output_projection", "vmla_pack_kv_weights", "vmla_explicit_workspace_bytes",
+            "vmla_chunk_attention_explicit", "vmla_status_string", "vmla_abi_version")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -105,6 +106,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vmla_layer_attention.restype = I32
     lib.vmla_output_projection.argtypes = [D, I32, ctypes.c_int64, P, P, P, P]
     lib.vmla_output_projection.restype = I32
+    lib.vmla_pack_kv_weights.argtypes = [D, I32, P, P, P, P]
+    lib.vmla_pack_kv_weights.restype = I32
+    lib.vmla_explicit_workspace_bytes.argtypes = [D, I32, I32, I32]
+    lib.vmla_explicit_workspace_bytes.restype = SZ
+    lib.vmla_chunk_attention_explicit.argtypes = [D, C, I32, P, P, P, I32, I32, I32, P, P, SZ, P]
+    lib.vmla_chunk_attention_explicit.restype = I32
     lib.vmla_status_string.argtypes = [I32]
     lib.vmla_status_string.restype = ctypes.c_char_p
     lib.vmla_abi_version.argtypes = []
@@ -488,4 +495,69 @@ def vmla_output_projection(heads: torch.Tensor, w_o: torch.Tensor, out: torch.Te
                                     _dev(w_o, "w_o"), _dev(out, "out"), _stream(stream))
     if st != VMLA_OK:
         raise VmlaError(st, "vmla_output_projection")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Explicit reconstruction (comparison point of the latent form)
+# ---------------------------------------------------------------------------
+
+def vmla_pack_kv_weights(w_k_up: torch.Tensor, w_v_up: torch.Tensor, out: torch.Tensor | None = None,
+                         dims: vmla_dims | None = None, stream=None) -> torch.Tensor:
+    """[d_c, n_heads * (d_nope + d_v)]: per head [W_K_up[h] | W_V_up[h]] (dtype of the inputs)."""
+    lib = load_library()
+    d = dims or default_dims()
+    _expect_shape(w_k_up, (d.n_heads, d.d_c, d.d_nope), "w_k_up")
+    _expect_shape(w_v_up, (d.n_heads, d.d_c, d.d_v), "w_v_up")
+    _same_dtype(w_k_up, w_v_up=w_v_up)
+    if out is None:
+        out = torch.empty((d.d_c, d.n_heads * (d.d_nope + d.d_v)), dtype=w_k_up.dtype,
+                          device=w_k_up.device)
+    _expect_shape(out, (d.d_c, d.n_heads * (d.d_nope + d.d_v)), "w_kv")
+    _same_dtype(w_k_up, w_kv=out)
+    st = lib.vmla_pack_kv_weights(ctypes.byref(d), _dtype_code(w_k_up), _dev(w_k_up, "w_k_up"),
+                                  _dev(w_v_up, "w_v_up"), _dev(out, "w_kv"), _stream(stream))
+    if st != VMLA_OK:
+        raise VmlaError(st, "vmla_pack_kv_weights")
+    return out
+
+
+def vmla_explicit_workspace_bytes(batch: int, n_q: int, n_k: int, dims: vmla_dims | None = None) -> int:
+    d = dims or default_dims()
+    return int(load_library().vmla_explicit_workspace_bytes(ctypes.byref(d), int(batch), int(n_q),
+                                                            int(n_k)))
+
+
+def vmla_chunk_attention_explicit(cache: LatentCache, x: torch.Tensor, w_q: torch.Tensor,
+                                  w_kv: torch.Tensor, t_first: int, n_frames: int, n_valid_frames: int,
+                                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                                  dims: vmla_dims | None = None, stream=None) -> torch.Tensor:
+    """Chunk attention through explicit per-head K/V reconstruction; returns
+    ``out`` [batch, n_q, n_heads, d_v] (the same result as vmla_chunk_attention)."""
+    lib = load_library()
+    d = dims or default_dims()
+    B, T = cache.batch, cache.tokens_per_frame
+    n_q = n_frames * T
+    _expect_shape(x, (B, n_q, d.d_model), "x")
+    _expect_shape(w_q, (d.d_model, d.n_heads * (d.d_nope + d.d_rope)), "w_q")
+    _expect_shape(w_kv, (d.d_c, d.n_heads * (d.d_nope + d.d_v)), "w_kv")
+    _same_dtype(cache.data, x=x, w_q=w_q, w_kv=w_kv)
+    if out is None:
+        out = torch.empty((B, n_q, d.n_heads, d.d_v), dtype=cache.data.dtype, device=x.device)
+    _expect_shape(out, (B, n_q, d.n_heads, d.d_v), "out")
+    _same_dtype(cache.data, out=out)
+    need = vmla_explicit_workspace_bytes(B, n_q, n_valid_frames * T, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold at least {need} bytes")
+    _dev(cache.data, "cache")
+    cs = cache.c_struct()
+    st = lib.vmla_chunk_attention_explicit(ctypes.byref(d), ctypes.byref(cs), _dtype_code(cache.data),
+                                           _dev(x, "x"), _dev(w_q, "w_q"), _dev(w_kv, "w_kv"),
+                                           int(t_first), int(n_frames), int(n_valid_frames),
+                                           _dev(out, "out"), _dev(workspace, "workspace"),
+                                           workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != VMLA_OK:
+        raise VmlaError(st, "vmla_chunk_attention_explicit")
     return out

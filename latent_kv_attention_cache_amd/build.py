@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["vmla_api.cpp", "append.hip", "qprologue.hip", "latent_attn.hip", "mixer_gemm.hip"]
+SOURCES = ["vmla_api.cpp", "append.hip", "qprologue.hip", "latent_attn.hip", "mixer_gemm.hip",
+           "explicit_attn.hip"]
 # Per-source extra flags. The attention kernel never reads NaNs (slots past the
 # valid prefix are not loaded), so max() needs no NaN canonicalization.
 EXTRA_FLAGS = {"latent_attn.hip": ["-fno-honor-nans"]}
@@ -48,7 +49,7 @@ def _compile(src: str, verbose: bool) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every HIP/C++ source and link ``libvmla.so``; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB_PATH + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]

@@ -65,17 +65,27 @@ struct AttnArgs {
 };
 
 // out = A W over row-major operands; A [m][lda >= k], W [k][n]. mode 0:
-// out [m][n]; mode 1: the Qhat epilogue (n = n_heads * kRow, A and W bf16).
+// out [m][n]; mode 1: per-head query rows out[b][h][n][head_w] (n = n_heads *
+// head_w, RoPE from column rope_off on, times qscale); mode 2: explicit K/V
+// rows out[h][m][2 kDHead] from W = per-head [W_K_up | W_V_up] and the k_R
+// columns of A.
 struct GemmArgs {
   const void* a;
   const void* w;
   void* out;
   int64_t m;
   int k, n, lda, mode;
-  // Qhat epilogue only
-  int n_q, n_heads, grid_w, tokens_per_frame, t_first;
+  // mode 1 only
+  int n_q, n_heads, grid_w, tokens_per_frame, t_first, head_w, rope_off;
   float inv_grid_w, inv_tokens_per_frame, qscale;
   RopeTable rope;
+};
+
+struct ExplicitArgs {
+  const uint16_t* q;    // [batch, n_heads, n_q, kDHead] bf16, pre-scaled by scale * log2(e)
+  const uint16_t* kv;   // [batch, n_heads, n_k, 2 kDHead] bf16: [k (128) | v (128)]
+  void* out;            // [batch, n_q, n_heads, kDV]
+  int batch, n_q, n_heads, n_k;
 };
 
 // One-time weight folds (bf16 results). Query: w_first = W_UQ [d_in][n_heads
@@ -96,5 +106,7 @@ hipError_t launch_latent_attn(const AttnArgs& a, bool f32, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, int a_f32, int out_f32, hipStream_t s);
 hipError_t launch_fold_query(const FoldArgs& a, bool f32, hipStream_t s);
 hipError_t launch_fold_output(const FoldArgs& a, bool f32, hipStream_t s);
+hipError_t launch_explicit_attn(const ExplicitArgs& a, bool f32, hipStream_t s);
+hipError_t launch_pack_kv(const FoldArgs& a, bool f32, hipStream_t s);
 
 }  // namespace vmla

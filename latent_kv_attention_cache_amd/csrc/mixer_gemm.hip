@@ -10,11 +10,16 @@
 // into the output mixer; "RoPE branch" keeps the positional columns separate.
 //
 //   gemm_kernel<TA, TO, kPlain>: out[m][n] = sum_k A[m][k] W[k][n]   (TO storage)
-//   gemm_kernel<bf16, bf16, kQhat>: the same product over the folded query
-//     weights [A_h | W_UQ^R[h]] of every head, whose epilogue rotates the rope
-//     columns with the token's (t, h, w), multiplies by scale * log2(e) and
-//     scatters each head's 224 values to Qhat[b][h][n] (the attention kernel's
-//     input layout).
+//   gemm_kernel<TA, bf16, kHead>: per-head query rows. The columns are head_w
+//     wide per head, the last ones from rope_off on are RoPE pairs; the
+//     epilogue rotates them with the token's (t, h, w), multiplies everything
+//     by scale * log2(e) and scatters each head's row to out[b][h][n]. Over the
+//     folded query weights [A_h | W_UQ^R[h]] (head_w 224) this is the latent
+//     attention's Qhat; over W_Q (head_w 128) the explicit form's queries.
+//   gemm_kernel<TA, bf16, kKV>: explicit reconstruction ([PL] §3 "On-demand
+//     reconstruction") over the cache rows of one batch element and the packed
+//     per-head [W_K_up[h] | W_V_up[h]] (224 columns per head): row m of head h
+//     becomes kv[h][m] = [c W_K_up[h] (96) | k_R of row m (32) | c W_V_up[h] (128)].
 //
 // Tile: 128 rows x 256 columns, four waves, one per SIMD; wave (rh, ch) owns
 // rows 64 rh .. +63 and columns 128 ch .. +127 of the tile and computes
@@ -53,7 +58,7 @@ constexpr int kWChunks = kColsT / 8;              // 32 chunks per W tile row
 static_assert(kXLoads % kWaves == 0 && kWLoads % kWaves == 0, "loads split evenly");
 static_assert(kStages * kStageElems * 2 <= 160 * 1024, "LDS budget");
 
-enum { kPlain = 0, kQhat = 1 };
+enum { kPlain = 0, kHead = 1, kKV = 2 };
 
 __device__ __forceinline__ float to_f32(bf16_t v) { return bf2f(v); }
 __device__ __forceinline__ float to_f32(float v) { return v; }
@@ -231,9 +236,35 @@ void gemm_kernel(GemmArgs a) {
         store4<TO>(out + m * a.n + col, v[0], v[1], v[2], v[3]);
       }
     }
+  } else if constexpr (kMode == kKV) {
+    // column col = h (kDNope + kDV) + ci: ci < kDNope key part, else value part;
+    // the lanes holding ci < kDRope also copy k_R (A columns kDC .. kRow - 1).
+    constexpr int kCols = kDNope + kDV;
+    uint16_t* kv = static_cast<uint16_t*>(a.out);
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      const int col = cbase + 16 * cb;
+      if (col >= a.n) continue;
+      const int h = col / kCols;
+      const int ci = col - h * kCols;
+      const int dst = ci < kDNope ? ci : ci + kDRope;
+#pragma unroll
+      for (int rb = 0; rb < kNRB; ++rb) {
+        const int64_t m = m0 + 64 * rh + 16 * rb + j;
+        if (m >= a.m) continue;
+        uint16_t* row = kv + ((int64_t)h * a.m + m) * (2 * kDHead);
+        const f32x4 v = acc[rb][cb];
+        store4<bf16_t>(row + dst, v[0], v[1], v[2], v[3]);
+        if (ci < kDRope) {
+          const TA* kr = static_cast<const TA*>(a.a) + m * a.lda + kDC + ci;
+          store4<bf16_t>(row + kDNope + ci, to_f32(kr[0]), to_f32(kr[1]), to_f32(kr[2]), to_f32(kr[3]));
+        }
+      }
+    }
   } else {
-    // Qhat: column col = kRow h + ci of head h; ci < kDC content (scaled),
-    // ci >= kDC rope pairs (ci - kDC) / 2 and +1 (rotated, then scaled).
+    // per-head rows: column col = head_w h + ci of head h; ci < rope_off plain
+    // (scaled), ci >= rope_off rope pairs (ci - rope_off) / 2 and +1 (rotated,
+    // then scaled).
     int64_t qrow[kNRB];                                // row of Qhat for head 0, -1 past m
     int pos[kNRB][3];                                  // (t, h, w) of each row
 #pragma unroll
@@ -255,10 +286,10 @@ void gemm_kernel(GemmArgs a) {
     for (int cb = 0; cb < kCB; ++cb) {
       const int col = cbase + 16 * cb;
       if (col >= a.n) continue;
-      const int h = col / kRow;
-      const int ci = col - h * kRow;
-      const bool rope = ci >= kDC;
-      const int pr = (ci - kDC) >> 1;                  // first of the lane's two pairs
+      const int h = col / a.head_w;
+      const int ci = col - h * a.head_w;
+      const bool rope = ci >= a.rope_off;
+      const int pr = (ci - a.rope_off) >> 1;           // first of the lane's two pairs
 #pragma unroll
       for (int rb = 0; rb < kNRB; ++rb) {
         if (qrow[rb] < 0) continue;
@@ -273,7 +304,7 @@ void gemm_kernel(GemmArgs a) {
             v[2 * q + 1] = x0 * sn + x1 * cs;
           }
         }
-        store4<bf16_t>(qhat + (qrow[rb] + (int64_t)h * a.n_q) * kRow + ci, v[0] * a.qscale,
+        store4<bf16_t>(qhat + (qrow[rb] + (int64_t)h * a.n_q) * a.head_w + ci, v[0] * a.qscale,
                        v[1] * a.qscale, v[2] * a.qscale, v[3] * a.qscale);
       }
     }
@@ -328,8 +359,12 @@ hipError_t launch_gemm(const GemmArgs& a, int a_f32, int out_f32, hipStream_t s)
   const int64_t n_rt = (a.m + kRowsT - 1) / kRowsT;
   const int n_ct = (a.n + kColsT - 1) / kColsT;
   const dim3 grid((unsigned)(8 * n_ct * ((n_rt + 7) / 8)));
-  if (a.mode == kQhat) {
-    hipLaunchKernelGGL((gemm_kernel<bf16_t, bf16_t, kQhat>), grid, dim3(kThreads), 0, s, a);
+  if (a.mode == kHead) {
+    if (a_f32) hipLaunchKernelGGL((gemm_kernel<float, bf16_t, kHead>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((gemm_kernel<bf16_t, bf16_t, kHead>), grid, dim3(kThreads), 0, s, a);
+  } else if (a.mode == kKV) {
+    if (a_f32) hipLaunchKernelGGL((gemm_kernel<float, bf16_t, kKV>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((gemm_kernel<bf16_t, bf16_t, kKV>), grid, dim3(kThreads), 0, s, a);
   } else if (a_f32) {
     if (out_f32) hipLaunchKernelGGL((gemm_kernel<float, float, kPlain>), grid, dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL((gemm_kernel<float, bf16_t, kPlain>), grid, dim3(kThreads), 0, s, a);

@@ -3,6 +3,7 @@
 #include "vmla.h"
 
 #include <cmath>
+#include <climits>
 #include <cstdint>
 
 #include "kernels.h"
@@ -320,6 +321,7 @@ int32_t launch_layer_prologue(const vmla_dims* dims, const vmla_cache* cache, in
   GemmArgs g2{};
   g2.a = c_q; g2.w = w_qa; g2.out = q.qhat;
   g2.m = g1.m; g2.k = d_q; g2.n = dims->n_heads * kRow; g2.lda = d_q; g2.mode = 1;
+  g2.head_w = kRow; g2.rope_off = kDC;
   g2.n_q = q.n_q; g2.n_heads = q.n_heads; g2.grid_w = q.grid_w; g2.tokens_per_frame = q.tokens_per_frame;
   g2.t_first = q.t_first; g2.inv_grid_w = q.inv_grid_w; g2.inv_tokens_per_frame = q.inv_tokens_per_frame;
   g2.qscale = q.qscale; g2.rope = q.rope;
@@ -390,6 +392,73 @@ int32_t vmla_chunk_attention_layer(const vmla_dims* dims, const vmla_cache* cach
   st = launch_layer_prologue(dims, cache, dtype, x, w_dq, d_q, w_qa, q, inner, s);
   if (st) return st;
   return launch_layer_attention(dims, cache, dtype, w_vo, out, a, inner, s);
+}
+
+// ---- explicit reconstruction: the comparison point of the latent form
+
+int32_t vmla_pack_kv_weights(const vmla_dims* dims, int32_t dtype, const void* w_k_up,
+                             const void* w_v_up, void* w_kv, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st) return st;
+  if (!w_k_up || !w_v_up || !w_kv) return VMLA_ERR_NULL;
+  if (dtype != VMLA_F32 && dtype != VMLA_BF16) return VMLA_ERR_DTYPE;
+  if (!aligned16(w_k_up) || !aligned16(w_v_up) || !aligned16(w_kv)) return VMLA_ERR_ALIGN;
+  FoldArgs f{};
+  f.w_first = w_k_up; f.w_second = w_v_up; f.out = w_kv; f.n_heads = dims->n_heads;
+  return hip_status(launch_pack_kv(f, dtype == VMLA_F32, static_cast<hipStream_t>(stream)));
+}
+
+size_t vmla_explicit_workspace_bytes(const vmla_dims* dims, int32_t batch, int32_t n_q, int32_t n_k) {
+  if (check_dims(dims) != VMLA_OK || batch < 1 || n_q < 1 || n_k < 1) return 0;
+  const size_t per = (size_t)batch * dims->n_heads * sizeof(uint16_t);
+  return per * ((size_t)n_q * kDHead + (size_t)n_k * 2 * kDHead);
+}
+
+int32_t vmla_chunk_attention_explicit(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                                      const void* x, const void* w_q, const void* w_kv,
+                                      int32_t t_first, int32_t n_frames, int32_t n_valid_frames,
+                                      void* out, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (!x || !w_q || !w_kv || !out) return VMLA_ERR_NULL;
+  QArgs q;
+  AttnArgs a;
+  // the attention checks, with the workspace size checked below
+  int32_t st = check_attention(dims, cache, dtype, t_first, n_frames, n_valid_frames, workspace,
+                               SIZE_MAX, &q, &a);
+  if (st) return st;
+  if (cache->rope_at_read) return VMLA_ERR_SHAPE;
+  if ((int64_t)a.n_k * 2 * kDHead * dims->n_heads > INT32_MAX) return VMLA_ERR_SHAPE;
+  if (workspace_bytes < vmla_explicit_workspace_bytes(dims, cache->batch, a.n_q, a.n_k))
+    return VMLA_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_kv) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool f32 = dtype == VMLA_F32;
+  uint16_t* qbuf = static_cast<uint16_t*>(workspace);
+  uint16_t* kvbuf = qbuf + (size_t)cache->batch * dims->n_heads * a.n_q * kDHead;
+  // queries: [q_nope | RoPE3D(q_rope)] * scale * log2(e), per head
+  GemmArgs g{};
+  g.a = x; g.w = w_q; g.out = qbuf;
+  g.m = (int64_t)cache->batch * a.n_q; g.k = dims->d_model; g.n = dims->n_heads * kDHead;
+  g.lda = dims->d_model; g.mode = 1; g.head_w = kDHead; g.rope_off = kDNope;
+  g.n_q = q.n_q; g.n_heads = q.n_heads; g.grid_w = q.grid_w; g.tokens_per_frame = q.tokens_per_frame;
+  g.t_first = q.t_first; g.inv_grid_w = q.inv_grid_w; g.inv_tokens_per_frame = q.inv_tokens_per_frame;
+  g.qscale = q.qscale; g.rope = q.rope;
+  st = hip_status(launch_gemm(g, f32, 0, s));
+  if (st) return st;
+  // per-head keys and values of every valid slot, one batch element at a time
+  const size_t elem = f32 ? sizeof(float) : sizeof(uint16_t);
+  for (int b = 0; b < cache->batch; ++b) {
+    GemmArgs r{};
+    r.a = static_cast<const char*>(cache->data) + (size_t)b * a.cache_rows * kRow * elem;
+    r.w = w_kv; r.out = kvbuf + (size_t)b * dims->n_heads * a.n_k * 2 * kDHead;
+    r.m = a.n_k; r.k = kDC; r.n = dims->n_heads * (kDNope + kDV); r.lda = kRow; r.mode = 2;
+    st = hip_status(launch_gemm(r, f32, 0, s));
+    if (st) return st;
+  }
+  ExplicitArgs e{};
+  e.q = qbuf; e.kv = kvbuf; e.out = out;
+  e.batch = cache->batch; e.n_q = a.n_q; e.n_heads = dims->n_heads; e.n_k = a.n_k;
+  return hip_status(launch_explicit_attn(e, f32, s));
 }
 
 int32_t vmla_output_projection(const vmla_dims* dims, int32_t dtype, int64_t m, const void* in,

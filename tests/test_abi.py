@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.vmla_abi_version() == 3
+    assert lib.vmla_abi_version() == 4
     for code in range(-7, 1):
         s = vm.vmla_status_string(code)
         assert s and s != "unknown status"
@@ -187,6 +187,28 @@ def test_layer_validation(lib):
     assert lib.vmla_output_projection(ctypes.byref(d), vm.VMLA_BF16, 1 << 25, A, B, C, None) == vm.VMLA_ERR_SHAPE
     assert lib.vmla_output_projection(ctypes.byref(d), vm.VMLA_BF16, 8, None, B, C, None) == vm.VMLA_ERR_NULL
     assert lib.vmla_output_projection(ctypes.byref(d), 3, 8, A, B, C, None) == vm.VMLA_ERR_DTYPE
+
+
+def test_explicit_validation(lib):
+    d = vm.default_dims()
+    assert vm.vmla_explicit_workspace_bytes(1, 4680, 32760, d) == 12 * 2 * (4680 * 128 + 32760 * 256)
+    assert vm.vmla_explicit_workspace_bytes(1, 4680, 0, d) == 0
+    cs = _cache()
+    big = 1 << 30
+
+    def call(cache=cs, dtype=vm.VMLA_BF16, x=A, wq=B, wkv=C, n_valid=3, ws=B, ws_bytes=big, out=C):
+        return lib.vmla_chunk_attention_explicit(ctypes.byref(d), ctypes.byref(cache), dtype, x, wq, wkv,
+                                                 2, 1, n_valid, out, ws, ws_bytes, None)
+    assert call(wkv=None) == vm.VMLA_ERR_NULL
+    assert call(dtype=vm.VMLA_F32) == vm.VMLA_ERR_DTYPE
+    assert call(n_valid=2) == vm.VMLA_ERR_RANGE
+    assert call(cache=_cache(rope_at_read=1)) == vm.VMLA_ERR_SHAPE       # read-time RoPE not supported
+    assert call(ws_bytes=1024) == vm.VMLA_ERR_WORKSPACE
+    assert call(ws=None) == vm.VMLA_ERR_WORKSPACE
+    assert call(wkv=MIS) == vm.VMLA_ERR_ALIGN
+    assert lib.vmla_pack_kv_weights(ctypes.byref(d), vm.VMLA_BF16, A, None, C, None) == vm.VMLA_ERR_NULL
+    assert lib.vmla_pack_kv_weights(ctypes.byref(d), 9, A, B, C, None) == vm.VMLA_ERR_DTYPE
+    assert lib.vmla_pack_kv_weights(ctypes.byref(d), vm.VMLA_BF16, A, B, MIS, None) == vm.VMLA_ERR_ALIGN
 
 
 def test_binding_cache_geometry():
