@@ -123,6 +123,9 @@ def main():
     ap.add_argument("--explicit", action="store_true",
                     help="the explicit-reconstruction route instead of the latent form: per-head "
                          "K/V rebuilt from the cache each step, then 128-dim attention")
+    ap.add_argument("--d-c", type=int, default=192, choices=(64, 128, 192),
+                    help="content-latent width of the cache (the latent-budget sweep); the "
+                         "--layer and --explicit routes run at 192 only")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device-to-device copy of MIB MiB, whose counter "
                          "readings calibrate FETCH_SIZE / WRITE_SIZE")
@@ -160,8 +163,13 @@ def main():
             sys.exit(2)
         w = w.with_(window_frames=6, sink_frames=1, rope_at_read=True,
                     name=w.name + ", sink 1 + window 6, read-time RoPE")
+    if args.d_c != 192:
+        if args.layer or args.explicit:
+            print("--d-c applies to the attention core (not --layer / --explicit)", file=sys.stderr)
+            sys.exit(2)
+        w = w.with_(d_c=args.d_c, name=w.name + f", d_c = {args.d_c}")
     log(f"[bench] workload: {w.name}")
-    dims = vm.default_dims()
+    dims = vm.default_dims(d_c=w.d_c)
     xs = None
     if args.config == 2:
         # seeded host inputs, the same as the parity tests use
@@ -176,7 +184,7 @@ def main():
             return torch.from_numpy(np.concatenate([xs[t] for t in frames]))[None].to(dev).to(torch.bfloat16)
 
         cache = vm.LatentCache.empty(w.batch, w.window_frames, w.grid_h, w.grid_w, device=dev,
-                                     sink_frames=w.sink_frames, rope_at_read=w.rope_at_read)
+                                     dims=dims, sink_frames=w.sink_frames, rope_at_read=w.rope_at_read)
         prior = w.prior_frames
         i = 0
         while i < len(prior):       # contiguous runs of earlier frames
@@ -184,7 +192,7 @@ def main():
             while j + 1 < len(prior) and prior[j + 1] == prior[j] + 1:
                 j += 1
             vm.vmla_cache_append(cache, xdev(prior[i:j + 1]), dw["w_down"], dw["w_kr"], prior[i],
-                                 j + 1 - i)
+                                 j + 1 - i, dims=dims)
             i = j + 1
         sets = [(xdev(list(w.chunk_frame_ids)).contiguous(), dw, cache)]
     else:
@@ -202,7 +210,8 @@ def main():
         for _ in range(n_sets):
             dw = {k: (torch.randn(shp, generator=g, device=dev) * shp[-2] ** -0.5).to(torch.bfloat16)
                   for k, shp in shapes.items()}
-            cache = vm.LatentCache.empty(w.batch, w.window_frames, w.grid_h, w.grid_w, device=dev)
+            cache = vm.LatentCache.empty(w.batch, w.window_frames, w.grid_h, w.grid_w, device=dev,
+                                         dims=dims)
             cache.data.normal_(generator=g)
             x = torch.randn((w.batch, w.n_q, w.d_model), generator=g, device=dev).to(torch.bfloat16)
             sets.append((x, dw, cache))
@@ -291,7 +300,7 @@ def main():
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "latent_attn_config2_traffic.json")
     if (args.config == 2 and not (args.long_horizon or args.layer or args.explicit)
-            and os.path.exists(tfile)):
+            and args.d_c == 192 and os.path.exists(tfile)):
         with open(tfile) as f:
             tr = json.load(f)
         if tr.get("kernel_source_sha") == _kernel_sha():
@@ -345,6 +354,8 @@ def main():
         result["config"]["workload"] = ("Wan-1.3B-shaped chunk-layer, long rollout: B=1, 30x52 "
                                         "grid, 3-frame query chunk at t=18..20 over one sink frame "
                                         "plus a 6-frame window, RoPE applied at read time")
+    if args.d_c != 192:
+        result["config"]["workload"] += f"; content latent d_c = {args.d_c} (latent-budget sweep)"
     if args.explicit:
         result["config"]["workload"] += ("; explicit route: per-head K/V rebuilt from the latent "
                                          "cache each step (201 MB at B=1), then 128-dim attention")

@@ -24,9 +24,13 @@
  *  - Errors: every argument is validated on the host before any HIP call; a
  *    negative vmla_status is returned and nothing is launched. A failed launch
  *    returns VMLA_ERR_HIP. No exception or abort crosses the ABI.
- *  - Supported geometry in this version: d_nope = 96, d_rope = 32, d_c = 192,
- *    d_v = 128 (the defaults of [PL] App. D.2-D.3), rope_pairs summing to
- *    d_rope / 2, d_model a multiple of 64, 1 <= n_heads <= 64.
+ *  - Supported geometry in this version: d_nope = 96, d_rope = 32, d_v = 128
+ *    (the defaults of [PL] App. D.2-D.3), rope_pairs summing to d_rope / 2,
+ *    d_model a multiple of 64, 1 <= n_heads <= 64; d_c = 192 (the default),
+ *    or 64 / 128 for vmla_cache_append, vmla_chunk_attention and its two
+ *    stages (the latent-budget sweep of [PL] §4 "Batch Scaling Under Fixed
+ *    Memory" and App. F "Latent dimension"). The whole-layer, explicit and
+ *    weight-fold entry points take d_c = 192 only.
  *
  * Token and position convention: token n of a latent frame sits at grid
  * position (h, w) = (n / grid_w, n % grid_w); t is the absolute latent-frame

@@ -52,12 +52,20 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kWChunks = kRow / 8;              // 28 chunks per weight row: 24 W_down + 4 W_KR
-constexpr int kWdElems = kStageK * kDC;         // W_down tile
-constexpr int kWElems = kStageK * kRow;         // W_down + W_KR tiles
-constexpr int kWdLoads = kWdElems * 2 / 1024;   // 24 wave-wide loads
-constexpr int kColBlocks = 7;                   // 16-wide column blocks per wave
 constexpr int kMaxRows = 160;
+
+// Weight-tile shape for a content width DC (192 by default; 64 and 128 for
+// the latent-budget sweep): a row of [W_down | W_KR] is DC + kDRope wide.
+template <int DC>
+struct WShape {
+  static constexpr int kRow = DC + kDRope;
+  static constexpr int kWChunks = kRow / 8;               // 28 chunks per weight row at DC 192
+  static constexpr int kWdElems = kStageK * DC;           // W_down tile
+  static constexpr int kWElems = kStageK * kRow;          // W_down + W_KR tiles
+  static constexpr int kWdLoads = kWdElems * 2 / 1024;    // 24 wave-wide loads at DC 192
+  static constexpr int kColBlocks = kRow / 32;            // 16-wide column blocks per wave (7)
+  static_assert(kRow % 32 == 0, "two column halves of 16-wide blocks");
+};
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -67,8 +75,11 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ int swz_wd(int k) { return 2 * (((k >> 1) & 1) | (((k >> 3) & 1) << 1)); }
 __device__ __forceinline__ int swz_wr(int k) { return 2 * ((k >> 3) & 1); }
 
-template <typename T, int NRB>
+template <typename T, int NRB, int DC>
 struct Tile {
+  static constexpr int kRow = WShape<DC>::kRow;
+  static constexpr int kWChunks = WShape<DC>::kWChunks;
+  static constexpr int kWElems = WShape<DC>::kWElems;
   static constexpr int kRows = 32 * NRB;                   // rows of a workgroup at most
   static constexpr int kXElems = kRows * kStageK;
   static constexpr int kXLoads = kXElems * 2 / 1024;       // 4 NRB
@@ -87,10 +98,15 @@ struct Tile {
   static_assert(kSmemElems * 2 <= 160 * 1024, "LDS budget");
 };
 
-template <typename T, int NRB>
+template <typename T, int NRB, int DC>
 __global__ __launch_bounds__(kThreads)
 void append_kernel(AppendArgs a) {
-  using Tl = Tile<T, NRB>;
+  using Tl = Tile<T, NRB, DC>;
+  constexpr int kDC = DC;
+  constexpr int kRow = WShape<DC>::kRow;
+  constexpr int kWdElems = WShape<DC>::kWdElems;
+  constexpr int kWdLoads = WShape<DC>::kWdLoads;
+  constexpr int kColBlocks = WShape<DC>::kColBlocks;
   constexpr bool kBf16 = std::is_same_v<T, bf16_t>;
   __shared__ __attribute__((aligned(16))) bf16_t smem[Tl::kSmemElems];
 
@@ -291,10 +307,10 @@ void append_kernel(AppendArgs a) {
       const int row = row0 + 16 * rb;
 #pragma unroll
       for (int cb = 0; cb < kColBlocks; ++cb) {
-        const int col = 112 * ch + 16 * cb + 4 * g;
+        const int col = 16 * kColBlocks * ch + 16 * cb + 4 * g;
         const f32x4 v = acc[rb][cb];
         if constexpr (kBf16) {
-          if (ch == 0 || cb < 5)
+          if (ch == 0 || cb < kDC / 16 - kColBlocks)   // c columns (half 1 ends with k_R)
             *reinterpret_cast<uint2*>(&ot[row * kOutLd + col]) = uint2{pack2(v[0], v[1]), pack2(v[2], v[3])};
           else
             *reinterpret_cast<f32x4*>(&kr[row * kKrLd + col - kDC]) = v;
@@ -341,15 +357,24 @@ void append_kernel(AppendArgs a) {
   }
 }
 
-template <typename T>
+template <typename T, int DC>
 void launch_t(const AppendArgs& a, int groups, int nrb, hipStream_t s) {
   const dim3 grid(groups), block(kThreads);
   switch (nrb) {
-    case 5: hipLaunchKernelGGL((append_kernel<T, 5>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((append_kernel<T, 4>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((append_kernel<T, 3>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((append_kernel<T, 2>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((append_kernel<T, 1>), grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL((append_kernel<T, 5, DC>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((append_kernel<T, 4, DC>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((append_kernel<T, 3, DC>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((append_kernel<T, 2, DC>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((append_kernel<T, 1, DC>), grid, block, 0, s, a); break;
+  }
+}
+
+template <typename T>
+void launch_dc(const AppendArgs& a, int groups, int nrb, hipStream_t s) {
+  switch (a.d_c) {
+    case 64: launch_t<T, 64>(a, groups, nrb, s); break;
+    case 128: launch_t<T, 128>(a, groups, nrb, s); break;
+    default: launch_t<T, kDC>(a, groups, nrb, s); break;
   }
 }
 
@@ -376,8 +401,8 @@ hipError_t launch_append(const AppendArgs& a, bool f32, hipStream_t s) {
   if (e != hipSuccess) return e;
   int nrb = 1;
   const int groups = append_plan((int64_t)a.batch * a.n_tok, cus > 0 ? cus : 1, &nrb);
-  if (f32) launch_t<float>(a, groups, nrb, s);
-  else launch_t<bf16_t>(a, groups, nrb, s);
+  if (f32) launch_dc<float>(a, groups, nrb, s);
+  else launch_dc<bf16_t>(a, groups, nrb, s);
   return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@ struct AppendArgs {
   float inv_grid_w, inv_tokens_per_frame, inv_window_frames;   // 1/x as float
   int sink_frames;      // 0 or 1: frame 0 kept in slots [0, T)
   int rope_at_read;     // 1: k_R stored unrotated
+  int d_c;              // content width: 64, 128 or kDC (cache rows are d_c + kDRope wide)
   RopeTable rope;
 };
 
@@ -46,6 +47,7 @@ struct QArgs {
   int grid_w, tokens_per_frame, t_first;
   float inv_grid_w, inv_tokens_per_frame;   // 1/x as float
   float qscale;         // softmax scale * log2(e)
+  int d_c;              // content width: 64, 128 or kDC (Qhat rows are d_c + kDRope wide)
   RopeTable rope;
 };
 
@@ -56,6 +58,7 @@ struct AttnArgs {
   void* out;            // [batch, n_q, n_heads, kDV]
   uint16_t* olat;       // null, or [batch * n_q, n_heads * kDC] bf16: O_lat / l instead of out
   int batch, n_q, n_heads, n_k, cache_rows;
+  int d_c;              // content width: 64, 128 or kDC (rows are d_c + kDRope wide)
   // Read-time RoPE of k_R (rope_at_read = 1): the key in slot frame fs sits at
   // temporal coordinate fs when fs < sink_frames, otherwise at
   // sink_frames + ((fs - sink_frames - shift_mod_w) mod window_frames).

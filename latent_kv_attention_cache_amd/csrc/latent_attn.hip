@@ -73,20 +73,27 @@ namespace {
 constexpr int kKT = 64;                     // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kChunks = kRow / 8;           // 16-byte chunks per key row (28)
 constexpr int kSlots = kKT + 4;             // slots per chunk column (padded)
-constexpr int kTileElems = kChunks * kSlots * 8;
-constexpr int kTileLoads = kChunks;         // wave-wide 16-byte loads per tile (one per chunk column)
 constexpr int kLoaders = kWaves / 2;        // the X waves issue the tile loads
-constexpr int kLoadsPerWave = kTileLoads / kLoaders;
 constexpr int kBufs = 4;
 constexpr int kVLd = kDV + 8;               // padded LDS row of W_V_up[h] (epilogue)
-constexpr int kFeatSteps = kRow / 16;       // 14
-constexpr int kLatTiles = kDC / 32;         // 6
 constexpr float kLazy = 8.f;                // lazy-rescale threshold (log2 units)
 
-static_assert(kTileLoads % kLoaders == 0, "tile loads must split evenly over the loading waves");
-static_assert(2 * kDC * kVLd <= kBufs * kTileElems, "W_V_up of two heads must fit in the tile buffers");
+// Shape of the latent row for a content width DC (192 by default; 64 and 128
+// for the latent-budget sweep): [c (DC) | k_R (kDRope)].
+template <int DC>
+struct AttnShape {
+  static constexpr int kDC = DC;
+  static constexpr int kRow = DC + kDRope;
+  static constexpr int kChunks = kRow / 8;          // 16-byte chunks per key row (28 at DC 192)
+  static constexpr int kTileElems = kChunks * kSlots * 8;
+  static constexpr int kLoadsPerWave = kChunks / kLoaders;   // one load per chunk column
+  static constexpr int kFeatSteps = kRow / 16;      // 14
+  static constexpr int kLatTiles = DC / 32;         // 6
+  static_assert(kChunks % kLoaders == 0, "tile loads must split evenly over the loading waves");
+  static_assert(2 * DC * kVLd <= kBufs * kTileElems, "W_V_up of two heads must fit in the tile buffers");
+  static_assert(DC % 32 == 0 && DC * kDV / 8 % kThreads == 0, "content width");
+};
 
 // Scheduling-group masks (instruction classes of sched_group_barrier).
 constexpr int kSchedMfma = 0x008;
@@ -102,9 +109,16 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
                :: "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory");
 }
 
-template <typename T, bool kRot, bool kFold>
+template <typename T, bool kRot, bool kFold, int DC>
 __global__ __launch_bounds__(kThreads)
 void latent_attn_kernel(AttnArgs a) {
+  using Sh = AttnShape<DC>;
+  constexpr int kDC = Sh::kDC;
+  constexpr int kRow = Sh::kRow;
+  constexpr int kTileElems = Sh::kTileElems;
+  constexpr int kLoadsPerWave = Sh::kLoadsPerWave;
+  constexpr int kFeatSteps = Sh::kFeatSteps;
+  constexpr int kLatTiles = Sh::kLatTiles;
   __shared__ __attribute__((aligned(16))) bf16_t kt[kBufs * kTileElems];
 
   const int tid = threadIdx.x;
@@ -241,7 +255,7 @@ void latent_attn_kernel(AttnArgs a) {
     }
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 22; ++i) {
+    for (int i = 0; i < 4 * kLatTiles - 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
@@ -261,7 +275,7 @@ void latent_attn_kernel(AttnArgs a) {
     }
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
 #pragma unroll
-    for (int i = 0; i < 12; ++i) {
+    for (int i = 0; i < kFeatSteps - 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 1);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
     }
@@ -423,28 +437,37 @@ void latent_attn_kernel(AttnArgs a) {
   }
 }
 
-}  // namespace
-
-hipError_t launch_latent_attn(const AttnArgs& a, bool f32, hipStream_t s) {
+template <int DC>
+hipError_t launch_dc(const AttnArgs& a, bool f32, hipStream_t s) {
   const int units = (a.n_q + 31) / 32;
   const int upad = units > kWaves ? units : kWaves;
   dim3 grid((a.n_heads * upad + kWaves - 1) / kWaves, 1, a.batch);
   if (a.olat) {
     if (a.rope_at_read) {
-      if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, true, true>), grid, dim3(kThreads), 0, s, a);
-      else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, true, true>), grid, dim3(kThreads), 0, s, a);
+      if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, true, true, DC>), grid, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, true, true, DC>), grid, dim3(kThreads), 0, s, a);
     } else {
-      if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, true>), grid, dim3(kThreads), 0, s, a);
-      else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, true>), grid, dim3(kThreads), 0, s, a);
+      if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, true, DC>), grid, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, true, DC>), grid, dim3(kThreads), 0, s, a);
     }
   } else if (a.rope_at_read) {
-    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, true, false>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, true, false>), grid, dim3(kThreads), 0, s, a);
+    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, true, false, DC>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, true, false, DC>), grid, dim3(kThreads), 0, s, a);
   } else {
-    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, false>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, false>), grid, dim3(kThreads), 0, s, a);
+    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, false, DC>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, false, DC>), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_latent_attn(const AttnArgs& a, bool f32, hipStream_t s) {
+  switch (a.d_c) {
+    case 64: return launch_dc<64>(a, f32, s);
+    case 128: return launch_dc<128>(a, f32, s);
+    default: return launch_dc<kDC>(a, f32, s);
+  }
 }
 
 }  // namespace vmla

@@ -64,9 +64,11 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // chunk permutation mask of W_Q tile row k (an involution on the chunks of a row)
 __device__ __forceinline__ int swz_q(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
 
-template <typename T>
+template <typename T, int DC>
 __global__ __launch_bounds__(kThreads)
 void qprologue_kernel(QArgs a) {
+  constexpr int kDC = DC;                   // content width (192 by default; 64, 128 in the sweep)
+  constexpr int kRow = DC + kDRope;         // Qhat row
   __shared__ __attribute__((aligned(16))) bf16_t smem[kStages * kStageElems];
 
   // Workgroups are dispatched round-robin over the 8 XCDs; id = 8 (HP q + hp) + x8
@@ -311,8 +313,19 @@ hipError_t launch_qprologue(const QArgs& a, bool f32, hipStream_t s) {
   const int64_t n_rt = (M + kRowsT - 1) / kRowsT;
   const int n_hp = (a.n_heads + kHeadsT - 1) / kHeadsT;
   const dim3 grid((unsigned)(8 * n_hp * ((n_rt + 7) / 8)));
-  if (f32) hipLaunchKernelGGL(qprologue_kernel<float>, grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(qprologue_kernel<bf16_t>, grid, dim3(kThreads), 0, s, a);
+  switch (a.d_c) {
+    case 64:
+      if (f32) hipLaunchKernelGGL((qprologue_kernel<float, 64>), grid, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((qprologue_kernel<bf16_t, 64>), grid, dim3(kThreads), 0, s, a);
+      break;
+    case 128:
+      if (f32) hipLaunchKernelGGL((qprologue_kernel<float, 128>), grid, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((qprologue_kernel<bf16_t, 128>), grid, dim3(kThreads), 0, s, a);
+      break;
+    default:
+      if (f32) hipLaunchKernelGGL((qprologue_kernel<float, kDC>), grid, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((qprologue_kernel<bf16_t, kDC>), grid, dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

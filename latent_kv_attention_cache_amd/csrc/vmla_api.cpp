@@ -20,7 +20,10 @@ constexpr int64_t kMaxFrameIndex = 1 << 20;
 
 int32_t check_dims(const vmla_dims* d) {
   if (!d) return VMLA_ERR_NULL;
-  if (d->d_nope != kDNope || d->d_rope != kDRope || d->d_c != kDC || d->d_v != kDV) return VMLA_ERR_SHAPE;
+  if (d->d_nope != kDNope || d->d_rope != kDRope || d->d_v != kDV) return VMLA_ERR_SHAPE;
+  // content width: the default 192, or 64 / 128 (latent-budget sweep) for the
+  // append and the attention core
+  if (d->d_c != kDC && d->d_c != 64 && d->d_c != 128) return VMLA_ERR_SHAPE;
   if (d->d_model < 64 || d->d_model % 64 != 0 || d->d_model > (1 << 16)) return VMLA_ERR_SHAPE;
   if (d->n_heads < 1 || d->n_heads > 64) return VMLA_ERR_SHAPE;
   int pairs = 0;
@@ -34,7 +37,14 @@ int32_t check_dims(const vmla_dims* d) {
   return VMLA_OK;
 }
 
-int32_t check_cache(const vmla_cache* c, int32_t dtype) {
+// The whole-layer, explicit and weight-fold entry points run at d_c = 192 only.
+int32_t check_dims_192(const vmla_dims* d) {
+  const int32_t st = check_dims(d);
+  if (st) return st;
+  return d->d_c == kDC ? VMLA_OK : VMLA_ERR_SHAPE;
+}
+
+int32_t check_cache(const vmla_cache* c, int32_t dtype, int row) {
   if (!c) return VMLA_ERR_NULL;
   if (!c->data) return VMLA_ERR_NULL;
   if (!aligned16(c->data)) return VMLA_ERR_ALIGN;
@@ -47,7 +57,7 @@ int32_t check_cache(const vmla_cache* c, int32_t dtype) {
   const int64_t t = (int64_t)c->grid_h * c->grid_w;
   const int64_t rows = t * ((int64_t)c->sink_frames + c->window_frames);
   // every element offset handled by the kernels must fit in int32 per batch element
-  if (rows * kRow > INT32_MAX || rows >= (1 << 24)) return VMLA_ERR_SHAPE;
+  if (rows * row > INT32_MAX || rows >= (1 << 24)) return VMLA_ERR_SHAPE;
   return VMLA_OK;
 }
 
@@ -109,7 +119,7 @@ int32_t vmla_cache_append(const vmla_dims* dims, const vmla_cache* cache, int32_
   int32_t st = check_dims(dims);
   if (st) return st;
   if (!x || !w_down || !w_kr) return VMLA_ERR_NULL;
-  st = check_cache(cache, dtype);
+  st = check_cache(cache, dtype, dims->d_c + kDRope);
   if (st) return st;
   if (!aligned16(x) || !aligned16(w_down) || !aligned16(w_kr)) return VMLA_ERR_ALIGN;
   if (t_first < 0 || n_frames < 1 || n_frames > cache->window_frames) return VMLA_ERR_RANGE;
@@ -128,13 +138,14 @@ int32_t vmla_cache_append(const vmla_dims* dims, const vmla_cache* cache, int32_
   a.inv_window_frames = 1.f / (float)cache->window_frames;
   a.sink_frames = cache->sink_frames;
   a.rope_at_read = cache->rope_at_read;
+  a.d_c = dims->d_c;
   a.rope = rope_table(dims);
   return hip_status(launch_append(a, dtype == VMLA_F32, static_cast<hipStream_t>(stream)));
 }
 
 size_t vmla_attention_workspace_bytes(const vmla_dims* dims, int32_t batch, int32_t n_q) {
   if (check_dims(dims) != VMLA_OK || batch < 1 || n_q < 1) return 0;
-  return (size_t)batch * dims->n_heads * (size_t)n_q * kRow * sizeof(uint16_t);
+  return (size_t)batch * dims->n_heads * (size_t)n_q * (dims->d_c + kDRope) * sizeof(uint16_t);
 }
 
 namespace {
@@ -145,7 +156,7 @@ int32_t check_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t 
                         const void* workspace, size_t workspace_bytes, QArgs* q, AttnArgs* a) {
   int32_t st = check_dims(dims);
   if (st) return st;
-  st = check_cache(cache, dtype);
+  st = check_cache(cache, dtype, dims->d_c + kDRope);
   if (st) return st;
   if (t_first < 0 || n_frames < 1 || n_frames > cache->window_frames) return VMLA_ERR_RANGE;
   if ((int64_t)t_first + n_frames > kMaxFrameIndex) return VMLA_ERR_RANGE;
@@ -170,6 +181,7 @@ int32_t check_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t 
   q->inv_grid_w = 1.f / (float)cache->grid_w;
   q->inv_tokens_per_frame = 1.f / (float)T;
   q->qscale = (float)((double)dims->scale * 1.4426950408889634);   // scale * log2(e)
+  q->d_c = dims->d_c;
   q->rope = rope_table(dims);
 
   *a = AttnArgs{};
@@ -177,6 +189,7 @@ int32_t check_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t 
   a->batch = cache->batch; a->n_q = (int)n_q; a->n_heads = dims->n_heads;
   a->n_k = (int)(T * n_valid_frames); a->cache_rows = (int)(T * span);
   a->rope_at_read = cache->rope_at_read;
+  a->d_c = dims->d_c;
   a->sink_frames = cache->sink_frames;
   a->window_frames = cache->window_frames;
   a->shift_mod_w = (int)(shift % cache->window_frames);
@@ -249,7 +262,7 @@ static int32_t check_d_q(int32_t d_q) {
 
 int32_t vmla_fold_query_weights(const vmla_dims* dims, int32_t dtype, int32_t d_q,
                                 const void* w_uq, const void* w_k_up, void* w_qa, void* stream) {
-  int32_t st = check_dims(dims);
+  int32_t st = check_dims_192(dims);
   if (st) return st;
   if (!w_uq || !w_k_up || !w_qa) return VMLA_ERR_NULL;
   if (dtype != VMLA_F32 && dtype != VMLA_BF16) return VMLA_ERR_DTYPE;
@@ -264,7 +277,7 @@ int32_t vmla_fold_query_weights(const vmla_dims* dims, int32_t dtype, int32_t d_
 
 int32_t vmla_fold_output_weights(const vmla_dims* dims, int32_t dtype, const void* w_v_up,
                                  const void* w_o, void* w_vo, void* stream) {
-  int32_t st = check_dims(dims);
+  int32_t st = check_dims_192(dims);
   if (st) return st;
   if (!w_v_up || !w_o || !w_vo) return VMLA_ERR_NULL;
   if (dtype != VMLA_F32 && dtype != VMLA_BF16) return VMLA_ERR_DTYPE;
@@ -276,7 +289,7 @@ int32_t vmla_fold_output_weights(const vmla_dims* dims, int32_t dtype, const voi
 }
 
 size_t vmla_layer_workspace_bytes(const vmla_dims* dims, int32_t d_q, int32_t batch, int32_t n_q) {
-  if (check_d_q(d_q) != VMLA_OK) return 0;
+  if (check_d_q(d_q) != VMLA_OK || check_dims_192(dims) != VMLA_OK) return 0;
   const size_t qhat = vmla_attention_workspace_bytes(dims, batch, n_q);
   if (!qhat) return 0;
   const size_t m = (size_t)batch * n_q;
@@ -294,6 +307,8 @@ int32_t check_layer(const vmla_dims* dims, const vmla_cache* cache, int32_t dtyp
                     const void* workspace, size_t workspace_bytes, QArgs* q, AttnArgs* a,
                     uint16_t** inner) {
   int32_t st = check_d_q(d_q);
+  if (st) return st;
+  st = check_dims_192(dims);
   if (st) return st;
   st = check_attention(dims, cache, dtype, t_first, n_frames, n_valid_frames, workspace,
                        workspace_bytes, q, a);
@@ -398,7 +413,7 @@ int32_t vmla_chunk_attention_layer(const vmla_dims* dims, const vmla_cache* cach
 
 int32_t vmla_pack_kv_weights(const vmla_dims* dims, int32_t dtype, const void* w_k_up,
                              const void* w_v_up, void* w_kv, void* stream) {
-  int32_t st = check_dims(dims);
+  int32_t st = check_dims_192(dims);
   if (st) return st;
   if (!w_k_up || !w_v_up || !w_kv) return VMLA_ERR_NULL;
   if (dtype != VMLA_F32 && dtype != VMLA_BF16) return VMLA_ERR_DTYPE;
@@ -409,7 +424,7 @@ int32_t vmla_pack_kv_weights(const vmla_dims* dims, int32_t dtype, const void* w
 }
 
 size_t vmla_explicit_workspace_bytes(const vmla_dims* dims, int32_t batch, int32_t n_q, int32_t n_k) {
-  if (check_dims(dims) != VMLA_OK || batch < 1 || n_q < 1 || n_k < 1) return 0;
+  if (check_dims_192(dims) != VMLA_OK || batch < 1 || n_q < 1 || n_k < 1) return 0;
   const size_t per = (size_t)batch * dims->n_heads * sizeof(uint16_t);
   return per * ((size_t)n_q * kDHead + (size_t)n_k * 2 * kDHead);
 }
@@ -423,8 +438,10 @@ int32_t vmla_chunk_attention_explicit(const vmla_dims* dims, const vmla_cache* c
   QArgs q;
   AttnArgs a;
   // the attention checks, with the workspace size checked below
-  int32_t st = check_attention(dims, cache, dtype, t_first, n_frames, n_valid_frames, workspace,
-                               SIZE_MAX, &q, &a);
+  int32_t st = check_dims_192(dims);
+  if (st) return st;
+  st = check_attention(dims, cache, dtype, t_first, n_frames, n_valid_frames, workspace,
+                       SIZE_MAX, &q, &a);
   if (st) return st;
   if (cache->rope_at_read) return VMLA_ERR_SHAPE;
   if ((int64_t)a.n_k * 2 * kDHead * dims->n_heads > INT32_MAX) return VMLA_ERR_SHAPE;
@@ -463,7 +480,7 @@ int32_t vmla_chunk_attention_explicit(const vmla_dims* dims, const vmla_cache* c
 
 int32_t vmla_output_projection(const vmla_dims* dims, int32_t dtype, int64_t m, const void* in,
                                const void* w_o, void* out, void* stream) {
-  int32_t st = check_dims(dims);
+  int32_t st = check_dims_192(dims);
   if (st) return st;
   if (!in || !w_o || !out) return VMLA_ERR_NULL;
   if (dtype != VMLA_F32 && dtype != VMLA_BF16) return VMLA_ERR_DTYPE;

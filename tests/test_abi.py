@@ -52,8 +52,11 @@ def test_workspace_bytes(lib):
     d = vm.default_dims()
     assert vm.vmla_attention_workspace_bytes(1, 4680, d) == 12 * 4680 * 224 * 2
     assert vm.vmla_attention_workspace_bytes(0, 4680, d) == 0
-    bad = vm.default_dims(d_c=128)
+    bad = vm.default_dims(d_c=96)
     assert vm.vmla_attention_workspace_bytes(1, 10, bad) == 0
+    # the latent-budget sweep widths: rows of d_c + 32
+    assert vm.vmla_attention_workspace_bytes(1, 10, vm.default_dims(d_c=64)) == 12 * 10 * 96 * 2
+    assert vm.vmla_attention_workspace_bytes(1, 10, vm.default_dims(d_c=128)) == 12 * 10 * 160 * 2
 
 
 # Fake, never-dereferenced device addresses: validation must fail before any use.
@@ -95,7 +98,8 @@ def test_append_validation(lib):
     assert _append(lib, cache=_cache(data=MIS)) == vm.VMLA_ERR_ALIGN
     assert _append(lib, dtype=7) == vm.VMLA_ERR_DTYPE
     assert _append(lib, dtype=vm.VMLA_F32) == vm.VMLA_ERR_DTYPE          # cache is bf16
-    assert _append(lib, dims=vm.default_dims(d_c=128)) == vm.VMLA_ERR_SHAPE
+    assert _append(lib, dims=vm.default_dims(d_c=96)) == vm.VMLA_ERR_SHAPE   # not 64, 128 or 192
+    assert _append(lib, dims=vm.default_dims(d_c=256)) == vm.VMLA_ERR_SHAPE
     assert _append(lib, dims=vm.default_dims(d_model=100)) == vm.VMLA_ERR_SHAPE
     assert _append(lib, dims=vm.default_dims(rope_pairs=(6, 5, 4))) == vm.VMLA_ERR_SHAPE
     assert _append(lib, dims=vm.default_dims(n_heads=0)) == vm.VMLA_ERR_SHAPE
@@ -187,6 +191,17 @@ def test_layer_validation(lib):
     assert lib.vmla_output_projection(ctypes.byref(d), vm.VMLA_BF16, 1 << 25, A, B, C, None) == vm.VMLA_ERR_SHAPE
     assert lib.vmla_output_projection(ctypes.byref(d), vm.VMLA_BF16, 8, None, B, C, None) == vm.VMLA_ERR_NULL
     assert lib.vmla_output_projection(ctypes.byref(d), 3, 8, A, B, C, None) == vm.VMLA_ERR_DTYPE
+
+
+def test_latent_budget_widths_only_on_the_core_path(lib):
+    # d_c 64 / 128 are accepted by the append and the attention core; the whole
+    # layer, the explicit route and the weight folds run at d_c = 192 only
+    d64 = vm.default_dims(d_c=64)
+    assert lib.vmla_layer_workspace_bytes(ctypes.byref(d64), 768, 1, 24) == 0
+    assert lib.vmla_explicit_workspace_bytes(ctypes.byref(d64), 1, 24, 72) == 0
+    assert lib.vmla_fold_query_weights(ctypes.byref(d64), vm.VMLA_BF16, 768, A, B, C, None) == vm.VMLA_ERR_SHAPE
+    assert lib.vmla_pack_kv_weights(ctypes.byref(d64), vm.VMLA_BF16, A, B, C, None) == vm.VMLA_ERR_SHAPE
+    assert _attn(lib, dims=d64, ws=None) == vm.VMLA_ERR_WORKSPACE        # validation passed up to the workspace
 
 
 def test_explicit_validation(lib):

@@ -1,0 +1,48 @@
+"""The closed-form capacity model against the figures the pages print."""
+import pytest
+
+from latent_kv_attention_cache_amd import capacity as cap
+
+
+def test_scalars_per_token_match_the_pages():
+    # [PL] App. D.2: 224 cached scalars per token per layer against 3072
+    assert cap.latent_scalars_per_token() == 224
+    assert cap.dense_scalars_per_token() == 3072
+
+
+def test_dense_window_matches_the_printed_scalar_count():
+    # 21 frames x 1560 tokens x 30 layers x 3072 scalars = 3.02 B scalars ([PL] §3),
+    # about 6.0 GB in bf16
+    b = cap.cache_bytes_per_request(cap.dense_scalars_per_token())
+    assert b == 2 * 3_019_161_600
+    assert abs(b / cap.GB - 6.04) < 0.01
+
+
+def test_measured_slopes_exceed_the_cache_by_a_similar_residual():
+    # [PL] §4 "Batch Scaling Under Fixed Memory": 6.26 GB per request (dense) and
+    # 0.57 / 1.43 GB per request at d_c = 64 / 512. The model's cache-only slope
+    # sits below every measured one, and the residual (per-request activations
+    # the pages do not itemise) is a few hundred MB in each case.
+    measured = {"mha": 6.26, 64: 0.57, 512: 1.43}
+    model = {"mha": cap.cache_bytes_per_request(3072) / cap.GB,
+             64: cap.cache_bytes_per_request(cap.latent_scalars_per_token(64)) / cap.GB,
+             512: cap.cache_bytes_per_request(cap.latent_scalars_per_token(512)) / cap.GB}
+    for k in measured:
+        residual = measured[k] - model[k]
+        assert 0.1 < residual < 0.45, (k, residual)
+    # the pages' 77-91 % reduction of the slope follows from their own numbers
+    assert round(100 * (1 - 1.43 / 6.26)) == 77 and round(100 * (1 - 0.57 / 6.26)) == 91
+
+
+def test_max_batch_and_sweep():
+    assert cap.max_batch(100.0, 30.0) == 3
+    assert cap.max_batch(100.0, 30.0, fixed_bytes=20.0) == 2
+    assert cap.max_batch(10.0, 30.0) == 0
+    with pytest.raises(ValueError):
+        cap.max_batch(1.0, 0.0)
+    s = cap.sweep(budget_bytes=288 * cap.GB)
+    assert s["mha"]["max_batch"] == 47                  # 288 GB / 6.04 GB
+    assert s["d_c=192"]["max_batch"] == 654             # 288 GB / 0.440 GB
+    assert s["d_c=64"]["cache_bytes"] < s["d_c=192"]["cache_bytes"] < s["d_c=512"]["cache_bytes"]
+    # a sink frame adds one frame of slots per layer
+    assert cap.cache_bytes_per_request(224, frames=6, sink_frames=1) == 30 * 7 * 1560 * 224 * 2
