@@ -41,22 +41,26 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsT = 128;                       // rows per workgroup
 constexpr int kColsT = 256;                       // columns per workgroup
-constexpr int kNRB = 4;                           // 16-row blocks per wave
 constexpr int kCB = 8;                            // 16-column blocks per wave
-constexpr int kXElems = kRowsT * kStageK;         // A slice of a stage
-constexpr int kXLoads = kXElems * 2 / 1024;       // 16 wave-wide 1 KB loads
 constexpr int kWElems = kStageK * kColsT;         // W slice of a stage
 constexpr int kWLoads = kWElems * 2 / 1024;       // 32
-constexpr int kStageElems = kXElems + kWElems;
 constexpr int kStages = 3;
-constexpr int kXPerWave = kXLoads / kWaves;       // 4
 constexpr int kWPerWave = kWLoads / kWaves;       // 8
-constexpr int kL = kXPerWave + kWPerWave;         // loads per wave per stage
 constexpr int kWChunks = kColsT / 8;              // 32 chunks per W tile row
-static_assert(kXLoads % kWaves == 0 && kWLoads % kWaves == 0, "loads split evenly");
-static_assert(kStages * kStageElems * 2 <= 160 * 1024, "LDS budget");
+
+// Row tile of NRB 16-row blocks per wave: 128 rows (NRB = 4), or 64 rows
+// (NRB = 2) for launches that would otherwise leave most compute units idle.
+template <int NRB>
+struct GShape {
+  static constexpr int kRowsT = 32 * NRB;                 // rows per workgroup
+  static constexpr int kXElems = kRowsT * kStageK;        // A slice of a stage
+  static constexpr int kXPerWave = kXElems * 2 / 1024 / kWaves;   // NRB wave-wide 1 KB loads
+  static constexpr int kStageElems = kXElems + kWElems;
+  static constexpr int kL = kXPerWave + kWPerWave;        // loads per wave per stage
+  static_assert(kXElems * 2 / 1024 % kWaves == 0 && kWLoads % kWaves == 0, "loads split evenly");
+  static_assert(kStages * kStageElems * 2 <= 160 * 1024, "LDS budget");
+};
 
 enum { kPlain = 0, kHead = 1, kKV = 2 };
 
@@ -78,9 +82,15 @@ template <> __device__ __forceinline__ void store4<float>(float* p, float a, flo
   *reinterpret_cast<float4*>(p) = float4{a, b, c, d};
 }
 
-template <typename TA, typename TO, int kMode>
+template <typename TA, typename TO, int kMode, int NRB>
 __global__ __launch_bounds__(kThreads)
 void gemm_kernel(GemmArgs a) {
+  constexpr int kNRB = NRB;
+  constexpr int kRowsT = GShape<NRB>::kRowsT;
+  constexpr int kXElems = GShape<NRB>::kXElems;
+  constexpr int kXPerWave = GShape<NRB>::kXPerWave;
+  constexpr int kStageElems = GShape<NRB>::kStageElems;
+  constexpr int kL = GShape<NRB>::kL;
   __shared__ __attribute__((aligned(16))) bf16_t smem[kStages * kStageElems];
   constexpr bool kBf16 = std::is_same_v<TA, bf16_t>;
 
@@ -151,7 +161,7 @@ void gemm_kernel(GemmArgs a) {
   int a_off[kNRB][2];
 #pragma unroll
   for (int rb = 0; rb < kNRB; ++rb) {
-    const int row = 64 * rh + 16 * rb + j;
+    const int row = 16 * kNRB * rh + 16 * rb + j;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) a_off[rb][kk] = 64 * row + 8 * ((4 * kk + g) ^ swz_a(row));
   }
@@ -226,7 +236,7 @@ void gemm_kernel(GemmArgs a) {
     TO* out = static_cast<TO*>(a.out);
 #pragma unroll
     for (int rb = 0; rb < kNRB; ++rb) {
-      const int64_t m = m0 + 64 * rh + 16 * rb + j;
+      const int64_t m = m0 + 16 * kNRB * rh + 16 * rb + j;
       if (m >= a.m) continue;
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) {
@@ -250,7 +260,7 @@ void gemm_kernel(GemmArgs a) {
       const int dst = ci < kDNope ? ci : ci + kDRope;
 #pragma unroll
       for (int rb = 0; rb < kNRB; ++rb) {
-        const int64_t m = m0 + 64 * rh + 16 * rb + j;
+        const int64_t m = m0 + 16 * kNRB * rh + 16 * rb + j;
         if (m >= a.m) continue;
         uint16_t* row = kv + ((int64_t)h * a.m + m) * (2 * kDHead);
         const f32x4 v = acc[rb][cb];
@@ -269,7 +279,7 @@ void gemm_kernel(GemmArgs a) {
     int pos[kNRB][3];                                  // (t, h, w) of each row
 #pragma unroll
     for (int rb = 0; rb < kNRB; ++rb) {
-      const int64_t m = m0 + 64 * rh + 16 * rb + j;
+      const int64_t m = m0 + 16 * kNRB * rh + 16 * rb + j;
       const int64_t mc = m < a.m ? m : a.m - 1;
       const int b = (int)(mc / a.n_q);
       const int n = (int)(mc - (int64_t)b * a.n_q);
@@ -353,25 +363,34 @@ void fold_output_kernel(FoldArgs a) {
   static_cast<bf16_t*>(a.out)[i] = f2bf(v);
 }
 
-}  // namespace
-
-hipError_t launch_gemm(const GemmArgs& a, int a_f32, int out_f32, hipStream_t s) {
-  const int64_t n_rt = (a.m + kRowsT - 1) / kRowsT;
+template <int NRB>
+void launch_nrb(const GemmArgs& a, int a_f32, int out_f32, hipStream_t s) {
+  const int64_t n_rt = (a.m + GShape<NRB>::kRowsT - 1) / GShape<NRB>::kRowsT;
   const int n_ct = (a.n + kColsT - 1) / kColsT;
   const dim3 grid((unsigned)(8 * n_ct * ((n_rt + 7) / 8)));
   if (a.mode == kHead) {
-    if (a_f32) hipLaunchKernelGGL((gemm_kernel<float, bf16_t, kHead>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((gemm_kernel<bf16_t, bf16_t, kHead>), grid, dim3(kThreads), 0, s, a);
+    if (a_f32) hipLaunchKernelGGL((gemm_kernel<float, bf16_t, kHead, NRB>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((gemm_kernel<bf16_t, bf16_t, kHead, NRB>), grid, dim3(kThreads), 0, s, a);
   } else if (a.mode == kKV) {
-    if (a_f32) hipLaunchKernelGGL((gemm_kernel<float, bf16_t, kKV>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((gemm_kernel<bf16_t, bf16_t, kKV>), grid, dim3(kThreads), 0, s, a);
+    if (a_f32) hipLaunchKernelGGL((gemm_kernel<float, bf16_t, kKV, NRB>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((gemm_kernel<bf16_t, bf16_t, kKV, NRB>), grid, dim3(kThreads), 0, s, a);
   } else if (a_f32) {
-    if (out_f32) hipLaunchKernelGGL((gemm_kernel<float, float, kPlain>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((gemm_kernel<float, bf16_t, kPlain>), grid, dim3(kThreads), 0, s, a);
+    if (out_f32) hipLaunchKernelGGL((gemm_kernel<float, float, kPlain, NRB>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((gemm_kernel<float, bf16_t, kPlain, NRB>), grid, dim3(kThreads), 0, s, a);
   } else {
-    if (out_f32) hipLaunchKernelGGL((gemm_kernel<bf16_t, float, kPlain>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((gemm_kernel<bf16_t, bf16_t, kPlain>), grid, dim3(kThreads), 0, s, a);
+    if (out_f32) hipLaunchKernelGGL((gemm_kernel<bf16_t, float, kPlain, NRB>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((gemm_kernel<bf16_t, bf16_t, kPlain, NRB>), grid, dim3(kThreads), 0, s, a);
   }
+}
+
+}  // namespace
+
+// 128-row tiles, unless they would occupy at most half of the compute units:
+// then 64-row tiles, twice as many workgroups in the same single round.
+hipError_t launch_gemm(const GemmArgs& a, int a_f32, int out_f32, hipStream_t s) {
+  const int64_t tiles = (a.m + 127) / 128 * ((a.n + kColsT - 1) / kColsT);
+  if (tiles <= 128) launch_nrb<2>(a, a_f32, out_f32, s);
+  else launch_nrb<4>(a, a_f32, out_f32, s);
   return hipGetLastError();
 }
 
