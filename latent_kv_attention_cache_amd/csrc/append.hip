@@ -341,7 +341,7 @@ void append_kernel(AppendArgs a) {
         const int pr = p0 + q;
         const float a0 = src[2 * q], a1 = src[2 * q + 1];
         float sn = 0.f, cs = 1.f;           // keys kept before RoPE: stored as computed
-        if (!a.rope_at_read) sincos_rev(ri[5 * row + 2 + a.rope.axis[pr]], a.rope.rev[pr], &sn, &cs);
+        if (!a.rope_at_read) sincos_rev(ri[5 * row + 2 + a.rope.axis[pr]], a.rope.rev_lo[pr], a.rope.rev_hi[pr], &sn, &cs);
         // pair (a0, a1) -> (a0 cos - a1 sin, a0 sin + a1 cos)
         o[2 * q] = a0 * cs - a1 * sn;
         o[2 * q + 1] = a0 * sn + a1 * cs;

@@ -99,13 +99,16 @@ __device__ __forceinline__ int div_small(int n, int d, float inv_d, int* rem) {
   return q;
 }
 
-// sin and cos of the angle pos * rev revolutions. The fractional part of the
-// revolution count is taken first (exact for an integer pos times a float rate
-// up to rounding of the product: |error| <= |pos * rev| * 2^-24 revolutions),
-// then v_sin_f32 / v_cos_f32, which take their input in revolutions.
-__device__ __forceinline__ void sincos_rev(int pos, float rev, float* s, float* c) {
-  float r = (float)pos * rev;
-  r -= floorf(r);
+// sin and cos of the angle pos * rate for a rate given in revolutions per
+// position step as a 64-bit binary fraction (hi:lo) = rate * 2^64. The
+// fractional revolution of the product is taken in integer arithmetic, exact
+// mod 1 up to the rate's own rounding (< pos * 2^-64 revolutions), then
+// truncated to 32 bits, so the angle error is below 2^-32 revolutions at any
+// position; v_sin_f32 / v_cos_f32 take their input in revolutions.
+__device__ __forceinline__ void sincos_rev(int pos, uint32_t lo, uint32_t hi, float* s, float* c) {
+  const uint32_t p = (uint32_t)pos;
+  const uint32_t frac = __umulhi(p, lo) + p * hi;        // bits 32..63 of pos * rate, mod 2^64
+  const float r = (float)frac * 2.3283064365386963e-10f;  // * 2^-32: [0, 1]
   *s = __builtin_amdgcn_sinf(r);
   *c = __builtin_amdgcn_cosf(r);
 }

@@ -17,10 +17,12 @@ constexpr int kDHead = kDNope + kDRope;   // 128
 constexpr int kRow = kDC + kDRope;        // 224 cached scalars per token
 constexpr int kPairs = kDRope / 2;        // 16 complex RoPE pairs
 
-// Rate of each RoPE pair in revolutions per position step (omega / 2 pi) and
-// its axis (0 = t, 1 = h, 2 = w).
+// Rate of each RoPE pair in revolutions per position step (omega / 2 pi) as a
+// 64-bit binary fraction rate * 2^64 = (rev_hi << 32) | rev_lo, and its axis
+// (0 = t, 1 = h, 2 = w).
 struct RopeTable {
-  float rev[kPairs];
+  uint32_t rev_lo[kPairs];
+  uint32_t rev_hi[kPairs];
   int axis[kPairs];
 };
 

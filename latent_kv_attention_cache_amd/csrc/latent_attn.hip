@@ -207,7 +207,7 @@ void latent_attn_kernel(AttnArgs a) {
       const int ax = a.rope.axis[pr];
       const float a0 = __uint_as_float(in[q] << 16), a1 = __uint_as_float(in[q] & 0xffff0000u);
       float sn, cs;
-      sincos_rev(ax == 0 ? tl : (ax == 1 ? hh : ww), a.rope.rev[pr], &sn, &cs);
+      sincos_rev(ax == 0 ? tl : (ax == 1 ? hh : ww), a.rope.rev_lo[pr], a.rope.rev_hi[pr], &sn, &cs);
       o[q] = pack2(a0 * cs - a1 * sn, a0 * sn + a1 * cs);
     }
     *reinterpret_cast<uint4*>(p) = uint4{o[0], o[1], o[2], o[3]};

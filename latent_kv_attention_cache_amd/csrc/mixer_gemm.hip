@@ -308,7 +308,7 @@ void gemm_kernel(GemmArgs a) {
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
             float sn, cs;
-            sincos_rev(pos[rb][a.rope.axis[pr + q]], a.rope.rev[pr + q], &sn, &cs);
+            sincos_rev(pos[rb][a.rope.axis[pr + q]], a.rope.rev_lo[pr + q], a.rope.rev_hi[pr + q], &sn, &cs);
             const float x0 = v[2 * q], x1 = v[2 * q + 1];
             v[2 * q] = x0 * cs - x1 * sn;
             v[2 * q + 1] = x0 * sn + x1 * cs;

@@ -260,7 +260,7 @@ void qprologue_kernel(QArgs a) {
       for (int q = 0; q < 2; ++q) {
         const int pr = 8 * (cb - kDNope / 16) + 2 * g + q;
         float sn, cs;
-        sincos_rev(pos[rb][a.rope.axis[pr]], a.rope.rev[pr], &sn, &cs);
+        sincos_rev(pos[rb][a.rope.axis[pr]], a.rope.rev_lo[pr], a.rope.rev_hi[pr], &sn, &cs);
         o[2 * q] = v[2 * q] * cs - v[2 * q + 1] * sn;
         o[2 * q + 1] = v[2 * q] * sn + v[2 * q + 1] * cs;
       }

@@ -14,8 +14,9 @@ using namespace vmla;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Largest t_first + n_frames accepted: keeps every position below 2^24 for the
-// exact float-reciprocal division and the RoPE angle error below 1e-4 rev.
+// Largest t_first + n_frames accepted: keeps every token index below 2^24 for
+// the exact float-reciprocal division (RoPE angles are exact fixed-point
+// fractions of a revolution at any position).
 constexpr int64_t kMaxFrameIndex = 1 << 20;
 
 int32_t check_dims(const vmla_dims* d) {
@@ -70,7 +71,12 @@ RopeTable rope_table(const vmla_dims* d) {
   for (int ax = 0; ax < 3; ++ax) {
     for (int i = 0; i < d->rope_pairs[ax]; ++i, ++j) {
       const double omega = std::pow((double)d->rope_theta, -2.0 * i / (double)d->rope_axis_dims[ax]);
-      r.rev[j] = (float)(omega / two_pi);
+      // revolutions per step as a 64-bit binary fraction (only the fractional
+      // revolution matters for the angle)
+      const double rev = omega / two_pi;
+      const uint64_t fx = (uint64_t)std::ldexp(rev - std::floor(rev), 64);
+      r.rev_lo[j] = (uint32_t)fx;
+      r.rev_hi[j] = (uint32_t)(fx >> 32);
       r.axis[j] = ax;
     }
   }

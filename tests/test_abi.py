@@ -108,6 +108,7 @@ def test_append_validation(lib):
     assert _append(lib, t_first=-1) == vm.VMLA_ERR_RANGE
     assert _append(lib, n_frames=0) == vm.VMLA_ERR_RANGE
     assert _append(lib, n_frames=4) == vm.VMLA_ERR_RANGE                 # > window_frames
+    assert _append(lib, t_first=(1 << 20) - 1, n_frames=2) == vm.VMLA_ERR_RANGE   # t_end > 2^20
 
 
 def test_attention_validation(lib):

@@ -245,3 +245,14 @@ def test_append_tile_heights(batch):
     r.append(0, 3)
     for b in (0, batch - 1):
         compare(r.cache_rows(0, 3, b=b), r.append_reference(0, 3, b=b), f"append B={batch} b={b}")
+
+
+def test_largest_frame_index():
+    # t_end = 2^20, the largest frame index the library accepts: RoPE angles of
+    # ~1e6 rad on the highest t band, at append (keys) and in the prologue (queries)
+    t0 = (1 << 20) - 3
+    w = custom(4, 6, window_frames=3, chunk_frames=3, t_first=t0)
+    r = Run(w)
+    out = _sync_np(r.chunk_step())
+    compare(out[0], r.reference(), "t_end = 2^20 output", per_head_axis=1)
+    compare(r.cache_rows(t0, 3), r.append_reference(t0, 3), "t_end = 2^20 cache rows")
