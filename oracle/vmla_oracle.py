@@ -29,7 +29,7 @@ rounding):
   softmax                  p = exp(s - max s) / sum exp(s - max s)
   output                   o_h = sum_k p_k v_{k,h}
 
-Readings of points the pages leave open (each is also listed in the design doc):
+Readings of points the pages leave open:
   * RoPE3D: 16 complex pairs, the first 6 on the t axis, then 5 on h, then 5 on
     w ([PL] App. D.3); pair j is the adjacent channels (2j, 2j+1); within an
     axis group of width D_a (12, 10, 10) pair i turns at
