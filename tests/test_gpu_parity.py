@@ -80,6 +80,7 @@ def test_heads_sharing_a_workgroup(grid_h, grid_w):
     (5, 13, 3, 640, 1),     # 65 queries, odd head count: a query-prologue head pair with one head
     (10, 29, 5, 1024, 2),   # 290 queries per element, row tiles across the batch boundary
     (4, 6, 1, 64, 3),       # one head, a single 64-deep stage of the contraction
+    (3, 5, 64, 2048, 1),    # the largest head count the library accepts
 ])
 def test_other_head_counts_and_model_widths(grid_h, grid_w, n_heads, d_model, batch):
     w = custom(grid_h, grid_w, window_frames=3, chunk_frames=1, t_first=2,
@@ -256,3 +257,14 @@ def test_largest_frame_index():
     out = _sync_np(r.chunk_step())
     compare(out[0], r.reference(), "t_end = 2^20 output", per_head_axis=1)
     compare(r.cache_rows(t0, 3), r.append_reference(t0, 3), "t_end = 2^20 cache rows")
+
+
+def test_large_batch_small_grid():
+    # 32 batch elements of 2 x 3 tokens: every workgroup index spans batch elements,
+    # and the append's row ranges cut across them
+    w = custom(2, 3, window_frames=4, chunk_frames=2, t_first=5, batch=32)
+    r = Run(w)
+    out = _sync_np(r.chunk_step())
+    for b in (0, 1, 17, 31):
+        compare(out[b], r.reference(b=b), f"B=32 b={b}", per_head_axis=1)
+        compare(r.cache_rows(5, 2, b=b), r.append_reference(5, 2, b=b), f"B=32 cache b={b}")
