@@ -51,6 +51,11 @@ Readings of points the pages leave open:
     followed by the most recent window frames, numbered 0, 1, 2, ... oldest
     first, and those local numbers are the temporal RoPE coordinate of keys
     and queries (``chunk_attention_reindexed_reference``).
+  * Whole clip under the chunk-causal block mask
+    (``clip_chunk_causal_reference``): a query of chunk c sees the frames
+    [e - window, e), e the end of chunk c -- its own chunk and earlier frames
+    of the rolling window, never a later chunk ([PL] App. D.4); positions are
+    absolute, as in the default cache mode.
   * Whole layer (``chunk_layer_reference``): queries through a query latent
     c_q = x W_DQ (d_q = 768, [PL] §4) and q = c_q W_UQ, no normalisation of
     c_q (the pages name none); the head outputs are concatenated head-major
@@ -338,6 +343,70 @@ def chunk_attention_reindexed_reference(w, wts, x_of_frame, query_tokens=None):
                              w.rope_pairs)
     scale = 1.0 / np.sqrt(w.d_nope + w.d_rope)
     return attention_explicit(q_nope, q_rope, k_nope, k_r, v, scale)
+
+
+# ---------------------------------------------------------------------------
+# A whole clip at once under the chunk-causal block mask ([PL] App. D.4
+# "Chunk-Causal Sliding-Window Attention"; [PL] §3 "Integration with causal
+# attention": causal block masks keep working on the reconstructed heads)
+# ---------------------------------------------------------------------------
+
+def chunk_causal_frame_mask(n_frames: int, chunk_frames: int, window: int) -> np.ndarray:
+    """allowed[fq, fk] over the latent frames of a clip cut into chunks of
+    ``chunk_frames`` frames (the last chunk may be shorter).
+
+    A query in chunk c = fq // chunk_frames attends inside its own chunk and to
+    earlier frames, never to a later chunk ([PL] App. D.4), and only to the
+    ``window`` frames that end with its chunk: e - window <= fk < e with
+    e = min((c + 1) chunk_frames, n_frames), i.e. exactly the frames a rolling
+    cache of ``window`` frames holds right after chunk c is appended."""
+    f = np.arange(n_frames)
+    end = np.minimum((f // chunk_frames + 1) * chunk_frames, n_frames)
+    return (f[None, :] < end[:, None]) & (f[None, :] >= end[:, None] - window)
+
+
+def masked_attention(q_nope, q_rope, k_nope, k_r, v, scale, allowed, row_block=256):
+    """``attention_explicit`` with a mask: scores of keys that are not allowed
+    are -inf before the softmax, so their weight is exactly 0.
+    allowed: bool [Nq, Nk], at least one key allowed per query row."""
+    nq, nh, _ = q_nope.shape
+    out = np.empty((nq, nh, v.shape[-1]), dtype=F64)
+    k_r = np.asarray(k_r, dtype=F64)
+    allowed = np.asarray(allowed, dtype=bool)
+    for h in range(nh):
+        kh = np.concatenate([k_nope[:, h, :], k_r], axis=1)
+        vh = np.ascontiguousarray(v[:, h, :])
+        for r0 in range(0, nq, row_block):
+            qh = np.concatenate([q_nope[r0:r0 + row_block, h, :],
+                                 q_rope[r0:r0 + row_block, h, :]], axis=1)
+            s = np.where(allowed[r0:r0 + row_block], (qh @ kh.T) * scale, -np.inf)
+            out[r0:r0 + row_block, h, :] = softmax_rows(s) @ vh
+    return out
+
+
+def clip_chunk_causal_reference(w, wts, x_of_frame, n_frames, window, query_tokens=None):
+    """Reference output of the whole-clip form for one batch element: frames
+    0 .. n_frames - 1 are cached at their absolute (t, h, w), every token of
+    the clip is a query (absolute positions as well), keys and values are
+    reconstructed per head, and the softmax runs over the keys that
+    ``chunk_causal_frame_mask`` (chunks of ``w.chunk_frames``, ``window``
+    frames) allows. ``query_tokens``: indices into the clip's n_frames * T
+    tokens (frame-major); default all. Returns [len(query_tokens), H, d_v]."""
+    omega = rope_frequencies(w.rope_pairs, w.rope_axis_dims, w.rope_theta)
+    T = w.tokens_per_frame
+    xs = [np.asarray(x_of_frame(t), dtype=F64) for t in range(n_frames)]
+    pos = np.concatenate([frame_positions(t, w.grid_h, w.grid_w) for t in range(n_frames)], axis=0)
+    xk = np.concatenate(xs, axis=0)
+    c, k_r = latent_entry(xk, wts["w_down"], wts["w_kr"], pos, omega, w.rope_pairs)
+    k_nope, v = reconstruct_heads(c, wts["w_k_up"], wts["w_v_up"])
+
+    qt = np.arange(n_frames * T) if query_tokens is None else np.asarray(query_tokens)
+    q_nope, q_rope = queries(xk[qt], wts["w_q"], pos[qt], omega, w.n_heads, w.d_nope, w.d_rope,
+                             w.rope_pairs)
+    frame_ok = chunk_causal_frame_mask(n_frames, w.chunk_frames, window)
+    allowed = frame_ok[qt // T][:, np.arange(n_frames * T) // T]
+    scale = 1.0 / np.sqrt(w.d_nope + w.d_rope)
+    return masked_attention(q_nope, q_rope, k_nope, k_r, v, scale, allowed)
 
 
 # ---------------------------------------------------------------------------

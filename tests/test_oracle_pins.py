@@ -634,6 +634,127 @@ def test_append_reference_rows_layout():
 
 
 # ---------------------------------------------------------------------------
+# A whole clip under the chunk-causal block mask ([PL] App. D.4; §3
+# "Integration with causal attention")
+# ---------------------------------------------------------------------------
+
+def test_chunk_causal_mask_hand_derived():
+    # 7 frames in chunks of 3 (the last chunk is frame 6 alone), a 5-frame
+    # window: chunk 0 sees frames 0-2; chunk 1 ends at frame 5 and sees 1-5;
+    # chunk 2 ends at frame 6 and sees 2-6. Written out by hand.
+    expect = {0: {0, 1, 2}, 1: {0, 1, 2}, 2: {0, 1, 2}, 3: {1, 2, 3, 4, 5},
+              4: {1, 2, 3, 4, 5}, 5: {1, 2, 3, 4, 5}, 6: {2, 3, 4, 5, 6}}
+    m = orc.chunk_causal_frame_mask(7, 3, 5)
+    for fq, keys in expect.items():
+        assert set(np.flatnonzero(m[fq]).tolist()) == keys
+    # a window as long as the clip: block lower triangular, full diagonal blocks
+    m = orc.chunk_causal_frame_mask(8, 2, 8)
+    for fq in range(8):
+        assert set(np.flatnonzero(m[fq]).tolist()) == set(range(2 * (fq // 2) + 2))
+    # one-frame chunks and a full window: ordinary frame-causal masking
+    assert np.array_equal(orc.chunk_causal_frame_mask(5, 1, 5), np.tril(np.ones((5, 5), bool)))
+
+
+def test_masked_attention_matches_torch_sdpa_bool_mask():
+    q_nope, q_rope, k_nope, k_r, v = _rand_heads(10, 13)
+    H = q_nope.shape[1]
+    d = q_nope.shape[2] + q_rope.shape[2]
+    allowed = RNG.random((10, 13)) < 0.4
+    allowed[np.arange(10), RNG.integers(0, 13, 10)] = True     # every row keeps a key
+    out = orc.masked_attention(q_nope, q_rope, k_nope, k_r, v, 1.0 / math.sqrt(d), allowed)
+    Q = torch.from_numpy(np.concatenate([q_nope, q_rope], -1)).permute(1, 0, 2)[None]
+    K = torch.from_numpy(np.concatenate([k_nope, np.repeat(k_r[:, None], H, 1)], -1)).permute(1, 0, 2)[None]
+    V = torch.from_numpy(v).permute(1, 0, 2)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=torch.from_numpy(allowed))
+    np.testing.assert_allclose(out, ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def _clip_rows_equal_rollout(F, C, W):
+    # The block mask gives chunk c the frames the rolling cache holds once c is
+    # appended, so its rows equal the chunk step at t_first = c C ([PL] App. D.4).
+    w = custom(2, 3, window_frames=W, chunk_frames=C, t_first=0, dtype="f32")
+    wt = weights(w)
+    xs = {t: x_frame(w, t) for t in range(F)}
+    clip = orc.clip_chunk_causal_reference(w, wt, lambda t: xs[t], F, W)
+    T = w.tokens_per_frame
+    for c0 in range(0, F, C):
+        n = min(C, F - c0)
+        step = orc.chunk_attention_reference(w.with_(t_first=c0, chunk_frames=n), wt, lambda t: xs[t])
+        assert rel(clip[c0 * T:(c0 + n) * T], step) < 1e-12
+
+
+def test_clip_chunk_rows_equal_rollout_steps():
+    for F, C, W in [(7, 3, 5), (6, 6, 6), (5, 1, 5), (7, 3, 7), (8, 2, 3)]:
+        _clip_rows_equal_rollout(F, C, W)
+
+
+def test_clip_chunk_causal_brute_force_tiny():
+    # Tiny dims. The keys each chunk may see come from a simulated FIFO of W
+    # frames filled chunk by chunk (the cache right after the chunk is
+    # appended); every sum is a scalar loop.
+    from collections import deque
+    F, C, W, gh, gw = 5, 2, 3, 1, 2
+    T = gh * gw
+    D, H, dn, dr, dc, dv = 3, 2, 2, 4, 3, 2
+    pairs, dims = (1, 1, 0), (2, 2, 2)
+    w = custom(gh, gw, window_frames=W, chunk_frames=C, t_first=0, dtype="f32").with_(
+        d_model=D, n_heads=H, d_nope=dn, d_rope=dr, d_c=dc, d_v=dv, rope_pairs=pairs,
+        rope_axis_dims=dims)
+    om = orc.rope_frequencies(pairs, dims)
+    wt = {"w_q": RNG.standard_normal((D, H * (dn + dr))), "w_down": RNG.standard_normal((D, dc)),
+          "w_kr": RNG.standard_normal((D, dr)), "w_k_up": RNG.standard_normal((H, dc, dn)),
+          "w_v_up": RNG.standard_normal((H, dc, dv))}
+    xs = RNG.standard_normal((F, T, D))
+    fifo, visible = deque(maxlen=W), {}
+    for c0 in range(0, F, C):
+        for f in range(c0, min(c0 + C, F)):
+            fifo.append(f)
+        for f in range(c0, min(c0 + C, F)):
+            visible[f] = list(fifo)
+    scale = 1 / math.sqrt(dn + dr)
+
+    def mv(x, W_, j):
+        return sum(x[i] * W_[i][j] for i in range(len(x)))
+
+    def rot(vec, p):
+        o = list(vec)
+        for j in range(2):
+            ang = p[j] * om[j]
+            a, b = vec[2 * j], vec[2 * j + 1]
+            o[2 * j] = a * math.cos(ang) - b * math.sin(ang)
+            o[2 * j + 1] = a * math.sin(ang) + b * math.cos(ang)
+        return o
+
+    def position(f, n):
+        return (f, n // gw, n % gw)
+
+    ref = np.zeros((F * T, H, dv))
+    for qi in range(F * T):
+        fq, nq = divmod(qi, T)
+        qfull = [mv(xs[fq][nq], wt["w_q"], j) for j in range(H * (dn + dr))]
+        for h in range(H):
+            qn = qfull[h * (dn + dr):h * (dn + dr) + dn]
+            qr = rot(qfull[h * (dn + dr) + dn:(h + 1) * (dn + dr)], position(fq, nq))
+            s, vals = [], []
+            for fk in visible[fq]:
+                for nk in range(T):
+                    c = [mv(xs[fk][nk], wt["w_down"], j) for j in range(dc)]
+                    kr = rot([mv(xs[fk][nk], wt["w_kr"], j) for j in range(dr)], position(fk, nk))
+                    kn = [sum(c[i] * wt["w_k_up"][h][i][j] for i in range(dc)) for j in range(dn)]
+                    vals.append([sum(c[i] * wt["w_v_up"][h][i][j] for i in range(dc)) for j in range(dv)])
+                    s.append(scale * (sum(qn[j] * kn[j] for j in range(dn)) +
+                                      sum(qr[j] * kr[j] for j in range(dr))))
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            z = sum(e)
+            for j in range(dv):
+                ref[qi, h, j] = sum(e[k] / z * vals[k][j] for k in range(len(e)))
+
+    out = orc.clip_chunk_causal_reference(w, wt, lambda t: xs[t], F, W)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: every one of them must trip at least one pin
 # ---------------------------------------------------------------------------
 
@@ -699,7 +820,36 @@ def _fold_output_wrong_head(w_v_up, w_o):
                            for h in range(H)], axis=0)
 
 
+def _mask_frame_causal(n_frames, chunk_frames, window):
+    f = np.arange(n_frames)
+    end = np.minimum((f // chunk_frames + 1) * chunk_frames, n_frames)
+    return (f[None, :] <= f[:, None]) & (f[None, :] >= end[:, None] - window)
+
+
+def _mask_window_from_chunk_start(n_frames, chunk_frames, window):
+    f = np.arange(n_frames)
+    start = (f // chunk_frames) * chunk_frames
+    end = np.minimum(start + chunk_frames, n_frames)
+    return (f[None, :] < end[:, None]) & (f[None, :] >= start[:, None] - window)
+
+
+def _mask_without_window(n_frames, chunk_frames, window):
+    return _ORIG_MASK(n_frames, chunk_frames, n_frames)
+
+
+def _masked_attention_weights_not_renormalised(q_nope, q_rope, k_nope, k_r, v, scale, allowed,
+                                               row_block=256):
+    nq, nh, _ = q_nope.shape
+    out = np.empty((nq, nh, v.shape[-1]))
+    for h in range(nh):
+        kh = np.concatenate([k_nope[:, h, :], k_r], axis=1)
+        qh = np.concatenate([q_nope[:, h, :], q_rope[:, h, :]], axis=1)
+        out[:, h, :] = (orc.softmax_rows((qh @ kh.T) * scale) * allowed) @ v[:, h, :]
+    return out
+
+
 _ORIG_CTX = orc.active_context
+_ORIG_MASK = orc.chunk_causal_frame_mask
 _ORIG_ATT = orc.attention_explicit
 _ORIG_REC = orc.reconstruct_heads
 _ORIG_POS = orc.frame_positions
@@ -711,7 +861,9 @@ PINS = [test_rope_is_complex_rotation, test_attention_matches_torch_sdpa_fp64,
         test_frame_positions_token_order, test_absorbed_equals_explicit,
         test_reindexed_sink_context_brute_force_tiny,
         test_layer_with_identity_query_latent_and_mixer_is_the_attention_reference,
-        test_layer_folded_latent_form_equals_explicit, test_layer_brute_force_scalar_loops_tiny]
+        test_layer_folded_latent_form_equals_explicit, test_layer_brute_force_scalar_loops_tiny,
+        test_chunk_causal_mask_hand_derived, test_masked_attention_matches_torch_sdpa_bool_mask,
+        test_clip_chunk_rows_equal_rollout_steps, test_clip_chunk_causal_brute_force_tiny]
 
 
 @pytest.mark.parametrize("name,patch", [
@@ -726,6 +878,10 @@ PINS = [test_rope_is_complex_rotation, test_attention_matches_torch_sdpa_fp64,
     ("output mixer transposed", ("output_mixer", _mixer_transposed)),
     ("A_h fold takes rope columns from the nope block", ("fold_query_weights", _fold_query_rope_from_nope)),
     ("B_h folded with another head's W_O rows", ("fold_output_weights", _fold_output_wrong_head)),
+    ("frame-causal instead of chunk-causal", ("chunk_causal_frame_mask", _mask_frame_causal)),
+    ("window counted from the chunk start", ("chunk_causal_frame_mask", _mask_window_from_chunk_start)),
+    ("window ignored", ("chunk_causal_frame_mask", _mask_without_window)),
+    ("masked weights not renormalised", ("masked_attention", _masked_attention_weights_not_renormalised)),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, patch):
     attr, fn = patch
