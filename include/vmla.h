@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define VMLA_ABI_VERSION 4
+#define VMLA_ABI_VERSION 5
 
 typedef enum vmla_status {
   VMLA_OK = 0,
@@ -57,7 +57,7 @@ typedef enum vmla_status {
   VMLA_ERR_SHAPE = -2,      /* unsupported or inconsistent dimensions */
   VMLA_ERR_DTYPE = -3,      /* unknown dtype, or cache dtype differs from the call's */
   VMLA_ERR_ALIGN = -4,      /* a pointer is not 16-byte aligned */
-  VMLA_ERR_RANGE = -5,      /* t_first / n_frames / n_valid_frames out of range */
+  VMLA_ERR_RANGE = -5,      /* t_first / n_frames / n_valid_frames / chunk or mask window out of range */
   VMLA_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than vmla_attention_workspace_bytes */
   VMLA_ERR_HIP = -7         /* a HIP launch failed (hipGetLastError after the launch) */
 } vmla_status;
@@ -321,6 +321,62 @@ int32_t vmla_chunk_attention_explicit(const vmla_dims* dims, const vmla_cache* c
                                       int32_t t_first, int32_t n_frames, int32_t n_valid_frames,
                                       void* out, void* workspace, size_t workspace_bytes,
                                       void* stream);
+
+/*
+ * A whole clip under the chunk-causal block mask.
+ * -----------------------------------------------
+ * Defined by: chunk-causal attention ([PL] App. D.4 "Chunk-Causal
+ * Sliding-Window Attention": attention inside a chunk is allowed, an earlier
+ * chunk never attends to a later one), the form in which causal block masks
+ * run over the reconstructed heads ([PL] §3 "Integration with causal
+ * attention"). Every token of the clip's frames 0 .. n_frames - 1 is a query
+ * at its absolute (t, h, w); frames are cut into chunks of chunk_frames (the
+ * last chunk may be shorter), and a query of chunk c attends to the key frames
+ * [max(0, e - mask_window_frames), e), e = min((c + 1) * chunk_frames,
+ * n_frames): its own chunk and the earlier frames of a window of
+ * mask_window_frames frames, which are the keys a rolling cache of that many
+ * frames holds right after chunk c is appended. mask_window_frames >= n_frames
+ * is the plain block-causal mask. Row c of the result equals
+ * vmla_chunk_attention for t_first = c * chunk_frames over such a cache.
+ *
+ *   cache  the clip's latent rows, written by vmla_cache_append for frames
+ *          0 .. n_frames - 1 (slot t * T + n): window_frames >= n_frames,
+ *          sink_frames = 0, rope_at_read = 0
+ *   x      [batch, n_frames * T, d_model]: activations of every frame
+ *   out    [batch, n_frames * T, n_heads, d_v] (dtype of the call)
+ *   workspace  vmla_chunk_causal_attention, vmla_chunk_causal_latent_attention:
+ *          >= vmla_attention_workspace_bytes(dims, batch, n_frames * T) (the
+ *          Qhat rows of vmla_query_prologue with t_first = 0 and n_frames);
+ *          vmla_chunk_causal_attention_explicit: >=
+ *          vmla_explicit_workspace_bytes(dims, batch, n_frames * T, n_frames * T).
+ * vmla_chunk_causal_latent_attention is the second stage alone: it reads the
+ * Qhat rows that vmla_query_prologue (t_first = 0, n_frames, n_valid_frames =
+ * n_frames) left in workspace. The explicit form takes d_c = 192 and w_kv of
+ * vmla_pack_kv_weights.
+ *
+ * Errors: as vmla_chunk_attention, plus VMLA_ERR_SHAPE for sink_frames = 1,
+ * rope_at_read = 1 or more than 65535 (chunk, batch element) pairs, and
+ * VMLA_ERR_RANGE for n_frames < 1, n_frames > window_frames, chunk_frames
+ * outside [1, n_frames] or mask_window_frames < chunk_frames.
+ */
+int32_t vmla_chunk_causal_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                                    const void* x, const void* w_q, const void* w_k_up,
+                                    const void* w_v_up, int32_t n_frames, int32_t chunk_frames,
+                                    int32_t mask_window_frames, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+int32_t vmla_chunk_causal_latent_attention(const vmla_dims* dims, const vmla_cache* cache,
+                                           int32_t dtype, const void* w_v_up, int32_t n_frames,
+                                           int32_t chunk_frames, int32_t mask_window_frames,
+                                           void* out, const void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
+int32_t vmla_chunk_causal_attention_explicit(const vmla_dims* dims, const vmla_cache* cache,
+                                             int32_t dtype, const void* x, const void* w_q,
+                                             const void* w_kv, int32_t n_frames,
+                                             int32_t chunk_frames, int32_t mask_window_frames,
+                                             void* out, void* workspace, size_t workspace_bytes,
+                                             void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* vmla_status_string(int32_t status);

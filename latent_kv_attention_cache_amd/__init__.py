@@ -13,7 +13,8 @@ from ._binding import (VMLA_OK, VMLA_ERR_NULL, VMLA_ERR_SHAPE, VMLA_ERR_DTYPE, V
                        vmla_fold_output_weights, vmla_layer_workspace_bytes,
                        vmla_chunk_attention_layer, vmla_layer_query_prologue, vmla_layer_attention,
                        vmla_output_projection, vmla_pack_kv_weights, vmla_explicit_workspace_bytes,
-                       vmla_chunk_attention_explicit)
+                       vmla_chunk_attention_explicit, vmla_chunk_causal_attention,
+                       vmla_chunk_causal_latent_attention, vmla_chunk_causal_attention_explicit)
 
 __all__ = [
     "VMLA_OK", "VMLA_ERR_NULL", "VMLA_ERR_SHAPE", "VMLA_ERR_DTYPE", "VMLA_ERR_ALIGN",
@@ -24,5 +25,6 @@ __all__ = [
     "vmla_fold_query_weights", "vmla_fold_output_weights", "vmla_layer_workspace_bytes",
     "vmla_chunk_attention_layer", "vmla_layer_query_prologue", "vmla_layer_attention",
     "vmla_output_projection", "vmla_pack_kv_weights", "vmla_explicit_workspace_bytes",
-    "vmla_chunk_attention_explicit",
+    "vmla_chunk_attention_explicit", "vmla_chunk_causal_attention",
+    "vmla_chunk_causal_latent_attention", "vmla_chunk_causal_attention_explicit",
 ]

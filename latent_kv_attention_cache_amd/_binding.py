@@ -61,7 +61,9 @@ EXPORTED = ("vmla_default_dims", "vmla_cache_append", "vmla_attention_workspace_
             "vmla_fold_query_weights", "vmla_fold_output_weights", "vmla_layer_workspace_bytes",
             "vmla_chunk_attention_layer", "vmla_layer_query_prologue", "vmla_layer_attention",
             "vmla_output_projection", "vmla_pack_kv_weights", "vmla_explicit_workspace_bytes",
-            "vmla_chunk_attention_explicit", "vmla_status_string", "vmla_abi_version")
+            "vmla_chunk_attention_explicit", "vmla_chunk_causal_attention",
+            "vmla_chunk_causal_latent_attention", "vmla_chunk_causal_attention_explicit",
+            "vmla_status_string", "vmla_abi_version")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -112,6 +114,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vmla_explicit_workspace_bytes.restype = SZ
     lib.vmla_chunk_attention_explicit.argtypes = [D, C, I32, P, P, P, I32, I32, I32, P, P, SZ, P]
     lib.vmla_chunk_attention_explicit.restype = I32
+    lib.vmla_chunk_causal_attention.argtypes = [D, C, I32, P, P, P, P, I32, I32, I32, P, P, SZ, P]
+    lib.vmla_chunk_causal_attention.restype = I32
+    lib.vmla_chunk_causal_latent_attention.argtypes = [D, C, I32, P, I32, I32, I32, P, P, SZ, P]
+    lib.vmla_chunk_causal_latent_attention.restype = I32
+    lib.vmla_chunk_causal_attention_explicit.argtypes = [D, C, I32, P, P, P, I32, I32, I32, P, P, SZ, P]
+    lib.vmla_chunk_causal_attention_explicit.restype = I32
     lib.vmla_status_string.argtypes = [I32]
     lib.vmla_status_string.restype = ctypes.c_char_p
     lib.vmla_abi_version.argtypes = []
@@ -560,4 +568,114 @@ def vmla_chunk_attention_explicit(cache: LatentCache, x: torch.Tensor, w_q: torc
                                            workspace.numel() * workspace.element_size(), _stream(stream))
     if st != VMLA_OK:
         raise VmlaError(st, "vmla_chunk_attention_explicit")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# A whole clip under the chunk-causal block mask
+# ---------------------------------------------------------------------------
+
+def _clip_out(cache, x, n_frames, out, d):
+    B, T = cache.batch, cache.tokens_per_frame
+    n_q = n_frames * T
+    if x is not None:
+        _expect_shape(x, (B, n_q, d.d_model), "x")
+    if out is None:
+        out = torch.empty((B, n_q, d.n_heads, d.d_v), dtype=cache.data.dtype, device=cache.data.device)
+    _expect_shape(out, (B, n_q, d.n_heads, d.d_v), "out")
+    _same_dtype(cache.data, out=out)
+    _dev(cache.data, "cache")
+    return out, n_q
+
+
+def vmla_chunk_causal_attention(cache: LatentCache, x: torch.Tensor, w_q: torch.Tensor,
+                                w_k_up: torch.Tensor, w_v_up: torch.Tensor, n_frames: int,
+                                chunk_frames: int, mask_window_frames: int,
+                                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                                dims: vmla_dims | None = None, stream=None) -> torch.Tensor:
+    """Every token of frames 0 .. n_frames - 1 attends under the chunk-causal
+    block mask (chunks of ``chunk_frames``, a window of ``mask_window_frames``);
+    ``cache`` holds the clip's rows at slots t * T + n. Returns ``out``
+    [batch, n_frames * T, n_heads, d_v]."""
+    lib = load_library()
+    d = dims or default_dims()
+    _expect_shape(w_q, (d.d_model, d.n_heads * (d.d_nope + d.d_rope)), "w_q")
+    _expect_shape(w_k_up, (d.n_heads, d.d_c, d.d_nope), "w_k_up")
+    _expect_shape(w_v_up, (d.n_heads, d.d_c, d.d_v), "w_v_up")
+    _same_dtype(cache.data, x=x, w_q=w_q, w_k_up=w_k_up, w_v_up=w_v_up)
+    out, n_q = _clip_out(cache, x, n_frames, out, d)
+    need = vmla_attention_workspace_bytes(cache.batch, n_q, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold at least {need} bytes")
+    cs = cache.c_struct()
+    st = lib.vmla_chunk_causal_attention(ctypes.byref(d), ctypes.byref(cs), _dtype_code(cache.data),
+                                         _dev(x, "x"), _dev(w_q, "w_q"), _dev(w_k_up, "w_k_up"),
+                                         _dev(w_v_up, "w_v_up"), int(n_frames), int(chunk_frames),
+                                         int(mask_window_frames), _dev(out, "out"),
+                                         _dev(workspace, "workspace"),
+                                         workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != VMLA_OK:
+        raise VmlaError(st, "vmla_chunk_causal_attention")
+    return out
+
+
+def vmla_chunk_causal_latent_attention(cache: LatentCache, w_v_up: torch.Tensor, n_frames: int,
+                                       chunk_frames: int, mask_window_frames: int, out: torch.Tensor,
+                                       workspace: torch.Tensor, dims: vmla_dims | None = None,
+                                       stream=None) -> torch.Tensor:
+    """Second stage of vmla_chunk_causal_attention: reads the Qhat rows that
+    vmla_query_prologue (t_first = 0, n_frames, n_valid_frames = n_frames) left
+    in ``workspace``."""
+    lib = load_library()
+    d = dims or default_dims()
+    _expect_shape(w_v_up, (d.n_heads, d.d_c, d.d_v), "w_v_up")
+    _same_dtype(cache.data, w_v_up=w_v_up)
+    out, n_q = _clip_out(cache, None, n_frames, out, d)
+    need = vmla_attention_workspace_bytes(cache.batch, n_q, d)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold at least {need} bytes")
+    cs = cache.c_struct()
+    st = lib.vmla_chunk_causal_latent_attention(ctypes.byref(d), ctypes.byref(cs),
+                                                _dtype_code(cache.data), _dev(w_v_up, "w_v_up"),
+                                                int(n_frames), int(chunk_frames),
+                                                int(mask_window_frames), _dev(out, "out"),
+                                                _dev(workspace, "workspace"),
+                                                workspace.numel() * workspace.element_size(),
+                                                _stream(stream))
+    if st != VMLA_OK:
+        raise VmlaError(st, "vmla_chunk_causal_latent_attention")
+    return out
+
+
+def vmla_chunk_causal_attention_explicit(cache: LatentCache, x: torch.Tensor, w_q: torch.Tensor,
+                                         w_kv: torch.Tensor, n_frames: int, chunk_frames: int,
+                                         mask_window_frames: int, out: torch.Tensor | None = None,
+                                         workspace: torch.Tensor | None = None,
+                                         dims: vmla_dims | None = None, stream=None) -> torch.Tensor:
+    """vmla_chunk_causal_attention through explicit per-head K/V of the whole
+    clip (``w_kv`` from vmla_pack_kv_weights)."""
+    lib = load_library()
+    d = dims or default_dims()
+    _expect_shape(w_q, (d.d_model, d.n_heads * (d.d_nope + d.d_rope)), "w_q")
+    _expect_shape(w_kv, (d.d_c, d.n_heads * (d.d_nope + d.d_v)), "w_kv")
+    _same_dtype(cache.data, x=x, w_q=w_q, w_kv=w_kv)
+    out, n_q = _clip_out(cache, x, n_frames, out, d)
+    need = vmla_explicit_workspace_bytes(cache.batch, n_q, n_q, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold at least {need} bytes")
+    cs = cache.c_struct()
+    st = lib.vmla_chunk_causal_attention_explicit(ctypes.byref(d), ctypes.byref(cs),
+                                                  _dtype_code(cache.data), _dev(x, "x"),
+                                                  _dev(w_q, "w_q"), _dev(w_kv, "w_kv"),
+                                                  int(n_frames), int(chunk_frames),
+                                                  int(mask_window_frames), _dev(out, "out"),
+                                                  _dev(workspace, "workspace"),
+                                                  workspace.numel() * workspace.element_size(),
+                                                  _stream(stream))
+    if st != VMLA_OK:
+        raise VmlaError(st, "vmla_chunk_causal_attention_explicit")
     return out

@@ -67,20 +67,28 @@ void explicit_attn_kernel(ExplicitArgs a) {
   const int half = lane >> 5;
   const int qi = lane & 31;
   const int lag = wave >= kLoaders ? 1 : 0;
-  const int b = blockIdx.z;
-  // Workgroup g of head h = blockIdx.x / G takes units 8 g .. 8 g + 7 of that head
-  // (G = ceil(units / 8) workgroups per head).
-  const int units = (a.n_q + 31) / 32;
-  const int groups = (units + kWaves - 1) / kWaves;
+  // Query chunk: blockIdx.z = (n_chunks - 1 - c) * batch + b (most keys first).
+  const int rc = blockIdx.z / a.batch;
+  const int b = blockIdx.z - rc * a.batch;
+  const int c = a.cm.n_chunks - 1 - rc;
+  const int q0 = c * a.cm.chunk_q;
+  const int nq = min(a.cm.chunk_q, a.n_q - q0);
+  const int k_end = min(a.n_k, (c + 1) * a.cm.key_step);
+  const int k0 = max(0, k_end - a.cm.key_span);
+  const int nk = k_end - k0;
+  // Workgroup g of head h = blockIdx.x / G takes units 8 g .. 8 g + 7 of that
+  // head's chunk (G = ceil(units / 8) workgroups per head for the longest chunk).
+  const int units = (nq + 31) / 32;
+  const int groups = ((a.cm.chunk_q + 31) / 32 + kWaves - 1) / kWaves;
   const int h = blockIdx.x / groups;
   const int qb = (blockIdx.x - h * groups) * kWaves + wave;
   const int qrow = 32 * qb + qi;
   const bool live = qb < units;
-  const bool qvalid = live && qrow < a.n_q;
+  const bool qvalid = live && qrow < nq;
 
   bf16x8 qf[kFeatSteps];
   {
-    const bf16_t* qp = a.q + (((size_t)b * a.n_heads + h) * a.n_q + (qvalid ? qrow : a.n_q - 1)) * kD;
+    const bf16_t* qp = a.q + (((size_t)b * a.n_heads + h) * a.n_q + q0 + (qvalid ? qrow : nq - 1)) * kD;
 #pragma unroll
     for (int ks = 0; ks < kFeatSteps; ++ks)
       qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + 8 * half);
@@ -88,14 +96,14 @@ void explicit_attn_kernel(ExplicitArgs a) {
     for (int ks = 0; ks < kFeatSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
   }
 
-  const bf16_t* kv = a.kv + ((size_t)b * a.n_heads + h) * (size_t)a.n_k * kKVRow;
-  const int ntiles = (a.n_k + kKT - 1) / kKT;
+  const bf16_t* kv = a.kv + (((size_t)b * a.n_heads + h) * (size_t)a.n_k + k0) * kKVRow;
+  const int ntiles = (nk + kKT - 1) / kKT;
 
   // Tile staging (X waves): load n moves chunk column n, lane r = key 64 j + r.
   const uint32_t kt_lds = (uint32_t)(uintptr_t)(VMLA_LDS bf16_t*)kt;
   auto issue_tile = [&](int j) {
     const int buf = j % kBufs;
-    const int kg = min(j * kKT + lane, a.n_k - 1);
+    const int kg = min(j * kKT + lane, nk - 1);
     const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
@@ -165,8 +173,8 @@ void explicit_attn_kernel(ExplicitArgs a) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 1);
   };
   auto softmax = [&](int key0) {
-    if (key0 + kKT > a.n_k) {
-      const int lim = a.n_k - key0 - 4 * half;
+    if (key0 + kKT > nk) {
+      const int lim = nk - key0 - 4 * half;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int k = 8 * (r >> 2) + (r & 3);
@@ -239,7 +247,7 @@ void explicit_attn_kernel(ExplicitArgs a) {
   // dim 32 t + 8 g + 4 half + e.
   if (!qvalid) return;
   const float inv = 1.f / sum_across_halves(l);
-  T* out = static_cast<T*>(a.out) + (((size_t)b * a.n_q + qrow) * a.n_heads + h) * kD;
+  T* out = static_cast<T*>(a.out) + (((size_t)b * a.n_q + q0 + qrow) * a.n_heads + h) * kD;
 #pragma unroll
   for (int t = 0; t < kValTiles; ++t)
 #pragma unroll
@@ -267,9 +275,9 @@ void pack_kv_kernel(FoldArgs a) {
 }  // namespace
 
 hipError_t launch_explicit_attn(const ExplicitArgs& a, bool f32, hipStream_t s) {
-  const int units = (a.n_q + 31) / 32;
+  const int units = (a.cm.chunk_q + 31) / 32;
   const int groups = (units + kWaves - 1) / kWaves;
-  const dim3 grid((unsigned)(a.n_heads * groups), 1, a.batch);
+  const dim3 grid((unsigned)(a.n_heads * groups), 1, (unsigned)(a.batch * a.cm.n_chunks));
   if (f32) hipLaunchKernelGGL(explicit_attn_kernel<float>, grid, dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL(explicit_attn_kernel<bf16_t>, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();

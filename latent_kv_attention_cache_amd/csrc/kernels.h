@@ -26,6 +26,15 @@ struct RopeTable {
   int axis[kPairs];
 };
 
+// Query chunks of one attention launch. Each batch element's n_q queries are
+// cut into n_chunks chunks of chunk_q (the last may be shorter); chunk c
+// attends to the keys [max(0, e - key_span), e) with e = min(n_k, (c + 1) *
+// key_step). n_chunks = 1, chunk_q = n_q, key_step = key_span = n_k is one
+// query chunk over all n_k keys.
+struct ChunkMask {
+  int n_chunks, chunk_q, key_step, key_span;
+};
+
 struct AppendArgs {
   const void* x;        // [batch, n_tok, d_model]
   const void* w_down;   // [d_model, kDC]
@@ -67,6 +76,7 @@ struct AttnArgs {
   int rope_at_read, sink_frames, window_frames, shift_mod_w, tokens_per_frame, grid_w;
   float inv_tokens_per_frame, inv_grid_w;
   RopeTable rope;
+  ChunkMask cm;
 };
 
 // out = A W over row-major operands; A [m][lda >= k], W [k][n]. mode 0:
@@ -91,6 +101,7 @@ struct ExplicitArgs {
   const uint16_t* kv;   // [batch, n_heads, n_k, 2 kDHead] bf16: [k (128) | v (128)]
   void* out;            // [batch, n_q, n_heads, kDV]
   int batch, n_q, n_heads, n_k;
+  ChunkMask cm;
 };
 
 // One-time weight folds (bf16 results). Query: w_first = W_UQ [d_in][n_heads

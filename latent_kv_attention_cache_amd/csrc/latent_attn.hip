@@ -109,7 +109,7 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
                :: "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory");
 }
 
-template <typename T, bool kRot, bool kFold, int DC>
+template <typename T, bool kRot, bool kFold, int DC, bool kChunked>
 __global__ __launch_bounds__(kThreads)
 void latent_attn_kernel(AttnArgs a) {
   using Sh = AttnShape<DC>;
@@ -127,10 +127,25 @@ void latent_attn_kernel(AttnArgs a) {
   const int half = lane >> 5;
   const int qi = lane & 31;
   const int lag = wave >= kLoaders ? 1 : 0;   // Y waves run one phase behind
-  const int b = blockIdx.z;
-  // This wave's unit: head h, query rows 32 qb .. 32 qb + 31.
-  const int units = (a.n_q + 31) / 32;
-  const int upad = units > kWaves ? units : kWaves;      // units per head, padded to >= 8
+  // Query chunk of this workgroup (kChunked): blockIdx.z = (n_chunks - 1 - c) *
+  // batch + b, so the chunks with the most keys are dispatched first. Without
+  // chunks: all n_q queries over keys [0, n_k).
+  int b = blockIdx.z, q0 = 0, nq = a.n_q, k0 = 0, nk = a.n_k, chunk_q = a.n_q;
+  if constexpr (kChunked) {
+    const int rc = blockIdx.z / a.batch;
+    const int c = a.cm.n_chunks - 1 - rc;
+    b = blockIdx.z - rc * a.batch;
+    chunk_q = a.cm.chunk_q;
+    q0 = c * chunk_q;                                     // first query of the chunk
+    nq = min(chunk_q, a.n_q - q0);
+    const int k_end = min(a.n_k, (c + 1) * a.cm.key_step);
+    k0 = max(0, k_end - a.cm.key_span);                   // first key of the chunk
+    nk = k_end - k0;
+  }
+  // This wave's unit: head h, chunk query rows 32 qb .. 32 qb + 31.
+  const int units = (nq + 31) / 32;
+  const int umax = (chunk_q + 31) / 32;
+  const int upad = umax > kWaves ? umax : kWaves;        // units per head, padded to >= 8
   const int u0 = blockIdx.x * kWaves;
   const int u = u0 + wave;
   const int h_lo = u0 / upad;                             // heads of this workgroup: h_lo, h_lo + 1
@@ -142,12 +157,12 @@ void latent_attn_kernel(AttnArgs a) {
   // skips the math: on a power-limited chip idle matrix cores raise the
   // others' clock.
   const bool live = u / upad < a.n_heads && qb < units;
-  const bool qvalid = live && qrow < a.n_q;
+  const bool qvalid = live && qrow < nq;
 
   // Qhat fragments (B operand of S^T): lane holds features ks*16 + 8*half + e of its query.
   bf16x8 qf[kFeatSteps];
   {
-    const bf16_t* qp = a.qhat + (((size_t)b * a.n_heads + h) * a.n_q + (qvalid ? qrow : a.n_q - 1)) * kRow;
+    const bf16_t* qp = a.qhat + (((size_t)b * a.n_heads + h) * a.n_q + q0 + (qvalid ? qrow : nq - 1)) * kRow;
 #pragma unroll
     for (int ks = 0; ks < kFeatSteps; ++ks)
       qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + 8 * half);
@@ -159,8 +174,8 @@ void latent_attn_kernel(AttnArgs a) {
     for (int ks = 0; ks < kFeatSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
   }
 
-  const T* cache = static_cast<const T*>(a.cache) + (size_t)b * a.cache_rows * kRow;
-  const int ntiles = (a.n_k + kKT - 1) / kKT;
+  const T* cache = static_cast<const T*>(a.cache) + ((size_t)b * a.cache_rows + k0) * kRow;
+  const int ntiles = (nk + kKT - 1) / kKT;
 
   // ---- tile staging (X waves only). Wave-wide load n moves chunk column n:
   // lane r reads features 8n .. 8n+7 of key 64 j + r into slot n * kSlots + r.
@@ -169,7 +184,7 @@ void latent_attn_kernel(AttnArgs a) {
   const uint32_t kt_lds = (uint32_t)(uintptr_t)(VMLA_LDS bf16_t*)kt;
   auto issue_tile = [&](int j) {
     const int buf = j % kBufs;
-    const int kg = min(j * kKT + lane, a.n_k - 1);
+    const int kg = min(j * kKT + lane, nk - 1);
     const int wv = __builtin_amdgcn_readfirstlane(wave);   // scalar load index and LDS address
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
@@ -188,7 +203,7 @@ void latent_attn_kernel(AttnArgs a) {
   auto rotate_tile = [&](int j) {
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     bf16_t* p = kt + (j % kBufs) * kTileElems + ((kDC / 8 + wv) * kSlots + lane) * 8;
-    const int kg = min(j * kKT + lane, a.n_k - 1);
+    const int kg = k0 + min(j * kKT + lane, nk - 1);        // cache slot
     int n_in, ww;
     const int fs = div_small(kg, a.tokens_per_frame, a.inv_tokens_per_frame, &n_in);
     const int hh = div_small(n_in, a.grid_w, a.inv_grid_w, &ww);
@@ -283,9 +298,9 @@ void latent_attn_kernel(AttnArgs a) {
   };
   // Online softmax of the current tile; leaves P^T (bf16) in pb.
   auto softmax = [&](int key0) {
-    if (key0 + kKT > a.n_k) {    // the window ends inside this tile (wave-uniform)
+    if (key0 + kKT > nk) {       // the keys end inside this tile (wave-uniform)
       // register r of key block kb holds key key0 + 32 kb + 8(r/4) + 4 half + r%4
-      const int lim = a.n_k - key0 - 4 * half;
+      const int lim = nk - key0 - 4 * half;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int k = 8 * (r >> 2) + (r & 3);
@@ -374,7 +389,7 @@ void latent_attn_kernel(AttnArgs a) {
     // ---- epilogue: olat = O / l. Register 8 jj + e of latent tile t holds
     // latent dim 32 t + 16 jj + 8 (e / 4) + 4 half + e % 4 of query qrow.
     if (!qvalid) return;   // no barrier follows
-    uint16_t* dst = a.olat + ((size_t)b * a.n_q + qrow) * ((size_t)a.n_heads * kDC) + (size_t)h * kDC;
+    uint16_t* dst = a.olat + ((size_t)b * a.n_q + q0 + qrow) * ((size_t)a.n_heads * kDC) + (size_t)h * kDC;
 #pragma unroll
     for (int t = 0; t < kLatTiles; ++t)
 #pragma unroll
@@ -413,7 +428,7 @@ void latent_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) ob[t][jj][e] = (__bf16)(o[t][8 * jj + e] * inv);
 
-  T* out = static_cast<T*>(a.out) + (((size_t)b * a.n_q + (qvalid ? qrow : 0)) * a.n_heads + h) * kDV;
+  T* out = static_cast<T*>(a.out) + (((size_t)b * a.n_q + q0 + (qvalid ? qrow : 0)) * a.n_heads + h) * kDV;
 #pragma unroll
   for (int et = 0; et < kDV / 32; ++et) {
     f32x16 acc = f32x16{};
@@ -439,23 +454,28 @@ void latent_attn_kernel(AttnArgs a) {
 
 template <int DC>
 hipError_t launch_dc(const AttnArgs& a, bool f32, hipStream_t s) {
-  const int units = (a.n_q + 31) / 32;
+  const int units = (a.cm.chunk_q + 31) / 32;
   const int upad = units > kWaves ? units : kWaves;
-  dim3 grid((a.n_heads * upad + kWaves - 1) / kWaves, 1, a.batch);
-  if (a.olat) {
+  dim3 grid((a.n_heads * upad + kWaves - 1) / kWaves, 1, a.batch * a.cm.n_chunks);
+  if (a.cm.n_chunks > 1) {
+    // query chunks come only with append-time RoPE and the W_V_up epilogue
+    if (a.rope_at_read || a.olat) return hipErrorInvalidValue;
+    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, false, DC, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, false, DC, true>), grid, dim3(kThreads), 0, s, a);
+  } else if (a.olat) {
     if (a.rope_at_read) {
-      if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, true, true, DC>), grid, dim3(kThreads), 0, s, a);
-      else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, true, true, DC>), grid, dim3(kThreads), 0, s, a);
+      if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, true, true, DC, false>), grid, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, true, true, DC, false>), grid, dim3(kThreads), 0, s, a);
     } else {
-      if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, true, DC>), grid, dim3(kThreads), 0, s, a);
-      else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, true, DC>), grid, dim3(kThreads), 0, s, a);
+      if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, true, DC, false>), grid, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, true, DC, false>), grid, dim3(kThreads), 0, s, a);
     }
   } else if (a.rope_at_read) {
-    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, true, false, DC>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, true, false, DC>), grid, dim3(kThreads), 0, s, a);
+    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, true, false, DC, false>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, true, false, DC, false>), grid, dim3(kThreads), 0, s, a);
   } else {
-    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, false, DC>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, false, DC>), grid, dim3(kThreads), 0, s, a);
+    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, false, DC, false>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, false, DC, false>), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }

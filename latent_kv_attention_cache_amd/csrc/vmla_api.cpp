@@ -112,7 +112,7 @@ const char* vmla_status_string(int32_t s) {
     case VMLA_ERR_SHAPE: return "unsupported or inconsistent dimensions";
     case VMLA_ERR_DTYPE: return "invalid dtype or dtype mismatch with the cache";
     case VMLA_ERR_ALIGN: return "pointer not 16-byte aligned";
-    case VMLA_ERR_RANGE: return "t_first / n_frames / n_valid_frames out of range";
+    case VMLA_ERR_RANGE: return "t_first / n_frames / n_valid_frames / chunk or mask window out of range";
     case VMLA_ERR_WORKSPACE: return "workspace missing or too small";
     case VMLA_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";
@@ -156,6 +156,9 @@ size_t vmla_attention_workspace_bytes(const vmla_dims* dims, int32_t batch, int3
 
 namespace {
 
+void fill_attention(const vmla_dims* dims, const vmla_cache* cache, const void* workspace,
+                    int64_t n_q, int64_t t_q, int64_t n_k, int64_t shift, QArgs* q, AttnArgs* a);
+
 // Shared validation of the attention stages; fills the launch arguments.
 int32_t check_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
                         int32_t t_first, int32_t n_frames, int32_t n_valid_frames,
@@ -179,11 +182,20 @@ int32_t check_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t 
   const size_t need = vmla_attention_workspace_bytes(dims, cache->batch, (int32_t)n_q);
   if (!workspace || workspace_bytes < need) return VMLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return VMLA_ERR_ALIGN;
+  fill_attention(dims, cache, workspace, n_q, t_first - shift, T * n_valid_frames, shift, q, a);
+  return VMLA_OK;
+}
 
+// Launch arguments of the query prologue and the attention: n_q queries from
+// absolute frame t_q, keys = slots [0, n_k), one query chunk over all of them.
+void fill_attention(const vmla_dims* dims, const vmla_cache* cache, const void* workspace,
+                    int64_t n_q, int64_t t_q, int64_t n_k, int64_t shift, QArgs* q, AttnArgs* a) {
+  const int64_t T = (int64_t)cache->grid_h * cache->grid_w;
+  const int64_t span = (int64_t)cache->sink_frames + cache->window_frames;
   *q = QArgs{};
   q->qhat = static_cast<uint16_t*>(const_cast<void*>(workspace));
   q->batch = cache->batch; q->n_q = (int)n_q; q->d_model = dims->d_model; q->n_heads = dims->n_heads;
-  q->grid_w = cache->grid_w; q->tokens_per_frame = (int)T; q->t_first = (int)(t_first - shift);
+  q->grid_w = cache->grid_w; q->tokens_per_frame = (int)T; q->t_first = (int)t_q;
   q->inv_grid_w = 1.f / (float)cache->grid_w;
   q->inv_tokens_per_frame = 1.f / (float)T;
   q->qscale = (float)((double)dims->scale * 1.4426950408889634);   // scale * log2(e)
@@ -193,7 +205,8 @@ int32_t check_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t 
   *a = AttnArgs{};
   a->qhat = q->qhat; a->cache = cache->data;
   a->batch = cache->batch; a->n_q = (int)n_q; a->n_heads = dims->n_heads;
-  a->n_k = (int)(T * n_valid_frames); a->cache_rows = (int)(T * span);
+  a->n_k = (int)n_k; a->cache_rows = (int)(T * span);
+  a->cm = ChunkMask{1, (int)n_q, (int)n_k, (int)n_k};
   a->rope_at_read = cache->rope_at_read;
   a->d_c = dims->d_c;
   a->sink_frames = cache->sink_frames;
@@ -204,7 +217,6 @@ int32_t check_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t 
   a->inv_tokens_per_frame = 1.f / (float)T;
   a->inv_grid_w = 1.f / (float)cache->grid_w;
   a->rope = q->rope;
-  return VMLA_OK;
 }
 
 }  // namespace
@@ -435,26 +447,14 @@ size_t vmla_explicit_workspace_bytes(const vmla_dims* dims, int32_t batch, int32
   return per * ((size_t)n_q * kDHead + (size_t)n_k * 2 * kDHead);
 }
 
-int32_t vmla_chunk_attention_explicit(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
-                                      const void* x, const void* w_q, const void* w_kv,
-                                      int32_t t_first, int32_t n_frames, int32_t n_valid_frames,
-                                      void* out, void* workspace, size_t workspace_bytes,
-                                      void* stream) {
-  if (!x || !w_q || !w_kv || !out) return VMLA_ERR_NULL;
-  QArgs q;
-  AttnArgs a;
-  // the attention checks, with the workspace size checked below
-  int32_t st = check_dims_192(dims);
-  if (st) return st;
-  st = check_attention(dims, cache, dtype, t_first, n_frames, n_valid_frames, workspace,
-                       SIZE_MAX, &q, &a);
-  if (st) return st;
-  if (cache->rope_at_read) return VMLA_ERR_SHAPE;
-  if ((int64_t)a.n_k * 2 * kDHead * dims->n_heads > INT32_MAX) return VMLA_ERR_SHAPE;
-  if (workspace_bytes < vmla_explicit_workspace_bytes(dims, cache->batch, a.n_q, a.n_k))
-    return VMLA_ERR_WORKSPACE;
-  if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_kv) || !aligned16(out)) return VMLA_ERR_ALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+namespace {
+
+// Query GEMM, per-head K/V rebuild of slots [0, a.n_k), explicit attention
+// with a's query chunks.
+int32_t run_explicit(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype, const void* x,
+                     const void* w_q, const void* w_kv, const QArgs& q, const AttnArgs& a, void* out,
+                     void* workspace, hipStream_t s) {
+  int32_t st;
   const bool f32 = dtype == VMLA_F32;
   uint16_t* qbuf = static_cast<uint16_t*>(workspace);
   uint16_t* kvbuf = qbuf + (size_t)cache->batch * dims->n_heads * a.n_q * kDHead;
@@ -481,7 +481,130 @@ int32_t vmla_chunk_attention_explicit(const vmla_dims* dims, const vmla_cache* c
   ExplicitArgs e{};
   e.q = qbuf; e.kv = kvbuf; e.out = out;
   e.batch = cache->batch; e.n_q = a.n_q; e.n_heads = dims->n_heads; e.n_k = a.n_k;
+  e.cm = a.cm;
   return hip_status(launch_explicit_attn(e, f32, s));
+}
+
+}  // namespace
+
+int32_t vmla_chunk_attention_explicit(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                                      const void* x, const void* w_q, const void* w_kv,
+                                      int32_t t_first, int32_t n_frames, int32_t n_valid_frames,
+                                      void* out, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (!x || !w_q || !w_kv || !out) return VMLA_ERR_NULL;
+  QArgs q;
+  AttnArgs a;
+  // the attention checks, with the workspace size checked below
+  int32_t st = check_dims_192(dims);
+  if (st) return st;
+  st = check_attention(dims, cache, dtype, t_first, n_frames, n_valid_frames, workspace,
+                       SIZE_MAX, &q, &a);
+  if (st) return st;
+  if (cache->rope_at_read) return VMLA_ERR_SHAPE;
+  if ((int64_t)a.n_k * 2 * kDHead * dims->n_heads > INT32_MAX) return VMLA_ERR_SHAPE;
+  if (workspace_bytes < vmla_explicit_workspace_bytes(dims, cache->batch, a.n_q, a.n_k))
+    return VMLA_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_kv) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  return run_explicit(dims, cache, dtype, x, w_q, w_kv, q, a, out, workspace,
+                      static_cast<hipStream_t>(stream));
+}
+
+
+// ---- a whole clip under the chunk-causal block mask
+
+namespace {
+
+// Validation of the whole-clip form. Frames 0 .. n_frames - 1 sit in slots
+// t T + n (a cache of at least n_frames frames, no sink frame, k_R rotated at
+// append); every token of the clip is a query at its absolute position; chunk
+// c (chunk_frames frames) sees the slots of frames [e - W, e), e its end.
+int32_t check_clip(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype, int32_t n_frames,
+                   int32_t chunk_frames, int32_t mask_window_frames, const void* workspace,
+                   QArgs* q, AttnArgs* a) {
+  int32_t st = check_dims(dims);
+  if (st) return st;
+  st = check_cache(cache, dtype, dims->d_c + kDRope);
+  if (st) return st;
+  if (cache->sink_frames || cache->rope_at_read) return VMLA_ERR_SHAPE;
+  if (n_frames < 1 || n_frames > cache->window_frames) return VMLA_ERR_RANGE;
+  if (chunk_frames < 1 || chunk_frames > n_frames || mask_window_frames < chunk_frames)
+    return VMLA_ERR_RANGE;
+  const int64_t T = (int64_t)cache->grid_h * cache->grid_w;
+  const int64_t n_q = T * n_frames;
+  if (n_q * dims->d_model > INT32_MAX || n_q * dims->n_heads * kDV > INT32_MAX) return VMLA_ERR_SHAPE;
+  const int64_t n_chunks = (n_frames + chunk_frames - 1) / chunk_frames;
+  if (n_chunks * cache->batch > 65535) return VMLA_ERR_SHAPE;   // one grid z index per (chunk, element)
+  if (!workspace) return VMLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return VMLA_ERR_ALIGN;
+  fill_attention(dims, cache, workspace, n_q, 0, n_q, 0, q, a);
+  const int64_t span = mask_window_frames < n_frames ? mask_window_frames : n_frames;
+  a->cm = ChunkMask{(int)n_chunks, (int)(T * chunk_frames), (int)(T * chunk_frames), (int)(T * span)};
+  return VMLA_OK;
+}
+
+}  // namespace
+
+int32_t vmla_chunk_causal_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                                    const void* x, const void* w_q, const void* w_k_up,
+                                    const void* w_v_up, int32_t n_frames, int32_t chunk_frames,
+                                    int32_t mask_window_frames, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (!x || !w_q || !w_k_up || !w_v_up || !out) return VMLA_ERR_NULL;
+  QArgs q;
+  AttnArgs a;
+  int32_t st = check_clip(dims, cache, dtype, n_frames, chunk_frames, mask_window_frames, workspace,
+                          &q, &a);
+  if (st) return st;
+  if (workspace_bytes < vmla_attention_workspace_bytes(dims, cache->batch, a.n_q))
+    return VMLA_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_k_up) || !aligned16(w_v_up) || !aligned16(out))
+    return VMLA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  q.x = x; q.w_q = w_q; q.w_k_up = w_k_up;
+  st = hip_status(launch_qprologue(q, dtype == VMLA_F32, s));
+  if (st) return st;
+  a.w_v_up = w_v_up; a.out = out;
+  return hip_status(launch_latent_attn(a, dtype == VMLA_F32, s));
+}
+
+int32_t vmla_chunk_causal_latent_attention(const vmla_dims* dims, const vmla_cache* cache,
+                                           int32_t dtype, const void* w_v_up, int32_t n_frames,
+                                           int32_t chunk_frames, int32_t mask_window_frames,
+                                           void* out, const void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  if (!w_v_up || !out) return VMLA_ERR_NULL;
+  QArgs q;
+  AttnArgs a;
+  int32_t st = check_clip(dims, cache, dtype, n_frames, chunk_frames, mask_window_frames, workspace,
+                          &q, &a);
+  if (st) return st;
+  if (workspace_bytes < vmla_attention_workspace_bytes(dims, cache->batch, a.n_q))
+    return VMLA_ERR_WORKSPACE;
+  if (!aligned16(w_v_up) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  a.w_v_up = w_v_up; a.out = out;
+  return hip_status(launch_latent_attn(a, dtype == VMLA_F32, static_cast<hipStream_t>(stream)));
+}
+
+int32_t vmla_chunk_causal_attention_explicit(const vmla_dims* dims, const vmla_cache* cache,
+                                             int32_t dtype, const void* x, const void* w_q,
+                                             const void* w_kv, int32_t n_frames,
+                                             int32_t chunk_frames, int32_t mask_window_frames,
+                                             void* out, void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  if (!x || !w_q || !w_kv || !out) return VMLA_ERR_NULL;
+  int32_t st = check_dims_192(dims);
+  if (st) return st;
+  QArgs q;
+  AttnArgs a;
+  st = check_clip(dims, cache, dtype, n_frames, chunk_frames, mask_window_frames, workspace, &q, &a);
+  if (st) return st;
+  if ((int64_t)a.n_k * 2 * kDHead * dims->n_heads > INT32_MAX) return VMLA_ERR_SHAPE;
+  if (workspace_bytes < vmla_explicit_workspace_bytes(dims, cache->batch, a.n_q, a.n_k))
+    return VMLA_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_kv) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  return run_explicit(dims, cache, dtype, x, w_q, w_kv, q, a, out, workspace,
+                      static_cast<hipStream_t>(stream));
 }
 
 int32_t vmla_output_projection(const vmla_dims* dims, int32_t dtype, int64_t m, const void* in,

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.vmla_abi_version() == 4
+    assert lib.vmla_abi_version() == 5
     for code in range(-7, 1):
         s = vm.vmla_status_string(code)
         assert s and s != "unknown status"
@@ -225,6 +225,53 @@ def test_explicit_validation(lib):
     assert lib.vmla_pack_kv_weights(ctypes.byref(d), vm.VMLA_BF16, A, None, C, None) == vm.VMLA_ERR_NULL
     assert lib.vmla_pack_kv_weights(ctypes.byref(d), 9, A, B, C, None) == vm.VMLA_ERR_DTYPE
     assert lib.vmla_pack_kv_weights(ctypes.byref(d), vm.VMLA_BF16, A, B, MIS, None) == vm.VMLA_ERR_ALIGN
+
+
+def test_chunk_causal_validation(lib):
+    d = vm.default_dims()
+    clip = _cache(window_frames=7)
+    need = vm.vmla_attention_workspace_bytes(1, 7 * 24, d)
+
+    def call(dims=d, cache=clip, dtype=vm.VMLA_BF16, x=A, out=C, n_frames=7, chunk=3, win=5,
+             ws=B, ws_bytes=need):
+        return lib.vmla_chunk_causal_attention(ctypes.byref(dims), ctypes.byref(cache), dtype, x, B, C,
+                                               A, n_frames, chunk, win, out, ws, ws_bytes, None)
+    assert call(x=None) == vm.VMLA_ERR_NULL
+    assert call(out=None) == vm.VMLA_ERR_NULL
+    assert call(dtype=vm.VMLA_F32) == vm.VMLA_ERR_DTYPE
+    assert call(cache=_cache(window_frames=7, rope_at_read=1)) == vm.VMLA_ERR_SHAPE
+    assert call(cache=_cache(window_frames=7, sink_frames=1, rope_at_read=1)) == vm.VMLA_ERR_SHAPE
+    assert call(cache=_cache(window_frames=7, batch=40000)) == vm.VMLA_ERR_SHAPE   # 120,000 grid z
+    assert call(n_frames=0) == vm.VMLA_ERR_RANGE
+    assert call(n_frames=8) == vm.VMLA_ERR_RANGE                          # > the cache's frames
+    assert call(chunk=0) == vm.VMLA_ERR_RANGE
+    assert call(n_frames=2, chunk=3) == vm.VMLA_ERR_RANGE                 # chunk longer than the clip
+    assert call(win=2) == vm.VMLA_ERR_RANGE                               # window shorter than a chunk
+    assert call(ws=None) == vm.VMLA_ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == vm.VMLA_ERR_WORKSPACE
+    assert call(ws=MIS) == vm.VMLA_ERR_ALIGN
+    assert call(out=MIS) == vm.VMLA_ERR_ALIGN
+    d64 = vm.default_dims(d_c=64)
+    assert call(dims=d64, ws=None) == vm.VMLA_ERR_WORKSPACE               # passed up to the workspace
+    # the attention stage alone
+    st = lib.vmla_chunk_causal_latent_attention(ctypes.byref(d), ctypes.byref(clip), vm.VMLA_BF16, A,
+                                                7, 3, 5, None, B, need, None)
+    assert st == vm.VMLA_ERR_NULL
+    st = lib.vmla_chunk_causal_latent_attention(ctypes.byref(d), ctypes.byref(clip), vm.VMLA_BF16, A,
+                                                7, 3, 5, C, B, 100, None)
+    assert st == vm.VMLA_ERR_WORKSPACE
+    # explicit form: d_c = 192 only, its own workspace size
+    big = vm.vmla_explicit_workspace_bytes(1, 7 * 24, 7 * 24, d)
+    assert big == 12 * 2 * (168 * 128 + 168 * 256)
+
+    def xcall(dims=d, ws_bytes=big, wkv=C):
+        return lib.vmla_chunk_causal_attention_explicit(ctypes.byref(dims), ctypes.byref(clip),
+                                                        vm.VMLA_BF16, A, B, wkv, 7, 3, 5, C, B,
+                                                        ws_bytes, None)
+    assert xcall(wkv=None) == vm.VMLA_ERR_NULL
+    assert xcall(dims=d64) == vm.VMLA_ERR_SHAPE
+    assert xcall(ws_bytes=need) == vm.VMLA_ERR_WORKSPACE
+    assert xcall(wkv=MIS) == vm.VMLA_ERR_ALIGN
 
 
 def test_binding_cache_geometry():
