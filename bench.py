@@ -21,8 +21,13 @@ with k_R rotated at read time; `--layer` runs the whole attention layer instead
 of the attention core: the d_q = 768 query latent, the latent attention, and
 the output mixer W_O with B_h folded in (out [B, N_q, d_model]).
 
+`--chunk-causal` times the whole-clip form instead: the 21 latent frames of a
+Wan-1.3B clip (32,760 tokens) appended, every token a query, 3-frame chunks
+under the chunk-causal block mask (with `--explicit`: through explicit per-head
+K/V of the whole clip).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--config 2|3|4]
-                       [--long-horizon] [--layer]
+                       [--long-horizon] [--layer] [--explicit] [--d-c 64|128|192] [--chunk-causal]
 """
 from __future__ import annotations
 
@@ -72,6 +77,34 @@ def work(w, layer=False, explicit=False):
     return dict(core=core, prologue=prologue, epilogue=epilogue, append=append,
                 attn_kernel=core + epilogue, step=core + prologue + epilogue + append,
                 bytes_append=bytes_append, bytes_prologue=bytes_prologue, bytes_attn=bytes_attn)
+
+
+def clip_work(w, n_frames, window, explicit=False, rows=None):
+    """Algorithmic flops of the whole-clip chunk-causal form: every token of
+    frames 0 .. n_frames - 1 is a query; chunk c (w.chunk_frames frames) sees
+    the frames [max(0, e - window), e), e its end. ``rows``: restrict the
+    query-side work to these chunk indices (the append stays whole)."""
+    T, H, D, B = w.tokens_per_frame, w.n_heads, w.d_model, w.batch
+    C = w.chunk_frames
+    n_chunks = -(-n_frames // C)
+    per_pair = 2 * (w.d_head + w.d_v) if explicit else 2 * (w.d_c + w.d_rope) + 2 * w.d_c
+    core = nq = 0
+    for c in range(n_chunks) if rows is None else rows:
+        e = min((c + 1) * C, n_frames)
+        q = (e - c * C) * T
+        core += per_pair * q * (e - max(0, e - window)) * T * H * B
+        nq += q * B
+    if explicit:
+        prologue = nq * 2 * D * H * w.d_head + B * n_frames * T * 2 * w.d_c * H * (w.d_nope + w.d_v)
+        epilogue = 0
+    else:
+        prologue = nq * (2 * D * H * w.d_head + H * 2 * w.d_nope * w.d_c)
+        epilogue = nq * H * 2 * w.d_c * w.d_v
+    append = B * n_frames * T * 2 * D * w.cache_row
+    bytes_append = B * n_frames * T * (D * 2 + 2 * w.cache_row) + D * w.cache_row * 2
+    return dict(core=core, prologue=prologue, epilogue=epilogue, append=append,
+                attn_kernel=core + epilogue, step=core + prologue + epilogue + append,
+                bytes_append=bytes_append)
 
 
 def cpu_baseline(w, wts, x_host, step_flops, mix=None):
@@ -126,6 +159,9 @@ def main():
     ap.add_argument("--d-c", type=int, default=192, choices=(64, 128, 192),
                     help="content-latent width of the cache (the latent-budget sweep); the "
                          "--layer and --explicit routes run at 192 only")
+    ap.add_argument("--chunk-causal", action="store_true",
+                    help="the whole-clip form: 21 latent frames, every token a query, 3-frame "
+                         "chunks under the chunk-causal block mask")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device-to-device copy of MIB MiB, whose counter "
                          "readings calibrate FETCH_SIZE / WRITE_SIZE")
@@ -156,6 +192,12 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy: {nbytes} bytes read and {nbytes} bytes written")
         del src, dst
+    if args.chunk_causal:
+        if args.config != 2 or args.long_horizon or args.layer or args.d_c != 192:
+            print("--chunk-causal runs the Wan-1.3B clip at B=1 (config 2 shapes), with or without "
+                  "--explicit", file=sys.stderr)
+            sys.exit(2)
+        return clip_bench(args, dev)
     w = config(args.config)
     if args.long_horizon:
         if args.config != 2:
@@ -375,6 +417,132 @@ def main():
         result["roofline"]["kernel"] = "latent_attn (folded epilogue) + output-mixer GEMM"
         result["config"]["sink_frames"] = w.sink_frames
         result["config"]["window_frames"] = w.window_frames
+    print(json.dumps(result), flush=True)
+
+
+def clip_bench(args, dev):
+    """The whole-clip chunk-causal form: append all frames, query prologue over
+    the clip, chunk-causal attention (or the explicit route). One step = one
+    forward of the clip through the attention of one layer."""
+    import numpy as np
+    import torch
+
+    import latent_kv_attention_cache_amd as vm
+    from workloads import config, weights, x_frame
+
+    F, W = 21, 21
+    w = config(2).with_(window_frames=F, chunk_frames=3, t_first=0,
+                        name="Wan-1.3B clip, B=1, 21 frames of 30x52, 3-frame chunks, chunk-causal mask")
+    log(f"[bench] workload: {w.name}")
+    dims = vm.default_dims()
+    wts = weights(w)
+    xs = {t: x_frame(w, t) for t in range(F)}
+    dw = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in wts.items()}
+    x = torch.from_numpy(np.concatenate([xs[t] for t in range(F)]))[None].to(dev).to(torch.bfloat16)
+    cache = vm.LatentCache.empty(1, F, w.grid_h, w.grid_w, device=dev, dims=dims)
+    n_q = F * w.tokens_per_frame
+    out = torch.empty((1, n_q, w.n_heads, w.d_v), dtype=torch.bfloat16, device=dev)
+    if args.explicit:
+        dw["w_kv"] = vm.vmla_pack_kv_weights(dw["w_k_up"], dw["w_v_up"], dims=dims)
+        ws = torch.empty(vm.vmla_explicit_workspace_bytes(1, n_q, n_q, dims), dtype=torch.uint8,
+                         device=dev)
+    else:
+        ws = torch.empty(vm.vmla_attention_workspace_bytes(1, n_q, dims), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        vm.vmla_cache_append(cache, x, dw["w_down"], dw["w_kr"], 0, F, dims=dims)
+        if ev is not None:
+            ev[1].record(stream)
+        if not args.explicit:
+            vm.vmla_query_prologue(cache, x, dw["w_q"], dw["w_k_up"], 0, F, F, ws, dims=dims)
+        if ev is not None:
+            ev[2].record(stream)
+        if args.explicit:
+            vm.vmla_chunk_causal_attention_explicit(cache, x, dw["w_q"], dw["w_kv"], F, w.chunk_frames,
+                                                    W, out, ws, dims=dims)
+        else:
+            vm.vmla_chunk_causal_latent_attention(cache, dw["w_v_up"], F, w.chunk_frames, W, out, ws,
+                                                  dims=dims)
+        if ev is not None:
+            ev[3].record(stream)
+
+    steps, warmup = max(1, args.steps // 5), max(1, args.warmup // 5)   # a clip is ~5 chunk steps
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    k_ms = [sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / steps for j in range(3)]
+    assert torch.isfinite(out.float()).all().item(), "non-finite output"
+
+    wk = clip_work(w, F, W, explicit=args.explicit)
+    tflops = wk["step"] / (ms_step * 1e-3) / 1e12
+    if args.explicit:
+        kflops, kname = wk["prologue"] + wk["core"], "explicit route (query GEMM + K/V rebuild + attention)"
+        kms = {"append": k_ms[0], "explicit_route": k_ms[2]}
+    else:
+        kflops, kname = wk["attn_kernel"], "latent_attn (chunk-causal instance)"
+        kms = {"append": k_ms[0], "query_prologue": k_ms[1], "latent_attn": k_ms[2]}
+    ach = kflops / (k_ms[2] * 1e-3) / 1e12
+    append_gbs = wk["bytes_append"] / (k_ms[0] * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": ("Wan-1.3B clip through one attention layer: B=1, 21 latent frames of "
+                         "30x52 tokens, every token a query, 3-frame chunks under the chunk-causal "
+                         "block mask (window = the clip)"
+                         + ("; explicit route: per-head K/V of the whole clip rebuilt, then "
+                            "128-dim attention" if args.explicit else "")),
+            "batch": 1, "n_q": n_q, "n_k": n_q, "n_frames": F, "chunk_frames": w.chunk_frames,
+            "mask_window_frames": W, "n_heads": w.n_heads, "d_model": w.d_model, "d_c": w.d_c,
+            "d_rope": w.d_rope, "d_nope": w.d_nope, "d_v": w.d_v, "flops_per_step": wk["step"],
+        },
+        "kernels_ms": {k: round(v, 4) for k, v in kms.items()},
+        "roofline": {"bound": "mfma", "kernel": kname, "achieved": round(ach, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": kflops},
+        "append_roofline": {"bound": "hbm", "achieved": round(append_gbs, 1), "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": round(append_gbs / PEAK_HBM_GBS, 4),
+                            "bytes_per_launch": wk["bytes_append"]},
+    }
+    if args.explicit:
+        result["absorbed_flops_per_step"] = clip_work(w, F, W)["step"]
+    log(f"[bench] ms/step {ms_step:.4f}  kernels {kms}  {kname} {ach:.1f} TFLOP/s")
+    if not args.no_cpu_baseline:
+        # bounded sample: the oracle on the last chunk's 4680 queries (each sees
+        # the whole clip), with the whole clip's cache build
+        import oracle.vmla_oracle as orc
+        n_chunks = -(-F // w.chunk_frames)
+        c = n_chunks - 1
+        T = w.tokens_per_frame
+        rows = np.arange(c * w.chunk_frames * T, F * T)
+        t0 = time.perf_counter()
+        orc.clip_chunk_causal_reference(w, wts, lambda t: xs[t], F, W, rows)
+        sec = time.perf_counter() - t0
+        fl = clip_work(w, F, W, rows=[c])["step"]
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            threads = len(os.sched_getaffinity(0))
+        log(f"[cpu_baseline] oracle on the last chunk: {sec:.2f} s")
+        result["cpu_baseline"] = {
+            "value": fl / sec / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"the last chunk's {len(rows)} queries (each attends to all {F * T} keys of "
+                       f"the clip) through the numpy fp64 oracle, the whole clip's cache build "
+                       f"included; {sec:.1f} s wall on the host, rated with that sample's "
+                       f"algorithmic flops"),
+        }
     print(json.dumps(result), flush=True)
 
 
