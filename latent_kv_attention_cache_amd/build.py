@@ -26,6 +26,10 @@ SOURCES = ["vmla_api.cpp", "append.hip", "qprologue.hip", "latent_attn.hip", "mi
 # Per-source extra flags. The attention kernel never reads NaNs (slots past the
 # valid prefix are not loaded), so max() needs no NaN canonicalization.
 EXTRA_FLAGS = {"latent_attn.hip": ["-fno-honor-nans"]}
+# The matrix-core peak probe (the measured roofline reference of bench.py) is
+# its own library, outside the C ABI of libvmla.so.
+PROBE_SOURCE = "peak_probe.hip"
+PROBE_PATH = os.path.join(PKG, "libvmla_probe.so")
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -47,19 +51,25 @@ def _compile(src: str, verbose: bool) -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP/C++ source and link ``libvmla.so``; returns its path."""
+    """Compile every HIP/C++ source, link ``libvmla.so`` and the peak-probe
+    library ``libvmla_probe.so``; returns the path of ``libvmla.so``."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+    with ThreadPoolExecutor(max_workers=min(7, len(SOURCES) + 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + [PROBE_SOURCE]))
+    _link(objs[:-1], LIB_PATH, verbose)
+    _link(objs[-1:], PROBE_PATH, verbose)
+    return LIB_PATH
+
+
+def _link(objs, path, verbose):
+    tmp = path + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+        raise RuntimeError(f"link of {os.path.basename(path)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, path)
 
 
 if __name__ == "__main__":

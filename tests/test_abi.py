@@ -293,3 +293,18 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError, match="GPU tensor"):
         vm.vmla_cache_append(cache, x, torch.zeros(1536, 192, dtype=torch.bfloat16),
                              torch.zeros(1536, 32, dtype=torch.bfloat16), 0, 1)
+
+
+def test_peak_probe_library():
+    # the matrix-core peak probe that bench.py times next to the published peak
+    path = os.path.join(ROOT, "latent_kv_attention_cache_amd", "libvmla_probe.so")
+    probe = ctypes.CDLL(path)
+    probe.vmla_probe_sink_floats.restype = ctypes.c_int64
+    probe.vmla_probe_mfma_flops.argtypes = [ctypes.c_int32]
+    probe.vmla_probe_mfma_flops.restype = ctypes.c_double
+    probe.vmla_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    assert probe.vmla_probe_sink_floats() == 1024 * 256
+    # 1024 blocks x 4 waves x 4 MFMAs of 2 * 32 * 32 * 16 flops per trip
+    assert probe.vmla_probe_mfma_flops(1) == 1024 * 4 * 4 * 32768
+    assert probe.vmla_probe_mfma_bf16(None, 1, None) == -1
+    assert probe.vmla_probe_mfma_bf16(A, 0, None) == -1
