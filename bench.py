@@ -140,6 +140,35 @@ def measured_mfma_peak():
     return best
 
 
+def measured_hbm_read():
+    """Sustained HBM read bandwidth of this GPU in GB/s: the best of five
+    launches of the stream probe (libvmla_probe.so) over a 2 GiB buffer, far
+    larger than the 256 MB Infinity Cache."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "latent_kv_attention_cache_amd", "libvmla_probe.so"))
+    lib.vmla_probe_read_sink_words.restype = ctypes.c_int64
+    lib.vmla_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.vmla_probe_hbm_read.restype = ctypes.c_int32
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(lib.vmla_probe_read_sink_words(), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = 0.0
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st = lib.vmla_probe_hbm_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                     ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if st != 0:
+            raise RuntimeError(f"HBM probe launch failed ({st})")
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf, sink
+    return best
+
+
 def cpu_baseline(w, wts, x_host, step_flops, mix=None):
     """Time the CPU fp64 oracle on the whole step: every query token of the
     chunk, all heads, the full key window (its explicit per-head K/V build
@@ -422,7 +451,7 @@ def main():
         },
     }
     log(f"[bench] ms/step {ms_step:.4f}  kernels {k_ms}  attention {attn_tflops:.1f} TFLOP/s")
-    _add_measured_peak(result["roofline"])
+    _add_measured_peak(result["roofline"], result["append_roofline"])
     if not args.no_cpu_baseline and args.config == 2:
         xh = lambda t: xs[t]  # noqa: E731
         result["cpu_baseline"] = cpu_baseline(w, wts, xh, wk["step"], mix)
@@ -553,7 +582,7 @@ def clip_bench(args, dev):
     if args.explicit:
         result["absorbed_flops_per_step"] = clip_work(w, F, W)["step"]
     log(f"[bench] ms/step {ms_step:.4f}  kernels {kms}  {kname} {ach:.1f} TFLOP/s")
-    _add_measured_peak(result["roofline"])
+    _add_measured_peak(result["roofline"], result["append_roofline"])
     if not args.no_cpu_baseline:
         # bounded sample: the oracle on the last chunk's 4680 queries (each sees
         # the whole clip), with the whole clip's cache build
@@ -582,11 +611,16 @@ def clip_bench(args, dev):
     print(json.dumps(result), flush=True)
 
 
-def _add_measured_peak(roof):
+def _add_measured_peak(roof, append_roof=None):
     peak = measured_mfma_peak()
     log(f"[bench] measured MFMA peak {peak:.1f} TFLOP/s")
     roof["measured_peak"] = round(peak, 1)
     roof["frac_of_measured_peak"] = round(roof["achieved"] / peak, 4)
+    if append_roof is not None:
+        bw = measured_hbm_read()
+        log(f"[bench] measured HBM read {bw:.1f} GB/s")
+        append_roof["measured_peak"] = round(bw, 1)
+        append_roof["frac_of_measured_peak"] = round(append_roof["achieved"] / bw, 4)
 
 
 def _kernel_sha():

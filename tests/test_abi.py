@@ -308,3 +308,9 @@ def test_peak_probe_library():
     assert probe.vmla_probe_mfma_flops(1) == 1024 * 4 * 4 * 32768
     assert probe.vmla_probe_mfma_bf16(None, 1, None) == -1
     assert probe.vmla_probe_mfma_bf16(A, 0, None) == -1
+    probe.vmla_probe_read_sink_words.restype = ctypes.c_int64
+    probe.vmla_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    assert probe.vmla_probe_read_sink_words() == 2048 * 256
+    assert probe.vmla_probe_hbm_read(A, 24, B, None) == -1          # not a multiple of 16
+    assert probe.vmla_probe_hbm_read(MIS, 32, B, None) == -1        # 8-byte aligned only
+    assert probe.vmla_probe_hbm_read(None, 32, B, None) == -1
