@@ -55,16 +55,21 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxRows = 160;
 
 // Weight-tile shape for a content width DC (192 by default; 64 and 128 for
-// the latent-budget sweep): a row of [W_down | W_KR] is DC + kDRope wide.
-template <int DC>
+// the latent-budget sweep) and a positional width DR (32 by default; 16, 64,
+// 96 for the NoPE/RoPE split variants): a row of [W_down | W_KR] is DC + DR
+// wide. Column half 0 takes the first kColBlocks 16-wide blocks, half 1 the
+// other kColBlocks1 (one fewer when the row has an odd number of blocks).
+template <int DC, int DR>
 struct WShape {
-  static constexpr int kRow = DC + kDRope;
+  static constexpr int kRow = DC + DR;
   static constexpr int kWChunks = kRow / 8;               // 28 chunks per weight row at DC 192
   static constexpr int kWdElems = kStageK * DC;           // W_down tile
   static constexpr int kWElems = kStageK * kRow;          // W_down + W_KR tiles
   static constexpr int kWdLoads = kWdElems * 2 / 1024;    // 24 wave-wide loads at DC 192
-  static constexpr int kColBlocks = kRow / 32;            // 16-wide column blocks per wave (7)
-  static_assert(kRow % 32 == 0, "two column halves of 16-wide blocks");
+  static constexpr int kColBlocks = (kRow / 16 + 1) / 2;  // 16-wide column blocks of half 0 (7)
+  static constexpr int kColBlocks1 = kRow / 16 - kColBlocks;
+  static constexpr int kWPerWave = (kWChunks + 3) / 4;    // W loads per wave (the last may repeat)
+  static_assert(kRow % 16 == 0 && 16 * kColBlocks <= DC, "half 0 holds content columns only");
 };
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -73,40 +78,53 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 // chunk permutation masks of W_down / W_KR row k (an involution per row)
 __device__ __forceinline__ int swz_wd(int k) { return 2 * (((k >> 1) & 1) | (((k >> 3) & 1) << 1)); }
-__device__ __forceinline__ int swz_wr(int k) { return 2 * ((k >> 3) & 1); }
+template <int DR>   // W_KR rows of DR / 8 chunks: flip bit 1 (4, 8 or 12 chunks), none for 2
+__device__ __forceinline__ int swz_wr(int k) { return DR == 16 ? 0 : 2 * ((k >> 3) & 1); }
 
-template <typename T, int NRB, int DC>
+template <typename T, int NRB, int DC, int DR>
 struct Tile {
-  static constexpr int kRow = WShape<DC>::kRow;
-  static constexpr int kWChunks = WShape<DC>::kWChunks;
-  static constexpr int kWElems = WShape<DC>::kWElems;
+  static constexpr int kRow = WShape<DC, DR>::kRow;
+  static constexpr int kWChunks = WShape<DC, DR>::kWChunks;
+  static constexpr int kWElems = WShape<DC, DR>::kWElems;
   static constexpr int kRows = 32 * NRB;                   // rows of a workgroup at most
   static constexpr int kXElems = kRows * kStageK;
   static constexpr int kXLoads = kXElems * 2 / 1024;       // 4 NRB
   static constexpr int kStageElems = kXElems + kWElems;
-  static constexpr int kStages = 4 * kStageElems * 2 <= 160 * 1024 ? 4 : 3;
-  static constexpr int kLoadsPerWave = (kXLoads + kWChunks) / kWaves;   // NRB x loads + 7 W chunks
+  static constexpr int kStages = 4 * kStageElems * 2 <= 160 * 1024 ? 4
+                                 : (3 * kStageElems * 2 <= 160 * 1024 ? 3 : 2);
+  static constexpr int kLoadsPerWave = NRB + WShape<DC, DR>::kWPerWave;   // NRB x loads + 7 W chunks
   // epilogue: bf16 storage keeps c as bf16 rows of 224 + 8 and k_R in fp32;
   // fp32 storage keeps all 224 columns in fp32 rows of 228; 5 ints of row info
   static constexpr int kOutLd = std::is_same_v<T, bf16_t> ? kRow + 8 : kRow + 4;
-  static constexpr int kKrLd = kDRope + 4;
+  static constexpr int kKrLd = DR + 4;
   static constexpr int kEpiBytes = std::is_same_v<T, bf16_t>
       ? kRows * (kOutLd * 2 + kKrLd * 4 + 20) : kRows * (kOutLd * 4 + 20);
   static constexpr int kSmemElems = std::max(kStages * kStageElems, (kEpiBytes + 1) / 2);
   static_assert(NRB >= 1 && NRB <= 5, "row blocks per wave");
-  static_assert((kXLoads + kWChunks) % kWaves == 0 && kXLoads == kWaves * NRB, "load split");
+  static_assert(kXLoads == kWaves * NRB, "load split");
   static_assert(kSmemElems * 2 <= 160 * 1024, "LDS budget");
 };
 
-template <typename T, int NRB, int DC>
+template <typename T, int NRB, int DC, int DR>
 __global__ __launch_bounds__(kThreads)
 void append_kernel(AppendArgs a) {
-  using Tl = Tile<T, NRB, DC>;
+  using Tl = Tile<T, NRB, DC, DR>;
   constexpr int kDC = DC;
-  constexpr int kRow = WShape<DC>::kRow;
-  constexpr int kWdElems = WShape<DC>::kWdElems;
-  constexpr int kWdLoads = WShape<DC>::kWdLoads;
-  constexpr int kColBlocks = WShape<DC>::kColBlocks;
+  constexpr int kDRope = DR;
+  constexpr int kRow = WShape<DC, DR>::kRow;
+  constexpr int kWdElems = WShape<DC, DR>::kWdElems;
+  constexpr int kWdLoads = WShape<DC, DR>::kWdLoads;
+  constexpr int kColBlocks = WShape<DC, DR>::kColBlocks;
+  constexpr int kColBlocks1 = WShape<DC, DR>::kColBlocks1;
+  constexpr int kWPerWave = WShape<DC, DR>::kWPerWave;
+  constexpr int kWChunks = WShape<DC, DR>::kWChunks;
+  // W load index of load i >= NRB of wave wv (a repeat of the last chunk when
+  // the chunks do not split evenly over the four waves)
+  auto w_load = [&](int wv_, int i) {
+    const int n = kWPerWave * wv_ + (i - NRB);
+    if constexpr (kWChunks % kWaves == 0) return n;
+    else return min(n, kWChunks - 1);
+  };
   constexpr bool kBf16 = std::is_same_v<T, bf16_t>;
   __shared__ __attribute__((aligned(16))) bf16_t smem[Tl::kSmemElems];
 
@@ -142,13 +160,13 @@ void append_kernel(AppendArgs a) {
       } else {
         // W load n: 1 KB of the W_down tile (n < 24) or of the W_KR tile; LDS
         // slot q holds chunk position q % rowchunks of row q / rowchunks
-        const int n = kColBlocks * wv + (i - NRB);
+        const int n = w_load(wv, i);
         if (n < kWdLoads) {
           const int q = 64 * n + lane, k = q / (kDC / 8), cp = q - k * (kDC / 8);
           voff[i] = (uint32_t)(k * (kDC / 8) + (cp ^ swz_wd(k))) * 16u;
         } else {
           const int q = 64 * (n - kWdLoads) + lane, k = q / (kDRope / 8), cp = q - k * (kDRope / 8);
-          voff[i] = (uint32_t)(k * (kDRope / 8) + (cp ^ swz_wr(k))) * 16u;
+          voff[i] = (uint32_t)(k * (kDRope / 8) + (cp ^ swz_wr<DR>(k))) * 16u;
         }
       }
     }
@@ -165,7 +183,7 @@ void append_kernel(AppendArgs a) {
         if constexpr (kBf16) dma16_lds(xw + k0, voff[i], lds_u32(st + 512 * n));
         else stage_a_load<T>(st, xw, a.d_model, 0, rows, k0, n, lane);
       } else {
-        const int n = kColBlocks * wv + (i - NRB);
+        const int n = w_load(wv, i);
         bf16_t* dst = st + Tl::kXElems + 512 * n;
         if constexpr (kBf16) {
           const bf16_t* src = n < kWdLoads ? wd + (size_t)k0 * kDC : wr + (size_t)k0 * kDRope;
@@ -177,7 +195,7 @@ void append_kernel(AppendArgs a) {
             src = wd + (size_t)(k0 + k) * kDC + 8 * (cp ^ swz_wd(k));
           } else {
             const int q = 64 * (n - kWdLoads) + lane, k = q / (kDRope / 8), cp = q - k * (kDRope / 8);
-            src = wr + (size_t)(k0 + k) * kDRope + 8 * (cp ^ swz_wr(k));
+            src = wr + (size_t)(k0 + k) * kDRope + 8 * (cp ^ swz_wr<DR>(k));
           }
           *reinterpret_cast<uint4*>(dst + 8 * lane) = load8_bf16<T>(src);
         }
@@ -208,7 +226,7 @@ void append_kernel(AppendArgs a) {
       const int gcb = kColBlocks * ch + cb;            // 16-column block of [c | k_R]
       const int c = (gcb < kDC / 16 ? 2 * gcb : 2 * (gcb - kDC / 16)) + ((j & 3) >> 1);
       b_off[cb] = gcb < kDC / 16 ? k * kDC + 8 * (c ^ swz_wd(k)) + 4 * (j & 1)
-                                 : kWdElems + k * kDRope + 8 * (c ^ swz_wr(k)) + 4 * (j & 1);
+                                 : kWdElems + k * kDRope + 8 * (c ^ swz_wr<DR>(k)) + 4 * (j & 1);
     }
   }
 
@@ -239,6 +257,10 @@ void append_kernel(AppendArgs a) {
     auto read_b = [&](int kk, bf16x8* bf) {
 #pragma unroll
       for (int cb = 0; cb < kColBlocks; ++cb) {
+        if (cb >= kColBlocks1 && ch != 0) {      // half 1 may hold one block fewer
+          bf[cb] = bf16x8{};
+          continue;
+        }
         const bf16_t* p = W + b_off[cb] + 32 * kk * (cb + kColBlocks * ch < kDC / 16 ? kDC : kDRope);
         const int up = 4 * (cb + kColBlocks * ch < kDC / 16 ? kDC : kDRope);
         const bf16x4 lo = lds_tr4(p);
@@ -260,7 +282,8 @@ void append_kernel(AppendArgs a) {
         issue(s + Tl::kStages - 1, sn, q * kL / (2 * NRB), (q + 1) * kL / (2 * NRB));
 #pragma unroll
         for (int cb = 0; cb < kColBlocks; ++cb)
-          acc[rb][cb] = mfma16(kk == 0 ? b0[cb] : b1[cb], av, acc[rb][cb]);
+          if (cb < kColBlocks1 || ch == 0)        // half 1 may hold one block fewer
+            acc[rb][cb] = mfma16(kk == 0 ? b0[cb] : b1[cb], av, acc[rb][cb]);
         av = an;
       }
     }
@@ -307,6 +330,7 @@ void append_kernel(AppendArgs a) {
       const int row = row0 + 16 * rb;
 #pragma unroll
       for (int cb = 0; cb < kColBlocks; ++cb) {
+        if (cb >= kColBlocks1 && ch != 0) continue;   // half 1 may hold one block fewer
         const int col = 16 * kColBlocks * ch + 16 * cb + 4 * g;
         const f32x4 v = acc[rb][cb];
         if constexpr (kBf16) {
@@ -357,24 +381,34 @@ void append_kernel(AppendArgs a) {
   }
 }
 
-template <typename T, int DC>
+template <typename T, int DC, int DR>
 void launch_t(const AppendArgs& a, int groups, int nrb, hipStream_t s) {
   const dim3 grid(groups), block(kThreads);
   switch (nrb) {
-    case 5: hipLaunchKernelGGL((append_kernel<T, 5, DC>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((append_kernel<T, 4, DC>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((append_kernel<T, 3, DC>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((append_kernel<T, 2, DC>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((append_kernel<T, 1, DC>), grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL((append_kernel<T, 5, DC, DR>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((append_kernel<T, 4, DC, DR>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((append_kernel<T, 3, DC, DR>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((append_kernel<T, 2, DC, DR>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((append_kernel<T, 1, DC, DR>), grid, block, 0, s, a); break;
   }
 }
 
 template <typename T>
 void launch_dc(const AppendArgs& a, int groups, int nrb, hipStream_t s) {
+  if (a.d_rope != kDRope) {                 // split variants: d_c = kDC, bf16 storage
+    if constexpr (std::is_same_v<T, bf16_t>) {
+      switch (a.d_rope) {
+        case 16: launch_t<T, kDC, 16>(a, groups, nrb, s); break;
+        case 64: launch_t<T, kDC, 64>(a, groups, nrb, s); break;
+        default: launch_t<T, kDC, 96>(a, groups, nrb, s); break;
+      }
+    }
+    return;
+  }
   switch (a.d_c) {
-    case 64: launch_t<T, 64>(a, groups, nrb, s); break;
-    case 128: launch_t<T, 128>(a, groups, nrb, s); break;
-    default: launch_t<T, kDC>(a, groups, nrb, s); break;
+    case 64: launch_t<T, 64, kDRope>(a, groups, nrb, s); break;
+    case 128: launch_t<T, 128, kDRope>(a, groups, nrb, s); break;
+    default: launch_t<T, kDC, kDRope>(a, groups, nrb, s); break;
   }
 }
 
@@ -401,6 +435,7 @@ hipError_t launch_append(const AppendArgs& a, bool f32, hipStream_t s) {
   if (e != hipSuccess) return e;
   int nrb = 1;
   const int groups = append_plan((int64_t)a.batch * a.n_tok, cus > 0 ? cus : 1, &nrb);
+  if (a.d_rope != kDRope && (f32 || a.d_c != kDC)) return hipErrorInvalidValue;   // not instantiated
   if (f32) launch_dc<float>(a, groups, nrb, s);
   else launch_dc<bf16_t>(a, groups, nrb, s);
   return hipGetLastError();

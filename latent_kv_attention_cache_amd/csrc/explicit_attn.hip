@@ -257,18 +257,20 @@ void explicit_attn_kernel(ExplicitArgs a) {
 }
 
 // W_KV[c][h (d_nope + d_v) + j] = W_K_up[h][c][j] (j < d_nope), W_V_up[h][c][j - d_nope]
+// (W_K_up[h] is [kDC][d_nope])
 template <typename T>
 __global__ __launch_bounds__(256)
 void pack_kv_kernel(FoldArgs a) {
-  constexpr int kCols = kDNope + kDV;
+  const int dn = a.d_nope;                  // NoPE width of a head's key
+  const int kCols = dn + kDV;
   const int64_t total = (int64_t)kDC * a.n_heads * kCols;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
   const int c = (int)(i / (a.n_heads * kCols));
   const int col = (int)(i - (int64_t)c * a.n_heads * kCols);
   const int h = col / kCols, j = col - h * kCols;
-  const T* src = j < kDNope ? static_cast<const T*>(a.w_first) + ((size_t)h * kDC + c) * kDNope + j
-                            : static_cast<const T*>(a.w_second) + ((size_t)h * kDC + c) * kDV + (j - kDNope);
+  const T* src = j < dn ? static_cast<const T*>(a.w_first) + ((size_t)h * kDC + c) * dn + j
+                        : static_cast<const T*>(a.w_second) + ((size_t)h * kDC + c) * kDV + (j - dn);
   static_cast<T*>(a.out)[i] = *src;
 }
 
@@ -284,7 +286,7 @@ hipError_t launch_explicit_attn(const ExplicitArgs& a, bool f32, hipStream_t s) 
 }
 
 hipError_t launch_pack_kv(const FoldArgs& a, bool f32, hipStream_t s) {
-  const int64_t total = (int64_t)kDC * a.n_heads * (kDNope + kDV);
+  const int64_t total = (int64_t)kDC * a.n_heads * (a.d_nope + kDV);
   const dim3 grid((unsigned)((total + 255) / 256));
   if (f32) hipLaunchKernelGGL(pack_kv_kernel<float>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(pack_kv_kernel<bf16_t>, grid, dim3(256), 0, s, a);

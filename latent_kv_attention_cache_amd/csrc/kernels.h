@@ -7,8 +7,9 @@
 
 namespace vmla {
 
-// Fixed widths of this version (VideoMLA defaults: 96/32 NoPE/RoPE split,
-// 192-wide content latent, 128-wide values).
+// Widths of the default configuration (VideoMLA: 96/32 NoPE/RoPE split,
+// 192-wide content latent, 128-wide values). The head width d_nope + d_rope
+// is always 128; the split variants move the boundary (64/64, 32/96, 112/16).
 constexpr int kDNope = 96;
 constexpr int kDRope = 32;
 constexpr int kDC = 192;
@@ -16,14 +17,15 @@ constexpr int kDV = 128;
 constexpr int kDHead = kDNope + kDRope;   // 128
 constexpr int kRow = kDC + kDRope;        // 224 cached scalars per token
 constexpr int kPairs = kDRope / 2;        // 16 complex RoPE pairs
+constexpr int kMaxPairs = 48;             // the RoPE-heavy 32/96 split
 
 // Rate of each RoPE pair in revolutions per position step (omega / 2 pi) as a
 // 64-bit binary fraction rate * 2^64 = (rev_hi << 32) | rev_lo, and its axis
 // (0 = t, 1 = h, 2 = w).
 struct RopeTable {
-  uint32_t rev_lo[kPairs];
-  uint32_t rev_hi[kPairs];
-  int axis[kPairs];
+  uint32_t rev_lo[kMaxPairs];
+  uint32_t rev_hi[kMaxPairs];
+  int axis[kMaxPairs];
 };
 
 // Query chunks of one attention launch. Each batch element's n_q queries are
@@ -45,7 +47,8 @@ struct AppendArgs {
   float inv_grid_w, inv_tokens_per_frame, inv_window_frames;   // 1/x as float
   int sink_frames;      // 0 or 1: frame 0 kept in slots [0, T)
   int rope_at_read;     // 1: k_R stored unrotated
-  int d_c;              // content width: 64, 128 or kDC (cache rows are d_c + kDRope wide)
+  int d_c;              // content width: 64, 128 or kDC (cache rows are d_c + d_rope wide)
+  int d_rope;           // positional width: kDRope, or 16 / 64 / 96 (split variants, d_c = kDC)
   RopeTable rope;
 };
 
@@ -58,7 +61,8 @@ struct QArgs {
   int grid_w, tokens_per_frame, t_first;
   float inv_grid_w, inv_tokens_per_frame;   // 1/x as float
   float qscale;         // softmax scale * log2(e)
-  int d_c;              // content width: 64, 128 or kDC (Qhat rows are d_c + kDRope wide)
+  int d_c;              // content width: 64, 128 or kDC (Qhat rows are d_c + d_rope wide)
+  int d_rope;           // positional width; the head's first kDHead - d_rope columns are NoPE
   RopeTable rope;
 };
 
@@ -69,7 +73,8 @@ struct AttnArgs {
   void* out;            // [batch, n_q, n_heads, kDV]
   uint16_t* olat;       // null, or [batch * n_q, n_heads * kDC] bf16: O_lat / l instead of out
   int batch, n_q, n_heads, n_k, cache_rows;
-  int d_c;              // content width: 64, 128 or kDC (rows are d_c + kDRope wide)
+  int d_c;              // content width: 64, 128 or kDC (rows are d_c + d_rope wide)
+  int d_rope;           // positional width of the rows
   // Read-time RoPE of k_R (rope_at_read = 1): the key in slot frame fs sits at
   // temporal coordinate fs when fs < sink_frames, otherwise at
   // sink_frames + ((fs - sink_frames - shift_mod_w) mod window_frames).
@@ -90,6 +95,8 @@ struct GemmArgs {
   void* out;
   int64_t m;
   int k, n, lda, mode;
+  // mode 2: NoPE width of a head's key (the k_R copy fills the rest of kDHead)
+  int d_nope;
   // mode 1 only
   int n_q, n_heads, grid_w, tokens_per_frame, t_first, head_w, rope_off;
   float inv_grid_w, inv_tokens_per_frame, qscale;
@@ -113,6 +120,7 @@ struct FoldArgs {
   const void* w_second;
   void* out;
   int d_in, d_out, n_heads;
+  int d_nope;           // NoPE width of a head (the K/V weight pack)
 };
 
 hipError_t launch_append(const AppendArgs& a, bool f32, hipStream_t s);

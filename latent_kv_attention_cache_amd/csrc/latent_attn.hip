@@ -80,17 +80,21 @@ constexpr int kVLd = kDV + 8;               // padded LDS row of W_V_up[h] (epil
 constexpr float kLazy = 8.f;                // lazy-rescale threshold (log2 units)
 
 // Shape of the latent row for a content width DC (192 by default; 64 and 128
-// for the latent-budget sweep): [c (DC) | k_R (kDRope)].
-template <int DC>
+// for the latent-budget sweep) and a positional width DR (32 by default; 16,
+// 64, 96 for the NoPE/RoPE split variants): [c (DC) | k_R (DR)].
+template <int DC, int DR>
 struct AttnShape {
   static constexpr int kDC = DC;
-  static constexpr int kRow = DC + kDRope;
+  static constexpr int kRow = DC + DR;
   static constexpr int kChunks = kRow / 8;          // 16-byte chunks per key row (28 at DC 192)
   static constexpr int kTileElems = kChunks * kSlots * 8;
-  static constexpr int kLoadsPerWave = kChunks / kLoaders;   // one load per chunk column
+  // one load per chunk column; with 26 columns (DR = 16) the last two loads of
+  // waves 2 and 3 are skipped
+  static constexpr int kLoadsPerWave = (kChunks + kLoaders - 1) / kLoaders;
   static constexpr int kFeatSteps = kRow / 16;      // 14
   static constexpr int kLatTiles = DC / 32;         // 6
-  static_assert(kChunks % kLoaders == 0, "tile loads must split evenly over the loading waves");
+  static_assert(kRow % 16 == 0, "whole 16-feature MFMA steps");
+  static_assert(kBufs * kTileElems * 2 <= 160 * 1024, "LDS budget");
   static_assert(2 * DC * kVLd <= kBufs * kTileElems, "W_V_up of two heads must fit in the tile buffers");
   static_assert(DC % 32 == 0 && DC * kDV / 8 % kThreads == 0, "content width");
 };
@@ -109,10 +113,11 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
                :: "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory");
 }
 
-template <typename T, bool kRot, bool kFold, int DC, bool kChunked>
+template <typename T, bool kRot, bool kFold, int DC, bool kChunked, int DR>
 __global__ __launch_bounds__(kThreads)
 void latent_attn_kernel(AttnArgs a) {
-  using Sh = AttnShape<DC>;
+  using Sh = AttnShape<DC, DR>;
+  static_assert(!kRot || DR == kDRope, "read-time RoPE rotates the default 32 positional columns");
   constexpr int kDC = Sh::kDC;
   constexpr int kRow = Sh::kRow;
   constexpr int kTileElems = Sh::kTileElems;
@@ -189,6 +194,7 @@ void latent_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
       const int n = wv + kLoaders * i;
+      if (Sh::kChunks % kLoaders != 0 && n >= Sh::kChunks) continue;   // wave-uniform
       if constexpr (std::is_same_v<T, bf16_t>) {
         dma16(cache, (uint32_t)(kg * (kRow * 2)) + (uint32_t)(16 * n),
               kt_lds + 2u * (uint32_t)(buf * kTileElems + n * kSlots * 8));
@@ -460,29 +466,49 @@ hipError_t launch_dc(const AttnArgs& a, bool f32, hipStream_t s) {
   if (a.cm.n_chunks > 1) {
     // query chunks come only with append-time RoPE and the W_V_up epilogue
     if (a.rope_at_read || a.olat) return hipErrorInvalidValue;
-    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, false, DC, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, false, DC, true>), grid, dim3(kThreads), 0, s, a);
+    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, false, DC, true, kDRope>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, false, DC, true, kDRope>), grid, dim3(kThreads), 0, s, a);
   } else if (a.olat) {
     if (a.rope_at_read) {
-      if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, true, true, DC, false>), grid, dim3(kThreads), 0, s, a);
-      else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, true, true, DC, false>), grid, dim3(kThreads), 0, s, a);
+      if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, true, true, DC, false, kDRope>), grid, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, true, true, DC, false, kDRope>), grid, dim3(kThreads), 0, s, a);
     } else {
-      if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, true, DC, false>), grid, dim3(kThreads), 0, s, a);
-      else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, true, DC, false>), grid, dim3(kThreads), 0, s, a);
+      if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, true, DC, false, kDRope>), grid, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, true, DC, false, kDRope>), grid, dim3(kThreads), 0, s, a);
     }
   } else if (a.rope_at_read) {
-    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, true, false, DC, false>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, true, false, DC, false>), grid, dim3(kThreads), 0, s, a);
+    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, true, false, DC, false, kDRope>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, true, false, DC, false, kDRope>), grid, dim3(kThreads), 0, s, a);
   } else {
-    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, false, DC, false>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, false, DC, false>), grid, dim3(kThreads), 0, s, a);
+    if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, false, DC, false, kDRope>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, false, DC, false, kDRope>), grid, dim3(kThreads), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+template <int DR>
+hipError_t launch_split(const AttnArgs& a, bool f32, hipStream_t s) {
+  const int units = (a.cm.chunk_q + 31) / 32;
+  const int upad = units > kWaves ? units : kWaves;
+  dim3 grid((a.n_heads * upad + kWaves - 1) / kWaves, 1, a.batch);
+  if (f32) hipLaunchKernelGGL((latent_attn_kernel<float, false, false, kDC, false, DR>), grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, false, kDC, false, DR>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_latent_attn(const AttnArgs& a, bool f32, hipStream_t s) {
+  if (a.d_rope != kDRope) {
+    // split variants: d_c = kDC, one query chunk, k_R rotated at append, W_V_up epilogue
+    if (a.d_c != kDC || a.cm.n_chunks != 1 || a.rope_at_read || a.olat) return hipErrorInvalidValue;
+    switch (a.d_rope) {
+      case 16: return launch_split<16>(a, f32, s);
+      case 64: return launch_split<64>(a, f32, s);
+      case 96: return launch_split<96>(a, f32, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.d_c) {
     case 64: return launch_dc<64>(a, f32, s);
     case 128: return launch_dc<128>(a, f32, s);

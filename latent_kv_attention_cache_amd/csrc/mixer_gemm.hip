@@ -247,9 +247,11 @@ void gemm_kernel(GemmArgs a) {
       }
     }
   } else if constexpr (kMode == kKV) {
-    // column col = h (kDNope + kDV) + ci: ci < kDNope key part, else value part;
-    // the lanes holding ci < kDRope also copy k_R (A columns kDC .. kRow - 1).
-    constexpr int kCols = kDNope + kDV;
+    // column col = h (d_nope + kDV) + ci: ci < d_nope key part, else value part;
+    // the lanes holding ci < d_rope = kDHead - d_nope also copy k_R (A columns
+    // kDC .. kDC + d_rope - 1).
+    const int d_nope = a.d_nope, d_rope = kDHead - a.d_nope;
+    const int kCols = d_nope + kDV;
     uint16_t* kv = static_cast<uint16_t*>(a.out);
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
@@ -257,7 +259,7 @@ void gemm_kernel(GemmArgs a) {
       if (col >= a.n) continue;
       const int h = col / kCols;
       const int ci = col - h * kCols;
-      const int dst = ci < kDNope ? ci : ci + kDRope;
+      const int dst = ci < d_nope ? ci : ci + d_rope;
 #pragma unroll
       for (int rb = 0; rb < kNRB; ++rb) {
         const int64_t m = m0 + 16 * kNRB * rh + 16 * rb + j;
@@ -265,9 +267,9 @@ void gemm_kernel(GemmArgs a) {
         uint16_t* row = kv + ((int64_t)h * a.m + m) * (2 * kDHead);
         const f32x4 v = acc[rb][cb];
         store4<bf16_t>(row + dst, v[0], v[1], v[2], v[3]);
-        if (ci < kDRope) {
+        if (ci < d_rope) {
           const TA* kr = static_cast<const TA*>(a.a) + m * a.lda + kDC + ci;
-          store4<bf16_t>(row + kDNope + ci, to_f32(kr[0]), to_f32(kr[1]), to_f32(kr[2]), to_f32(kr[3]));
+          store4<bf16_t>(row + d_nope + ci, to_f32(kr[0]), to_f32(kr[1]), to_f32(kr[2]), to_f32(kr[3]));
         }
       }
     }

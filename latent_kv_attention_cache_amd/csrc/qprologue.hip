@@ -1,7 +1,8 @@
-// Query prologue for gfx950: per head h,
-//   q_h     = x @ W_Q[:, h*128 : h*128+128]            (nope 96 | rope 32)
-//   q_rope  = RoPE3D(q_h[96:128], (t, h, w))
-//   q_lat   = q_h[0:96] @ W_K_up[h]^T                   (96 -> 192)
+// Query prologue for gfx950: per head h, with the NoPE/RoPE split DN / 128 - DN
+// (96 / 32 by default; 64 / 64, 32 / 96 and 112 / 16 are the split variants),
+//   q_h     = x @ W_Q[:, h*128 : h*128+128]            (nope DN | rope 128 - DN)
+//   q_rope  = RoPE3D(q_h[DN:128], (t, h, w))
+//   q_lat   = q_h[0:DN] @ W_K_up[h]^T                   (DN -> d_c)
 //   Qhat_h  = (scale * log2 e) * [q_lat | q_rope]       stored bf16
 //
 // VideoMLA (paperlayer.ai summary of arXiv:2605.30351v1), App. E
@@ -52,10 +53,8 @@ constexpr int kXPerWave = kXLoads / kWaves;       // 4
 constexpr int kWPerWave = kWLoads / kWaves;       // 8
 constexpr int kL = kXPerWave + kWPerWave;         // loads per wave per stage
 constexpr int kWChunks = kColsT / 8;              // 32 chunks per W_Q tile row
-constexpr int kQnLd = kDNope + 8;                 // q_nope staging row (bf16)
 static_assert(kXLoads % kWaves == 0 && kWLoads % kWaves == 0, "loads split evenly");
 static_assert(kStages * kStageElems * 2 <= 160 * 1024, "LDS budget");
-static_assert(kWaves * 64 * kQnLd <= kStages * kStageElems, "epilogue staging fits");
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -64,11 +63,15 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // chunk permutation mask of W_Q tile row k (an involution on the chunks of a row)
 __device__ __forceinline__ int swz_q(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
 
-template <typename T, int DC>
+template <typename T, int DC, int DN>
 __global__ __launch_bounds__(kThreads)
 void qprologue_kernel(QArgs a) {
   constexpr int kDC = DC;                   // content width (192 by default; 64, 128 in the sweep)
-  constexpr int kRow = DC + kDRope;         // Qhat row
+  constexpr int kDNope = DN;                // NoPE width of a head (96 by default)
+  constexpr int kRow = DC + kDHead - DN;    // Qhat row: [q_lat (DC) | q_rope (128 - DN)]
+  constexpr int kQnLd = kDNope + 8;         // q_nope staging row (bf16)
+  static_assert(DN % 16 == 0 && DN > 0 && DN < kDHead, "NoPE width");
+  static_assert(kWaves * 64 * kQnLd <= kStages * kStageElems, "epilogue staging fits");
   __shared__ __attribute__((aligned(16))) bf16_t smem[kStages * kStageElems];
 
   // Workgroups are dispatched round-robin over the 8 XCDs; id = 8 (HP q + hp) + x8
@@ -222,12 +225,16 @@ void qprologue_kernel(QArgs a) {
   // requested now and land during the RoPE and q_nope work; each register set
   // is refilled with tile ct + 6 once tile ct has been consumed.
   constexpr int kCT = kDC / 16;                        // 12 column tiles of q_lat
-  constexpr int kKS = kDNope / 32;                     // 3 steps
+  constexpr int kKS = (kDNope + 31) / 32;              // 3 steps (DN = 112: 4, the last half empty)
+  // lanes whose n = 32 ks + 8 g .. +7 lies past the NoPE width (DN % 32 = 16,
+  // last step) contribute zeros on both operands
+  auto n_live = [&](int ks) { return kDNope % 32 == 0 || 32 * ks + 8 * g < kDNope; };
   const T* wku = static_cast<const T*>(a.w_k_up) + (size_t)h * kDC * kDNope;
   auto load_wk = [&](int ct, bf16x8 (&w)[kKS]) {
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks)
-      w[ks] = __builtin_bit_cast(bf16x8, load8_bf16<T>(wku + (size_t)(16 * ct + j) * kDNope + 32 * ks + 8 * g));
+      w[ks] = n_live(ks) ? __builtin_bit_cast(bf16x8, load8_bf16<T>(wku + (size_t)(16 * ct + j) * kDNope + 32 * ks + 8 * g))
+                         : bf16x8{};
   };
   bf16x8 wk[kCT / 2][kKS];
 #pragma unroll
@@ -249,7 +256,7 @@ void qprologue_kernel(QArgs a) {
     qrow[rb] = m < M ? ((int64_t)b * a.n_heads + h) * a.n_q + n : -1;
   }
   uint16_t* qhat = a.qhat;
-  // RoPE: columns 96 + 16 (cb - 6) + 4 g + r, pairs 8 (cb - 6) + 2 g + {0, 1}
+  // RoPE: columns DN + 16 (cb - DN/16) + 4 g + r, pairs 8 (cb - DN/16) + 2 g + {0, 1}
 #pragma unroll
   for (int cb = kDNope / 16; cb < kCB; ++cb) {
 #pragma unroll
@@ -271,7 +278,7 @@ void qprologue_kernel(QArgs a) {
       }
     }
   }
-  // q_nope of this wave's 64 rows to LDS: qn[row][0..95] (bf16)
+  // q_nope of this wave's 64 rows to LDS: qn[row][0..DN-1] (bf16)
   bf16_t* qn = smem + wv * 64 * kQnLd;
 #pragma unroll
   for (int rb = 0; rb < kNRB; ++rb)
@@ -288,7 +295,7 @@ void qprologue_kernel(QArgs a) {
   for (int rb = 0; rb < kNRB; ++rb)
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks)
-      qb[rb][ks] = lds_row8(&qn[(16 * rb + j) * kQnLd + 32 * ks + 8 * g]);
+      qb[rb][ks] = n_live(ks) ? lds_row8(&qn[(16 * rb + j) * kQnLd + 32 * ks + 8 * g]) : bf16x8{};
 #pragma unroll
   for (int ct = 0; ct < kCT; ++ct) {
     bf16x8 (&w)[kKS] = wk[ct % (kCT / 2)];
@@ -306,6 +313,12 @@ void qprologue_kernel(QArgs a) {
   }
 }
 
+template <int DC, int DN>
+void launch_t(const QArgs& a, bool f32, dim3 grid, hipStream_t s) {
+  if (f32) hipLaunchKernelGGL((qprologue_kernel<float, DC, DN>), grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((qprologue_kernel<bf16_t, DC, DN>), grid, dim3(kThreads), 0, s, a);
+}
+
 }  // namespace
 
 hipError_t launch_qprologue(const QArgs& a, bool f32, hipStream_t s) {
@@ -313,18 +326,19 @@ hipError_t launch_qprologue(const QArgs& a, bool f32, hipStream_t s) {
   const int64_t n_rt = (M + kRowsT - 1) / kRowsT;
   const int n_hp = (a.n_heads + kHeadsT - 1) / kHeadsT;
   const dim3 grid((unsigned)(8 * n_hp * ((n_rt + 7) / 8)));
+  if (a.d_rope != kDRope) {                 // split variants: d_c = kDC
+    switch (a.d_rope) {
+      case 16: launch_t<kDC, 112>(a, f32, grid, s); break;
+      case 64: launch_t<kDC, 64>(a, f32, grid, s); break;
+      case 96: launch_t<kDC, 32>(a, f32, grid, s); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (a.d_c) {
-    case 64:
-      if (f32) hipLaunchKernelGGL((qprologue_kernel<float, 64>), grid, dim3(kThreads), 0, s, a);
-      else hipLaunchKernelGGL((qprologue_kernel<bf16_t, 64>), grid, dim3(kThreads), 0, s, a);
-      break;
-    case 128:
-      if (f32) hipLaunchKernelGGL((qprologue_kernel<float, 128>), grid, dim3(kThreads), 0, s, a);
-      else hipLaunchKernelGGL((qprologue_kernel<bf16_t, 128>), grid, dim3(kThreads), 0, s, a);
-      break;
-    default:
-      if (f32) hipLaunchKernelGGL((qprologue_kernel<float, kDC>), grid, dim3(kThreads), 0, s, a);
-      else hipLaunchKernelGGL((qprologue_kernel<bf16_t, kDC>), grid, dim3(kThreads), 0, s, a);
+    case 64: launch_t<64, kDNope>(a, f32, grid, s); break;
+    case 128: launch_t<128, kDNope>(a, f32, grid, s); break;
+    default: launch_t<kDC, kDNope>(a, f32, grid, s); break;
   }
   return hipGetLastError();
 }

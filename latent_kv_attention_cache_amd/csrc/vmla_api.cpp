@@ -19,12 +19,20 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // fractions of a revolution at any position).
 constexpr int64_t kMaxFrameIndex = 1 << 20;
 
+// NoPE/RoPE split of the 128-wide head: the default 96 / 32, or one of the
+// split variants 64 / 64, 32 / 96, 112 / 16 (with d_c = 192).
+bool split_ok(const vmla_dims* d) {
+  if (d->d_nope + d->d_rope != kDHead) return false;
+  return d->d_rope == kDRope || d->d_rope == 16 || d->d_rope == 64 || d->d_rope == 96;
+}
+
 int32_t check_dims(const vmla_dims* d) {
   if (!d) return VMLA_ERR_NULL;
-  if (d->d_nope != kDNope || d->d_rope != kDRope || d->d_v != kDV) return VMLA_ERR_SHAPE;
+  if (!split_ok(d) || d->d_v != kDV) return VMLA_ERR_SHAPE;
   // content width: the default 192, or 64 / 128 (latent-budget sweep) for the
-  // append and the attention core
+  // append and the attention core; the split variants run at 192
   if (d->d_c != kDC && d->d_c != 64 && d->d_c != 128) return VMLA_ERR_SHAPE;
+  if (d->d_rope != kDRope && d->d_c != kDC) return VMLA_ERR_SHAPE;
   if (d->d_model < 64 || d->d_model % 64 != 0 || d->d_model > (1 << 16)) return VMLA_ERR_SHAPE;
   if (d->n_heads < 1 || d->n_heads > 64) return VMLA_ERR_SHAPE;
   int pairs = 0;
@@ -32,17 +40,31 @@ int32_t check_dims(const vmla_dims* d) {
     if (d->rope_pairs[i] < 0 || d->rope_axis_dims[i] < 1) return VMLA_ERR_SHAPE;
     pairs += d->rope_pairs[i];
   }
-  if (pairs != kPairs) return VMLA_ERR_SHAPE;
+  if (2 * pairs != d->d_rope) return VMLA_ERR_SHAPE;
   if (!(d->rope_theta > 0.f) || !std::isfinite(d->rope_theta)) return VMLA_ERR_SHAPE;
   if (!(d->scale > 0.f) || !std::isfinite(d->scale)) return VMLA_ERR_SHAPE;
   return VMLA_OK;
 }
 
-// The whole-layer, explicit and weight-fold entry points run at d_c = 192 only.
+// The explicit route runs at d_c = 192 (any split); the whole-layer and
+// weight-fold entry points at d_c = 192 and the default split only.
 int32_t check_dims_192(const vmla_dims* d) {
   const int32_t st = check_dims(d);
   if (st) return st;
   return d->d_c == kDC ? VMLA_OK : VMLA_ERR_SHAPE;
+}
+
+int32_t check_dims_default(const vmla_dims* d) {
+  const int32_t st = check_dims_192(d);
+  if (st) return st;
+  return d->d_rope == kDRope ? VMLA_OK : VMLA_ERR_SHAPE;
+}
+
+// The split variants store bf16 and use neither read-time RoPE nor a sink.
+int32_t check_split_cache(const vmla_dims* d, const vmla_cache* c, int32_t dtype) {
+  if (d->d_rope == kDRope) return VMLA_OK;
+  if (dtype != VMLA_BF16) return VMLA_ERR_DTYPE;
+  return c->rope_at_read || c->sink_frames ? VMLA_ERR_SHAPE : VMLA_OK;
 }
 
 int32_t check_cache(const vmla_cache* c, int32_t dtype, int row) {
@@ -70,6 +92,7 @@ RopeTable rope_table(const vmla_dims* d) {
   int j = 0;
   for (int ax = 0; ax < 3; ++ax) {
     for (int i = 0; i < d->rope_pairs[ax]; ++i, ++j) {
+      if (j >= kMaxPairs) return r;           // excluded by check_dims
       const double omega = std::pow((double)d->rope_theta, -2.0 * i / (double)d->rope_axis_dims[ax]);
       // revolutions per step as a 64-bit binary fraction (only the fractional
       // revolution matters for the angle)
@@ -125,7 +148,9 @@ int32_t vmla_cache_append(const vmla_dims* dims, const vmla_cache* cache, int32_
   int32_t st = check_dims(dims);
   if (st) return st;
   if (!x || !w_down || !w_kr) return VMLA_ERR_NULL;
-  st = check_cache(cache, dtype, dims->d_c + kDRope);
+  st = check_cache(cache, dtype, dims->d_c + dims->d_rope);
+  if (st) return st;
+  st = check_split_cache(dims, cache, dtype);
   if (st) return st;
   if (!aligned16(x) || !aligned16(w_down) || !aligned16(w_kr)) return VMLA_ERR_ALIGN;
   if (t_first < 0 || n_frames < 1 || n_frames > cache->window_frames) return VMLA_ERR_RANGE;
@@ -145,13 +170,14 @@ int32_t vmla_cache_append(const vmla_dims* dims, const vmla_cache* cache, int32_
   a.sink_frames = cache->sink_frames;
   a.rope_at_read = cache->rope_at_read;
   a.d_c = dims->d_c;
+  a.d_rope = dims->d_rope;
   a.rope = rope_table(dims);
   return hip_status(launch_append(a, dtype == VMLA_F32, static_cast<hipStream_t>(stream)));
 }
 
 size_t vmla_attention_workspace_bytes(const vmla_dims* dims, int32_t batch, int32_t n_q) {
   if (check_dims(dims) != VMLA_OK || batch < 1 || n_q < 1) return 0;
-  return (size_t)batch * dims->n_heads * (size_t)n_q * (dims->d_c + kDRope) * sizeof(uint16_t);
+  return (size_t)batch * dims->n_heads * (size_t)n_q * (dims->d_c + dims->d_rope) * sizeof(uint16_t);
 }
 
 namespace {
@@ -165,7 +191,9 @@ int32_t check_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t 
                         const void* workspace, size_t workspace_bytes, QArgs* q, AttnArgs* a) {
   int32_t st = check_dims(dims);
   if (st) return st;
-  st = check_cache(cache, dtype, dims->d_c + kDRope);
+  st = check_cache(cache, dtype, dims->d_c + dims->d_rope);
+  if (st) return st;
+  st = check_split_cache(dims, cache, dtype);
   if (st) return st;
   if (t_first < 0 || n_frames < 1 || n_frames > cache->window_frames) return VMLA_ERR_RANGE;
   if ((int64_t)t_first + n_frames > kMaxFrameIndex) return VMLA_ERR_RANGE;
@@ -200,6 +228,7 @@ void fill_attention(const vmla_dims* dims, const vmla_cache* cache, const void* 
   q->inv_tokens_per_frame = 1.f / (float)T;
   q->qscale = (float)((double)dims->scale * 1.4426950408889634);   // scale * log2(e)
   q->d_c = dims->d_c;
+  q->d_rope = dims->d_rope;
   q->rope = rope_table(dims);
 
   *a = AttnArgs{};
@@ -209,6 +238,7 @@ void fill_attention(const vmla_dims* dims, const vmla_cache* cache, const void* 
   a->cm = ChunkMask{1, (int)n_q, (int)n_k, (int)n_k};
   a->rope_at_read = cache->rope_at_read;
   a->d_c = dims->d_c;
+  a->d_rope = dims->d_rope;
   a->sink_frames = cache->sink_frames;
   a->window_frames = cache->window_frames;
   a->shift_mod_w = (int)(shift % cache->window_frames);
@@ -280,7 +310,7 @@ static int32_t check_d_q(int32_t d_q) {
 
 int32_t vmla_fold_query_weights(const vmla_dims* dims, int32_t dtype, int32_t d_q,
                                 const void* w_uq, const void* w_k_up, void* w_qa, void* stream) {
-  int32_t st = check_dims_192(dims);
+  int32_t st = check_dims_default(dims);
   if (st) return st;
   if (!w_uq || !w_k_up || !w_qa) return VMLA_ERR_NULL;
   if (dtype != VMLA_F32 && dtype != VMLA_BF16) return VMLA_ERR_DTYPE;
@@ -295,7 +325,7 @@ int32_t vmla_fold_query_weights(const vmla_dims* dims, int32_t dtype, int32_t d_
 
 int32_t vmla_fold_output_weights(const vmla_dims* dims, int32_t dtype, const void* w_v_up,
                                  const void* w_o, void* w_vo, void* stream) {
-  int32_t st = check_dims_192(dims);
+  int32_t st = check_dims_default(dims);
   if (st) return st;
   if (!w_v_up || !w_o || !w_vo) return VMLA_ERR_NULL;
   if (dtype != VMLA_F32 && dtype != VMLA_BF16) return VMLA_ERR_DTYPE;
@@ -307,7 +337,7 @@ int32_t vmla_fold_output_weights(const vmla_dims* dims, int32_t dtype, const voi
 }
 
 size_t vmla_layer_workspace_bytes(const vmla_dims* dims, int32_t d_q, int32_t batch, int32_t n_q) {
-  if (check_d_q(d_q) != VMLA_OK || check_dims_192(dims) != VMLA_OK) return 0;
+  if (check_d_q(d_q) != VMLA_OK || check_dims_default(dims) != VMLA_OK) return 0;
   const size_t qhat = vmla_attention_workspace_bytes(dims, batch, n_q);
   if (!qhat) return 0;
   const size_t m = (size_t)batch * n_q;
@@ -326,7 +356,7 @@ int32_t check_layer(const vmla_dims* dims, const vmla_cache* cache, int32_t dtyp
                     uint16_t** inner) {
   int32_t st = check_d_q(d_q);
   if (st) return st;
-  st = check_dims_192(dims);
+  st = check_dims_default(dims);
   if (st) return st;
   st = check_attention(dims, cache, dtype, t_first, n_frames, n_valid_frames, workspace,
                        workspace_bytes, q, a);
@@ -438,6 +468,7 @@ int32_t vmla_pack_kv_weights(const vmla_dims* dims, int32_t dtype, const void* w
   if (!aligned16(w_k_up) || !aligned16(w_v_up) || !aligned16(w_kv)) return VMLA_ERR_ALIGN;
   FoldArgs f{};
   f.w_first = w_k_up; f.w_second = w_v_up; f.out = w_kv; f.n_heads = dims->n_heads;
+  f.d_nope = dims->d_nope;
   return hip_status(launch_pack_kv(f, dtype == VMLA_F32, static_cast<hipStream_t>(stream)));
 }
 
@@ -462,7 +493,7 @@ int32_t run_explicit(const vmla_dims* dims, const vmla_cache* cache, int32_t dty
   GemmArgs g{};
   g.a = x; g.w = w_q; g.out = qbuf;
   g.m = (int64_t)cache->batch * a.n_q; g.k = dims->d_model; g.n = dims->n_heads * kDHead;
-  g.lda = dims->d_model; g.mode = 1; g.head_w = kDHead; g.rope_off = kDNope;
+  g.lda = dims->d_model; g.mode = 1; g.head_w = kDHead; g.rope_off = dims->d_nope;
   g.n_q = q.n_q; g.n_heads = q.n_heads; g.grid_w = q.grid_w; g.tokens_per_frame = q.tokens_per_frame;
   g.t_first = q.t_first; g.inv_grid_w = q.inv_grid_w; g.inv_tokens_per_frame = q.inv_tokens_per_frame;
   g.qscale = q.qscale; g.rope = q.rope;
@@ -472,9 +503,11 @@ int32_t run_explicit(const vmla_dims* dims, const vmla_cache* cache, int32_t dty
   const size_t elem = f32 ? sizeof(float) : sizeof(uint16_t);
   for (int b = 0; b < cache->batch; ++b) {
     GemmArgs r{};
-    r.a = static_cast<const char*>(cache->data) + (size_t)b * a.cache_rows * kRow * elem;
+    const int row = dims->d_c + dims->d_rope;
+    r.a = static_cast<const char*>(cache->data) + (size_t)b * a.cache_rows * row * elem;
     r.w = w_kv; r.out = kvbuf + (size_t)b * dims->n_heads * a.n_k * 2 * kDHead;
-    r.m = a.n_k; r.k = kDC; r.n = dims->n_heads * (kDNope + kDV); r.lda = kRow; r.mode = 2;
+    r.m = a.n_k; r.k = kDC; r.n = dims->n_heads * (dims->d_nope + kDV); r.lda = row; r.mode = 2;
+    r.d_nope = dims->d_nope;
     st = hip_status(launch_gemm(r, f32, 0, s));
     if (st) return st;
   }
@@ -524,7 +557,8 @@ int32_t check_clip(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype
                    QArgs* q, AttnArgs* a) {
   int32_t st = check_dims(dims);
   if (st) return st;
-  st = check_cache(cache, dtype, dims->d_c + kDRope);
+  if (dims->d_rope != kDRope) return VMLA_ERR_SHAPE;        // default split only
+  st = check_cache(cache, dtype, dims->d_c + dims->d_rope);
   if (st) return st;
   if (cache->sink_frames || cache->rope_at_read) return VMLA_ERR_SHAPE;
   if (n_frames < 1 || n_frames > cache->window_frames) return VMLA_ERR_RANGE;
@@ -609,7 +643,7 @@ int32_t vmla_chunk_causal_attention_explicit(const vmla_dims* dims, const vmla_c
 
 int32_t vmla_output_projection(const vmla_dims* dims, int32_t dtype, int64_t m, const void* in,
                                const void* w_o, void* out, void* stream) {
-  int32_t st = check_dims_192(dims);
+  int32_t st = check_dims_default(dims);
   if (st) return st;
   if (!in || !w_o || !out) return VMLA_ERR_NULL;
   if (dtype != VMLA_F32 && dtype != VMLA_BF16) return VMLA_ERR_DTYPE;

@@ -58,7 +58,9 @@ class Run:
         self.step_of_frame = step_of_frame or (lambda t: 0)
         self.wts = weights(w, layer)
         self.dw = dev_weights(w, self.wts, device)
-        self.dims = vm.default_dims(d_model=w.d_model, n_heads=w.n_heads, d_c=w.d_c)
+        self.dims = vm.default_dims(d_model=w.d_model, n_heads=w.n_heads, d_c=w.d_c, d_nope=w.d_nope,
+                                    d_rope=w.d_rope, rope_pairs=w.rope_pairs,
+                                    rope_axis_dims=w.rope_axis_dims)
         self.cache = vm.LatentCache.empty(w.batch, w.window_frames, w.grid_h, w.grid_w,
                                           dtype=tdtype(w), device=device, dims=self.dims, fill=fill,
                                           sink_frames=w.sink_frames, rope_at_read=w.rope_at_read)

@@ -274,6 +274,37 @@ def test_chunk_causal_validation(lib):
     assert xcall(wkv=MIS) == vm.VMLA_ERR_ALIGN
 
 
+def test_split_variant_validation(lib):
+    # NoPE/RoPE split variants: d_rope 16 / 64 / 96 at d_c = 192, bf16, k_R
+    # rotated at append, the attention core and the explicit route only
+    def split(d_rope, **kw):
+        pairs = {16: (3, 3, 2), 64: (12, 10, 10), 96: (18, 15, 15)}[d_rope]
+        f = dict(d_nope=128 - d_rope, d_rope=d_rope, rope_pairs=pairs,
+                 rope_axis_dims=tuple(2 * p for p in pairs))
+        f.update(kw)
+        return vm.default_dims(**f)
+    for dr in (16, 64, 96):
+        d = split(dr)
+        cache = _cache(window_frames=3)
+        assert vm.vmla_attention_workspace_bytes(1, 24, d) == 12 * 24 * (192 + dr) * 2
+        assert _attn(lib, dims=d, cache=cache, ws=None) == vm.VMLA_ERR_WORKSPACE   # valid up to there
+        assert _append(lib, dims=d, x=MIS) == vm.VMLA_ERR_ALIGN                      # valid up to there
+        assert _attn(lib, dims=d, cache=_cache(dtype=vm.VMLA_F32), dtype=vm.VMLA_F32) == vm.VMLA_ERR_DTYPE
+        assert _append(lib, dims=d, cache=_cache(dtype=vm.VMLA_F32), dtype=vm.VMLA_F32) == vm.VMLA_ERR_DTYPE
+        assert _attn(lib, dims=d, cache=_cache(rope_at_read=1)) == vm.VMLA_ERR_SHAPE
+        assert _append(lib, dims=split(dr, d_c=128)) == vm.VMLA_ERR_SHAPE      # splits run at d_c = 192
+        assert vm.vmla_layer_workspace_bytes(1, 24, 768, d) == 0              # default split only
+        assert lib.vmla_fold_query_weights(ctypes.byref(d), vm.VMLA_BF16, 768, A, B, C, None) == vm.VMLA_ERR_SHAPE
+        assert vm.vmla_explicit_workspace_bytes(1, 24, 72, d) > 0              # the explicit route takes splits
+        st = lib.vmla_chunk_causal_attention(ctypes.byref(d), ctypes.byref(_cache(window_frames=7)),
+                                             vm.VMLA_BF16, A, B, C, A, 7, 3, 5, C, B, 1 << 30, None)
+        assert st == vm.VMLA_ERR_SHAPE                                        # default split only
+    # pair counts must sum to d_rope / 2; d_nope + d_rope must be 128; only the listed splits
+    assert _append(lib, dims=split(64, rope_pairs=(6, 5, 5))) == vm.VMLA_ERR_SHAPE
+    assert _append(lib, dims=vm.default_dims(d_nope=80, d_rope=48, rope_pairs=(9, 8, 7))) == vm.VMLA_ERR_SHAPE
+    assert _append(lib, dims=vm.default_dims(d_nope=64, d_rope=32)) == vm.VMLA_ERR_SHAPE
+
+
 def test_binding_cache_geometry():
     import torch
     c = vm.LatentCache(torch.zeros(1, 7 * 24, 224), 6, 4, 6, sink_frames=1, rope_at_read=True)

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle.vmla_oracle as orc
-from workloads import config, custom, weights, x_frame
+from workloads import config, custom, split_variant, weights, x_frame
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 RNG = np.random.default_rng(12345)
@@ -271,6 +271,61 @@ def test_mla_equals_dense_mha_with_composed_weights_real_dims():
         torch.from_numpy(np.stack(Qs))[None], torch.from_numpy(np.stack(Ks))[None],
         torch.from_numpy(np.stack(Vs))[None])[0].permute(1, 0, 2).numpy()
     assert rel(out, ref) < 1e-12
+
+
+def _rope_complex_split(v, pos, pairs, axis_dims, theta=10000.0):
+    """RoPE of a d_rope vector as multiplication of complex pairs by e^{i phi},
+    the frequencies written out from theta^(-2 i / D_a) per axis group."""
+    out = np.empty(len(v), dtype=np.float64)
+    j = 0
+    for ax in range(3):
+        for i in range(pairs[ax]):
+            om = theta ** (-2.0 * i / axis_dims[ax])
+            z = complex(v[2 * j], v[2 * j + 1]) * complex(math.cos(pos[ax] * om), math.sin(pos[ax] * om))
+            out[2 * j], out[2 * j + 1] = z.real, z.imag
+            j += 1
+    assert 2 * j == len(v)
+    return out
+
+
+@pytest.mark.parametrize("d_rope", [16, 64, 96])
+def test_split_variants_equal_dense_mha_with_composed_weights(d_rope):
+    # [PL] App. F NoPE/RoPE split variants at the real widths: the oracle with
+    # the (128 - d_rope) / d_rope split equals a dense MHA whose head h has
+    # W_K,h = W_down W_K_up[h] on its first 128 - d_rope columns and the shared,
+    # rotated k_R on the rest (SDPA from torch, RoPE as complex multiplication).
+    w = split_variant(custom(2, 3, window_frames=2, chunk_frames=1, t_first=1, dtype="f32"), d_rope)
+    wt = weights(w)
+    assert wt["w_kr"].shape == (1536, d_rope) and wt["w_k_up"].shape == (12, 192, 128 - d_rope)
+    xs = {t: x_frame(w, t) for t in range(2)}
+    out = orc.chunk_attention_reference(w, wt, lambda t: xs[t])
+    dn = w.d_nope
+    xk = np.concatenate([xs[0], xs[1]]).astype(np.float64)
+    pk = np.concatenate([orc.frame_positions(t, 2, 3) for t in (0, 1)])
+    xq = xs[1].astype(np.float64)
+    pq = orc.frame_positions(1, 2, 3)
+    rot = lambda a, p: _rope_complex_split(a, p, w.rope_pairs, w.rope_axis_dims)  # noqa: E731
+    krot = np.stack([rot(r, p) for r, p in zip(xk @ wt["w_kr"].astype(np.float64), pk)])
+    Qs, Ks, Vs = [], [], []
+    for h in range(w.n_heads):
+        WK = wt["w_down"].astype(np.float64) @ wt["w_k_up"][h].astype(np.float64)
+        WV = wt["w_down"].astype(np.float64) @ wt["w_v_up"][h].astype(np.float64)
+        qh = xq @ wt["w_q"][:, h * 128:(h + 1) * 128].astype(np.float64)
+        Qs.append(np.concatenate([qh[:, :dn], np.stack([rot(r, p) for r, p in zip(qh[:, dn:], pq)])], 1))
+        Ks.append(np.concatenate([xk @ WK, krot], 1))
+        Vs.append(xk @ WV)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.stack(Qs))[None], torch.from_numpy(np.stack(Ks))[None],
+        torch.from_numpy(np.stack(Vs))[None])[0].permute(1, 0, 2).numpy()
+    assert rel(out, ref) < 1e-12
+
+
+def test_split_rope_allocation():
+    # the variants' t/h/w pair counts sum to d_rope / 2 and keep 6:5:5 (R17)
+    from workloads import SPLIT_ROPE
+    for d_rope, (pairs, dims) in SPLIT_ROPE.items():
+        assert 2 * sum(pairs) == d_rope and tuple(2 * p for p in pairs) == tuple(dims)
+    assert SPLIT_ROPE[32] == ((6, 5, 5), (12, 10, 10))
 
 
 def test_brute_force_scalar_loops_tiny():

@@ -113,3 +113,19 @@ def custom(grid_h: int, grid_w: int, window_frames: int, chunk_frames: int,
     return Workload(cfg_id, name, batch=batch, grid_h=grid_h, grid_w=grid_w,
                     window_frames=window_frames, chunk_frames=chunk_frames,
                     t_first=t_first, dtype=dtype)
+
+
+# NoPE/RoPE split variants of the 128-wide head ([PL] App. F "NoPE/RoPE
+# split"): d_rope = 16, 64 or 96 next to the default 32. The pages give the
+# t/h/w allocation of the default 16 complex pairs only, (6, 5, 5) over axis
+# groups 12/10/10 wide; the variants keep its proportions (t takes 3/8 of the
+# pairs, h the larger half of the rest) with groups twice as wide as their pair
+# counts, so every axis keeps its highest-frequency band.
+SPLIT_ROPE = {16: ((3, 3, 2), (6, 6, 4)), 32: ((6, 5, 5), (12, 10, 10)),
+              64: ((12, 10, 10), (24, 20, 20)), 96: ((18, 15, 15), (36, 30, 30))}
+
+
+def split_variant(w: Workload, d_rope: int) -> Workload:
+    """Workload ``w`` with the NoPE/RoPE split (128 - d_rope) / d_rope."""
+    pairs, dims = SPLIT_ROPE[d_rope]
+    return w.with_(d_nope=128 - d_rope, d_rope=d_rope, rope_pairs=pairs, rope_axis_dims=dims)
