@@ -221,6 +221,9 @@ def main():
     ap.add_argument("--d-c", type=int, default=192, choices=(64, 128, 192),
                     help="content-latent width of the cache (the latent-budget sweep); the "
                          "--layer and --explicit routes run at 192 only")
+    ap.add_argument("--split", type=int, default=32, choices=(16, 32, 64, 96), metavar="D_ROPE",
+                    help="NoPE/RoPE split of the 128-wide head: positional width 16, 32 (the "
+                         "default 96/32), 64 or 96, at d_c = 192")
     ap.add_argument("--chunk-causal", action="store_true",
                     help="the whole-clip form: 21 latent frames, every token a query, 3-frame "
                          "chunks under the chunk-causal block mask")
@@ -255,7 +258,7 @@ def main():
         log(f"[bench] calibration copy: {nbytes} bytes read and {nbytes} bytes written")
         del src, dst
     if args.chunk_causal:
-        if args.config != 2 or args.long_horizon or args.layer or args.d_c != 192:
+        if args.config != 2 or args.long_horizon or args.layer or args.d_c != 192 or args.split != 32:
             print("--chunk-causal runs the Wan-1.3B clip at B=1 (config 2 shapes), with or without "
                   "--explicit", file=sys.stderr)
             sys.exit(2)
@@ -272,8 +275,17 @@ def main():
             print("--d-c applies to the attention core (not --layer / --explicit)", file=sys.stderr)
             sys.exit(2)
         w = w.with_(d_c=args.d_c, name=w.name + f", d_c = {args.d_c}")
+    if args.split != 32:
+        if args.layer or args.long_horizon or args.d_c != 192:
+            print("--split runs the attention core or --explicit at d_c = 192 with k_R rotated at "
+                  "append", file=sys.stderr)
+            sys.exit(2)
+        from workloads import split_variant
+        w = split_variant(w, args.split).with_(
+            name=w.name + f", NoPE/RoPE split {128 - args.split}/{args.split}")
     log(f"[bench] workload: {w.name}")
-    dims = vm.default_dims(d_c=w.d_c)
+    dims = vm.default_dims(d_c=w.d_c, d_nope=w.d_nope, d_rope=w.d_rope, rope_pairs=w.rope_pairs,
+                           rope_axis_dims=w.rope_axis_dims)
     xs = None
     if args.config == 2:
         # seeded host inputs, the same as the parity tests use
@@ -461,6 +473,9 @@ def main():
                                         "plus a 6-frame window, RoPE applied at read time")
     if args.d_c != 192:
         result["config"]["workload"] += f"; content latent d_c = {args.d_c} (latent-budget sweep)"
+    if args.split != 32:
+        result["config"]["workload"] += (f"; NoPE/RoPE split {128 - args.split}/{args.split}, "
+                                         f"rope pairs {tuple(w.rope_pairs)}")
     if args.explicit:
         result["config"]["workload"] += ("; explicit route: per-head K/V rebuilt from the latent "
                                          "cache each step (201 MB at B=1), then 128-dim attention")

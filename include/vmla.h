@@ -24,13 +24,20 @@
  *  - Errors: every argument is validated on the host before any HIP call; a
  *    negative vmla_status is returned and nothing is launched. A failed launch
  *    returns VMLA_ERR_HIP. No exception or abort crosses the ABI.
- *  - Supported geometry in this version: d_nope = 96, d_rope = 32, d_v = 128
- *    (the defaults of [PL] App. D.2-D.3), rope_pairs summing to d_rope / 2,
- *    d_model a multiple of 64, 1 <= n_heads <= 64; d_c = 192 (the default),
- *    or 64 / 128 for vmla_cache_append, vmla_chunk_attention and its two
- *    stages (the latent-budget sweep of [PL] §4 "Batch Scaling Under Fixed
- *    Memory" and App. F "Latent dimension"). The whole-layer, explicit and
- *    weight-fold entry points take d_c = 192 only.
+ *  - Supported geometry in this version: d_v = 128, d_model a multiple of 64,
+ *    1 <= n_heads <= 64, rope_pairs summing to d_rope / 2 (at most 48 pairs);
+ *    d_nope / d_rope = 96 / 32 (the default of [PL] App. D.2-D.3) with d_c =
+ *    192 (the default), or 64 / 128 for vmla_cache_append,
+ *    vmla_chunk_attention and its two stages (the latent-budget sweep of [PL]
+ *    §4 "Batch Scaling Under Fixed Memory" and App. F "Latent dimension").
+ *    The NoPE/RoPE split variants d_nope / d_rope = 112 / 16, 64 / 64 and
+ *    32 / 96 ([PL] App. F "NoPE/RoPE split") are accepted at d_c = 192 by the
+ *    same three entry points and by vmla_pack_kv_weights /
+ *    vmla_chunk_attention_explicit, with VMLA_BF16 storage and a cache with
+ *    rope_at_read = 0 and no sink frame (VMLA_ERR_DTYPE / VMLA_ERR_SHAPE
+ *    otherwise); cache and Qhat rows are then d_c + d_rope wide. The
+ *    whole-layer, weight-fold and chunk-causal entry points take d_c = 192 and
+ *    the default split only.
  *
  * Token and position convention: token n of a latent frame sits at grid
  * position (h, w) = (n / grid_w, n % grid_w); t is the absolute latent-frame
@@ -49,7 +56,7 @@
 extern "C" {
 #endif
 
-#define VMLA_ABI_VERSION 5
+#define VMLA_ABI_VERSION 6
 
 typedef enum vmla_status {
   VMLA_OK = 0,
