@@ -218,7 +218,7 @@ def main():
     ap.add_argument("--explicit", action="store_true",
                     help="the explicit-reconstruction route instead of the latent form: per-head "
                          "K/V rebuilt from the cache each step, then 128-dim attention")
-    ap.add_argument("--d-c", type=int, default=192, choices=(64, 128, 192),
+    ap.add_argument("--d-c", type=int, default=192, choices=(64, 128, 192, 256, 512),
                     help="content-latent width of the cache (the latent-budget sweep); the "
                          "--layer and --explicit routes run at 192 only")
     ap.add_argument("--split", type=int, default=32, choices=(16, 32, 64, 96), metavar="D_ROPE",

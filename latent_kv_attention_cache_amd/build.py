@@ -21,11 +21,11 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["vmla_api.cpp", "append.hip", "qprologue.hip", "latent_attn.hip", "mixer_gemm.hip",
-           "explicit_attn.hip"]
+SOURCES = ["vmla_api.cpp", "append.hip", "qprologue.hip", "latent_attn.hip", "latent_attn_wide.hip",
+           "mixer_gemm.hip", "explicit_attn.hip"]
 # Per-source extra flags. The attention kernel never reads NaNs (slots past the
 # valid prefix are not loaded), so max() needs no NaN canonicalization.
-EXTRA_FLAGS = {"latent_attn.hip": ["-fno-honor-nans"]}
+EXTRA_FLAGS = {"latent_attn.hip": ["-fno-honor-nans"], "latent_attn_wide.hip": ["-fno-honor-nans"]}
 # The matrix-core peak probe (the measured roofline reference of bench.py) is
 # its own library, outside the C ABI of libvmla.so.
 PROBE_SOURCE = "peak_probe.hip"
@@ -54,7 +54,7 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP/C++ source, link ``libvmla.so`` and the peak-probe
     library ``libvmla_probe.so``; returns the path of ``libvmla.so``."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(7, len(SOURCES) + 1)) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + [PROBE_SOURCE]))
     _link(objs[:-1], LIB_PATH, verbose)
     _link(objs[-1:], PROBE_PATH, verbose)

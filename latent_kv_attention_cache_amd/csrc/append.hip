@@ -408,6 +408,16 @@ void launch_dc(const AppendArgs& a, int groups, int nrb, hipStream_t s) {
   switch (a.d_c) {
     case 64: launch_t<T, 64, kDRope>(a, groups, nrb, s); break;
     case 128: launch_t<T, 128, kDRope>(a, groups, nrb, s); break;
+    case 256:                                 // wide latents: bf16 storage only
+      if constexpr (std::is_same_v<T, bf16_t>) launch_t<T, 256, kDRope>(a, groups, nrb, s);
+      break;
+    case 512:                                 // at most 2 row blocks per wave (64-row ranges)
+      if constexpr (std::is_same_v<T, bf16_t>) {
+        const dim3 grid(groups), block(kThreads);
+        if (nrb == 2) hipLaunchKernelGGL((append_kernel<T, 2, 512, kDRope>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((append_kernel<T, 1, 512, kDRope>), grid, block, 0, s, a);
+      }
+      break;
     default: launch_t<T, kDC, kDRope>(a, groups, nrb, s); break;
   }
 }
@@ -419,8 +429,8 @@ void launch_dc(const AppendArgs& a, int groups, int nrb, hipStream_t s) {
 // workgroups, in rounds, beyond that), but no range below 32 rows, since each
 // workgroup streams the whole weight. A range of r rows is 16-row blocks split
 // over the two row halves: ceil(ceil(r / 16) / 2) blocks per wave.
-int append_plan(int64_t m, int cus, int* nrb) {
-  const int64_t lo = (m + kMaxRows - 1) / kMaxRows;
+int append_plan(int64_t m, int cus, int max_rows, int* nrb) {
+  const int64_t lo = (m + max_rows - 1) / max_rows;
   const int64_t groups = std::max<int64_t>(lo, std::min<int64_t>(cus, (m + 31) / 32));
   const int64_t rows = (m + groups - 1) / groups;
   *nrb = (int)(((rows + 15) / 16 + 1) / 2);
@@ -434,8 +444,11 @@ hipError_t launch_append(const AppendArgs& a, bool f32, hipStream_t s) {
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   int nrb = 1;
-  const int groups = append_plan((int64_t)a.batch * a.n_tok, cus > 0 ? cus : 1, &nrb);
+  // d_c = 512: row ranges of at most 64 rows, so two 64-deep stages fit the LDS
+  const int max_rows = a.d_c == 512 ? 64 : kMaxRows;
+  const int groups = append_plan((int64_t)a.batch * a.n_tok, cus > 0 ? cus : 1, max_rows, &nrb);
   if (a.d_rope != kDRope && (f32 || a.d_c != kDC)) return hipErrorInvalidValue;   // not instantiated
+  if ((a.d_c == 256 || a.d_c == 512) && f32) return hipErrorInvalidValue;
   if (f32) launch_dc<float>(a, groups, nrb, s);
   else launch_dc<bf16_t>(a, groups, nrb, s);
   return hipGetLastError();

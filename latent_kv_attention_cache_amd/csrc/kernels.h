@@ -47,7 +47,7 @@ struct AppendArgs {
   float inv_grid_w, inv_tokens_per_frame, inv_window_frames;   // 1/x as float
   int sink_frames;      // 0 or 1: frame 0 kept in slots [0, T)
   int rope_at_read;     // 1: k_R stored unrotated
-  int d_c;              // content width: 64, 128 or kDC (cache rows are d_c + d_rope wide)
+  int d_c;              // content width: 64, 128, kDC, 256 or 512 (rows are d_c + d_rope wide)
   int d_rope;           // positional width: kDRope, or 16 / 64 / 96 (split variants, d_c = kDC)
   RopeTable rope;
 };
@@ -124,9 +124,10 @@ struct FoldArgs {
 };
 
 hipError_t launch_append(const AppendArgs& a, bool f32, hipStream_t s);
-int append_plan(int64_t m, int cus, int* nrb);   // append workgroups for m rows; row blocks per wave
+int append_plan(int64_t m, int cus, int max_rows, int* nrb);   // append workgroups; row blocks per wave
 hipError_t launch_qprologue(const QArgs& a, bool f32, hipStream_t s);
 hipError_t launch_latent_attn(const AttnArgs& a, bool f32, hipStream_t s);
+hipError_t launch_latent_attn_wide(const AttnArgs& a, hipStream_t s);   // d_c 256 / 512, bf16
 hipError_t launch_gemm(const GemmArgs& a, int a_f32, int out_f32, hipStream_t s);
 hipError_t launch_fold_query(const FoldArgs& a, bool f32, hipStream_t s);
 hipError_t launch_fold_output(const FoldArgs& a, bool f32, hipStream_t s);

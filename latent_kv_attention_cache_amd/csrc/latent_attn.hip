@@ -499,6 +499,12 @@ hipError_t launch_split(const AttnArgs& a, bool f32, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_latent_attn(const AttnArgs& a, bool f32, hipStream_t s) {
+  if (a.d_c == 256 || a.d_c == 512) {
+    // wide latents: bf16, one query chunk, k_R rotated at append, W_V_up epilogue
+    if (f32 || a.cm.n_chunks != 1 || a.rope_at_read || a.olat || a.d_rope != kDRope)
+      return hipErrorInvalidValue;
+    return launch_latent_attn_wide(a, s);
+  }
   if (a.d_rope != kDRope) {
     // split variants: d_c = kDC, one query chunk, k_R rotated at append, W_V_up epilogue
     if (a.d_c != kDC || a.cm.n_chunks != 1 || a.rope_at_read || a.olat) return hipErrorInvalidValue;

@@ -1,0 +1,317 @@
+// Latent-form chunk attention for wide content latents (d_c = 256, 512) on
+// gfx950.
+//
+// VideoMLA (paperlayer.ai summary of arXiv:2605.30351v1): the latent widths of
+// the batch-scaling measurement (§4 "Batch Scaling Under Fixed Memory", d_c up
+// to 512) and the latent-dimension ablation (App. F). The math is the one of
+// latent_attn_kernel (App. E "Inference-Time Reparameterization"): scores of the
+// absorbed queries Qhat_h = [q_lat | q_rope] against the cached rows [c | k_R],
+// online softmax, O_lat += P c, out = (O_lat / l) W_V_up[h].
+//
+// Why a second kernel. Per wave of 32 queries the O^T accumulators take d_c x 32
+// fp32 (128 or 256 registers per lane) and the Qhat fragments d_c + 32 bf16
+// (72 or 136): more than the 256 registers of a wave when two waves share a
+// SIMD. Here a workgroup is four waves, one per SIMD, each with the SIMD's
+// whole register file (the O^T accumulators live in the accumulation
+// registers). Without a partner wave there is no ping-pong: a wave runs the
+// scores, the softmax and P.C of a tile in turn, while the next tile streams
+// into the second LDS buffer.
+//
+// Work split. Units of 32 queries of one head, numbered head-major with the
+// units of a head padded to a multiple of the units per workgroup, so that a
+// workgroup's units belong to one head (its W_V_up[h] is staged once for the
+// epilogue). At d_c = 256 each of the four waves takes one unit. At d_c = 512
+// the whole O^T (256 registers) and Qhat (136) still do not fit one wave
+// without spills, so two waves share a unit: both compute the same scores
+// and softmax (identical instruction streams, so identical m and l), and each
+// accumulates one half of the latent dimensions (128 accumulation registers);
+// the two halves of (O / l) W_V_up[h] are summed through LDS in the epilogue.
+// That doubles the score MFMAs (200 instead of 132 per unit and tile).
+//
+// Tile. 64 keys, chunk-major and padded in LDS as in latent_attn_kernel (chunk
+// c of key row r at slot c * 68 + r), copied by 16-byte LDS-DMA loads that all
+// four waves share; two buffers (78 KB at d_c = 256, 148 KB at 512).
+//
+// Per tile, per wave: S^T = K Qhat^T (2 x (d_c + 32) / 16 MFMAs 32x32x16),
+// softmax of its 64 keys with the lazy reference max, P^T packed to bf16 in
+// place, O^T += C^T P^T (d_c / 32 x 4 MFMAs) with C^T read by the LDS
+// transpose read. One barrier per tile.
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace vmla {
+namespace {
+
+constexpr int kKT = 64;                     // keys per tile
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSlots = kKT + 4;             // slots per chunk column (padded)
+constexpr int kVLd = kDV + 8;               // padded LDS row of W_V_up[h] (epilogue)
+constexpr float kLazy = 8.f;                // lazy-rescale threshold (log2 units)
+// Scheduling-group masks (instruction classes of sched_group_barrier).
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+template <int DC>
+struct WideShape {
+  static constexpr bool kPair = DC > 256;                  // two waves per unit (latent halves)
+  static constexpr int kUnitsWG = kPair ? kWaves / 2 : kWaves;
+  static constexpr int kRow = DC + kDRope;
+  static constexpr int kChunks = kRow / 8;                 // 36 / 68
+  static constexpr int kTileElems = kChunks * kSlots * 8;
+  static constexpr int kLoadsPerWave = kChunks / kWaves;   // 9 / 17
+  static constexpr int kFeatSteps = kRow / 16;             // 18 / 34
+  static constexpr int kLatTiles = DC / 32;                // 8 / 16
+  static constexpr int kOTiles = kPair ? kLatTiles / 2 : kLatTiles;   // latent tiles of one wave
+  static_assert(kChunks % kWaves == 0, "tile loads split evenly over the four waves");
+  static_assert(!kPair || (DC / 2) * kVLd * 2 + kUnitsWG * (kDV / 32) * 16 * 64 * 4 <= 2 * kTileElems * 2,
+                "epilogue staging of one W_V_up half and the partial outputs fits the tile buffers");
+  static_assert(2 * kTileElems * 2 <= 160 * 1024, "two tile buffers in LDS");
+  static_assert((kPair ? DC / 2 : DC) * kVLd <= 2 * kTileElems, "staged W_V_up rows fit the tile buffers");
+};
+
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory");
+}
+
+template <int DC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void latent_attn_wide_kernel(AttnArgs a) {
+  using Sh = WideShape<DC>;
+  constexpr int kRow = Sh::kRow;
+  constexpr int kTileElems = Sh::kTileElems;
+  constexpr int kFeatSteps = Sh::kFeatSteps;
+  constexpr int kOTiles = Sh::kOTiles;
+  constexpr int kUnitsWG = Sh::kUnitsWG;
+  __shared__ __attribute__((aligned(16))) bf16_t kt[2 * kTileElems];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int qi = lane & 31;
+  const int b = blockIdx.z;
+  const int unit = Sh::kPair ? wave >> 1 : wave;             // unit of this wave in the workgroup
+  const int lat_half = Sh::kPair ? wave & 1 : 0;             // latent half of this wave (d_c 512)
+  const int units = (a.n_q + 31) / 32;
+  const int upad = (units + kUnitsWG - 1) / kUnitsWG * kUnitsWG;   // units per head, padded
+  const int h = (blockIdx.x * kUnitsWG) / upad;              // one head per workgroup
+  const int qb = blockIdx.x * kUnitsWG - h * upad + unit;
+  const int qrow = 32 * qb + qi;
+  const bool live = qb < units;                              // wave-uniform
+  const bool qvalid = live && qrow < a.n_q;
+
+  // Qhat fragments (B operand of S^T): lane holds features 16 ks + 8 half .. +7 of its query.
+  bf16x8 qf[kFeatSteps];
+  {
+    const bf16_t* qp = a.qhat + (((size_t)b * a.n_heads + h) * a.n_q + (qvalid ? qrow : a.n_q - 1)) * kRow;
+#pragma unroll
+    for (int ks = 0; ks < kFeatSteps; ++ks)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + 8 * half);
+#pragma unroll
+    for (int ks = 0; ks < kFeatSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
+  }
+
+  const bf16_t* cache = static_cast<const bf16_t*>(a.cache) + (size_t)b * a.cache_rows * kRow;
+  const int nk = a.n_k;
+  const int ntiles = (nk + kKT - 1) / kKT;
+  const uint32_t kt_lds = (uint32_t)(uintptr_t)(VMLA_LDS bf16_t*)kt;
+  // Wave-wide load n moves chunk column n of tile j: lane r reads features
+  // 8n .. 8n+7 of key 64 j + r (clamped to the last key; masked scores).
+  auto issue_tile = [&](int j) {
+    const int kg = min(j * kKT + lane, nk - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+    for (int i = 0; i < Sh::kLoadsPerWave; ++i) {
+      const int n = wv + kWaves * i;
+      dma16(cache, (uint32_t)(kg * (kRow * 2)) + (uint32_t)(16 * n),
+            kt_lds + 2u * (uint32_t)((j & 1) * kTileElems + n * kSlots * 8));
+    }
+  };
+
+  const int a_base = (half * kSlots + qi) * 8;
+  const int jl = lane & 15;
+  const int x4 = ((lane & 16) >> 3) + ((jl & 3) >> 1);
+  const int sub = 4 * (jl & 1);
+  const int v_off1 = (x4 * kSlots + 4 * half + (jl >> 2)) * 8 + sub;
+  const int v_off2 = v_off1 + 8 * 8;
+
+  f32x16 o[kOTiles];                     // this wave's latent tiles: kOTiles lat_half + t
+#pragma unroll
+  for (int t = 0; t < kOTiles; ++t) o[t] = f32x16{};
+  float m = -INFINITY;
+  float l = 0.f;
+
+  issue_tile(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int jt = 0; jt < ntiles; ++jt) {
+    if (jt + 1 < ntiles) issue_tile(jt + 1);     // into the buffer read in tile jt - 1
+    const bf16_t* K = kt + (jt & 1) * kTileElems;
+    if (live) {
+      // S^T of the tile: register r of key block kb holds key 32 kb + 8(r/4) + 4 half + r%4
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < kFeatSteps; ++ks) {
+        const int off = a_base + 2 * kSlots * 8 * ks;
+        s0 = mfma32(lds_row8(K + off), qf[ks], s0);
+        s1 = mfma32(lds_row8(K + off + 32 * 8), qf[ks], s1);
+      }
+      // operand reads run two steps ahead of the MFMAs, no further (register budget)
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+      for (int i = 0; i < kFeatSteps - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+      const int key0 = jt * kKT;
+      if (key0 + kKT > nk) {
+        const int lim = nk - key0 - 4 * half;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int k = 8 * (r >> 2) + (r & 3);
+          if (k >= lim) s0[r] = -INFINITY;
+          if (k + 32 >= lim) s1[r] = -INFINITY;
+        }
+      }
+      float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+      mx = max_across_halves(mx);
+      const bool grow = mx > m + kLazy;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int t = 0; t < kOTiles; ++t) o[t] *= alpha;
+        m = m_new;
+      }
+      float ls = 0.f;
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] = __builtin_amdgcn_exp2f(s0[r] - m);
+        s1[r] = __builtin_amdgcn_exp2f(s1[r] - m);
+        ls += s0[r] + s1[r];
+      }
+      l += ls;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pb[0][jj][e] = (__bf16)s0[8 * jj + e];
+          pb[1][jj][e] = (__bf16)s1[8 * jj + e];
+        }
+      // O^T += C^T(tile) P^T
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const bf16_t* Kb = K + (kb * 32 + jj * 16) * 8;
+#pragma unroll
+          for (int t = 0; t < kOTiles; ++t) {
+            const int ct = 4 * kSlots * 8 * (t + kOTiles * lat_half);
+            const bf16x4 lo = lds_tr4(Kb + v_off1 + ct);
+            const bf16x4 hi = lds_tr4(Kb + v_off2 + ct);
+            o[t] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb[kb][jj], o[t]);
+          }
+        }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
+#pragma unroll
+      for (int i = 0; i < 4 * kOTiles - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 1);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of tile jt + 1
+    __syncthreads();                                    // tile jt + 1 complete, buffer jt free
+  }
+
+  // ---- epilogue: out = (O / l) @ W_V_up[h]. The W_V_up[h] rows of a latent
+  // half, [DC / 2][kVLd] (or all DC rows), are staged in LDS; with two waves
+  // per unit the half-0 wave leaves its partial product in LDS (fp32) and the
+  // half-1 wave adds it before the store.
+  const float inv = 1.f / sum_across_halves(l);
+  bf16x8 ob[kOTiles][2];
+#pragma unroll
+  for (int t = 0; t < kOTiles; ++t)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ob[t][jj][e] = (__bf16)(o[t][8 * jj + e] * inv);
+  bf16_t* out = static_cast<bf16_t*>(a.out) + (((size_t)b * a.n_q + (qvalid ? qrow : 0)) * a.n_heads + h) * kDV;
+  constexpr int kStageRows = kOTiles * 32;                   // W_V_up rows staged per phase
+  constexpr int kPhases = Sh::kPair ? 2 : 1;
+  float* xch = reinterpret_cast<float*>(kt + kStageRows * kVLd);   // [unit][et][r][lane] partials
+  const bf16_t* wsrc = static_cast<const bf16_t*>(a.w_v_up) + (size_t)h * DC * kDV;
+  for (int ph = 0; ph < kPhases; ++ph) {
+    for (int c = tid; c < kStageRows * kDV / 8; c += kThreads) {
+      const int row = c / (kDV / 8), cc = c % (kDV / 8);
+      *reinterpret_cast<uint4*>(&kt[row * kVLd + 8 * cc]) =
+          *reinterpret_cast<const uint4*>(wsrc + ((size_t)ph * kStageRows + row) * kDV + 8 * cc);
+    }
+    __syncthreads();
+    if (live && lat_half == ph) {
+#pragma unroll
+      for (int et = 0; et < kDV / 32; ++et) {
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int t = 0; t < kOTiles; ++t)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int dbase = 32 * t + 16 * jj;
+            acc = mfma32(lds_tr8(kt, kVLd, dbase + 4 * half, dbase + 8 + 4 * half, 32 * et, lane), ob[t][jj], acc);
+          }
+        float* xp = xch + ((unit * (kDV / 32) + et) * 16) * 64 + lane;
+        if (ph + 1 < kPhases) {                              // half 0 of a pair: leave the partial
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xp[64 * r] = acc[r];
+          continue;
+        }
+        if constexpr (Sh::kPair) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] += xp[64 * r];
+        }
+        if (qvalid) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int e0 = 32 * et + 8 * g + 4 * half;
+            *reinterpret_cast<uint2*>(out + e0) =
+                uint2{pack2(acc[4 * g], acc[4 * g + 1]), pack2(acc[4 * g + 2], acc[4 * g + 3])};
+          }
+        }
+      }
+    }
+    __syncthreads();                                         // staging area and partials reused
+  }
+}
+
+template <int DC>
+hipError_t launch_wide_dc(const AttnArgs& a, hipStream_t s) {
+  constexpr int kU = WideShape<DC>::kUnitsWG;
+  const int units = (a.n_q + 31) / 32;
+  const int upad = (units + kU - 1) / kU * kU;
+  const dim3 grid((unsigned)(a.n_heads * upad / kU), 1, (unsigned)a.batch);
+  hipLaunchKernelGGL(latent_attn_wide_kernel<DC>, grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// bf16 cache, one query chunk, k_R rotated at append, W_V_up epilogue, the
+// default 96/32 split (validated by the host layer).
+hipError_t launch_latent_attn_wide(const AttnArgs& a, hipStream_t s) {
+  switch (a.d_c) {
+    case 256: return launch_wide_dc<256>(a, s);
+    case 512: return launch_wide_dc<512>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace vmla

@@ -338,6 +338,12 @@ hipError_t launch_qprologue(const QArgs& a, bool f32, hipStream_t s) {
   switch (a.d_c) {
     case 64: launch_t<64, kDNope>(a, f32, grid, s); break;
     case 128: launch_t<128, kDNope>(a, f32, grid, s); break;
+    case 256:
+    case 512:                                 // wide latents: bf16 storage only
+      if (f32) return hipErrorInvalidValue;
+      if (a.d_c == 256) hipLaunchKernelGGL((qprologue_kernel<bf16_t, 256, kDNope>), grid, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((qprologue_kernel<bf16_t, 512, kDNope>), grid, dim3(kThreads), 0, s, a);
+      break;
     default: launch_t<kDC, kDNope>(a, f32, grid, s); break;
   }
   return hipGetLastError();

@@ -29,9 +29,10 @@ bool split_ok(const vmla_dims* d) {
 int32_t check_dims(const vmla_dims* d) {
   if (!d) return VMLA_ERR_NULL;
   if (!split_ok(d) || d->d_v != kDV) return VMLA_ERR_SHAPE;
-  // content width: the default 192, or 64 / 128 (latent-budget sweep) for the
-  // append and the attention core; the split variants run at 192
-  if (d->d_c != kDC && d->d_c != 64 && d->d_c != 128) return VMLA_ERR_SHAPE;
+  // content width: the default 192, or 64 / 128 / 256 / 512 (latent-budget
+  // sweep) for the append and the attention core; the split variants run at 192
+  if (d->d_c != kDC && d->d_c != 64 && d->d_c != 128 && d->d_c != 256 && d->d_c != 512)
+    return VMLA_ERR_SHAPE;
   if (d->d_rope != kDRope && d->d_c != kDC) return VMLA_ERR_SHAPE;
   if (d->d_model < 64 || d->d_model % 64 != 0 || d->d_model > (1 << 16)) return VMLA_ERR_SHAPE;
   if (d->n_heads < 1 || d->n_heads > 64) return VMLA_ERR_SHAPE;
@@ -60,9 +61,10 @@ int32_t check_dims_default(const vmla_dims* d) {
   return d->d_rope == kDRope ? VMLA_OK : VMLA_ERR_SHAPE;
 }
 
-// The split variants store bf16 and use neither read-time RoPE nor a sink.
+// The split variants and the wide latents (d_c 256, 512) store bf16 and use
+// neither read-time RoPE nor a sink.
 int32_t check_split_cache(const vmla_dims* d, const vmla_cache* c, int32_t dtype) {
-  if (d->d_rope == kDRope) return VMLA_OK;
+  if (d->d_rope == kDRope && d->d_c <= kDC) return VMLA_OK;
   if (dtype != VMLA_BF16) return VMLA_ERR_DTYPE;
   return c->rope_at_read || c->sink_frames ? VMLA_ERR_SHAPE : VMLA_OK;
 }
@@ -557,7 +559,7 @@ int32_t check_clip(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype
                    QArgs* q, AttnArgs* a) {
   int32_t st = check_dims(dims);
   if (st) return st;
-  if (dims->d_rope != kDRope) return VMLA_ERR_SHAPE;        // default split only
+  if (dims->d_rope != kDRope || dims->d_c > kDC) return VMLA_ERR_SHAPE;   // default split, d_c <= 192
   st = check_cache(cache, dtype, dims->d_c + dims->d_rope);
   if (st) return st;
   if (cache->sink_frames || cache->rope_at_read) return VMLA_ERR_SHAPE;

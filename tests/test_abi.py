@@ -98,8 +98,8 @@ def test_append_validation(lib):
     assert _append(lib, cache=_cache(data=MIS)) == vm.VMLA_ERR_ALIGN
     assert _append(lib, dtype=7) == vm.VMLA_ERR_DTYPE
     assert _append(lib, dtype=vm.VMLA_F32) == vm.VMLA_ERR_DTYPE          # cache is bf16
-    assert _append(lib, dims=vm.default_dims(d_c=96)) == vm.VMLA_ERR_SHAPE   # not 64, 128 or 192
-    assert _append(lib, dims=vm.default_dims(d_c=256)) == vm.VMLA_ERR_SHAPE
+    assert _append(lib, dims=vm.default_dims(d_c=96)) == vm.VMLA_ERR_SHAPE   # not 64 / 128 / 192 / 256 / 512
+    assert _append(lib, dims=vm.default_dims(d_c=384)) == vm.VMLA_ERR_SHAPE
     assert _append(lib, dims=vm.default_dims(d_model=100)) == vm.VMLA_ERR_SHAPE
     assert _append(lib, dims=vm.default_dims(rope_pairs=(6, 5, 4))) == vm.VMLA_ERR_SHAPE
     assert _append(lib, dims=vm.default_dims(n_heads=0)) == vm.VMLA_ERR_SHAPE
@@ -303,6 +303,24 @@ def test_split_variant_validation(lib):
     assert _append(lib, dims=split(64, rope_pairs=(6, 5, 5))) == vm.VMLA_ERR_SHAPE
     assert _append(lib, dims=vm.default_dims(d_nope=80, d_rope=48, rope_pairs=(9, 8, 7))) == vm.VMLA_ERR_SHAPE
     assert _append(lib, dims=vm.default_dims(d_nope=64, d_rope=32)) == vm.VMLA_ERR_SHAPE
+
+
+def test_wide_latent_validation(lib):
+    # d_c = 256 / 512 (the wide-latent kernel): bf16, k_R rotated at append,
+    # the append and the attention core only
+    for dc in (256, 512):
+        d = vm.default_dims(d_c=dc)
+        assert vm.vmla_attention_workspace_bytes(1, 24, d) == 12 * 24 * (dc + 32) * 2
+        assert _attn(lib, dims=d, ws=None) == vm.VMLA_ERR_WORKSPACE              # valid up to there
+        assert _append(lib, dims=d, x=MIS) == vm.VMLA_ERR_ALIGN                   # valid up to there
+        assert _attn(lib, dims=d, cache=_cache(dtype=vm.VMLA_F32), dtype=vm.VMLA_F32) == vm.VMLA_ERR_DTYPE
+        assert _append(lib, dims=d, cache=_cache(dtype=vm.VMLA_F32), dtype=vm.VMLA_F32) == vm.VMLA_ERR_DTYPE
+        assert _attn(lib, dims=d, cache=_cache(rope_at_read=1)) == vm.VMLA_ERR_SHAPE
+        assert vm.vmla_explicit_workspace_bytes(1, 24, 72, d) == 0
+        assert vm.vmla_layer_workspace_bytes(1, 24, 768, d) == 0
+        st = lib.vmla_chunk_causal_attention(ctypes.byref(d), ctypes.byref(_cache(window_frames=7)),
+                                             vm.VMLA_BF16, A, B, C, A, 7, 3, 5, C, B, 1 << 30, None)
+        assert st == vm.VMLA_ERR_SHAPE
 
 
 def test_binding_cache_geometry():

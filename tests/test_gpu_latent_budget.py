@@ -1,5 +1,6 @@
 """GPU parity of the append and the attention core at other content widths:
-d_c = 64 and 128 next to the default 192 (the latent-budget sweep, [PL] §4
+d_c = 64, 128, 256 and 512 next to the default 192 (256 and 512 run the
+wide-latent attention kernel, one wave per SIMD) (the latent-budget sweep, [PL] §4
 "Batch Scaling Under Fixed Memory" over d_c in {64, 128, 192, 256, 512} and
 App. F "Latent dimension"). The oracle is the same, dims-generic CPU fp64
 reference; same acceptance bar (relative Frobenius <= 1e-2, max abs <= 3e-2).
@@ -82,3 +83,48 @@ def test_wan_shape_sampled_rows(d_c):
                                     rng.choice(w.n_q, 40, replace=False)]))
     compare(out[0, idx], r.reference(query_tokens=idx), f"d_c={d_c} config 2 sampled", per_head_axis=1)
     compare(r.cache_rows(18, 3), r.append_reference(18, 3), f"d_c={d_c} config 2 cache rows")
+
+
+@pytest.mark.parametrize("d_c", [256, 512])
+def test_wide_small_full_with_nan_ring(d_c):
+    # 4x6 grid, 2-frame chunk at t = 3 after a wrap, B = 2, NaN-filled ring
+    print(f"[case] wide d_c={d_c} small", flush=True)
+    w = custom(4, 6, window_frames=3, chunk_frames=2, t_first=3, batch=2).with_(d_c=d_c)
+    r = Run(w, fill=float("nan"))
+    out = _np(r.chunk_step())
+    for b in range(2):
+        compare(out[b], r.reference(b=b), f"d_c={d_c} 4x6 b={b}", per_head_axis=1)
+        compare(r.cache_rows(3, 2, b=b), r.append_reference(3, 2, b=b), f"d_c={d_c} cache rows b={b}")
+
+
+@pytest.mark.parametrize("d_c", [256, 512])
+def test_wide_ragged_odd_heads(d_c):
+    # 7x9 grid: 126 queries (a partial unit, 4 units padded per head), 252
+    # keys (a ragged last tile), 5 heads
+    print(f"[case] wide d_c={d_c} ragged", flush=True)
+    w = custom(7, 9, window_frames=4, chunk_frames=2, t_first=5).with_(d_c=d_c, n_heads=5)
+    r = Run(w)
+    out = _np(r.chunk_step())
+    compare(out[0], r.reference(), f"d_c={d_c} ragged 5 heads", per_head_axis=1)
+
+
+@pytest.mark.parametrize("d_c,n_rows", [(256, 160), (256, 4680), (512, 64), (512, 4680)])
+def test_wide_append_tile_heights(d_c, n_rows):
+    # 160-row ranges (5 blocks per wave) at 256; 64-row ranges (2 blocks) at 512
+    print(f"[case] wide d_c={d_c} append {n_rows}", flush=True)
+    w = custom(1, n_rows, window_frames=2, chunk_frames=1, t_first=0).with_(d_c=d_c)
+    r = Run(w)
+    r.append(0, 1)
+    compare(r.cache_rows(0, 1), r.append_reference(0, 1), f"d_c={d_c} append {n_rows} rows")
+
+
+@pytest.mark.parametrize("d_c", [256, 512])
+def test_wide_wan_shape_sampled_rows(d_c):
+    print(f"[case] wide d_c={d_c} Wan shape", flush=True)
+    w = config(2).with_(d_c=d_c)
+    r = Run(w)
+    out = _np(r.chunk_step())
+    rng = np.random.default_rng(d_c)
+    idx = np.unique(np.concatenate([[0, 127, 128, w.n_q - 1], rng.choice(w.n_q, 28, replace=False)]))
+    compare(out[0, idx], r.reference(query_tokens=idx), f"d_c={d_c} Wan sampled", per_head_axis=1)
+    compare(r.cache_rows(18, 3), r.append_reference(18, 3), f"d_c={d_c} Wan chunk rows")
