@@ -27,9 +27,11 @@
  *  - Supported geometry in this version: d_v = 128, d_model a multiple of 64,
  *    1 <= n_heads <= 64, rope_pairs summing to d_rope / 2 (at most 48 pairs);
  *    d_nope / d_rope = 96 / 32 (the default of [PL] App. D.2-D.3) with d_c =
- *    192 (the default), or 64 / 128 for vmla_cache_append,
+ *    192 (the default), or 64 / 128 / 256 / 512 for vmla_cache_append,
  *    vmla_chunk_attention and its two stages (the latent-budget sweep of [PL]
- *    §4 "Batch Scaling Under Fixed Memory" and App. F "Latent dimension").
+ *    §4 "Batch Scaling Under Fixed Memory" and App. F "Latent dimension");
+ *    d_c = 256 and 512 take VMLA_BF16 storage and a cache with rope_at_read =
+ *    0 and no sink frame.
  *    The NoPE/RoPE split variants d_nope / d_rope = 112 / 16, 64 / 64 and
  *    32 / 96 ([PL] App. F "NoPE/RoPE split") are accepted at d_c = 192 by the
  *    same three entry points and by vmla_pack_kv_weights /
@@ -56,7 +58,7 @@
 extern "C" {
 #endif
 
-#define VMLA_ABI_VERSION 6
+#define VMLA_ABI_VERSION 7
 
 typedef enum vmla_status {
   VMLA_OK = 0,

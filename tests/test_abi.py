@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.vmla_abi_version() == 6
+    assert lib.vmla_abi_version() == 7
     for code in range(-7, 1):
         s = vm.vmla_status_string(code)
         assert s and s != "unknown status"
