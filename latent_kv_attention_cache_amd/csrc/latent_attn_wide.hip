@@ -22,11 +22,14 @@
 // workgroup's units belong to one head (its W_V_up[h] is staged once for the
 // epilogue). At d_c = 256 each of the four waves takes one unit. At d_c = 512
 // the whole O^T (256 registers) and Qhat (136) still do not fit one wave
-// without spills, so two waves share a unit: both compute the same scores
-// and softmax (identical instruction streams, so identical m and l), and each
-// accumulates one half of the latent dimensions (128 accumulation registers);
-// the two halves of (O / l) W_V_up[h] are summed through LDS in the epilogue.
-// That doubles the score MFMAs (200 instead of 132 per unit and tile).
+// without spills, so two waves share a unit: wave k of the pair scores keys
+// 32 k .. 32 k + 31 of each tile, the pair swaps its maxima through LDS (both
+// then hold the same reference max), each wave packs its P^T to bf16 and
+// swaps it too, and each accumulates one half of the latent dimensions over
+// all 64 keys (128 accumulation registers). The exponent sums and the two
+// halves of (O / l) W_V_up[h] are combined through LDS in the epilogue. Per
+// unit and tile the pair issues the 132 MFMAs of one wave with the whole
+// row, at three barriers per tile instead of one.
 //
 // Tile. 64 keys, chunk-major and padded in LDS as in latent_attn_kernel (chunk
 // c of key row r at slot c * 68 + r), copied by 16-byte LDS-DMA loads that all
@@ -68,7 +71,10 @@ struct WideShape {
   static_assert(kChunks % kWaves == 0, "tile loads split evenly over the four waves");
   static_assert(!kPair || (DC / 2) * kVLd * 2 + kUnitsWG * (kDV / 32) * 16 * 64 * 4 <= 2 * kTileElems * 2,
                 "epilogue staging of one W_V_up half and the partial outputs fits the tile buffers");
-  static_assert(2 * kTileElems * 2 <= 160 * 1024, "two tile buffers in LDS");
+  // pair exchange area after the tile buffers: maxima [wave][lane] (fp32)
+  // and packed P^T [wave][step][lane] (16 bytes)
+  static constexpr int kXchElems = kPair ? (kWaves * 64 * 4 + kWaves * 2 * 64 * 16) / 2 : 0;
+  static_assert(2 * kTileElems * 2 + kXchElems * 2 <= 160 * 1024, "two tile buffers in LDS");
   static_assert((kPair ? DC / 2 : DC) * kVLd <= 2 * kTileElems, "staged W_V_up rows fit the tile buffers");
 };
 
@@ -86,7 +92,7 @@ void latent_attn_wide_kernel(AttnArgs a) {
   constexpr int kFeatSteps = Sh::kFeatSteps;
   constexpr int kOTiles = Sh::kOTiles;
   constexpr int kUnitsWG = Sh::kUnitsWG;
-  __shared__ __attribute__((aligned(16))) bf16_t kt[2 * kTileElems];
+  __shared__ __attribute__((aligned(16))) bf16_t kt[2 * kTileElems + Sh::kXchElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -148,89 +154,189 @@ void latent_attn_wide_kernel(AttnArgs a) {
   issue_tile(0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int jt = 0; jt < ntiles; ++jt) {
-    if (jt + 1 < ntiles) issue_tile(jt + 1);     // into the buffer read in tile jt - 1
-    const bf16_t* K = kt + (jt & 1) * kTileElems;
-    if (live) {
-      // S^T of the tile: register r of key block kb holds key 32 kb + 8(r/4) + 4 half + r%4
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
+  if constexpr (Sh::kPair) {
+    float* xmax = reinterpret_cast<float*>(kt + 2 * kTileElems);          // [wave][lane]
+    uint4* xp = reinterpret_cast<uint4*>(xmax + kWaves * 64);             // [wave][step][lane]
+    const int partner = wave ^ 1;
+    const int kb_own = lat_half;                                          // this wave's key block
+    for (int jt = 0; jt < ntiles; ++jt) {
+      if (jt + 1 < ntiles) issue_tile(jt + 1);     // into the buffer read in tile jt - 1
+      const bf16_t* K = kt + (jt & 1) * kTileElems;
+      f32x16 sc = f32x16{};                        // S^T of keys 32 kb_own + 8(r/4) + 4 half + r%4
+      float mx = -INFINITY;
+      if (live) {
 #pragma unroll
-      for (int ks = 0; ks < kFeatSteps; ++ks) {
-        const int off = a_base + 2 * kSlots * 8 * ks;
-        s0 = mfma32(lds_row8(K + off), qf[ks], s0);
-        s1 = mfma32(lds_row8(K + off + 32 * 8), qf[ks], s1);
-      }
-      // operand reads run two steps ahead of the MFMAs, no further (register budget)
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+        for (int ks = 0; ks < kFeatSteps; ++ks)
+          sc = mfma32(lds_row8(K + a_base + 2 * kSlots * 8 * ks + 32 * 8 * kb_own), qf[ks], sc);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
-      for (int i = 0; i < kFeatSteps - 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        for (int i = 0; i < kFeatSteps - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+        const int key0 = jt * kKT;
+        if (key0 + kKT > nk) {
+          const int lim = nk - key0 - 4 * half;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb_own + 8 * (r >> 2) + (r & 3) >= lim) sc[r] = -INFINITY;
+        }
+        mx = sc[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+        mx = max_across_halves(mx);
+        xmax[wave * 64 + lane] = mx;
       }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
-      const int key0 = jt * kKT;
-      if (key0 + kKT > nk) {
-        const int lim = nk - key0 - 4 * half;
+      __syncthreads();                             // both halves' maxima visible
+      bf16x8 pown[2];
+      if (live) {
+        mx = fmaxf(mx, xmax[partner * 64 + lane]); // the same value in both waves of the pair
+        const bool grow = mx > m + kLazy;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float m_new = grow ? mx : m;
+          const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+          l *= alpha;
+#pragma unroll
+          for (int t = 0; t < kOTiles; ++t) o[t] *= alpha;
+          m = m_new;
+        }
+        float ls = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int k = 8 * (r >> 2) + (r & 3);
-          if (k >= lim) s0[r] = -INFINITY;
-          if (k + 32 >= lim) s1[r] = -INFINITY;
+          sc[r] = __builtin_amdgcn_exp2f(sc[r] - m);
+          ls += sc[r];
         }
-      }
-      float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-      mx = max_across_halves(mx);
-      const bool grow = mx > m + kLazy;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? mx : m;
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-        l *= alpha;
-#pragma unroll
-        for (int t = 0; t < kOTiles; ++t) o[t] *= alpha;
-        m = m_new;
-      }
-      float ls = 0.f;
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] = __builtin_amdgcn_exp2f(s0[r] - m);
-        s1[r] = __builtin_amdgcn_exp2f(s1[r] - m);
-        ls += s0[r] + s1[r];
-      }
-      l += ls;
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pb[0][jj][e] = (__bf16)s0[8 * jj + e];
-          pb[1][jj][e] = (__bf16)s1[8 * jj + e];
-        }
-      // O^T += C^T(tile) P^T
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        l += ls;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-          const bf16_t* Kb = K + (kb * 32 + jj * 16) * 8;
 #pragma unroll
-          for (int t = 0; t < kOTiles; ++t) {
-            const int ct = 4 * kSlots * 8 * (t + kOTiles * lat_half);
-            const bf16x4 lo = lds_tr4(Kb + v_off1 + ct);
-            const bf16x4 hi = lds_tr4(Kb + v_off2 + ct);
-            o[t] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb[kb][jj], o[t]);
+          for (int e = 0; e < 8; ++e) pown[jj][e] = (__bf16)sc[8 * jj + e];
+          xp[(wave * 2 + jj) * 64 + lane] = __builtin_bit_cast(uint4, pown[jj]);
+        }
+      }
+      __syncthreads();                             // both halves' P^T visible
+      if (live) {
+        bf16x8 ppart[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) ppart[jj] = __builtin_bit_cast(bf16x8, xp[(partner * 2 + jj) * 64 + lane]);
+        // O^T(latent half) += C^T(tile) P^T over all 64 keys
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const bf16_t* Kb = K + (kb * 32 + jj * 16) * 8;
+            const bf16x8 pv = kb == kb_own ? pown[jj] : ppart[jj];
+#pragma unroll
+            for (int t = 0; t < kOTiles; ++t) {
+              const int ct = 4 * kSlots * 8 * (t + kOTiles * lat_half);
+              const bf16x4 lo = lds_tr4(Kb + v_off1 + ct);
+              const bf16x4 hi = lds_tr4(Kb + v_off2 + ct);
+              o[t] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pv, o[t]);
+            }
+          }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 1);
+#pragma unroll
+        for (int i = 0; i < 4 * kOTiles - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 1);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of tile jt + 1
+      __syncthreads();                                    // tile jt + 1 complete, buffer jt free
+    }
+    // the exponent sums of the two key halves: l of the pair = l + l(partner)
+    xmax[wave * 64 + lane] = l;
+    __syncthreads();
+    l += xmax[partner * 64 + lane];
+    __syncthreads();                               // the exchange area is free again
+  } else {
+    for (int jt = 0; jt < ntiles; ++jt) {
+      if (jt + 1 < ntiles) issue_tile(jt + 1);     // into the buffer read in tile jt - 1
+      const bf16_t* K = kt + (jt & 1) * kTileElems;
+      if (live) {
+        // S^T of the tile: register r of key block kb holds key 32 kb + 8(r/4) + 4 half + r%4
+        f32x16 s0 = f32x16{}, s1 = f32x16{};
+  #pragma unroll
+        for (int ks = 0; ks < kFeatSteps; ++ks) {
+          const int off = a_base + 2 * kSlots * 8 * ks;
+          s0 = mfma32(lds_row8(K + off), qf[ks], s0);
+          s1 = mfma32(lds_row8(K + off + 32 * 8), qf[ks], s1);
+        }
+        // operand reads run four steps ahead of the MFMAs (one wave per SIMD: the LDS latency is not hidden by a partner wave)
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+  #pragma unroll
+        for (int i = 0; i < kFeatSteps - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 0);
+        const int key0 = jt * kKT;
+        if (key0 + kKT > nk) {
+          const int lim = nk - key0 - 4 * half;
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int k = 8 * (r >> 2) + (r & 3);
+            if (k >= lim) s0[r] = -INFINITY;
+            if (k + 32 >= lim) s1[r] = -INFINITY;
           }
         }
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
-#pragma unroll
-      for (int i = 0; i < 4 * kOTiles - 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+        float mx = fmaxf(s0[0], s1[0]);
+  #pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+        mx = max_across_halves(mx);
+        const bool grow = mx > m + kLazy;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float m_new = grow ? mx : m;
+          const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+          l *= alpha;
+  #pragma unroll
+          for (int t = 0; t < kOTiles; ++t) o[t] *= alpha;
+          m = m_new;
+        }
+        float ls = 0.f;
+        bf16x8 pb[2][2];
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s0[r] = __builtin_amdgcn_exp2f(s0[r] - m);
+          s1[r] = __builtin_amdgcn_exp2f(s1[r] - m);
+          ls += s0[r] + s1[r];
+        }
+        l += ls;
+  #pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pb[0][jj][e] = (__bf16)s0[8 * jj + e];
+            pb[1][jj][e] = (__bf16)s1[8 * jj + e];
+          }
+        // O^T += C^T(tile) P^T
+  #pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+  #pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const bf16_t* Kb = K + (kb * 32 + jj * 16) * 8;
+  #pragma unroll
+            for (int t = 0; t < kOTiles; ++t) {
+              const int ct = 4 * kSlots * 8 * (t + kOTiles * lat_half);
+              const bf16x4 lo = lds_tr4(Kb + v_off1 + ct);
+              const bf16x4 hi = lds_tr4(Kb + v_off2 + ct);
+              o[t] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb[kb][jj], o[t]);
+            }
+          }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 1);
+  #pragma unroll
+        for (int i = 0; i < 4 * kOTiles - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 1);
       }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of tile jt + 1
+      __syncthreads();                                    // tile jt + 1 complete, buffer jt free
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of tile jt + 1
-    __syncthreads();                                    // tile jt + 1 complete, buffer jt free
+
   }
 
   // ---- epilogue: out = (O / l) @ W_V_up[h]. The W_V_up[h] rows of a latent
