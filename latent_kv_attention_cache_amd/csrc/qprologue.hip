@@ -14,9 +14,10 @@
 //
 // Tile: 128 query rows (batch x tokens flattened, so a tile may span two batch
 // elements) x two heads (256 columns of W_Q). Per output the L2 traffic of the
-// projection is (1/128 + 1/256) of the operand bytes. Four waves, one per
-// SIMD: wave (rh, hh) computes rows 64 rh .. 64 rh + 63 and the 128 columns of
-// head hh of the pair with v_mfma_f32_16x16x32_bf16 as out^T = W^T x^T, so that
+// projection is (1/128 + 1/256) of the operand bytes. Eight waves, two per
+// SIMD (one wave's LDS and barrier waits overlap the other's MFMAs): wave
+// (rh, hh) computes rows 32 rh .. 32 rh + 31 and the 128 columns of head hh of
+// the pair with v_mfma_f32_16x16x32_bf16 as out^T = W^T x^T, so that
 // a lane holds four consecutive columns of one row (a RoPE pair sits in one
 // lane). The d_model contraction runs as a 3-stage pipeline of 64-deep slices
 // of x (row-major, chunk-swizzled) and W_Q (row-major, 512-byte rows, chunk c
@@ -36,10 +37,11 @@
 namespace vmla {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsT = 128;                       // query rows per workgroup
-constexpr int kNRB = 4;                           // 16-row blocks per wave
+constexpr int kNRB = 2;                           // 16-row blocks per wave
+constexpr int kRowsW = 16 * kNRB;                 // query rows per wave
 constexpr int kHeadsT = 2;                        // heads per workgroup
 constexpr int kColsT = kHeadsT * kDHead;          // 256 columns of W_Q
 constexpr int kCB = kDHead / 16;                  // 8 column blocks per wave
@@ -49,8 +51,8 @@ constexpr int kWElems = kStageK * kColsT;         // W_Q slice of a stage
 constexpr int kWLoads = kWElems * 2 / 1024;       // 32
 constexpr int kStageElems = kXElems + kWElems;
 constexpr int kStages = 3;
-constexpr int kXPerWave = kXLoads / kWaves;       // 4
-constexpr int kWPerWave = kWLoads / kWaves;       // 8
+constexpr int kXPerWave = kXLoads / kWaves;       // 2
+constexpr int kWPerWave = kWLoads / kWaves;       // 4
 constexpr int kL = kXPerWave + kWPerWave;         // loads per wave per stage
 constexpr int kWChunks = kColsT / 8;              // 32 chunks per W_Q tile row
 static_assert(kXLoads % kWaves == 0 && kWLoads % kWaves == 0, "loads split evenly");
@@ -71,7 +73,7 @@ void qprologue_kernel(QArgs a) {
   constexpr int kRow = DC + kDHead - DN;    // Qhat row: [q_lat (DC) | q_rope (128 - DN)]
   constexpr int kQnLd = kDNope + 8;         // q_nope staging row (bf16)
   static_assert(DN % 16 == 0 && DN > 0 && DN < kDHead, "NoPE width");
-  static_assert(kWaves * 64 * kQnLd <= kStages * kStageElems, "epilogue staging fits");
+  static_assert(kWaves * kRowsW * kQnLd <= kStages * kStageElems, "epilogue staging fits");
   __shared__ __attribute__((aligned(16))) bf16_t smem[kStages * kStageElems];
 
   // Workgroups are dispatched round-robin over the 8 XCDs; id = 8 (HP q + hp) + x8
@@ -101,9 +103,9 @@ void qprologue_kernel(QArgs a) {
   const T* wq = static_cast<const T*>(a.w_q) + col0;
   const int nst = a.d_model / kStageK;
 
-  // Load offsets (bytes; bf16 sources). x load n = 4 wv + i moves rows
+  // Load offsets (bytes; bf16 sources). x load n = 2 wv + i moves rows
   // 8n .. 8n+7 of the tile (clamped to the last row); W load n = 8 wv + i moves
-  // rows 2n, 2n+1 of the W_Q slice. A head pair with one head (odd head count)
+  // rows 2n, 2n+1 of the W_Q slice (n = 4 wv + i). A head pair with one head (odd head count)
   // reads the existing head's columns in place of the missing one.
   uint32_t voff[kL];
   if constexpr (std::is_same_v<T, bf16_t>) {
@@ -143,11 +145,11 @@ void qprologue_kernel(QArgs a) {
   };
 
   // Operand offsets (elements, relative to a stage's tiles).
-  // x (B operand): lane (j, g) of block rb = row 64 rh + 16 rb + j, chunk 4 kk + g.
+  // x (B operand): lane (j, g) of block rb = row 32 rh + 16 rb + j, chunk 4 kk + g.
   int a_off[kNRB][2];
 #pragma unroll
   for (int rb = 0; rb < kNRB; ++rb) {
-    const int row = 64 * rh + 16 * rb + j;
+    const int row = kRowsW * rh + 16 * rb + j;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) a_off[rb][kk] = 64 * row + 8 * ((4 * kk + g) ^ swz_a(row));
   }
@@ -173,7 +175,7 @@ void qprologue_kernel(QArgs a) {
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Stage s: two 32-deep steps of 4 x 8 MFMAs; the next x fragment and the W
+  // Stage s: two 32-deep steps of 2 x 8 MFMAs; the next x fragment and the W
   // fragments of the second step are read while the current MFMAs run. Past
   // the last stage the loads repeat the last stage into a buffer that is not
   // read again, so the stage body has no branch; every iteration issues one
@@ -216,16 +218,17 @@ void qprologue_kernel(QArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // the trailing loads have landed
   __syncthreads();                                     // the stage buffers are free
 
-  // ---- epilogue. Register r of acc[rb][cb] in lane (j, g): row 64 rh + 16 rb + j
+  // ---- epilogue. Register r of acc[rb][cb] in lane (j, g): row 32 rh + 16 rb + j
   // of the tile, column 16 cb + 4 g + r of head h.
   const int h = kHeadsT * hp + hh;
   if (h >= a.n_heads) return;                         // no barrier follows
   // W_K_up[h] fragments of the absorption, A operand: lane (j, g) of column
-  // tile ct holds row 16 ct + j, n = 32 ks + 8 g .. +7. The first six tiles are
-  // requested now and land during the RoPE and q_nope work; each register set
-  // is refilled with tile ct + 6 once tile ct has been consumed.
+  // tile ct holds row 16 ct + j, n = 32 ks + 8 g .. +7. The first kWkD tiles
+  // are requested now and land during the RoPE and q_nope work; each register
+  // set is refilled with tile ct + kWkD once tile ct has been consumed.
   constexpr int kCT = kDC / 16;                        // 12 column tiles of q_lat
   constexpr int kKS = (kDNope + 31) / 32;              // 3 steps (DN = 112: 4, the last half empty)
+  constexpr int kWkD = kCT / 2 < 6 ? kCT / 2 : (kKS > 3 ? 4 : 6);   // tiles in flight
   // lanes whose n = 32 ks + 8 g .. +7 lies past the NoPE width (DN % 32 = 16,
   // last step) contribute zeros on both operands
   auto n_live = [&](int ks) { return kDNope % 32 == 0 || 32 * ks + 8 * g < kDNope; };
@@ -236,14 +239,14 @@ void qprologue_kernel(QArgs a) {
       w[ks] = n_live(ks) ? __builtin_bit_cast(bf16x8, load8_bf16<T>(wku + (size_t)(16 * ct + j) * kDNope + 32 * ks + 8 * g))
                          : bf16x8{};
   };
-  bf16x8 wk[kCT / 2][kKS];
+  bf16x8 wk[kWkD][kKS];
 #pragma unroll
-  for (int c = 0; c < kCT / 2; ++c) load_wk(c, wk[c]);
+  for (int c = 0; c < kWkD; ++c) load_wk(c, wk[c]);
   int64_t qrow[kNRB];                                  // Qhat row index, -1 past the last row
   int pos[kNRB][3];                                    // (t, h, w) of each row
 #pragma unroll
   for (int rb = 0; rb < kNRB; ++rb) {
-    const int64_t m = m0 + 64 * rh + 16 * rb + j;
+    const int64_t m = m0 + kRowsW * rh + 16 * rb + j;
     const int64_t mc = m < M ? m : M - 1;
     const int b = (int)(mc / a.n_q);
     const int n = (int)(mc - (int64_t)b * a.n_q);
@@ -278,8 +281,8 @@ void qprologue_kernel(QArgs a) {
       }
     }
   }
-  // q_nope of this wave's 64 rows to LDS: qn[row][0..DN-1] (bf16)
-  bf16_t* qn = smem + wv * 64 * kQnLd;
+  // q_nope of this wave's 32 rows to LDS: qn[row][0..DN-1] (bf16)
+  bf16_t* qn = smem + wv * kRowsW * kQnLd;
 #pragma unroll
   for (int rb = 0; rb < kNRB; ++rb)
 #pragma unroll
@@ -298,7 +301,7 @@ void qprologue_kernel(QArgs a) {
       qb[rb][ks] = n_live(ks) ? lds_row8(&qn[(16 * rb + j) * kQnLd + 32 * ks + 8 * g]) : bf16x8{};
 #pragma unroll
   for (int ct = 0; ct < kCT; ++ct) {
-    bf16x8 (&w)[kKS] = wk[ct % (kCT / 2)];
+    bf16x8 (&w)[kKS] = wk[ct % kWkD];
 #pragma unroll
     for (int rb = 0; rb < kNRB; ++rb) {
       f32x4 ql = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -309,7 +312,7 @@ void qprologue_kernel(QArgs a) {
         *reinterpret_cast<uint2*>(qhat + qrow[rb] * kRow + 16 * ct + 4 * g) =
             uint2{pack2(ql[0] * a.qscale, ql[1] * a.qscale), pack2(ql[2] * a.qscale, ql[3] * a.qscale)};
     }
-    if (ct + kCT / 2 < kCT) load_wk(ct + kCT / 2, w);
+    if (ct + kWkD < kCT) load_wk(ct + kWkD, w);
   }
 }
 
