@@ -76,6 +76,24 @@ def test_heads_sharing_a_workgroup(grid_h, grid_w):
     compare(out[0], r.reference(), f"n_q={w.n_q}", per_head_axis=1)
 
 
+@pytest.mark.parametrize("grid_h,grid_w,batch", [
+    (3, 43, 1),     # M = 129: the last 128-row prologue tile holds one row (wave 0 only)
+    (10, 16, 1),    # 160: it ends at the end of wave 0's 32 rows
+    (7, 23, 1),     # 161: one row into wave 1
+    (15, 15, 1),    # 225: one row into wave 3
+    (15, 17, 1),    # 255: one row short of a full tile
+    (9, 9, 2),      # 2 x 81 = 162: the tail tile starts inside batch element 1
+])
+def test_query_tile_tails(grid_h, grid_w, batch):
+    # The query prologue cuts the batch x tokens rows into tiles of 128, 32 rows
+    # per wave; these counts end the last tile inside each wave's slice.
+    w = custom(grid_h, grid_w, window_frames=2, chunk_frames=1, t_first=1, batch=batch)
+    r = Run(w)
+    out = _sync_np(r.chunk_step())
+    for b in range(batch):
+        compare(out[b], r.reference(b=b), f"M={batch * w.n_q} b={b}", per_head_axis=1)
+
+
 @pytest.mark.parametrize("grid_h,grid_w,n_heads,d_model,batch", [
     (5, 13, 3, 640, 1),     # 65 queries, odd head count: a query-prologue head pair with one head
     (10, 29, 5, 1024, 2),   # 290 queries per element, row tiles across the batch boundary
