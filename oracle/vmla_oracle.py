@@ -34,9 +34,10 @@ Readings of points the pages leave open:
     w ([PL] App. D.3); pair j is the adjacent channels (2j, 2j+1); within an
     axis group of width D_a (12, 10, 10) pair i turns at
     omega_i = theta^(-2 i / D_a), theta = 10000, so i = 0 is the group's
-    highest-frequency band. PARITY UNPINNED for the table values: the pages
-    print no frequencies; only the (6,5,5) split and "highest bands first"
-    are pinned.
+    highest-frequency band. The pages print no frequencies; the law is
+    pinned per axis group against the standard RoPE inverse frequencies of
+    the transformers library (widths 12 / 10 / 10 and the split variants'
+    groups), next to the (6,5,5) split and "highest bands first".
   * k^R is rotated with absolute (t, h, w) when it is cached. The pages rotate
     at window-assembly time with window-local t ([PL] App. D.5, App. E); with
     no sink frame both give the same scores by RoPE's relative invariance,
@@ -61,9 +62,11 @@ Readings of points the pages leave open:
     c_q (the pages name none); the head outputs are concatenated head-major
     and mixed by W_O [H d_v, d_model]; A_h and B_h W_O[h] are the folded
     weights of [PL] App. E.
-PARITY UNPINNED: final output values at the benchmark shapes (the pages print
-no worked example); they are pinned only through the identities checked in
-tests/test_oracle_pins.py.
+The pages print no worked example, so no output value comes from them; the
+outputs are pinned through the identities, library routines (torch SDPA in
+fp64, transformers' RoPE rates), closed forms and brute force of
+tests/test_oracle_pins.py, at the benchmark geometry (30x52 grid, t up to 20,
+the real widths) among others.
 """
 from __future__ import annotations
 

@@ -125,6 +125,39 @@ def test_rope_axis_split_6_5_5_and_highest_bands():
         assert list(moved) == list(range(lo, hi))
 
 
+def _standard_rope_inv_freq(dim, theta):
+    """Inverse frequencies of plain (unscaled) RoPE over a head of width
+    ``dim``, as the transformers library computes them: its linear-scaling
+    routine at factor 1.0 is the original RoPE law."""
+    transformers = pytest.importorskip("transformers")
+    from transformers import modeling_rope_utils
+    cfg = transformers.LlamaConfig(hidden_size=dim, num_attention_heads=1, head_dim=dim,
+                                   rope_parameters={"rope_type": "linear", "factor": 1.0,
+                                                    "rope_theta": float(theta)})
+    inv_freq, _ = modeling_rope_utils._compute_linear_scaling_rope_parameters(cfg)
+    return inv_freq.double().numpy()
+
+
+def test_rope_frequency_law_matches_standard_rope_per_axis():
+    # [PL] App. C.1: the t, h and w axes are rotated separately and the results
+    # concatenated; [PL] App. D.3: 16 pairs split (6, 5, 5). Reading R1: each
+    # axis group of width D_a = 12 / 10 / 10 is an ordinary RoPE subspace, so
+    # its pair rates are exactly those of standard RoPE over a D_a-wide head at
+    # theta = 10^4. The split variants' groups (6/6/4, 24/20/20, 36/30/30) too.
+    from workloads import SPLIT_ROPE
+    tables = [((6, 5, 5), (12, 10, 10))] + [tuple(v) for v in SPLIT_ROPE.values()]
+    for pairs, dims in tables:
+        om = orc.rope_frequencies(pairs, dims)
+        assert om.shape == (sum(pairs),)
+        lo = 0
+        for n_pairs, dim in zip(pairs, dims):
+            ref = _standard_rope_inv_freq(dim, 10000.0)[:n_pairs]
+            # transformers computes in fp32: a few ulps of 2^-24
+            np.testing.assert_allclose(om[lo:lo + n_pairs], ref, rtol=1e-6, atol=0,
+                                       err_msg=f"axis group {dim} of {pairs}/{dims}")
+            lo += n_pairs
+
+
 def test_frame_positions_token_order():
     p = orc.frame_positions(5, 3, 4)
     assert p.shape == (12, 3)
@@ -271,6 +304,49 @@ def test_mla_equals_dense_mha_with_composed_weights_real_dims():
         torch.from_numpy(np.stack(Qs))[None], torch.from_numpy(np.stack(Ks))[None],
         torch.from_numpy(np.stack(Vs))[None])[0].permute(1, 0, 2).numpy()
     assert rel(out, ref) < 1e-12
+
+
+def test_oracle_at_wan_geometry_equals_dense_mha_with_composed_weights():
+    # The benchmark geometry: a 30x52 grid (h up to 29, w up to 51) and t up to
+    # 20, the real widths, a 3-frame window of 4680 keys; sampled query rows of
+    # the last frame, corner tokens included. Reference: a dense MHA whose head
+    # h uses W_K,h = W_down W_K_up[h] and W_V,h = W_down W_V_up[h] (the other
+    # association of the products), RoPE by complex multiplication with the
+    # per-axis standard-RoPE rates of transformers, torch SDPA in fp64.
+    w = custom(30, 52, window_frames=3, chunk_frames=1, t_first=20, dtype="f32")
+    wt = weights(w)
+    frames = (18, 19, 20)
+    xs = {t: x_frame(w, t) for t in frames}
+    rows = np.array([0, 51, 52, 777, 1508, 1559])
+    out = orc.chunk_attention_reference(w, wt, lambda t: xs[t], rows)
+    om = np.concatenate([_standard_rope_inv_freq(d, 10000.0)[:n]
+                         for n, d in zip(w.rope_pairs, w.rope_axis_dims)])
+
+    def rot(v, p):
+        ang = np.concatenate([np.full(n, float(p[a])) for a, n in enumerate(w.rope_pairs)]) * om
+        z = (v[0::2] + 1j * v[1::2]) * np.exp(1j * ang)
+        o = np.empty_like(v)
+        o[0::2], o[1::2] = z.real, z.imag
+        return o
+
+    H, dn = w.n_heads, w.d_nope
+    xk = np.concatenate([xs[t] for t in frames]).astype(np.float64)
+    pk = [(t, n // 52, n % 52) for t in frames for n in range(1560)]
+    krot = np.stack([rot(r, p) for r, p in zip(xk @ wt["w_kr"].astype(np.float64), pk)])
+    xq = xs[20][rows].astype(np.float64)
+    pq = [(20, n // 52, n % 52) for n in rows]
+    wdown = wt["w_down"].astype(np.float64)
+    Qs, Ks, Vs = [], [], []
+    for h in range(H):
+        qh = xq @ wt["w_q"][:, h * 128:(h + 1) * 128].astype(np.float64)
+        Qs.append(np.concatenate([qh[:, :dn], np.stack([rot(r, p) for r, p in zip(qh[:, dn:], pq)])], 1))
+        Ks.append(np.concatenate([xk @ (wdown @ wt["w_k_up"][h].astype(np.float64)), krot], 1))
+        Vs.append(xk @ (wdown @ wt["w_v_up"][h].astype(np.float64)))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.stack(Qs))[None], torch.from_numpy(np.stack(Ks))[None],
+        torch.from_numpy(np.stack(Vs))[None])[0].permute(1, 0, 2).numpy()
+    # fp32 rates from transformers: angles up to ~50 rad carry ~1e-5 relative error
+    assert rel(out, ref) < 1e-5
 
 
 def _rope_complex_split(v, pos, pairs, axis_dims, theta=10000.0):
@@ -903,15 +979,27 @@ def _masked_attention_weights_not_renormalised(q_nope, q_rope, k_nope, k_r, v, s
     return out
 
 
+def _rope_frequencies_no_factor_two(pairs=(6, 5, 5), axis_dims=(12, 10, 10), theta=10000.0):
+    # theta^(-i / D_a): the exponent misses its factor 2
+    return np.array([float(theta) ** (-i / d) for n, d in zip(pairs, axis_dims) for i in range(n)])
+
+
+def _rope_frequencies_width_is_pair_count(pairs=(6, 5, 5), axis_dims=(12, 10, 10), theta=10000.0):
+    # D_a taken as the group's pair count instead of its channel width
+    return np.array([float(theta) ** (-2.0 * i / n) for n in pairs for i in range(n)])
+
+
 _ORIG_CTX = orc.active_context
 _ORIG_MASK = orc.chunk_causal_frame_mask
 _ORIG_ATT = orc.attention_explicit
 _ORIG_REC = orc.reconstruct_heads
 _ORIG_POS = orc.frame_positions
 
-PINS = [test_rope_is_complex_rotation, test_attention_matches_torch_sdpa_fp64,
+PINS = [test_rope_is_complex_rotation, test_rope_frequency_law_matches_standard_rope_per_axis,
+        test_attention_matches_torch_sdpa_fp64,
         test_mla_reduces_to_dense_mha_with_selection_up_projections,
         test_mla_equals_dense_mha_with_composed_weights_real_dims,
+        test_oracle_at_wan_geometry_equals_dense_mha_with_composed_weights,
         test_brute_force_scalar_loops_tiny, test_append_reference_rows_layout,
         test_frame_positions_token_order, test_absorbed_equals_explicit,
         test_reindexed_sink_context_brute_force_tiny,
@@ -937,6 +1025,8 @@ PINS = [test_rope_is_complex_rotation, test_attention_matches_torch_sdpa_fp64,
     ("window counted from the chunk start", ("chunk_causal_frame_mask", _mask_window_from_chunk_start)),
     ("window ignored", ("chunk_causal_frame_mask", _mask_without_window)),
     ("masked weights not renormalised", ("masked_attention", _masked_attention_weights_not_renormalised)),
+    ("RoPE exponent without its factor 2", ("rope_frequencies", _rope_frequencies_no_factor_two)),
+    ("RoPE axis width taken as the pair count", ("rope_frequencies", _rope_frequencies_width_is_pair_count)),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, patch):
     attr, fn = patch
