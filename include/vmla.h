@@ -24,6 +24,13 @@
  *  - Errors: every argument is validated on the host before any HIP call; a
  *    negative vmla_status is returned and nothing is launched. A failed launch
  *    returns VMLA_ERR_HIP. No exception or abort crosses the ABI.
+ *  - Aliasing: a buffer that a call writes (the cache for the append; the
+ *    workspace and out for the attention calls; the folded or packed weights)
+ *    may share no byte with any other buffer argument of the same call, read
+ *    or written. The byte range of each argument follows from the call's
+ *    shapes (the whole cache, the workspace bytes the call needs). This is
+ *    checked last, after every other check, and an overlap returns
+ *    VMLA_ERR_OVERLAP with nothing launched.
  *  - Supported geometry in this version: d_v = 128, d_model a multiple of 64,
  *    1 <= n_heads <= 64, rope_pairs summing to d_rope / 2 (at most 48 pairs);
  *    d_nope / d_rope = 96 / 32 (the default of [PL] App. D.2-D.3) with d_c =
@@ -58,7 +65,7 @@
 extern "C" {
 #endif
 
-#define VMLA_ABI_VERSION 7
+#define VMLA_ABI_VERSION 8
 
 typedef enum vmla_status {
   VMLA_OK = 0,
@@ -68,7 +75,8 @@ typedef enum vmla_status {
   VMLA_ERR_ALIGN = -4,      /* a pointer is not 16-byte aligned */
   VMLA_ERR_RANGE = -5,      /* t_first / n_frames / n_valid_frames / chunk or mask window out of range */
   VMLA_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than vmla_attention_workspace_bytes */
-  VMLA_ERR_HIP = -7         /* a HIP launch failed (hipGetLastError after the launch) */
+  VMLA_ERR_HIP = -7,        /* a HIP launch failed (hipGetLastError after the launch) */
+  VMLA_ERR_OVERLAP = -8     /* a buffer the call writes overlaps another buffer argument */
 } vmla_status;
 
 typedef enum vmla_dtype { VMLA_F32 = 0, VMLA_BF16 = 1 } vmla_dtype;

@@ -23,6 +23,7 @@ VMLA_ERR_ALIGN = -4
 VMLA_ERR_RANGE = -5
 VMLA_ERR_WORKSPACE = -6
 VMLA_ERR_HIP = -7
+VMLA_ERR_OVERLAP = -8
 
 VMLA_F32 = 0
 VMLA_BF16 = 1
@@ -66,11 +67,15 @@ EXPORTED = ("vmla_default_dims", "vmla_cache_append", "vmla_attention_workspace_
             "vmla_status_string", "vmla_abi_version")
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libvmla.so once; raise if it has not been built."""
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libvmla.so once; raise if it has not been built.
+
+    ``VMLA_LIBRARY`` in the environment names another build of the same ABI
+    (the CPU tests use it for the host-only sanitizer build)."""
     global _LIB
     if _LIB is not None:
         return _LIB
+    path = path or os.environ.get("VMLA_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
                           "`python -m latent_kv_attention_cache_amd.build`")

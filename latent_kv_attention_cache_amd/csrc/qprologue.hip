@@ -104,8 +104,8 @@ void qprologue_kernel(QArgs a) {
   const int nst = a.d_model / kStageK;
 
   // Load offsets (bytes; bf16 sources). x load n = 2 wv + i moves rows
-  // 8n .. 8n+7 of the tile (clamped to the last row); W load n = 8 wv + i moves
-  // rows 2n, 2n+1 of the W_Q slice (n = 4 wv + i). A head pair with one head (odd head count)
+  // 8n .. 8n+7 of the tile (clamped to the last row); W load n = 4 wv + i moves
+  // rows 2n, 2n+1 of the W_Q slice. A head pair with one head (odd head count)
   // reads the existing head's columns in place of the missing one.
   uint32_t voff[kL];
   if constexpr (std::is_same_v<T, bf16_t>) {

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <climits>
 #include <cstdint>
+#include <initializer_list>
 
 #include "kernels.h"
 
@@ -110,6 +111,59 @@ RopeTable rope_table(const vmla_dims* d) {
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? VMLA_OK : VMLA_ERR_HIP; }
 
+// ---- aliasing: the byte range of every tensor argument of a call
+
+struct Span {
+  uintptr_t lo, hi;   // [lo, hi)
+};
+
+Span bytes_at(const void* p, size_t n) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return {a, n > UINTPTR_MAX - a ? UINTPTR_MAX : a + n};
+}
+
+size_t esize(int32_t dtype) { return dtype == VMLA_F32 ? sizeof(float) : sizeof(uint16_t); }
+
+Span cache_span(const vmla_dims* d, const vmla_cache* c) {
+  const size_t rows = (size_t)c->grid_h * c->grid_w * ((size_t)c->sink_frames + c->window_frames);
+  return bytes_at(c->data, (size_t)c->batch * rows * (d->d_c + d->d_rope) * esize(c->dtype));
+}
+
+// A buffer that a call writes may share no byte with any other buffer of the
+// call, read or written: the kernels of one call read and write them
+// concurrently, so an alias would corrupt results (or the cache) silently.
+int32_t check_disjoint(std::initializer_list<Span> written, std::initializer_list<Span> read) {
+  for (auto w = written.begin(); w != written.end(); ++w) {
+    for (auto o = w + 1; o != written.end(); ++o)
+      if (w->lo < o->hi && o->lo < w->hi) return VMLA_ERR_OVERLAP;
+    for (const Span& r : read)
+      if (w->lo < r.hi && r.lo < w->hi) return VMLA_ERR_OVERLAP;
+  }
+  return VMLA_OK;
+}
+
+// Spans of the attention-core arguments: activations x [B, n_q, d_model],
+// W_Q [d_model, H (d_nope + d_rope)], W_K_up [H, d_c, d_nope], W_V_up
+// [H, d_c, d_v], head outputs [B, n_q, H, d_v], and the Qhat workspace.
+struct AttnSpans {
+  Span x, w_q, w_k_up, w_v_up, out, ws, cache;
+};
+
+AttnSpans attn_spans(const vmla_dims* d, const vmla_cache* c, int32_t dtype, int64_t n_q, const void* x,
+                     const void* w_q, const void* w_k_up, const void* w_v_up, const void* out,
+                     const void* ws) {
+  const size_t e = esize(dtype), m = (size_t)c->batch * n_q, h = d->n_heads;
+  AttnSpans s;
+  s.x = bytes_at(x, m * d->d_model * e);
+  s.w_q = bytes_at(w_q, (size_t)d->d_model * h * (d->d_nope + d->d_rope) * e);
+  s.w_k_up = bytes_at(w_k_up, h * d->d_c * d->d_nope * e);
+  s.w_v_up = bytes_at(w_v_up, h * d->d_c * d->d_v * e);
+  s.out = bytes_at(out, m * h * d->d_v * e);
+  s.ws = bytes_at(ws, vmla_attention_workspace_bytes(d, c->batch, (int32_t)n_q));
+  s.cache = cache_span(d, c);
+  return s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -140,6 +194,7 @@ const char* vmla_status_string(int32_t s) {
     case VMLA_ERR_RANGE: return "t_first / n_frames / n_valid_frames / chunk or mask window out of range";
     case VMLA_ERR_WORKSPACE: return "workspace missing or too small";
     case VMLA_ERR_HIP: return "HIP launch failed";
+    case VMLA_ERR_OVERLAP: return "a buffer the call writes overlaps another buffer of the call";
     default: return "unknown status";
   }
 }
@@ -160,6 +215,12 @@ int32_t vmla_cache_append(const vmla_dims* dims, const vmla_cache* cache, int32_
   const int64_t T = (int64_t)cache->grid_h * cache->grid_w;
   const int64_t n_tok = T * n_frames;
   if (n_tok * dims->d_model > INT32_MAX) return VMLA_ERR_SHAPE;
+  const size_t e = esize(dtype);
+  st = check_disjoint({cache_span(dims, cache)},
+                      {bytes_at(x, (size_t)cache->batch * n_tok * dims->d_model * e),
+                       bytes_at(w_down, (size_t)dims->d_model * dims->d_c * e),
+                       bytes_at(w_kr, (size_t)dims->d_model * dims->d_rope * e)});
+  if (st) return st;
 
   AppendArgs a{};
   a.x = x; a.w_down = w_down; a.w_kr = w_kr; a.cache = cache->data;
@@ -264,6 +325,9 @@ int32_t vmla_query_prologue(const vmla_dims* dims, const vmla_cache* cache, int3
                                workspace_bytes, &q, &a);
   if (st) return st;
   if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_k_up)) return VMLA_ERR_ALIGN;
+  const AttnSpans sp = attn_spans(dims, cache, dtype, q.n_q, x, w_q, w_k_up, nullptr, nullptr, workspace);
+  st = check_disjoint({sp.ws}, {sp.x, sp.w_q, sp.w_k_up, sp.cache});
+  if (st) return st;
   q.x = x; q.w_q = w_q; q.w_k_up = w_k_up;
   return hip_status(launch_qprologue(q, dtype == VMLA_F32, static_cast<hipStream_t>(stream)));
 }
@@ -279,6 +343,10 @@ int32_t vmla_latent_attention(const vmla_dims* dims, const vmla_cache* cache, in
                                workspace_bytes, &q, &a);
   if (st) return st;
   if (!aligned16(w_v_up) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  const AttnSpans sp = attn_spans(dims, cache, dtype, a.n_q, nullptr, nullptr, nullptr, w_v_up, out,
+                                  workspace);
+  st = check_disjoint({sp.out}, {sp.ws, sp.w_v_up, sp.cache});
+  if (st) return st;
   a.w_v_up = w_v_up; a.out = out;
   return hip_status(launch_latent_attn(a, dtype == VMLA_F32, static_cast<hipStream_t>(stream)));
 }
@@ -296,6 +364,9 @@ int32_t vmla_chunk_attention(const vmla_dims* dims, const vmla_cache* cache, int
   if (st) return st;
   if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_k_up) || !aligned16(w_v_up) || !aligned16(out))
     return VMLA_ERR_ALIGN;
+  const AttnSpans sp = attn_spans(dims, cache, dtype, q.n_q, x, w_q, w_k_up, w_v_up, out, workspace);
+  st = check_disjoint({sp.ws, sp.out}, {sp.x, sp.w_q, sp.w_k_up, sp.w_v_up, sp.cache});
+  if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   q.x = x; q.w_q = w_q; q.w_k_up = w_k_up;
   st = hip_status(launch_qprologue(q, dtype == VMLA_F32, s));
@@ -319,6 +390,10 @@ int32_t vmla_fold_query_weights(const vmla_dims* dims, int32_t dtype, int32_t d_
   st = check_d_q(d_q);
   if (st) return st;
   if (!aligned16(w_uq) || !aligned16(w_k_up) || !aligned16(w_qa)) return VMLA_ERR_ALIGN;
+  const size_t e = esize(dtype), h = dims->n_heads;
+  st = check_disjoint({bytes_at(w_qa, (size_t)d_q * h * kRow * sizeof(uint16_t))},
+                      {bytes_at(w_uq, (size_t)d_q * h * kDHead * e), bytes_at(w_k_up, h * kDC * kDNope * e)});
+  if (st) return st;
   FoldArgs f{};
   f.w_first = w_uq; f.w_second = w_k_up; f.out = w_qa;
   f.d_in = d_q; f.n_heads = dims->n_heads;
@@ -332,6 +407,10 @@ int32_t vmla_fold_output_weights(const vmla_dims* dims, int32_t dtype, const voi
   if (!w_v_up || !w_o || !w_vo) return VMLA_ERR_NULL;
   if (dtype != VMLA_F32 && dtype != VMLA_BF16) return VMLA_ERR_DTYPE;
   if (!aligned16(w_v_up) || !aligned16(w_o) || !aligned16(w_vo)) return VMLA_ERR_ALIGN;
+  const size_t e = esize(dtype), h = dims->n_heads;
+  st = check_disjoint({bytes_at(w_vo, h * kDC * dims->d_model * sizeof(uint16_t))},
+                      {bytes_at(w_v_up, h * kDC * kDV * e), bytes_at(w_o, h * kDV * dims->d_model * e)});
+  if (st) return st;
   FoldArgs f{};
   f.w_first = w_v_up; f.w_second = w_o; f.out = w_vo;
   f.d_out = dims->d_model; f.n_heads = dims->n_heads;
@@ -406,6 +485,28 @@ int32_t launch_layer_attention(const vmla_dims* dims, const vmla_cache* cache, i
   return hip_status(launch_gemm(g, 0, dtype == VMLA_F32, s));
 }
 
+// Spans of the layer arguments: x [B, n_q, d_model], W_DQ [d_model, d_q],
+// W_QA [d_q, H 224] and W_VO [H 192, d_model] (bf16), out [B, n_q, d_model],
+// the layer workspace and the cache.
+struct LayerSpans {
+  Span x, w_dq, w_qa, w_vo, out, ws, cache;
+};
+
+LayerSpans layer_spans(const vmla_dims* d, const vmla_cache* c, int32_t dtype, int32_t d_q, int64_t n_q,
+                       const void* x, const void* w_dq, const void* w_qa, const void* w_vo,
+                       const void* out, const void* ws) {
+  const size_t e = esize(dtype), m = (size_t)c->batch * n_q, h = d->n_heads;
+  LayerSpans s;
+  s.x = bytes_at(x, m * d->d_model * e);
+  s.w_dq = bytes_at(w_dq, (size_t)d->d_model * d_q * e);
+  s.w_qa = bytes_at(w_qa, (size_t)d_q * h * kRow * sizeof(uint16_t));
+  s.w_vo = bytes_at(w_vo, h * kDC * d->d_model * sizeof(uint16_t));
+  s.out = bytes_at(out, m * d->d_model * e);
+  s.ws = bytes_at(ws, vmla_layer_workspace_bytes(d, d_q, c->batch, (int32_t)n_q));
+  s.cache = cache_span(d, c);
+  return s;
+}
+
 }  // namespace
 
 int32_t vmla_layer_query_prologue(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
@@ -420,6 +521,10 @@ int32_t vmla_layer_query_prologue(const vmla_dims* dims, const vmla_cache* cache
                            workspace_bytes, &q, &a, &inner);
   if (st) return st;
   if (!aligned16(x) || !aligned16(w_dq) || !aligned16(w_qa)) return VMLA_ERR_ALIGN;
+  const LayerSpans sp = layer_spans(dims, cache, dtype, d_q, q.n_q, x, w_dq, w_qa, nullptr, nullptr,
+                                    workspace);
+  st = check_disjoint({sp.ws}, {sp.x, sp.w_dq, sp.w_qa, sp.cache});
+  if (st) return st;
   return launch_layer_prologue(dims, cache, dtype, x, w_dq, d_q, w_qa, q, inner,
                                static_cast<hipStream_t>(stream));
 }
@@ -436,6 +541,10 @@ int32_t vmla_layer_attention(const vmla_dims* dims, const vmla_cache* cache, int
                            workspace_bytes, &q, &a, &inner);
   if (st) return st;
   if (!aligned16(w_vo) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  const LayerSpans sp = layer_spans(dims, cache, dtype, d_q, q.n_q, nullptr, nullptr, nullptr, w_vo, out,
+                                    workspace);
+  st = check_disjoint({sp.ws, sp.out}, {sp.w_vo, sp.cache});
+  if (st) return st;
   return launch_layer_attention(dims, cache, dtype, w_vo, out, a, inner, static_cast<hipStream_t>(stream));
 }
 
@@ -453,6 +562,9 @@ int32_t vmla_chunk_attention_layer(const vmla_dims* dims, const vmla_cache* cach
   if (st) return st;
   if (!aligned16(x) || !aligned16(w_dq) || !aligned16(w_qa) || !aligned16(w_vo) || !aligned16(out))
     return VMLA_ERR_ALIGN;
+  const LayerSpans sp = layer_spans(dims, cache, dtype, d_q, q.n_q, x, w_dq, w_qa, w_vo, out, workspace);
+  st = check_disjoint({sp.ws, sp.out}, {sp.x, sp.w_dq, sp.w_qa, sp.w_vo, sp.cache});
+  if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = launch_layer_prologue(dims, cache, dtype, x, w_dq, d_q, w_qa, q, inner, s);
   if (st) return st;
@@ -468,6 +580,10 @@ int32_t vmla_pack_kv_weights(const vmla_dims* dims, int32_t dtype, const void* w
   if (!w_k_up || !w_v_up || !w_kv) return VMLA_ERR_NULL;
   if (dtype != VMLA_F32 && dtype != VMLA_BF16) return VMLA_ERR_DTYPE;
   if (!aligned16(w_k_up) || !aligned16(w_v_up) || !aligned16(w_kv)) return VMLA_ERR_ALIGN;
+  const size_t e = esize(dtype), h = dims->n_heads;
+  st = check_disjoint({bytes_at(w_kv, kDC * h * (dims->d_nope + kDV) * e)},
+                      {bytes_at(w_k_up, h * kDC * dims->d_nope * e), bytes_at(w_v_up, h * kDC * kDV * e)});
+  if (st) return st;
   FoldArgs f{};
   f.w_first = w_k_up; f.w_second = w_v_up; f.out = w_kv; f.n_heads = dims->n_heads;
   f.d_nope = dims->d_nope;
@@ -481,6 +597,19 @@ size_t vmla_explicit_workspace_bytes(const vmla_dims* dims, int32_t batch, int32
 }
 
 namespace {
+
+// The explicit route writes its workspace (queries, then per-head K/V rows)
+// and out; it reads x, W_Q, the packed [W_K_up[h] | W_V_up[h]] and the cache.
+int32_t check_explicit_disjoint(const vmla_dims* d, const vmla_cache* c, int32_t dtype, int64_t n_q,
+                                int64_t n_k, const void* x, const void* w_q, const void* w_kv,
+                                const void* out, const void* ws) {
+  const size_t e = esize(dtype), m = (size_t)c->batch * n_q, h = d->n_heads;
+  return check_disjoint(
+      {bytes_at(ws, vmla_explicit_workspace_bytes(d, c->batch, (int32_t)n_q, (int32_t)n_k)),
+       bytes_at(out, m * h * d->d_v * e)},
+      {bytes_at(x, m * d->d_model * e), bytes_at(w_q, (size_t)d->d_model * h * kDHead * e),
+       bytes_at(w_kv, kDC * h * (d->d_nope + kDV) * e), cache_span(d, c)});
+}
 
 // Query GEMM, per-head K/V rebuild of slots [0, a.n_k), explicit attention
 // with a's query chunks.
@@ -541,6 +670,8 @@ int32_t vmla_chunk_attention_explicit(const vmla_dims* dims, const vmla_cache* c
   if (workspace_bytes < vmla_explicit_workspace_bytes(dims, cache->batch, a.n_q, a.n_k))
     return VMLA_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_kv) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  st = check_explicit_disjoint(dims, cache, dtype, a.n_q, a.n_k, x, w_q, w_kv, out, workspace);
+  if (st) return st;
   return run_explicit(dims, cache, dtype, x, w_q, w_kv, q, a, out, workspace,
                       static_cast<hipStream_t>(stream));
 }
@@ -596,6 +727,9 @@ int32_t vmla_chunk_causal_attention(const vmla_dims* dims, const vmla_cache* cac
     return VMLA_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_k_up) || !aligned16(w_v_up) || !aligned16(out))
     return VMLA_ERR_ALIGN;
+  const AttnSpans sp = attn_spans(dims, cache, dtype, q.n_q, x, w_q, w_k_up, w_v_up, out, workspace);
+  st = check_disjoint({sp.ws, sp.out}, {sp.x, sp.w_q, sp.w_k_up, sp.w_v_up, sp.cache});
+  if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   q.x = x; q.w_q = w_q; q.w_k_up = w_k_up;
   st = hip_status(launch_qprologue(q, dtype == VMLA_F32, s));
@@ -618,6 +752,10 @@ int32_t vmla_chunk_causal_latent_attention(const vmla_dims* dims, const vmla_cac
   if (workspace_bytes < vmla_attention_workspace_bytes(dims, cache->batch, a.n_q))
     return VMLA_ERR_WORKSPACE;
   if (!aligned16(w_v_up) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  const AttnSpans sp = attn_spans(dims, cache, dtype, a.n_q, nullptr, nullptr, nullptr, w_v_up, out,
+                                  workspace);
+  st = check_disjoint({sp.out}, {sp.ws, sp.w_v_up, sp.cache});
+  if (st) return st;
   a.w_v_up = w_v_up; a.out = out;
   return hip_status(launch_latent_attn(a, dtype == VMLA_F32, static_cast<hipStream_t>(stream)));
 }
@@ -639,6 +777,8 @@ int32_t vmla_chunk_causal_attention_explicit(const vmla_dims* dims, const vmla_c
   if (workspace_bytes < vmla_explicit_workspace_bytes(dims, cache->batch, a.n_q, a.n_k))
     return VMLA_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_kv) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  st = check_explicit_disjoint(dims, cache, dtype, a.n_q, a.n_k, x, w_q, w_kv, out, workspace);
+  if (st) return st;
   return run_explicit(dims, cache, dtype, x, w_q, w_kv, q, a, out, workspace,
                       static_cast<hipStream_t>(stream));
 }
@@ -651,6 +791,10 @@ int32_t vmla_output_projection(const vmla_dims* dims, int32_t dtype, int64_t m, 
   if (dtype != VMLA_F32 && dtype != VMLA_BF16) return VMLA_ERR_DTYPE;
   if (m < 1 || m > ((int64_t)1 << 31) / 128) return VMLA_ERR_SHAPE;
   if (!aligned16(in) || !aligned16(w_o) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  const size_t e = esize(dtype), hv = (size_t)dims->n_heads * kDV;
+  st = check_disjoint({bytes_at(out, (size_t)m * dims->d_model * e)},
+                      {bytes_at(in, (size_t)m * hv * e), bytes_at(w_o, hv * dims->d_model * e)});
+  if (st) return st;
   GemmArgs g{};
   g.a = in; g.w = w_o; g.out = out;
   g.m = m; g.k = dims->n_heads * kDV; g.n = dims->d_model; g.lda = g.k; g.mode = 0;

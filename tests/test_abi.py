@@ -33,8 +33,8 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.vmla_abi_version() == 7
-    for code in range(-7, 1):
+    assert lib.vmla_abi_version() == 8
+    for code in range(-8, 1):
         s = vm.vmla_status_string(code)
         assert s and s != "unknown status"
     assert vm.vmla_status_string(-99) == "unknown status"
@@ -321,6 +321,129 @@ def test_wide_latent_validation(lib):
         st = lib.vmla_chunk_causal_attention(ctypes.byref(d), ctypes.byref(_cache(window_frames=7)),
                                              vm.VMLA_BF16, A, B, C, A, 7, 3, 5, C, B, 1 << 30, None)
         assert st == vm.VMLA_ERR_SHAPE
+
+
+# Widely spaced fake device addresses (16 GiB apart) for the aliasing checks:
+# every call below is valid except for the one overlap it tests, which the
+# host validation must reject before any launch.
+def R(i):
+    return (1 << 40) + i * (1 << 34)
+
+
+def test_overlapping_buffers_are_rejected(lib):
+    d = vm.default_dims()
+    OV = vm.VMLA_ERR_OVERLAP
+    cache = _cache(data=R(0))            # 1 x 72 slots x 224 bf16 = 32,256 bytes
+    row = 224 * 2
+    ws_need = vm.vmla_attention_workspace_bytes(1, 24, d)      # 12 x 24 x 224 x 2
+    dr = ctypes.byref(d)
+    cr = ctypes.byref(cache)
+
+    # append: x, W_down or W_KR inside the cache it writes
+    assert _append(lib, cache=cache, x=R(0) + 10 * row, wd=R(2), wk=R(3)) == OV
+    assert _append(lib, cache=cache, x=R(1), wd=R(0) + 71 * row, wk=R(3)) == OV
+    assert _append(lib, cache=cache, x=R(1), wd=R(2), wk=R(0) - 16) == OV    # W_KR ends inside slot 0
+
+    def attn(x=R(1), wq=R(2), wku=R(3), wvu=R(4), out=R(5), ws=R(6)):
+        return lib.vmla_chunk_attention(dr, cr, vm.VMLA_BF16, x, wq, wku, wvu, 2, 1, 3, out, ws,
+                                        ws_need, None)
+    assert attn(ws=R(0) + 32256 - 16) == OV            # workspace starts in the cache's last row
+    assert attn(ws=R(0) - ws_need + 16) == OV          # workspace ends in the cache's first row
+    assert attn(out=R(6) + ws_need - 16) == OV         # out starts in the workspace's tail
+    assert attn(out=R(1)) == OV                        # out is x
+    assert attn(ws=R(2) + 1536 * 1536 * 2 - 16) == OV  # workspace starts in W_Q's tail
+    assert attn(wvu=R(5) + 16) == OV                   # out overlaps W_V_up
+    # the two stages
+    assert lib.vmla_query_prologue(dr, cr, vm.VMLA_BF16, R(1), R(2), R(3), 2, 1, 3, R(0), ws_need,
+                                   None) == OV
+    assert lib.vmla_latent_attention(dr, cr, vm.VMLA_BF16, R(4), 2, 1, 3, R(0) + 64, R(6), ws_need,
+                                     None) == OV
+    assert lib.vmla_latent_attention(dr, cr, vm.VMLA_BF16, R(4), 2, 1, 3, R(6) + 32, R(6), ws_need,
+                                     None) == OV
+
+    # the whole layer
+    lw = lib.vmla_layer_workspace_bytes(dr, 768, 1, 24)
+    assert lib.vmla_chunk_attention_layer(dr, cr, vm.VMLA_BF16, R(1), R(2), 768, R(3), R(4), 2, 1, 3,
+                                          R(6) + lw - 16, R(6), lw, None) == OV
+    assert lib.vmla_layer_query_prologue(dr, cr, vm.VMLA_BF16, R(1), R(2), 768, R(3), 2, 1, 3, R(0),
+                                         lw, None) == OV
+    assert lib.vmla_layer_attention(dr, cr, vm.VMLA_BF16, 768, R(4), 2, 1, 3, R(5), R(4), lw,
+                                     None) == OV
+    # explicit route
+    xw = vm.vmla_explicit_workspace_bytes(1, 24, 72, d)
+    assert lib.vmla_chunk_attention_explicit(dr, cr, vm.VMLA_BF16, R(1), R(2), R(3), 2, 1, 3, R(5),
+                                             R(0), xw, None) == OV
+    # whole clip
+    clip = _cache(data=R(0), window_frames=7)
+    need = vm.vmla_attention_workspace_bytes(1, 7 * 24, d)
+    assert lib.vmla_chunk_causal_attention(dr, ctypes.byref(clip), vm.VMLA_BF16, R(1), R(2), R(3),
+                                           R(4), 7, 3, 5, R(6), R(6), need, None) == OV
+    assert lib.vmla_chunk_causal_latent_attention(dr, ctypes.byref(clip), vm.VMLA_BF16, R(4), 7, 3, 5,
+                                                  R(0), R(6), need, None) == OV
+    big = vm.vmla_explicit_workspace_bytes(1, 7 * 24, 7 * 24, d)
+    assert lib.vmla_chunk_causal_attention_explicit(dr, ctypes.byref(clip), vm.VMLA_BF16, R(1), R(2),
+                                                    R(3), 7, 3, 5, R(5), R(1), big, None) == OV
+    # weight folds and packing, the unfolded mixer
+    assert lib.vmla_fold_query_weights(dr, vm.VMLA_BF16, 768, R(1), R(2), R(1) + 32, None) == OV
+    assert lib.vmla_fold_output_weights(dr, vm.VMLA_BF16, R(1), R(2), R(2), None) == OV
+    assert lib.vmla_pack_kv_weights(dr, vm.VMLA_BF16, R(1), R(2), R(1), None) == OV
+    assert lib.vmla_output_projection(dr, vm.VMLA_BF16, 8, R(1), R(2), R(1) + 16, None) == OV
+
+
+def test_valid_calls_reach_the_launchers(lib):
+    # Only in the host-only sanitizer build, whose launchers are counting stubs
+    # that return hipErrorNoDevice: every entry point, called with valid
+    # arguments at disjoint fake addresses, passes validation, fills its launch
+    # arguments and reaches a launcher (VMLA_ERR_HIP). No device is touched.
+    if not hasattr(lib, "vmla_stub_launch_count"):
+        pytest.skip("needs the host-only stub build (tests/test_abi_sanitizers.py)")
+    count = lib.vmla_stub_launch_count
+    count.restype = ctypes.c_int
+    HIP = vm.VMLA_ERR_HIP
+
+    def reaches(st):
+        before = reaches.n
+        reaches.n = count()
+        return st == HIP and reaches.n == before + 1
+    reaches.n = count()
+
+    for dims, cache_kw in [(vm.default_dims(), {}), (vm.default_dims(d_c=64), {}),
+                           (vm.default_dims(d_c=512), {}),
+                           (vm.default_dims(), dict(sink_frames=1, rope_at_read=1))]:
+        d = dims
+        cache = _cache(data=R(0), window_frames=21, grid_h=30, grid_w=52, batch=8, **cache_kw)
+        dr, cr = ctypes.byref(d), ctypes.byref(cache)
+        n_q = 3 * 1560
+        t_first = 18 + 4 * cache.sink_frames
+        n_valid = min(t_first + 3, 21 + cache.sink_frames)
+        ws = vm.vmla_attention_workspace_bytes(8, n_q, d)
+        assert reaches(lib.vmla_cache_append(dr, cr, vm.VMLA_BF16, R(1), R(2), R(3), t_first, 3, None))
+        assert reaches(lib.vmla_query_prologue(dr, cr, vm.VMLA_BF16, R(1), R(2), R(3), t_first, 3,
+                                               n_valid, R(6), ws, None))
+        assert reaches(lib.vmla_latent_attention(dr, cr, vm.VMLA_BF16, R(4), t_first, 3, n_valid, R(5),
+                                                 R(6), ws, None))
+        # the fused call stops at its first launcher
+        assert reaches(lib.vmla_chunk_attention(dr, cr, vm.VMLA_BF16, R(1), R(2), R(3), R(4), t_first, 3,
+                                                n_valid, R(5), R(6), ws, None))
+    d = vm.default_dims()
+    dr = ctypes.byref(d)
+    cache = _cache(data=R(0), window_frames=21, grid_h=30, grid_w=52, batch=2)
+    cr = ctypes.byref(cache)
+    lw = lib.vmla_layer_workspace_bytes(dr, 768, 2, 4680)
+    assert reaches(lib.vmla_chunk_attention_layer(dr, cr, vm.VMLA_BF16, R(1), R(2), 768, R(3), R(4), 18, 3,
+                                                  21, R(5), R(6), lw, None))
+    assert reaches(lib.vmla_layer_attention(dr, cr, vm.VMLA_BF16, 768, R(4), 18, 3, 21, R(5), R(6), lw,
+                                            None))
+    xw = vm.vmla_explicit_workspace_bytes(2, 4680, 32760, d)
+    assert reaches(lib.vmla_chunk_attention_explicit(dr, cr, vm.VMLA_BF16, R(1), R(2), R(3), 18, 3, 21,
+                                                     R(5), R(6), xw, None))
+    need = vm.vmla_attention_workspace_bytes(2, 21 * 1560, d)
+    assert reaches(lib.vmla_chunk_causal_latent_attention(dr, cr, vm.VMLA_BF16, R(4), 21, 3, 21, R(5),
+                                                          R(6), need, None))
+    assert reaches(lib.vmla_fold_query_weights(dr, vm.VMLA_BF16, 768, R(1), R(2), R(3), None))
+    assert reaches(lib.vmla_fold_output_weights(dr, vm.VMLA_BF16, R(1), R(2), R(3), None))
+    assert reaches(lib.vmla_pack_kv_weights(dr, vm.VMLA_BF16, R(1), R(2), R(3), None))
+    assert reaches(lib.vmla_output_projection(dr, vm.VMLA_BF16, 4680, R(1), R(2), R(3), None))
 
 
 def test_binding_cache_geometry():

@@ -77,16 +77,17 @@ def test_heads_sharing_a_workgroup(grid_h, grid_w):
 
 
 @pytest.mark.parametrize("grid_h,grid_w,batch", [
-    (3, 43, 1),     # M = 129: the last 128-row prologue tile holds one row (wave 0 only)
-    (10, 16, 1),    # 160: it ends at the end of wave 0's 32 rows
-    (7, 23, 1),     # 161: one row into wave 1
-    (15, 15, 1),    # 225: one row into wave 3
+    (3, 43, 1),     # M = 129: the last 128-row prologue tile holds one row (32-row slice 0)
+    (10, 16, 1),    # 160: it ends at the end of slice 0
+    (7, 23, 1),     # 161: one row into slice 1
+    (15, 15, 1),    # 225: one row into slice 3
     (15, 17, 1),    # 255: one row short of a full tile
     (9, 9, 2),      # 2 x 81 = 162: the tail tile starts inside batch element 1
 ])
 def test_query_tile_tails(grid_h, grid_w, batch):
-    # The query prologue cuts the batch x tokens rows into tiles of 128, 32 rows
-    # per wave; these counts end the last tile inside each wave's slice.
+    # The query prologue cuts the batch x tokens rows into tiles of 128; 32-row
+    # slice rh of a tile belongs to the wave pair 2 rh, 2 rh + 1 (one head
+    # each). These counts end the last tile inside each slice.
     w = custom(grid_h, grid_w, window_frames=2, chunk_frames=1, t_first=1, batch=batch)
     r = Run(w)
     out = _sync_np(r.chunk_step())

@@ -15,6 +15,13 @@ from workloads import config, custom, split_variant
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs an MI355X")
+    vm.load_library()
+
+
 def _np(t):
     torch.cuda.synchronize()
     return t.float().cpu().numpy()
