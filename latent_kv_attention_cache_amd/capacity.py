@@ -40,6 +40,33 @@ def max_batch(budget_bytes: float, per_request_bytes: float, fixed_bytes: float 
     return max(0, int((budget_bytes - fixed_bytes) // per_request_bytes))
 
 
+# Per-request memory slopes measured on the pages ([PL] §4 "Batch Scaling
+# Under Fixed Memory"), in GB per request: dense attention and the two ends of
+# the d_c sweep.
+PAGE_SLOPES_GB = {"mha": 6.26, 64: 0.57, 512: 1.43}
+
+
+def _model_cache_bytes(key, **window) -> int:
+    if key == "mha":
+        return cache_bytes_per_request(dense_scalars_per_token(), **window)
+    return cache_bytes_per_request(latent_scalars_per_token(key), **window)
+
+
+def overhead_from_slopes(slopes=PAGE_SLOPES_GB, **window) -> float:
+    """Per-request memory next to the cache, in bytes: the mean, over the
+    measured slopes, of slope minus the closed-form cache bytes. It does not
+    depend on the cache layout (activations of one request), so one value
+    serves every width."""
+    res = [slopes[k] * GB - _model_cache_bytes(k, **window) for k in slopes]
+    return sum(res) / len(res)
+
+
+def budget_window(limit_batch: int, per_request_bytes: float) -> tuple:
+    """Budgets (bytes, next to the fixed part) under which ``limit_batch`` is
+    the largest batch that fits: [B s, (B + 1) s)."""
+    return limit_batch * per_request_bytes, (limit_batch + 1) * per_request_bytes
+
+
 def sweep(d_cs=(64, 128, 192, 256, 512), budget_bytes: float = 288 * GB, fixed_bytes: float = 0.0,
           overhead_per_request: float = 0.0, **window) -> dict:
     """Cache bytes per request and the batch that fits, for dense attention and

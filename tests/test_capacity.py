@@ -46,3 +46,28 @@ def test_max_batch_and_sweep():
     assert s["d_c=64"]["cache_bytes"] < s["d_c=192"]["cache_bytes"] < s["d_c=512"]["cache_bytes"]
     # a sink frame adds one frame of slots per layer
     assert cap.cache_bytes_per_request(224, frames=6, sink_frames=1) == 30 * 7 * 1560 * 224 * 2
+
+
+def test_one_budget_reproduces_the_pages_batch_limits():
+    # [PL] §4 "Batch Scaling Under Fixed Memory": dense MHA reaches the memory
+    # limit at B = 28; d_c = 64 stays within budget at B = 320; 4.6x to at
+    # least 11.4x larger batches (8.0x at d_c = 192, [PL] "Key results").
+    # Reading: B = 28 is the largest dense batch that fits. Per request the
+    # model holds its closed-form cache plus one common overhead taken from the
+    # pages' slopes; the dense limit then fixes a budget window.
+    r = cap.overhead_from_slopes()
+    assert 0.25 * cap.GB < r < 0.40 * cap.GB            # ~0.32 GB of activations per request
+    mha = cap.cache_bytes_per_request(cap.dense_scalars_per_token()) + r
+    lo, hi = cap.budget_window(28, mha)
+    assert 178.0 * cap.GB < lo < 178.1 * cap.GB and 184.4 * cap.GB < hi < 184.5 * cap.GB
+    for budget in (lo + 1, 180 * cap.GB, hi - 1):
+        s = cap.sweep(budget_bytes=budget, overhead_per_request=r)
+        b = {k: v["max_batch"] for k, v in s.items()}
+        assert b["mha"] == 28                           # a 29th dense request runs out of memory
+        assert b["d_c=64"] >= 320                       # d_c = 64 still fits at B = 320
+        assert b["d_c=64"] / b["mha"] >= 11.4
+        assert round(b["d_c=512"] / b["mha"], 1) in (4.6, 4.7)   # the low end, 4.6x
+        assert 7.5 < b["d_c=192"] / b["mha"] < 8.7      # 8.0x at the default width
+    # at 180 GB: 28 dense requests against 352 / 236 / 129 at d_c = 64 / 192 / 512
+    s = cap.sweep(budget_bytes=180 * cap.GB, overhead_per_request=r)
+    assert [s[k]["max_batch"] for k in ("mha", "d_c=64", "d_c=192", "d_c=512")] == [28, 352, 236, 129]
