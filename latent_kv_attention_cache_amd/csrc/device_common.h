@@ -113,6 +113,36 @@ __device__ __forceinline__ void sincos_rev(int pos, uint32_t lo, uint32_t hi, fl
   *c = __builtin_amdgcn_cosf(r);
 }
 
+// RoPE rates of pair j0 + 2 g for the lane's 16-lane group g (0..3), with
+// j0 uniform across the wave, from a by-value kernel-argument table (arrays
+// rev_lo, rev_hi, axis). The four candidates are read with scalar loads and
+// each lane keeps its own: indexing a kernel argument with a per-lane index
+// compiles to per-lane loads from the kernel-argument segment, whose latency
+// then sits in the epilogue's critical path.
+template <typename Table>
+__device__ __forceinline__ void rope_rate_by_group(const Table& t, int j0, int g, uint32_t* lo,
+                                                   uint32_t* hi, int* ax) {
+  // readfirstlane on each loaded candidate keeps the compiler from turning
+  // "select after load" back into a per-lane load of the selected entry
+  const int j = __builtin_amdgcn_readfirstlane(j0);
+  uint32_t l = __builtin_amdgcn_readfirstlane(t.rev_lo[j]), h = __builtin_amdgcn_readfirstlane(t.rev_hi[j]);
+  int x = __builtin_amdgcn_readfirstlane(t.axis[j]);
+#pragma unroll
+  for (int k = 1; k < 4; ++k) {
+    const uint32_t lk = __builtin_amdgcn_readfirstlane(t.rev_lo[j + 2 * k]);
+    const uint32_t hk = __builtin_amdgcn_readfirstlane(t.rev_hi[j + 2 * k]);
+    const int xk = __builtin_amdgcn_readfirstlane(t.axis[j + 2 * k]);
+    if (g == k) {
+      l = lk;
+      h = hk;
+      x = xk;
+    }
+  }
+  *lo = l;
+  *hi = h;
+  *ax = x;
+}
+
 __device__ __forceinline__ float max_across_halves(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

@@ -301,7 +301,9 @@ void gemm_kernel(GemmArgs a) {
       const int h = col / a.head_w;
       const int ci = col - h * a.head_w;
       const bool rope = ci >= a.rope_off;
-      const int pr = (ci - a.rope_off) >> 1;           // first of the lane's two pairs
+      // first of the lane's two pairs: (ci - rope_off) / 2 = pb + 2 g, pb the
+      // 16-column block's first pair (blocks never straddle a head)
+      const int pb = (ci - 4 * g - a.rope_off) >> 1;
 #pragma unroll
       for (int rb = 0; rb < kNRB; ++rb) {
         if (qrow[rb] < 0) continue;
@@ -309,8 +311,11 @@ void gemm_kernel(GemmArgs a) {
         if (rope) {
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
+            uint32_t lo, hi;
+            int ax;
+            rope_rate_by_group(a.rope, pb + q, g, &lo, &hi, &ax);
             float sn, cs;
-            sincos_rev(pos[rb][a.rope.axis[pr + q]], a.rope.rev_lo[pr + q], a.rope.rev_hi[pr + q], &sn, &cs);
+            sincos_rev(pos[rb][ax], lo, hi, &sn, &cs);
             const float x0 = v[2 * q], x1 = v[2 * q + 1];
             v[2 * q] = x0 * cs - x1 * sn;
             v[2 * q + 1] = x0 * sn + x1 * cs;

@@ -268,9 +268,11 @@ void qprologue_kernel(QArgs a) {
       float o[4];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const int pr = 8 * (cb - kDNope / 16) + 2 * g + q;
+        uint32_t lo, hi;
+        int ax;
+        rope_rate_by_group(a.rope, 8 * (cb - kDNope / 16) + q, g, &lo, &hi, &ax);   // pair 8 (cb - DN/16) + 2 g + q
         float sn, cs;
-        sincos_rev(pos[rb][a.rope.axis[pr]], a.rope.rev_lo[pr], a.rope.rev_hi[pr], &sn, &cs);
+        sincos_rev(pos[rb][ax], lo, hi, &sn, &cs);
         o[2 * q] = v[2 * q] * cs - v[2 * q + 1] * sn;
         o[2 * q + 1] = v[2 * q] * sn + v[2 * q + 1] * cs;
       }
