@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define VMLA_ABI_VERSION 8
+#define VMLA_ABI_VERSION 9
 
 typedef enum vmla_status {
   VMLA_OK = 0,
@@ -200,6 +200,33 @@ int32_t vmla_chunk_attention(const vmla_dims* dims, const vmla_cache* cache, int
                              const void* w_v_up, int32_t t_first, int32_t n_frames,
                              int32_t n_valid_frames, void* out, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* Size of the library-owned scratch array of vmla_chunk_attention_noalloc:
+ * 32 MiB on each GPU the library runs on, held until the process ends. */
+#define VMLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * vmla_chunk_attention_noalloc -- vmla_chunk_attention without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. It
+ * calls no hipMalloc, hipFree or allocating routine. The query rows go to a
+ * library-owned array of VMLA_NOALLOC_SCRATCH_BYTES on the current device
+ * (its address is looked up on the first call on that device).
+ *
+ * Arguments, results and errors as vmla_chunk_attention; the call needs
+ * vmla_attention_workspace_bytes(dims, batch, n_q) <= VMLA_NOALLOC_SCRATCH_BYTES
+ * (e.g. 4680 query tokens at batch 1 with the default widths: 25.2 MB) and
+ * returns VMLA_ERR_WORKSPACE otherwise, before any HIP call.
+ *
+ * Every call on a GPU uses that GPU's one array: calls that overlap in time
+ * on one GPU (concurrent streams, other host threads) race and corrupt each
+ * other's results; serialize them. The array keeps the last call's contents;
+ * nothing in it needs to start at zero.
+ */
+int32_t vmla_chunk_attention_noalloc(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                                     const void* x, const void* w_q, const void* w_k_up,
+                                     const void* w_v_up, int32_t t_first, int32_t n_frames,
+                                     int32_t n_valid_frames, void* out, void* stream);
 
 /*
  * The two stages of vmla_chunk_attention, callable separately (same arguments,

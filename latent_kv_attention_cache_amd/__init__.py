@@ -14,7 +14,8 @@ from ._binding import (VMLA_OK, VMLA_ERR_NULL, VMLA_ERR_SHAPE, VMLA_ERR_DTYPE, V
                        vmla_chunk_attention_layer, vmla_layer_query_prologue, vmla_layer_attention,
                        vmla_output_projection, vmla_pack_kv_weights, vmla_explicit_workspace_bytes,
                        vmla_chunk_attention_explicit, vmla_chunk_causal_attention,
-                       vmla_chunk_causal_latent_attention, vmla_chunk_causal_attention_explicit)
+                       vmla_chunk_causal_latent_attention, vmla_chunk_causal_attention_explicit,
+                       vmla_chunk_attention_noalloc, VMLA_NOALLOC_SCRATCH_BYTES)
 
 __all__ = [
     "VMLA_OK", "VMLA_ERR_NULL", "VMLA_ERR_SHAPE", "VMLA_ERR_DTYPE", "VMLA_ERR_ALIGN",
@@ -28,4 +29,5 @@ __all__ = [
     "vmla_output_projection", "vmla_pack_kv_weights", "vmla_explicit_workspace_bytes",
     "vmla_chunk_attention_explicit", "vmla_chunk_causal_attention",
     "vmla_chunk_causal_latent_attention", "vmla_chunk_causal_attention_explicit",
+    "vmla_chunk_attention_noalloc", "VMLA_NOALLOC_SCRATCH_BYTES",
 ]

@@ -64,7 +64,10 @@ EXPORTED = ("vmla_default_dims", "vmla_cache_append", "vmla_attention_workspace_
             "vmla_output_projection", "vmla_pack_kv_weights", "vmla_explicit_workspace_bytes",
             "vmla_chunk_attention_explicit", "vmla_chunk_causal_attention",
             "vmla_chunk_causal_latent_attention", "vmla_chunk_causal_attention_explicit",
-            "vmla_status_string", "vmla_abi_version")
+            "vmla_chunk_attention_noalloc", "vmla_status_string", "vmla_abi_version")
+
+# Size of the library-owned scratch array of vmla_chunk_attention_noalloc.
+VMLA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def load_library(path: str | None = None) -> ctypes.CDLL:
@@ -92,6 +95,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.vmla_chunk_attention.argtypes = [ctypes.POINTER(vmla_dims), ctypes.POINTER(vmla_cache), I32,
                                          P, P, P, P, I32, I32, I32, P, P, ctypes.c_size_t, P]
     lib.vmla_chunk_attention.restype = I32
+    lib.vmla_chunk_attention_noalloc.argtypes = [ctypes.POINTER(vmla_dims), ctypes.POINTER(vmla_cache), I32,
+                                                 P, P, P, P, I32, I32, I32, P, P]
+    lib.vmla_chunk_attention_noalloc.restype = I32
     lib.vmla_query_prologue.argtypes = [ctypes.POINTER(vmla_dims), ctypes.POINTER(vmla_cache), I32,
                                         P, P, P, I32, I32, I32, P, ctypes.c_size_t, P]
     lib.vmla_query_prologue.restype = I32
@@ -288,6 +294,36 @@ def vmla_chunk_attention(cache: LatentCache, x: torch.Tensor, w_q: torch.Tensor,
                                   workspace.numel() * workspace.element_size(), _stream(stream))
     if st != VMLA_OK:
         raise VmlaError(st, "vmla_chunk_attention")
+    return out
+
+
+def vmla_chunk_attention_noalloc(cache: LatentCache, x: torch.Tensor, w_q: torch.Tensor,
+                                 w_k_up: torch.Tensor, w_v_up: torch.Tensor, t_first: int,
+                                 n_frames: int, n_valid_frames: int, out: torch.Tensor,
+                                 dims: vmla_dims | None = None, stream=None) -> torch.Tensor:
+    """vmla_chunk_attention with the library's own scratch array instead of a
+    workspace: the call allocates nothing (``out`` is the caller's). Calls that
+    overlap in time on one GPU race on that array."""
+    lib = load_library()
+    d = dims or default_dims()
+    B, T = cache.batch, cache.tokens_per_frame
+    n_q = n_frames * T
+    _expect_shape(x, (B, n_q, d.d_model), "x")
+    _expect_shape(w_q, (d.d_model, d.n_heads * (d.d_nope + d.d_rope)), "w_q")
+    _expect_shape(w_k_up, (d.n_heads, d.d_c, d.d_nope), "w_k_up")
+    _expect_shape(w_v_up, (d.n_heads, d.d_c, d.d_v), "w_v_up")
+    _expect_shape(out, (B, n_q, d.n_heads, d.d_v), "out")
+    for t, n in ((x, "x"), (w_q, "w_q"), (w_k_up, "w_k_up"), (w_v_up, "w_v_up"), (out, "out")):
+        if t.dtype != cache.data.dtype:
+            raise TypeError(f"{n} dtype {t.dtype} differs from the cache's {cache.data.dtype}")
+    _dev(cache.data, "cache")
+    cs = cache.c_struct()
+    st = lib.vmla_chunk_attention_noalloc(ctypes.byref(d), ctypes.byref(cs), _dtype_code(cache.data),
+                                          _dev(x, "x"), _dev(w_q, "w_q"), _dev(w_k_up, "w_k_up"),
+                                          _dev(w_v_up, "w_v_up"), int(t_first), int(n_frames),
+                                          int(n_valid_frames), _dev(out, "out"), _stream(stream))
+    if st != VMLA_OK:
+        raise VmlaError(st, "vmla_chunk_attention_noalloc")
     return out
 
 

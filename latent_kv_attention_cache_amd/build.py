@@ -22,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["vmla_api.cpp", "append.hip", "qprologue.hip", "latent_attn.hip", "latent_attn_wide.hip",
-           "mixer_gemm.hip", "explicit_attn.hip"]
+           "mixer_gemm.hip", "explicit_attn.hip", "noalloc.hip"]
 # Per-source extra flags. The attention kernel never reads NaNs (slots past the
 # valid prefix are not loaded), so max() needs no NaN canonicalization.
 EXTRA_FLAGS = {"latent_attn.hip": ["-fno-honor-nans"], "latent_attn_wide.hip": ["-fno-honor-nans"]}

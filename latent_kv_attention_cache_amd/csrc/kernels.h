@@ -133,5 +133,8 @@ hipError_t launch_fold_query(const FoldArgs& a, bool f32, hipStream_t s);
 hipError_t launch_fold_output(const FoldArgs& a, bool f32, hipStream_t s);
 hipError_t launch_explicit_attn(const ExplicitArgs& a, bool f32, hipStream_t s);
 hipError_t launch_pack_kv(const FoldArgs& a, bool f32, hipStream_t s);
+// Device address of this GPU's library-owned scratch array
+// (VMLA_NOALLOC_SCRATCH_BYTES), looked up once per device.
+hipError_t scratch_buffer(void** ptr);
 
 }  // namespace vmla

@@ -351,28 +351,62 @@ int32_t vmla_latent_attention(const vmla_dims* dims, const vmla_cache* cache, in
   return hip_status(launch_latent_attn(a, dtype == VMLA_F32, static_cast<hipStream_t>(stream)));
 }
 
-int32_t vmla_chunk_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
-                             const void* x, const void* w_q, const void* w_k_up,
-                             const void* w_v_up, int32_t t_first, int32_t n_frames,
-                             int32_t n_valid_frames, void* out, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+namespace {
+
+// The attention core: the query prologue into the workspace, then the latent
+// attention. With use_scratch the Qhat rows go to the library's scratch array
+// instead of a caller's workspace: every host-side check runs first, against
+// its size at a stand-in address, and its device address is looked up last.
+int32_t chunk_attention_run(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                            const void* x, const void* w_q, const void* w_k_up, const void* w_v_up,
+                            int32_t t_first, int32_t n_frames, int32_t n_valid_frames, void* out,
+                            void* workspace, size_t workspace_bytes, bool use_scratch,
+                            void* stream) {
   if (!x || !w_q || !w_k_up || !w_v_up || !out) return VMLA_ERR_NULL;
   QArgs q;
   AttnArgs a;
-  int32_t st = check_attention(dims, cache, dtype, t_first, n_frames, n_valid_frames, workspace,
-                               workspace_bytes, &q, &a);
+  void* ws = use_scratch ? reinterpret_cast<void*>(uintptr_t{256}) : workspace;
+  const size_t ws_bytes = use_scratch ? (size_t)VMLA_NOALLOC_SCRATCH_BYTES : workspace_bytes;
+  int32_t st = check_attention(dims, cache, dtype, t_first, n_frames, n_valid_frames, ws, ws_bytes,
+                               &q, &a);
   if (st) return st;
   if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_k_up) || !aligned16(w_v_up) || !aligned16(out))
     return VMLA_ERR_ALIGN;
-  const AttnSpans sp = attn_spans(dims, cache, dtype, q.n_q, x, w_q, w_k_up, w_v_up, out, workspace);
+  AttnSpans sp = attn_spans(dims, cache, dtype, q.n_q, x, w_q, w_k_up, w_v_up, out, workspace);
+  if (use_scratch) sp.ws = Span{0, 0};        // library memory: no caller buffer can overlap it
   st = check_disjoint({sp.ws, sp.out}, {sp.x, sp.w_q, sp.w_k_up, sp.w_v_up, sp.cache});
   if (st) return st;
+  if (use_scratch) {
+    void* p = nullptr;
+    if (scratch_buffer(&p) != hipSuccess) return VMLA_ERR_HIP;
+    q.qhat = static_cast<uint16_t*>(p);
+    a.qhat = q.qhat;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   q.x = x; q.w_q = w_q; q.w_k_up = w_k_up;
   st = hip_status(launch_qprologue(q, dtype == VMLA_F32, s));
   if (st) return st;
   a.w_v_up = w_v_up; a.out = out;
   return hip_status(launch_latent_attn(a, dtype == VMLA_F32, s));
+}
+
+}  // namespace
+
+int32_t vmla_chunk_attention(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                             const void* x, const void* w_q, const void* w_k_up,
+                             const void* w_v_up, int32_t t_first, int32_t n_frames,
+                             int32_t n_valid_frames, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return chunk_attention_run(dims, cache, dtype, x, w_q, w_k_up, w_v_up, t_first, n_frames,
+                             n_valid_frames, out, workspace, workspace_bytes, false, stream);
+}
+
+int32_t vmla_chunk_attention_noalloc(const vmla_dims* dims, const vmla_cache* cache, int32_t dtype,
+                                     const void* x, const void* w_q, const void* w_k_up,
+                                     const void* w_v_up, int32_t t_first, int32_t n_frames,
+                                     int32_t n_valid_frames, void* out, void* stream) {
+  return chunk_attention_run(dims, cache, dtype, x, w_q, w_k_up, w_v_up, t_first, n_frames,
+                             n_valid_frames, out, nullptr, 0, true, stream);
 }
 
 // ---- the whole attention layer: query latent and folded output mixer

@@ -26,6 +26,7 @@ hipError_t launch_fold_query(const FoldArgs&, bool, hipStream_t) { return counte
 hipError_t launch_fold_output(const FoldArgs&, bool, hipStream_t) { return counted(); }
 hipError_t launch_explicit_attn(const ExplicitArgs&, bool, hipStream_t) { return counted(); }
 hipError_t launch_pack_kv(const FoldArgs&, bool, hipStream_t) { return counted(); }
+hipError_t scratch_buffer(void**) { return hipErrorNoDevice; }
 }  // namespace vmla
 
 // Number of launcher calls reached so far (present only in the stub build).

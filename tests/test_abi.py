@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.vmla_abi_version() == 8
+    assert lib.vmla_abi_version() == 9
     for code in range(-8, 1):
         s = vm.vmla_status_string(code)
         assert s and s != "unknown status"
@@ -444,6 +444,42 @@ def test_valid_calls_reach_the_launchers(lib):
     assert reaches(lib.vmla_fold_output_weights(dr, vm.VMLA_BF16, R(1), R(2), R(3), None))
     assert reaches(lib.vmla_pack_kv_weights(dr, vm.VMLA_BF16, R(1), R(2), R(3), None))
     assert reaches(lib.vmla_output_projection(dr, vm.VMLA_BF16, 4680, R(1), R(2), R(3), None))
+    # the no-allocation entry point passes every check and stops at the scratch
+    # lookup (a stub without a device here), before any launch
+    wan1 = _cache(data=R(0), window_frames=21, grid_h=30, grid_w=52)
+    before = count()
+    assert lib.vmla_chunk_attention_noalloc(dr, ctypes.byref(wan1), vm.VMLA_BF16, R(1), R(2), R(3), R(4), 18,
+                                            3, 21, R(5), None) == HIP
+    assert count() == before
+
+
+def test_noalloc_validation(lib):
+    # every host-side check runs before the scratch array is looked up (the
+    # only HIP call before the launches); none of these calls reaches it
+    d = vm.default_dims()
+    dr = ctypes.byref(d)
+
+    def call(cache, x=R(1), wq=R(2), wku=R(3), wvu=R(4), out=R(5), t_first=18, n_frames=3, n_valid=21,
+             dtype=vm.VMLA_BF16, dims=dr):
+        return lib.vmla_chunk_attention_noalloc(dims, ctypes.byref(cache), dtype, x, wq, wku, wvu, t_first,
+                                                n_frames, n_valid, out, None)
+    wan = _cache(data=R(0), window_frames=21, grid_h=30, grid_w=52)
+    assert vm.VMLA_NOALLOC_SCRATCH_BYTES == 32 << 20
+    # 4680 queries at B = 1 need 25.2 MB: fits; at B = 2, 50.3 MB: too large
+    assert vm.vmla_attention_workspace_bytes(1, 4680, d) <= vm.VMLA_NOALLOC_SCRATCH_BYTES
+    assert call(_cache(data=R(0), window_frames=21, grid_h=30, grid_w=52, batch=2)) == vm.VMLA_ERR_WORKSPACE
+    assert call(_cache(data=R(0), window_frames=21, grid_h=30, grid_w=52, batch=16), t_first=20,
+                n_frames=1) == vm.VMLA_ERR_WORKSPACE
+    assert call(wan, x=None) == vm.VMLA_ERR_NULL
+    assert call(wan, out=None) == vm.VMLA_ERR_NULL
+    assert lib.vmla_chunk_attention_noalloc(None, ctypes.byref(wan), 1, R(1), R(2), R(3), R(4), 18, 3, 21,
+                                            R(5), None) == vm.VMLA_ERR_NULL
+    assert call(wan, out=MIS) == vm.VMLA_ERR_ALIGN
+    assert call(wan, dtype=vm.VMLA_F32) == vm.VMLA_ERR_DTYPE
+    assert call(wan, n_valid=20) == vm.VMLA_ERR_RANGE
+    assert call(wan, dims=ctypes.byref(vm.default_dims(d_v=64))) == vm.VMLA_ERR_SHAPE
+    assert call(wan, out=R(1)) == vm.VMLA_ERR_OVERLAP                    # out is x
+    assert call(wan, out=R(0) + 64) == vm.VMLA_ERR_OVERLAP               # out inside the cache
 
 
 def test_binding_cache_geometry():
