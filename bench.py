@@ -26,7 +26,15 @@ Wan-1.3B clip (32,760 tokens) appended, every token a query, 3-frame chunks
 under the chunk-causal block mask (with `--explicit`: through explicit per-head
 K/V of the whole clip).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--config 2|3|4]
+`--config 5` times the minute-scale rollout at B=8 (80 chunks x 4 denoising steps
+x 30 layers over a 21-frame ring) as one step-layer per distinct window length,
+weighted by how often the rollout runs it.
+
+The default run also times the append at the batch-8 shape on cold buffers
+(`append_cold`, the HBM-graded figure) and reports the attention kernel's
+algorithmic GB/s next to its TFLOP/s.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--config 2|3|4|5]
                        [--long-horizon] [--layer] [--explicit] [--d-c 64|128|192] [--chunk-causal]
 """
 from __future__ import annotations
@@ -198,6 +206,110 @@ def cpu_baseline(w, wts, x_host, step_flops, mix=None):
     }
 
 
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_sampled(w, rows=512):
+    """The oracle on a bounded sample of a batch-B step: one batch element of
+    one layer (seeded host inputs), its cache window built, then ``rows`` of
+    the chunk's query rows over the full window. Rows are independent, so the
+    step time is extrapolated linearly: B x (window build + N_q / rows x the
+    rows' time); the rate is the sample's own algorithmic flops over its time."""
+    import numpy as np
+    import oracle.vmla_oracle as orc
+    from workloads import weights, x_frame
+    wts = weights(w)
+    xs = {t: x_frame(w, t) for t in range(w.t_first + w.chunk_frames - min(w.window_frames, w.t_first + w.chunk_frames),
+                                           w.t_first + w.chunk_frames)}
+    idx = np.linspace(0, w.n_q - 1, rows).astype(np.int64)
+    t0 = time.perf_counter()
+    orc.chunk_attention_reference(w, wts, lambda t: xs[t], idx[:1])
+    t_build = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    orc.chunk_attention_reference(w, wts, lambda t: xs[t], idx)
+    t_all = time.perf_counter() - t0
+    t_rows = max(t_all - t_build, 1e-9)
+    per_q = 2 * (w.d_c + w.d_rope) * w.n_k * w.n_heads + 2 * w.n_heads * w.d_c * w.d_v + \
+        2 * w.d_model * w.n_heads * w.d_head + w.n_heads * 2 * w.d_nope * w.d_c
+    step_s = w.batch * (t_build + t_rows * w.n_q / rows)
+    log(f"[cpu_baseline] oracle sample: window build {t_build:.2f} s, {rows} rows {t_rows:.2f} s; "
+        f"extrapolated step {step_s:.1f} s")
+    return {
+        "value": rows * per_q / t_all / 1e12, "unit": "TFLOP/s", "cores": int(_threads()),
+        "kind": "oracle", "ms_per_step": step_s * 1e3, "extrapolated": True,
+        "sample": (f"one batch element of one layer: numpy fp64 oracle (explicit per-head K/V) "
+                   f"building its {w.n_k}-key window ({t_build:.1f} s), then {rows} of the "
+                   f"chunk's {w.n_q} query rows over it ({t_rows:.1f} s); rate = the sample's "
+                   f"algorithmic flops / its time; ms_per_step extrapolated linearly to "
+                   f"{w.batch} elements x {w.n_q} rows"),
+    }
+
+
+def _noise_sets(w, dims, n_sets, dev, seed, layer=False):
+    """Device-noise buffer sets (x, weights, cache) for the batched workloads:
+    values do not change the work, and one set per layer keeps the append and
+    the prologue reading HBM rather than the Infinity Cache."""
+    import torch
+    import latent_kv_attention_cache_amd as vm
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    shapes = {"w_q": (w.d_model, w.n_heads * w.d_head), "w_down": (w.d_model, w.d_c),
+              "w_kr": (w.d_model, w.d_rope), "w_k_up": (w.n_heads, w.d_c, w.d_nope),
+              "w_v_up": (w.n_heads, w.d_c, w.d_v)}
+    if layer:
+        shapes.update({"w_dq": (w.d_model, w.d_q), "w_uq": (w.d_q, w.n_heads * w.d_head),
+                       "w_o": (w.n_heads * w.d_v, w.d_model)})
+    sets = []
+    for _ in range(n_sets):
+        dw = {k: (torch.randn(shp, generator=g, device=dev) * shp[-2] ** -0.5).to(torch.bfloat16)
+              for k, shp in shapes.items()}
+        cache = vm.LatentCache.empty(w.batch, w.window_frames, w.grid_h, w.grid_w, device=dev, dims=dims)
+        cache.data.normal_(generator=g)
+        x = torch.randn((w.batch, w.n_q, w.d_model), generator=g, device=dev).to(torch.bfloat16)
+        sets.append((x, dw, cache))
+    return sets
+
+
+def append_cold(dev, reps=60):
+    """The append at the batch-8 chunk shape (8 x 4680 tokens, 132.5 MB of
+    algorithmic traffic) on 30 rotating buffer sets (7 GB, far beyond the 256 MB
+    Infinity Cache), timed with HIP events on the launch stream: the HBM-graded
+    append figure."""
+    import torch
+    import latent_kv_attention_cache_amd as vm
+    from workloads import config
+    w = config(3)
+    dims = vm.default_dims()
+    sets = _noise_sets(w, dims, w.n_layers, dev, seed=33)
+    stream = torch.cuda.current_stream()
+    for i in range(10):
+        x, dw, cache = sets[i % len(sets)]
+        vm.vmla_cache_append(cache, x, dw["w_down"], dw["w_kr"], w.t_first, w.chunk_frames, dims=dims)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        x, dw, cache = sets[i % len(sets)]
+        ev[i][0].record(stream)
+        vm.vmla_cache_append(cache, x, dw["w_down"], dw["w_kr"], w.t_first, w.chunk_frames, dims=dims)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    med = us[len(us) // 2]
+    nbytes = work(w)["bytes_append"]
+    del sets
+    torch.cuda.empty_cache()
+    gbs = nbytes / (med * 1e-6) / 1e9
+    log(f"[bench] cold append (B=8, 4680 tokens, 30 buffer sets): {med:.1f} us = {gbs:.0f} GB/s")
+    return {"workload": "append at the batch-8 chunk shape: 8 x 4680 tokens, 30 rotating buffer sets "
+                        "(7 GB, cold: not served by the Infinity Cache)",
+            "bound": "hbm", "us": round(med, 2), "bytes_per_launch": nbytes, "achieved": round(gbs, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,9 +317,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed steps first; the shader clock needs tens of ms of load to settle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4),
+    ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4, 5),
                     help="2: Wan-1.3B chunk-layer at B=1 (the reported workload); 3: B=8, 30 "
-                         "layers; 4: B=16, one-frame chunk")
+                         "layers; 4: B=16, one-frame chunk; 5: the minute-scale rollout at B=8 "
+                         "(80 chunks x 4 steps x 30 layers, as a weighted sum over its window lengths)")
     ap.add_argument("--long-horizon", action="store_true",
                     help="with --config 2: the long-rollout cache instead of the 21-frame window -- "
                          "one sink frame plus a 6-frame window, k_R cached before RoPE and "
@@ -257,6 +370,12 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy: {nbytes} bytes read and {nbytes} bytes written")
         del src, dst
+    if args.config == 5:
+        if args.chunk_causal or args.long_horizon or args.layer or args.explicit or args.d_c != 192 \
+                or args.split != 32:
+            print("--config 5 runs the attention core at the default widths", file=sys.stderr)
+            sys.exit(2)
+        return rollout_bench(args, dev)
     if args.chunk_causal:
         if args.config != 2 or args.long_horizon or args.layer or args.d_c != 192 or args.split != 32:
             print("--chunk-causal runs the Wan-1.3B clip at B=1 (config 2 shapes), with or without "
@@ -314,23 +433,7 @@ def main():
     else:
         # one buffer set per layer (config 3) or eight rotating sets (config 4)
         n_sets = w.n_layers if w.n_layers > 1 else 8
-        g = torch.Generator(device=dev)
-        g.manual_seed(w.cfg_id)
-        shapes = {"w_q": (w.d_model, w.n_heads * w.d_head), "w_down": (w.d_model, w.d_c),
-                  "w_kr": (w.d_model, w.d_rope), "w_k_up": (w.n_heads, w.d_c, w.d_nope),
-                  "w_v_up": (w.n_heads, w.d_c, w.d_v)}
-        if args.layer:
-            shapes.update({"w_dq": (w.d_model, w.d_q), "w_uq": (w.d_q, w.n_heads * w.d_head),
-                           "w_o": (w.n_heads * w.d_v, w.d_model)})
-        sets = []
-        for _ in range(n_sets):
-            dw = {k: (torch.randn(shp, generator=g, device=dev) * shp[-2] ** -0.5).to(torch.bfloat16)
-                  for k, shp in shapes.items()}
-            cache = vm.LatentCache.empty(w.batch, w.window_frames, w.grid_h, w.grid_w, device=dev,
-                                         dims=dims)
-            cache.data.normal_(generator=g)
-            x = torch.randn((w.batch, w.n_q, w.d_model), generator=g, device=dev).to(torch.bfloat16)
-            sets.append((x, dw, cache))
+        sets = _noise_sets(w, dims, n_sets, dev, seed=w.cfg_id, layer=args.layer)
         log(f"[bench] {n_sets} buffer sets of "
             f"{(sets[0][0].numel() + sets[0][2].data.numel()) * 2 / 1e6:.0f} MB")
     n_valid = w.n_valid_frames
@@ -456,6 +559,11 @@ def main():
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "flops_per_launch": wk["attn_kernel"],
+            # algorithmic bytes (Qhat, the window's cache rows, W_V_up, out) per
+            # launch over its time, next to the 8 TB/s of HBM
+            "bytes_per_launch": wk["bytes_attn"],
+            "gbs": round(wk["bytes_attn"] / (k_ms["latent_attn"] * 1e-3) / 1e9, 1),
+            "gbs_frac_of_hbm": round(wk["bytes_attn"] / (k_ms["latent_attn"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         },
         "append_roofline": {
             "bound": "hbm", "achieved": round(append_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -467,6 +575,16 @@ def main():
     if not args.no_cpu_baseline and args.config == 2:
         xh = lambda t: xs[t]  # noqa: E731
         result["cpu_baseline"] = cpu_baseline(w, wts, xh, wk["step"], mix)
+    elif not args.no_cpu_baseline and args.config in (3, 4) and not (args.layer or args.explicit) \
+            and args.d_c == 192 and args.split == 32:
+        result["cpu_baseline"] = cpu_baseline_sampled(w)
+    if args.config == 2 and not (args.long_horizon or args.layer or args.explicit) and args.d_c == 192 \
+            and args.split == 32:
+        # the HBM-graded append figure: the batch-8 shape on cold buffers
+        ac = append_cold(dev)
+        ac["measured_peak"] = result["append_roofline"]["measured_peak"]
+        ac["frac_of_measured_peak"] = round(ac["achieved"] / ac["measured_peak"], 4)
+        result["append_cold"] = ac
     if args.long_horizon:
         result["config"]["workload"] = ("Wan-1.3B-shaped chunk-layer, long rollout: B=1, 30x52 "
                                         "grid, 3-frame query chunk at t=18..20 over one sink frame "
@@ -496,6 +614,103 @@ def main():
         result["roofline"]["kernel"] = "latent_attn (folded epilogue) + output-mixer GEMM"
         result["config"]["sink_frames"] = w.sink_frames
         result["config"]["window_frames"] = w.window_frames
+    print(json.dumps(result), flush=True)
+
+
+def rollout_bench(args, dev):
+    """The minute-scale rollout (B=8): 240 latent frames in 80 chunks of 3, each
+    chunk re-appended and attended at each of 4 denoising steps in each of 30
+    layers, over a 21-frame ring (t continues to 239). A step-layer's work
+    depends only on its window length, min(3k + 3, 21) frames for chunk k, so
+    one step-layer (append + query prologue + attention) is timed at each
+    distinct length on 30 rotating layer buffer sets, and the rollout total is
+    the sum over the 80 chunks x 4 steps x 30 layers of the matching times."""
+    import torch
+
+    import latent_kv_attention_cache_amd as vm
+    from workloads import config
+
+    w5 = config(5)
+    dims = vm.default_dims()
+    log(f"[bench] workload: {w5.name}")
+    per_chunk = w5.n_steps * w5.n_layers
+    nf_of = [min(w5.chunk_frames * (k + 1), w5.window_frames) for k in range(w5.n_chunks)]
+    distinct = sorted(set(nf_of))
+    sets = _noise_sets(w5.with_(t_first=18), dims, w5.n_layers, dev, seed=5)
+    ws = torch.empty(vm.vmla_attention_workspace_bytes(w5.batch, w5.n_q, dims), dtype=torch.uint8, device=dev)
+    out = torch.empty((w5.batch, w5.n_q, w5.n_heads, w5.d_v), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    rows, tot_s, tot_fl, attn_s, attn_fl, app_s = [], 0.0, 0, 0.0, 0, 0.0
+    for nf in distinct:
+        # the last chunk with this window length: t_first = 3k, the ring wrapped for nf = 21
+        k = max(i for i, v in enumerate(nf_of) if v == nf)
+        w = w5.with_(t_first=w5.chunk_frames * k)
+        n_valid = w.n_valid_frames
+        assert n_valid == nf
+
+        def step(i, ev=None):
+            x, dw, cache = sets[i % len(sets)]
+            if ev is not None:
+                ev[0].record(stream)
+            vm.vmla_cache_append(cache, x, dw["w_down"], dw["w_kr"], w.t_first, w.chunk_frames, dims=dims)
+            if ev is not None:
+                ev[1].record(stream)
+            vm.vmla_query_prologue(cache, x, dw["w_q"], dw["w_k_up"], w.t_first, w.chunk_frames, n_valid, ws,
+                                   dims=dims)
+            if ev is not None:
+                ev[2].record(stream)
+            vm.vmla_latent_attention(cache, dw["w_v_up"], w.t_first, w.chunk_frames, n_valid, out, ws,
+                                     dims=dims)
+            if ev is not None:
+                ev[3].record(stream)
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, evs[i])
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        km = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(3)]
+        wk = work(w)
+        n = nf_of.count(nf) * per_chunk
+        tot_s += n * ms * 1e-3
+        tot_fl += n * wk["step"]
+        attn_s += n * km[2] * 1e-3
+        attn_fl += n * wk["attn_kernel"]
+        app_s += n * km[0] * 1e-3
+        rows.append({"window_frames": nf, "n_k": w.n_k, "chunks": nf_of.count(nf), "step_layers": n,
+                     "ms_per_step_layer": round(ms, 4), "append_us": round(km[0] * 1e3, 2),
+                     "query_prologue_us": round(km[1] * 1e3, 2), "latent_attn_ms": round(km[2], 4),
+                     "latent_attn_tflops": round(wk["attn_kernel"] / (km[2] * 1e-3) / 1e12, 1)})
+        log(f"[bench] window {nf} frames: {ms:.3f} ms per step-layer, attention {km[2]:.3f} ms "
+            f"({rows[-1]['latent_attn_tflops']} TFLOP/s) x {n} step-layers")
+    assert torch.isfinite(out.float()).all().item(), "non-finite output"
+    n_total = w5.n_chunks * per_chunk
+    achieved = attn_fl / attn_s / 1e12
+    result = {
+        "metric": METRIC, "value": round(tot_fl / tot_s / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(tot_s * 1e3 / n_total, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": ("minute-scale streaming rollout at B=8: 240 latent frames of 30x52 in 80 "
+                                "3-frame chunks, each appended and attended at 4 denoising steps in 30 "
+                                "layers over a 21-frame ring; one step-layer timed per window length, "
+                                "the total weighted by the rollout's counts"),
+                   "batch": w5.batch, "n_q": w5.n_q, "n_chunks": w5.n_chunks, "n_steps": w5.n_steps,
+                   "n_layers": w5.n_layers, "window_frames": w5.window_frames, "d_c": w5.d_c,
+                   "d_rope": w5.d_rope, "step_layers": n_total, "flops_total": tot_fl},
+        "rollout": {"total_s": round(tot_s, 3), "attention_s": round(attn_s, 3), "append_s": round(app_s, 4),
+                    "by_window": rows},
+        "roofline": {"bound": "mfma", "kernel": "latent_attn (flop-weighted over the rollout)",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": None},
+    }
+    log(f"[bench] rollout: {tot_s:.2f} s in all ({attn_s:.2f} s of attention at {achieved:.1f} TFLOP/s)")
+    _add_measured_peak(result["roofline"])
     print(json.dumps(result), flush=True)
 
 
