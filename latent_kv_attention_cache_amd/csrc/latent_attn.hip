@@ -44,7 +44,11 @@
 //
 // MFMA formulation (keys on MFMA rows): S^T[key][q] = K[key][:] . Qhat[q][:];
 // per query (= per lane) max and sum over the lane's own keys, the other half
-// of the keys sitting in lane l^32 (one permlane32 swap); O^T[d][q] +=
+// of the keys sitting in lane l^32 (one permlane32 swap). The score
+// accumulators start at -m (m the running reference max), so the MFMAs deliver
+// s - m and the exp2 needs no subtraction unless m moves; at d_c = 64, where
+// the VALU bounds the loop, the row sum comes from 4 more MFMAs per tile
+// against a register fragment of ones instead of VALU adds. O^T[d][q] +=
 // C^T[d][key] . P^T[key][q] with C^T read straight from the row-major tile by
 // the LDS transpose read and P^T the S^T accumulator packed to bf16 in place
 // (the MFMA contraction order of keys is permuted identically on both sides).
@@ -255,6 +259,15 @@ void latent_attn_kernel(AttnArgs a) {
   // l: running sum over this lane's half of the keys, relative to m.
   float m = -INFINITY;
   float l = 0.f;
+  // Narrow latents keep the matrix cores idle half the time; there the row
+  // sum l comes from 4 more MFMAs per tile against a constant fragment whose
+  // row 0 is all ones (O_sum^T[0][q] = sum over keys of P^T[key][q]), off the
+  // VALU, which bounds those widths.
+  constexpr bool kSumMfma = DC <= 64;
+  f32x16 osum = f32x16{};
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)(qi == 0 ? 1.f : 0.f);
   f32x16 s0, s1;          // S^T of the current tile: register r holds key 32 kb + 8(r/4) + 4 half + r%4
   bf16x8 pb[2][2];        // P^T of the previous tile, bf16, per (key block, 16-key step)
 
@@ -272,6 +285,7 @@ void latent_attn_kernel(AttnArgs a) {
           const bf16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           o[t] = mfma32(av, pb[kb][jj], o[t]);
         }
+        if constexpr (kSumMfma) osum = mfma32(ones, pb[kb][jj], osum);
       }
     }
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
@@ -280,12 +294,19 @@ void latent_attn_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kSumMfma ? 6 : 2, 0);
   };
   // S^T of one tile: 28 MFMAs, 28 row reads issued two steps ahead.
+  // The score accumulators start at -mo, mo = the reference max m (0 before
+  // the first tile): the MFMAs deliver s - m, and the softmax needs no
+  // subtraction unless m moves.
   auto scores = [&](const bf16_t* K) {
-    s0 = f32x16{};
-    s1 = f32x16{};
+    const float mo = m > -INFINITY ? -m : 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = mo;
+      s1[r] = mo;
+    }
 #pragma unroll
     for (int ks = 0; ks < kFeatSteps; ++ks) {
       const int off = a_base + 2 * kSlots * 8 * ks;
@@ -314,10 +335,12 @@ void latent_attn_kernel(AttnArgs a) {
         if (k + 32 >= lim) s1[r] = -INFINITY;
       }
     }
+    // the registers hold s - mo with mo = m (0 before the first tile)
+    const float mo = m > -INFINITY ? m : 0.f;
     float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    mx = max_across_halves(mx);
+    mx = max_across_halves(mx) + mo;
     // Lazy rescaling: the reference max only moves when a score exceeds it by
     // more than 2^kLazy, so exp2(s - m) <= 2^kLazy stays exact in fp32/bf16 and
     // the O / l rescale runs on few tiles. Wave-uniform branch.
@@ -326,18 +349,33 @@ void latent_attn_kernel(AttnArgs a) {
       const float m_new = grow ? mx : m;
       const float alpha = __builtin_amdgcn_exp2f(m - m_new);
       l *= alpha;
+      osum *= alpha;
 #pragma unroll
       for (int t = 0; t < kLatTiles; ++t) o[t] *= alpha;
+      const float dm = m_new - mo;             // scores to the new reference
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] -= dm;
+        s1[r] -= dm;
+      }
       m = m_new;
     }
-    float ls = 0.f;
+    if constexpr (kSumMfma) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s0[r] = __builtin_amdgcn_exp2f(s0[r] - m);
-      s1[r] = __builtin_amdgcn_exp2f(s1[r] - m);
-      ls += s0[r] + s1[r];
+      for (int r = 0; r < 16; ++r) {
+        s0[r] = __builtin_amdgcn_exp2f(s0[r]);
+        s1[r] = __builtin_amdgcn_exp2f(s1[r]);
+      }
+    } else {
+      float ls = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] = __builtin_amdgcn_exp2f(s0[r]);
+        s1[r] = __builtin_amdgcn_exp2f(s1[r]);
+        ls += s0[r] + s1[r];
+      }
+      l += ls;
     }
-    l += ls;
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -390,7 +428,8 @@ void latent_attn_kernel(AttnArgs a) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  const float inv = 1.f / sum_across_halves(l);
+  // osum register 0: row 0 (the sum) in lanes 0-31, row 4 (zero) in lanes 32-63
+  const float inv = 1.f / sum_across_halves(kSumMfma ? osum[0] : l);
   if constexpr (kFold) {
     // ---- epilogue: olat = O / l. Register 8 jj + e of latent tile t holds
     // latent dim 32 t + 16 jj + 8 (e / 4) + 4 half + e % 4 of query qrow.
