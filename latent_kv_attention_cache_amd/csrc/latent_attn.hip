@@ -18,6 +18,13 @@
 // straight into LDS (16-byte LDS-DMA loads, no VGPR staging) and read by all 8
 // waves, so every cache read is shared by all 256 queries of the block.
 //
+// Two schedules share this layout and arithmetic. The split-role schedule
+// (latent_attn_pair_kernel, further below) runs the content widths 128 and 192
+// at the default positional width: the two waves of a SIMD divide the work of
+// 64 queries by role, so every LDS operand fragment feeds two MFMAs. The
+// ping-pong schedule (latent_attn_kernel) runs d_c = 64 and the NoPE/RoPE
+// split variants, whose wider rows leave no LDS for the split-role hand-over.
+//
 // Ping-pong schedule. Time is cut into phases separated by workgroup barriers.
 // Waves 0-3 ("X") and 4-7 ("Y", one per SIMD next to an X wave) run the same
 // program, Y one phase behind X. In its matrix phase for tile j a wave runs
@@ -497,8 +504,524 @@ void latent_attn_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split-role schedule (content widths 128 and 192, default positional width):
+// the two waves of a SIMD
+// share two 32-query units (64 queries) and split the work by role instead of
+// by query.
+//   X (waves 0-3): scores of both units, S^T(j) = K(j) Qhat^T: each K fragment
+//       read from LDS feeds two MFMAs (56 per tile); then the online softmax
+//       of both units, handing P^T(j) (bf16) and each query's rescale factor
+//       to its partner through LDS.
+//   Y (waves 4-7): the tile loads (and the read-time rotation), then
+//       O^T += C^T(j-1) P^T(j-1) for both units: each C^T fragment feeds two
+//       MFMAs (48 per tile); at the end the W_V_up epilogue of both units.
+// Phase A(j): X issues the score MFMAs while Y issues the next tile's loads
+// and reads P^T(j-1) into registers. Phase B(j): Y issues the P.C MFMAs while
+// X runs the softmax of tile j, so X's vector work overlaps Y's matrix work.
+// Every wave executes one barrier per phase; the role branches are wave-
+// uniform (scalar) branches around loops of the same trip count. LDS operand
+// traffic per tile and SIMD: 28 KB of K, 24 KB of C^T and 16 KB of P^T, where
+// two waves of 32 queries each would read 104 KB.
+//
+// Buffers: tile j is read in B(j-1) (X's first K fragments), A(j) (K) and
+// B(j+1) (C^T); four tile buffers. Y requests tile j+2 at the start of A(j)
+// into the buffer of tile j-2 (last read in B(j-1)) and waits for tile j+1
+// (requested in A(j-1)) at the end of A(j), before the barrier that publishes
+// it; X then reads the first K fragments of tile j+1 and resets its score
+// accumulators in B(j), next to its softmax, so A(j+1) starts with MFMAs.
+// The hand-over region of a pair holds P^T of one tile (8 fragments per lane)
+// and one float per lane and unit (the rescale factor; after the last tile,
+// 1/l): X writes it in B(j); Y reads it into registers in A(j+1), where it
+// has no matrix work, together with the first two C^T fragments of its next
+// P.C, so B(j+1) starts without waiting for LDS.
+constexpr int kPairs = 4;
+constexpr int kHandPBytes = 8 * 64 * 16;                       // P^T of one tile
+constexpr int kHandBytes = kHandPBytes + 2 * 64 * 4;            // + one float per lane and unit
+
+template <typename T, bool kRot, bool kFold, int DC, bool kChunked>
+__global__ __launch_bounds__(kThreads)
+void latent_attn_pair_kernel(AttnArgs a) {
+  using Sh = AttnShape<DC, kDRope>;
+  constexpr int kDC = Sh::kDC;
+  constexpr int kRow = Sh::kRow;
+  constexpr int kTileElems = Sh::kTileElems;
+  constexpr int kLoadsPerWave = Sh::kLoadsPerWave;
+  constexpr int kFeatSteps = Sh::kFeatSteps;
+  constexpr int kLatTiles = Sh::kLatTiles;
+  constexpr int kHandElems = kHandBytes / 2;
+  constexpr int kHandOff = kBufs * kTileElems;            // elements
+  static_assert(Sh::kChunks % kLoaders == 0, "every loading wave moves the same number of chunk columns");
+  static_assert((kHandOff + kPairs * kHandElems) * 2 <= 160 * 1024, "LDS budget");
+  static_assert(2 * DC * kVLd <= kHandOff, "W_V_up staging inside the tile buffers");
+  __shared__ __attribute__((aligned(16))) bf16_t kt[kHandOff + kPairs * kHandElems];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // wave-uniform by construction; readfirstlane makes it uniform to the
+  // compiler, so the role branches (which hold barriers) are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int qi = lane & 31;
+  const int pair = wave & (kPairs - 1);
+  const bool is_y = wave >= kPairs;
+  int b = blockIdx.z, q0 = 0, nq = a.n_q, k0 = 0, nk = a.n_k, chunk_q = a.n_q;
+  if constexpr (kChunked) {
+    const int rc = blockIdx.z / a.batch;
+    const int c = a.cm.n_chunks - 1 - rc;
+    b = blockIdx.z - rc * a.batch;
+    chunk_q = a.cm.chunk_q;
+    q0 = c * chunk_q;
+    nq = min(chunk_q, a.n_q - q0);
+    const int k_end = min(a.n_k, (c + 1) * a.cm.key_step);
+    k0 = max(0, k_end - a.cm.key_span);
+    nk = k_end - k0;
+  }
+  // The pair's units u0 + 2 pair + i, i = 0, 1: head hu[i], query rows qrow[i].
+  const int units = (nq + 31) / 32;
+  const int umax = (chunk_q + 31) / 32;
+  const int upad = umax > kWaves ? umax : kWaves;
+  const int u0 = blockIdx.x * kWaves;
+  const int h_lo = u0 / upad;
+  int hu[2], qrow[2];
+  bool live_u[2], qvalid[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int u = u0 + 2 * pair + i;
+    const int qb = u - (u / upad) * upad;
+    hu[i] = min(u / upad, a.n_heads - 1);
+    qrow[i] = 32 * qb + qi;
+    live_u[i] = u / upad < a.n_heads && qb < units;
+    qvalid[i] = live_u[i] && qrow[i] < nq;
+  }
+  const bool live = live_u[0] || live_u[1];
+
+  const T* cache = static_cast<const T*>(a.cache) + ((size_t)b * a.cache_rows + k0) * kRow;
+  const int ntiles = (nk + kKT - 1) / kKT;
+  // the pair's hand-over region: P^T at hand_p, the floats at hand_f
+  bf16_t* const hand_p = kt + kHandOff + pair * kHandElems;
+  float* const hand_f = reinterpret_cast<float*>(hand_p + kHandPBytes / 2);
+  constexpr bool kSumMfma = DC <= 128;
+
+  // W_V_up of the workgroup's one or two heads into the tile buffers, [kDC][kVLd] each.
+  auto stage_w_v_up = [&]() {
+    const int nh = min((u0 + kWaves - 1) / upad, a.n_heads - 1) - h_lo + 1;
+    const T* wsrc = static_cast<const T*>(a.w_v_up) + (size_t)h_lo * kDC * kDV;
+    for (int hh = 0; hh < nh; ++hh) {
+#pragma unroll
+      for (int i = 0; i < kDC * kDV / 8 / kThreads; ++i) {
+        const int c = tid + i * kThreads;
+        const int row = c / (kDV / 8), cc = c % (kDV / 8);
+        *reinterpret_cast<uint4*>(&kt[(hh * kDC + row) * kVLd + 8 * cc]) =
+            load8_bf16<T>(wsrc + ((size_t)hh * kDC + row) * kDV + 8 * cc);
+      }
+    }
+  };
+
+  if (!is_y) {
+    // ================= X: scores and softmax of the pair's two units
+    bf16x8 qf[2][kFeatSteps];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bf16_t* qp = a.qhat + (((size_t)b * a.n_heads + hu[i]) * a.n_q + q0 + (qvalid[i] ? qrow[i] : nq - 1)) * kRow;
+#pragma unroll
+      for (int ks = 0; ks < kFeatSteps; ++ks)
+        qf[i][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + 8 * half);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int ks = 0; ks < kFeatSteps; ++ks) asm volatile("" : "+v"(qf[i][ks]));
+    const int a_base = (half * kSlots + qi) * 8;
+    float m[2] = {-INFINITY, -INFINITY};
+    float l[2] = {0.f, 0.f};
+    f32x16 s[2][2];     // [unit][key block]: register r holds key 32 kb + 8(r/4) + 4 half + r%4
+
+    // K fragment (key block kb, feature step ks) of a tile
+    auto k_frag = [&](const bf16_t* K, int ks, int kb) {
+      return lds_row8(K + a_base + 2 * kSlots * 8 * ks + kb * 32 * 8);
+    };
+    // score accumulators start at -m (m the running reference max; 0 before
+    // the first key), so the MFMAs deliver s - m
+    auto init_scores = [&]() {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float mo = m[i] > -INFINITY ? -m[i] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[i][0][r] = mo;
+          s[i][1][r] = mo;
+        }
+      }
+    };
+    // S^T of one tile for both units: 56 MFMAs; the fragments of feature
+    // steps 0 and 1 come in already read, later ones are read two steps ahead.
+    bf16x8 kpre[2][2];
+    auto scores = [&](const bf16_t* K) {
+      bf16x8 fr[3][2];
+      fr[0][0] = kpre[0][0];
+      fr[0][1] = kpre[0][1];
+      fr[1][0] = kpre[1][0];
+      fr[1][1] = kpre[1][1];
+#pragma unroll
+      for (int ks = 0; ks < kFeatSteps; ++ks) {
+        if (ks + 2 < kFeatSteps) {
+          fr[(ks + 2) % 3][0] = k_frag(K, ks + 2, 0);
+          fr[(ks + 2) % 3][1] = k_frag(K, ks + 2, 1);
+        }
+        s[0][0] = mfma32(fr[ks % 3][0], qf[0][ks], s[0][0]);
+        s[1][0] = mfma32(fr[ks % 3][0], qf[1][ks], s[1][0]);
+        s[0][1] = mfma32(fr[ks % 3][1], qf[0][ks], s[0][1]);
+        s[1][1] = mfma32(fr[ks % 3][1], qf[1][ks], s[1][1]);
+      }
+#pragma unroll
+      for (int i = 0; i < kFeatSteps - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 0);
+    };
+    auto prefetch_k = [&](const bf16_t* K) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        kpre[ks][0] = k_frag(K, ks, 0);
+        kpre[ks][1] = k_frag(K, ks, 1);
+      }
+    };
+    // Online softmax of both units; hands P^T and the rescale factors over.
+    auto softmax = [&](int key0) {
+      if (key0 + kKT > nk) {       // the keys end inside this tile (wave-uniform)
+        const int lim = nk - key0 - 4 * half;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int k = 8 * (r >> 2) + (r & 3);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            if (k >= lim) s[i][0][r] = -INFINITY;
+            if (k + 32 >= lim) s[i][1][r] = -INFINITY;
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float mo = m[i] > -INFINITY ? m[i] : 0.f;
+        float mx = fmaxf(s[i][0][0], s[i][1][0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[i][0][r], s[i][1][r]));
+        mx = max_across_halves(mx) + mo;
+        const bool grow = mx > m[i] + kLazy;
+        float alpha = 1.f;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float m_new = grow ? mx : m[i];
+          alpha = __builtin_amdgcn_exp2f(m[i] - m_new);
+          l[i] *= alpha;
+          const float dm = m_new - mo;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s[i][0][r] -= dm;
+            s[i][1][r] -= dm;
+          }
+          m[i] = m_new;
+        }
+        hand_f[i * 64 + lane] = alpha;
+        if constexpr (kSumMfma) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s[i][0][r] = __builtin_amdgcn_exp2f(s[i][0][r]);
+            s[i][1][r] = __builtin_amdgcn_exp2f(s[i][1][r]);
+          }
+        } else {
+          float ls = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s[i][0][r] = __builtin_amdgcn_exp2f(s[i][0][r]);
+            s[i][1][r] = __builtin_amdgcn_exp2f(s[i][1][r]);
+            ls += s[i][0][r] + s[i][1][r];
+          }
+          l[i] += ls;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            bf16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (__bf16)s[i][kb][8 * jj + e];
+            *reinterpret_cast<bf16x8*>(hand_p + ((4 * i + 2 * kb + jj) * 64 + lane) * 8) = v;
+          }
+      }
+    };
+
+    __syncthreads();               // tile 0 published
+    // per tile j: A(j) scores, B(j) softmax (and the head of tile j+1's
+    // scores); then A(ntiles), B(ntiles) idle
+    if (live) {
+      prefetch_k(kt);
+      init_scores();
+      for (int j = 0; j < ntiles; ++j) {
+        __builtin_amdgcn_s_setprio(1);
+        scores(kt + (j % kBufs) * kTileElems);
+        __builtin_amdgcn_s_setprio(0);
+        __syncthreads();
+        if (j + 1 < ntiles) prefetch_k(kt + ((j + 1) % kBufs) * kTileElems);
+        softmax(j * kKT);
+        init_scores();
+        __syncthreads();
+      }
+    } else {
+      for (int j = 0; j < ntiles; ++j) {
+        __syncthreads();
+        __syncthreads();
+      }
+    }
+    __syncthreads();
+    __syncthreads();
+    if constexpr (!kSumMfma) {
+      if (live) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) hand_f[i * 64 + lane] = 1.f / sum_across_halves(l[i]);
+      }
+    }
+    __syncthreads();               // 1 / l handed over
+    if constexpr (!kFold) {
+      stage_w_v_up();
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ================= Y: tile loads, P.C of the pair's two units, epilogue
+  const int wl = wave - kPairs;     // loading wave index 0..3
+  const uint32_t kt_lds = (uint32_t)(uintptr_t)(VMLA_LDS bf16_t*)kt;
+  auto issue_tile = [&](int j) {
+    const int buf = j % kBufs;
+    const int kg = min(j * kKT + lane, nk - 1);
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+      const int n = wl + kLoaders * i;
+      if constexpr (std::is_same_v<T, bf16_t>) {
+        dma16(cache, (uint32_t)(kg * (kRow * 2)) + (uint32_t)(16 * n),
+              kt_lds + 2u * (uint32_t)(buf * kTileElems + n * kSlots * 8));
+      } else {
+        const T* src = cache + (size_t)kg * kRow + 8 * n;
+        *reinterpret_cast<uint4*>(kt + buf * kTileElems + (n * kSlots + lane) * 8) = load8_bf16<T>(src);
+      }
+    }
+  };
+  auto rotate_tile = [&](int j) {
+    bf16_t* p = kt + (j % kBufs) * kTileElems + ((kDC / 8 + wl) * kSlots + lane) * 8;
+    const int kg = k0 + min(j * kKT + lane, nk - 1);
+    int n_in, ww;
+    const int fs = div_small(kg, a.tokens_per_frame, a.inv_tokens_per_frame, &n_in);
+    const int hh = div_small(n_in, a.grid_w, a.inv_grid_w, &ww);
+    int tl = fs;
+    if (fs >= a.sink_frames) {
+      int r = fs - a.sink_frames - a.shift_mod_w;
+      if (r < 0) r += a.window_frames;
+      tl = a.sink_frames + r;
+    }
+    const uint4 raw = *reinterpret_cast<const uint4*>(p);
+    const uint32_t in[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t o4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pr = 4 * wl + q;
+      const int ax = a.rope.axis[pr];
+      const float a0 = __uint_as_float(in[q] << 16), a1 = __uint_as_float(in[q] & 0xffff0000u);
+      float sn, cs;
+      sincos_rev(ax == 0 ? tl : (ax == 1 ? hh : ww), a.rope.rev_lo[pr], a.rope.rev_hi[pr], &sn, &cs);
+      o4[q] = pack2(a0 * cs - a1 * sn, a0 * sn + a1 * cs);
+    }
+    *reinterpret_cast<uint4*>(p) = uint4{o4[0], o4[1], o4[2], o4[3]};
+  };
+
+  const int jl = lane & 15;
+  const int x4 = ((lane & 16) >> 3) + ((jl & 3) >> 1);
+  const int sub = 4 * (jl & 1);
+  const int v_off1 = (x4 * kSlots + 4 * half + (jl >> 2)) * 8 + sub;
+  const int v_off2 = v_off1 + 8 * 8;
+
+  f32x16 o[2][kLatTiles];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int t = 0; t < kLatTiles; ++t) o[i][t] = f32x16{};
+  f32x16 osum[2] = {f32x16{}, f32x16{}};
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)(qi == 0 ? 1.f : 0.f);
+
+  bf16x8 pb[2][4];        // P^T of the tile being accumulated: [unit][(key block, 16-key step)]
+  // C^T fragment f = g * kLatTiles + t of a tile: key group g = (key block,
+  // 16-key step), latent block t; two transpose reads.
+  constexpr int kFrags = 4 * kLatTiles;
+  auto ct_frag = [&](const bf16_t* K, int f) {
+    const int g = f / kLatTiles, t = f % kLatTiles;
+    const bf16_t* Kb = K + ((g >> 1) * 32 + (g & 1) * 16) * 8 + 4 * kSlots * 8 * t;
+    const bf16x4 lo = lds_tr4(Kb + v_off1);
+    const bf16x4 hi = lds_tr4(Kb + v_off2);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  // O^T += C^T P^T for both units: kFrags fragments, each feeding two MFMAs
+  // (+2 row-sum MFMAs per key group at narrow latents); fragments 0 and 1
+  // come in already read, later ones are read two fragments ahead.
+  auto accumulate = [&](const bf16_t* K, bf16x8 f0, bf16x8 f1) {
+    bf16x8 fr[3];
+    fr[0] = f0;
+    fr[1] = f1;
+#pragma unroll
+    for (int f = 0; f < kFrags; ++f) {
+      if (f + 2 < kFrags) fr[(f + 2) % 3] = ct_frag(K, f + 2);
+      const int g = f / kLatTiles, t = f % kLatTiles;
+      o[0][t] = mfma32(fr[f % 3], pb[0][g], o[0][t]);
+      o[1][t] = mfma32(fr[f % 3], pb[1][g], o[1][t]);
+      if constexpr (kSumMfma) {
+        if (t == kLatTiles - 1) {
+          osum[0] = mfma32(ones, pb[0][g], osum[0]);
+          osum[1] = mfma32(ones, pb[1][g], osum[1]);
+        }
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < kFrags - 2; ++f) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kSumMfma ? 12 : 4, 0);
+  };
+
+  issue_tile(0);
+  if (ntiles > 1) issue_tile(1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (kRot) rotate_tile(0);
+  __syncthreads();
+
+  // A(j) ends by publishing tile j+1: this wave waits for its loads of it
+  // (requested in A(j-1); tile j+2's, requested at the start of A(j), may
+  // still be in flight) and rotates its column
+  auto publish_next = [&](int j) {
+    if (j + 1 < ntiles) {
+      if (j + 2 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kLoadsPerWave) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if constexpr (kRot) rotate_tile(j + 1);
+    }
+  };
+  // A(0), B(0): no P.C yet
+  if (2 < ntiles) issue_tile(2);
+  publish_next(0);
+  __syncthreads();
+  __syncthreads();
+  if (live) {
+    for (int j = 1; j <= ntiles; ++j) {
+      // A(j): request tile j+2; P^T(j-1), its rescale factors and the first
+      // two C^T fragments of tile j-1 into registers; publish tile j+1
+      if (j + 2 < ntiles) issue_tile(j + 2);
+      const bf16_t* K = kt + ((j - 1) % kBufs) * kTileElems;
+      // the read-time rotation runs before P^T occupies its registers
+      if constexpr (kRot) publish_next(j);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) pb[i][g] = lds_row8(hand_p + ((4 * i + g) * 64 + lane) * 8);
+      const float al0 = hand_f[lane], al1 = hand_f[64 + lane];
+      const bf16x8 f0 = ct_frag(K, 0), f1 = ct_frag(K, 1);
+      if constexpr (!kRot) publish_next(j);
+      __syncthreads();
+      // B(j): P.C of tile j-1
+      if (__builtin_amdgcn_ballot_w64(al0 != 1.f || al1 != 1.f)) {
+#pragma unroll
+        for (int t = 0; t < kLatTiles; ++t) {
+          o[0][t] *= al0;
+          o[1][t] *= al1;
+        }
+        osum[0] *= al0;
+        osum[1] *= al1;
+      }
+      __builtin_amdgcn_s_setprio(1);
+      accumulate(K, f0, f1);
+      __builtin_amdgcn_s_setprio(0);
+      __syncthreads();
+    }
+  } else {
+    for (int j = 1; j <= ntiles; ++j) {
+      if (j + 2 < ntiles) issue_tile(j + 2);
+      publish_next(j);
+      __syncthreads();
+      __syncthreads();
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();                 // 1 / l handed over
+  float inv[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    // osum register 0: row 0 (the sum) in lanes 0-31, row 4 (zero) in lanes 32-63
+    if constexpr (kSumMfma) inv[i] = 1.f / sum_across_halves(osum[i][0]);
+    else inv[i] = hand_f[i * 64 + lane];
+  }
+
+  if constexpr (kFold) {
+    // olat = O / l; register 8 jj + e of latent tile t holds latent dim
+    // 32 t + 16 jj + 8 (e / 4) + 4 half + e % 4 of the unit's query.
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (!qvalid[i]) continue;
+      uint16_t* dst = a.olat + ((size_t)b * a.n_q + q0 + qrow[i]) * ((size_t)a.n_heads * kDC) + (size_t)hu[i] * kDC;
+#pragma unroll
+      for (int t = 0; t < kLatTiles; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int e4 = 0; e4 < 2; ++e4) {
+            const int r = 8 * jj + 4 * e4;
+            *reinterpret_cast<uint2*>(dst + 32 * t + 16 * jj + 8 * e4 + 4 * half) =
+                uint2{pack2(o[i][t][r] * inv[i], o[i][t][r + 1] * inv[i]),
+                      pack2(o[i][t][r + 2] * inv[i], o[i][t][r + 3] * inv[i])};
+          }
+    }
+    return;
+  } else {
+    stage_w_v_up();
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (!live_u[i]) continue;
+      const bf16_t* wv = kt + (hu[i] - h_lo) * kDC * kVLd;
+      bf16x8 ob[kLatTiles][2];
+#pragma unroll
+      for (int t = 0; t < kLatTiles; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ob[t][jj][e] = (__bf16)(o[i][t][8 * jj + e] * inv[i]);
+      T* out = static_cast<T*>(a.out) + (((size_t)b * a.n_q + q0 + (qvalid[i] ? qrow[i] : 0)) * a.n_heads + hu[i]) * kDV;
+#pragma unroll
+      for (int et = 0; et < kDV / 32; ++et) {
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int t = 0; t < kLatTiles; ++t) {
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int dbase = 32 * t + 16 * jj;
+            const bf16x8 av = lds_tr8(wv, kVLd, dbase + 4 * half, dbase + 8 + 4 * half, 32 * et, lane);
+            acc = mfma32(av, ob[t][jj], acc);
+          }
+        }
+        if (qvalid[i]) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int e0 = 32 * et + 8 * g + 4 * half;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e0 + e] = from_f32<T>(acc[4 * g + e]);
+          }
+        }
+      }
+    }
+  }
+}
+
 template <int DC>
-hipError_t launch_dc(const AttnArgs& a, bool f32, hipStream_t s) {
+hipError_t launch_dc_pingpong(const AttnArgs& a, bool f32, hipStream_t s) {
   const int units = (a.cm.chunk_q + 31) / 32;
   const int upad = units > kWaves ? units : kWaves;
   dim3 grid((a.n_heads * upad + kWaves - 1) / kWaves, 1, a.batch * a.cm.n_chunks);
@@ -523,6 +1046,44 @@ hipError_t launch_dc(const AttnArgs& a, bool f32, hipStream_t s) {
     else hipLaunchKernelGGL((latent_attn_kernel<bf16_t, false, false, DC, false, kDRope>), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
+}
+
+
+template <int DC>
+hipError_t launch_dc_pair(const AttnArgs& a, bool f32, hipStream_t s) {
+  const int units = (a.cm.chunk_q + 31) / 32;
+  const int upad = units > kWaves ? units : kWaves;
+  dim3 grid((a.n_heads * upad + kWaves - 1) / kWaves, 1, a.batch * a.cm.n_chunks);
+  if (a.cm.n_chunks > 1) {
+    // query chunks come only with append-time RoPE and the W_V_up epilogue
+    if (a.rope_at_read || a.olat) return hipErrorInvalidValue;
+    if (f32) hipLaunchKernelGGL((latent_attn_pair_kernel<float, false, false, DC, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((latent_attn_pair_kernel<bf16_t, false, false, DC, true>), grid, dim3(kThreads), 0, s, a);
+  } else if (a.olat) {
+    if (a.rope_at_read) {
+      if (f32) hipLaunchKernelGGL((latent_attn_pair_kernel<float, true, true, DC, false>), grid, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((latent_attn_pair_kernel<bf16_t, true, true, DC, false>), grid, dim3(kThreads), 0, s, a);
+    } else {
+      if (f32) hipLaunchKernelGGL((latent_attn_pair_kernel<float, false, true, DC, false>), grid, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((latent_attn_pair_kernel<bf16_t, false, true, DC, false>), grid, dim3(kThreads), 0, s, a);
+    }
+  } else if (a.rope_at_read) {
+    if (f32) hipLaunchKernelGGL((latent_attn_pair_kernel<float, true, false, DC, false>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((latent_attn_pair_kernel<bf16_t, true, false, DC, false>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (f32) hipLaunchKernelGGL((latent_attn_pair_kernel<float, false, false, DC, false>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((latent_attn_pair_kernel<bf16_t, false, false, DC, false>), grid, dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+
+// d_c 128 and 192: the split-role schedule; d_c 64, where the softmax's
+// vector work bounds either schedule, the ping-pong one measured faster.
+template <int DC>
+hipError_t launch_dc(const AttnArgs& a, bool f32, hipStream_t s) {
+  if constexpr (DC <= 64) return launch_dc_pingpong<DC>(a, f32, s);
+  else return launch_dc_pair<DC>(a, f32, s);
 }
 
 template <int DR>
