@@ -519,7 +519,7 @@ def main():
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "latent_attn_config2_traffic.json")
     if (args.config == 2 and not (args.long_horizon or args.layer or args.explicit)
-            and args.d_c == 192 and os.path.exists(tfile)):
+            and args.d_c == 192 and args.split == 32 and os.path.exists(tfile)):
         with open(tfile) as f:
             tr = json.load(f)
         if tr.get("kernel_source_sha") == _kernel_sha():
