@@ -865,10 +865,10 @@ void latent_attn_pair_kernel(AttnArgs a) {
   // O^T += C^T P^T for both units: kFrags fragments, each feeding two MFMAs
   // (+2 row-sum MFMAs per key group at narrow latents); fragments 0 and 1
   // come in already read, later ones are read two fragments ahead.
-  auto accumulate = [&](const bf16_t* K, bf16x8 f0, bf16x8 f1) {
-    bf16x8 fr[3];
-    fr[0] = f0;
-    fr[1] = f1;
+  // fragments 0 and 1 are read into the ring fr (slot f % 3) before the
+  // phase's barrier; later ones are read two fragments ahead
+  bf16x8 fr[3];
+  auto accumulate = [&](const bf16_t* K) {
 #pragma unroll
     for (int f = 0; f < kFrags; ++f) {
       if (f + 2 < kFrags) fr[(f + 2) % 3] = ct_frag(K, f + 2);
@@ -924,10 +924,10 @@ void latent_attn_pair_kernel(AttnArgs a) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) pb[i][g] = lds_row8(hand_p + ((4 * i + g) * 64 + lane) * 8);
       const float al0 = hand_f[lane], al1 = hand_f[64 + lane];
-      const bf16x8 f0 = ct_frag(K, 0), f1 = ct_frag(K, 1);
+      fr[0] = ct_frag(K, 0);
+      fr[1] = ct_frag(K, 1);
       if constexpr (!kRot) publish_next(j);
-      __syncthreads();
-      // B(j): P.C of tile j-1
+      // the (rare) rescale of O by the factors of tile j-1 also runs here
       if (__builtin_amdgcn_ballot_w64(al0 != 1.f || al1 != 1.f)) {
 #pragma unroll
         for (int t = 0; t < kLatTiles; ++t) {
@@ -937,8 +937,10 @@ void latent_attn_pair_kernel(AttnArgs a) {
         osum[0] *= al0;
         osum[1] *= al1;
       }
+      __syncthreads();
+      // B(j): P.C of tile j-1
       __builtin_amdgcn_s_setprio(1);
-      accumulate(K, f0, f1);
+      accumulate(K);
       __builtin_amdgcn_s_setprio(0);
       __syncthreads();
     }
