@@ -506,9 +506,8 @@ void latent_attn_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Split-role schedule (content widths 128 and 192, default positional width):
-// the two waves of a SIMD
-// share two 32-query units (64 queries) and split the work by role instead of
-// by query.
+// the two waves of a SIMD share two 32-query units (64 queries) and split the
+// work by role instead of by query.
 //   X (waves 0-3): scores of both units, S^T(j) = K(j) Qhat^T: each K fragment
 //       read from LDS feeds two MFMAs (56 per tile); then the online softmax
 //       of both units, handing P^T(j) (bf16) and each query's rescale factor
@@ -516,8 +515,9 @@ void latent_attn_kernel(AttnArgs a) {
 //   Y (waves 4-7): the tile loads (and the read-time rotation), then
 //       O^T += C^T(j-1) P^T(j-1) for both units: each C^T fragment feeds two
 //       MFMAs (48 per tile); at the end the W_V_up epilogue of both units.
-// Phase A(j): X issues the score MFMAs while Y issues the next tile's loads
-// and reads P^T(j-1) into registers. Phase B(j): Y issues the P.C MFMAs while
+// Phase A(j): X issues the score MFMAs while Y issues the next tile's loads,
+// reads P^T(j-1) into registers and applies the (rare) rescale of O.
+// Phase B(j): Y issues the P.C MFMAs while
 // X runs the softmax of tile j, so X's vector work overlaps Y's matrix work.
 // Every wave executes one barrier per phase; the role branches are wave-
 // uniform (scalar) branches around loops of the same trip count. LDS operand
@@ -528,8 +528,8 @@ void latent_attn_kernel(AttnArgs a) {
 // B(j+1) (C^T); four tile buffers. Y requests tile j+2 at the start of A(j)
 // into the buffer of tile j-2 (last read in B(j-1)) and waits for tile j+1
 // (requested in A(j-1)) at the end of A(j), before the barrier that publishes
-// it; X then reads the first K fragments of tile j+1 and resets its score
-// accumulators in B(j), next to its softmax, so A(j+1) starts with MFMAs.
+// it; X then reads the first K fragments of tile j+1 in B(j), next to its
+// softmax, so A(j+1) starts with MFMAs.
 // The hand-over region of a pair holds P^T of one tile (8 fragments per lane)
 // and one float per lane and unit (the rescale factor; after the last tile,
 // 1/l): X writes it in B(j); Y reads it into registers in A(j+1), where it
