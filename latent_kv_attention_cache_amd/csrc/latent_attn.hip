@@ -514,11 +514,16 @@ void latent_attn_kernel(AttnArgs a) {
 //       to its partner through LDS.
 //   Y (waves 4-7): the tile loads (and the read-time rotation), then
 //       O^T += C^T(j-1) P^T(j-1) for both units: each C^T fragment feeds two
-//       MFMAs (48 per tile); at the end the W_V_up epilogue of both units.
+//       MFMAs (48 per tile); Y also keeps the row sums l (from the same bf16
+//       P^T that multiplies the latents) and at the end runs the W_V_up
+//       epilogue of both units.
 // Phase A(j): X issues the score MFMAs while Y issues the next tile's loads,
-// reads P^T(j-1) into registers and applies the (rare) rescale of O.
+// reads P^T(j-1) into registers, applies the (rare) rescale of O and l and
+// adds P^T(j-1)'s row sums to l.
 // Phase B(j): Y issues the P.C MFMAs while
 // X runs the softmax of tile j, so X's vector work overlaps Y's matrix work.
+// X is the busier role (its score MFMAs and its softmax run in series), so
+// every vector operation that does not need the scores runs on Y.
 // Every wave executes one barrier per phase; the role branches are wave-
 // uniform (scalar) branches around loops of the same trip count. LDS operand
 // traffic per tile and SIMD: 28 KB of K, 24 KB of C^T and 16 KB of P^T, where
@@ -531,10 +536,11 @@ void latent_attn_kernel(AttnArgs a) {
 // it; X then reads the first K fragments of tile j+1 in B(j), next to its
 // softmax, so A(j+1) starts with MFMAs.
 // The hand-over region of a pair holds P^T of one tile (8 fragments per lane)
-// and one float per lane and unit (the rescale factor; after the last tile,
-// 1/l): X writes it in B(j); Y reads it into registers in A(j+1), where it
-// has no matrix work, together with the first two C^T fragments of its next
-// P.C, so B(j+1) starts without waiting for LDS.
+// and one float per lane and unit (the rescale factor): X writes it in B(j);
+// Y reads it into registers in A(j+1), where it has no matrix work, together
+// with the first two C^T fragments of its next P.C, so B(j+1) starts without
+// waiting for LDS.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kPairs = 4;
 constexpr int kHandPBytes = 8 * 64 * 16;                       // P^T of one tile
 constexpr int kHandBytes = kHandPBytes + 2 * 64 * 4;            // + one float per lane and unit
@@ -601,7 +607,6 @@ void latent_attn_pair_kernel(AttnArgs a) {
   // the pair's hand-over region: P^T at hand_p, the floats at hand_f
   bf16_t* const hand_p = kt + kHandOff + pair * kHandElems;
   float* const hand_f = reinterpret_cast<float*>(hand_p + kHandPBytes / 2);
-  constexpr bool kSumMfma = DC <= 128;
 
   // W_V_up of the workgroup's one or two heads into the tile buffers, [kDC][kVLd] each.
   auto stage_w_v_up = [&]() {
@@ -634,7 +639,6 @@ void latent_attn_pair_kernel(AttnArgs a) {
       for (int ks = 0; ks < kFeatSteps; ++ks) asm volatile("" : "+v"(qf[i][ks]));
     const int a_base = (half * kSlots + qi) * 8;
     float m[2] = {-INFINITY, -INFINITY};
-    float l[2] = {0.f, 0.f};
     f32x16 s[2][2];     // [unit][key block]: register r holds key 32 kb + 8(r/4) + 4 half + r%4
 
     // K fragment (key block kb, feature step ks) of a tile
@@ -642,16 +646,18 @@ void latent_attn_pair_kernel(AttnArgs a) {
       return lds_row8(K + a_base + 2 * kSlots * 8 * ks + kb * 32 * 8);
     };
     // score accumulators start at -m (m the running reference max; 0 before
-    // the first key), so the MFMAs deliver s - m
+    // the first key), so the MFMAs deliver s - m: the first MFMA of each key
+    // block takes the block negm[unit] as its addend. The block is built in
+    // the softmax phase; pinning it there keeps the 32 moves out of the score
+    // phase, whose matrix work would otherwise wait for them.
+    f32x16 negm[2];
     auto init_scores = [&]() {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const float mo = m[i] > -INFINITY ? -m[i] : 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[i][0][r] = mo;
-          s[i][1][r] = mo;
-        }
+        for (int r = 0; r < 16; ++r) negm[i][r] = mo;
+        asm volatile("" : "+v"(negm[i]));
       }
     };
     // S^T of one tile for both units: 56 MFMAs; the fragments of feature
@@ -669,10 +675,10 @@ void latent_attn_pair_kernel(AttnArgs a) {
           fr[(ks + 2) % 3][0] = k_frag(K, ks + 2, 0);
           fr[(ks + 2) % 3][1] = k_frag(K, ks + 2, 1);
         }
-        s[0][0] = mfma32(fr[ks % 3][0], qf[0][ks], s[0][0]);
-        s[1][0] = mfma32(fr[ks % 3][0], qf[1][ks], s[1][0]);
-        s[0][1] = mfma32(fr[ks % 3][1], qf[0][ks], s[0][1]);
-        s[1][1] = mfma32(fr[ks % 3][1], qf[1][ks], s[1][1]);
+        s[0][0] = mfma32(fr[ks % 3][0], qf[0][ks], ks == 0 ? negm[0] : s[0][0]);
+        s[1][0] = mfma32(fr[ks % 3][0], qf[1][ks], ks == 0 ? negm[1] : s[1][0]);
+        s[0][1] = mfma32(fr[ks % 3][1], qf[0][ks], ks == 0 ? negm[0] : s[0][1]);
+        s[1][1] = mfma32(fr[ks % 3][1], qf[1][ks], ks == 0 ? negm[1] : s[1][1]);
       }
 #pragma unroll
       for (int i = 0; i < kFeatSteps - 2; ++i) {
@@ -702,20 +708,30 @@ void latent_attn_pair_kernel(AttnArgs a) {
           }
         }
       }
+      // both units side by side (two independent max trees, one wave-uniform
+      // rescale check, then the exps and bf16 packing of both), so the
+      // dependent steps of one unit overlap those of the other
+      float mo[2], mx[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const float mo = m[i] > -INFINITY ? m[i] : 0.f;
-        float mx = fmaxf(s[i][0][0], s[i][1][0]);
+        mo[i] = m[i] > -INFINITY ? m[i] : 0.f;
+        float t[4];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[i][0][r], s[i][1][r]));
-        mx = max_across_halves(mx) + mo;
-        const bool grow = mx > m[i] + kLazy;
-        float alpha = 1.f;
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-          const float m_new = grow ? mx : m[i];
-          alpha = __builtin_amdgcn_exp2f(m[i] - m_new);
-          l[i] *= alpha;
-          const float dm = m_new - mo;
+        for (int c = 0; c < 4; ++c)
+          t[c] = fmaxf(fmaxf(fmaxf(s[i][0][4 * c], s[i][1][4 * c]), fmaxf(s[i][0][4 * c + 1], s[i][1][4 * c + 1])),
+                       fmaxf(fmaxf(s[i][0][4 * c + 2], s[i][1][4 * c + 2]), fmaxf(s[i][0][4 * c + 3], s[i][1][4 * c + 3])));
+        mx[i] = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) mx[i] = max_across_halves(mx[i]) + mo[i];
+      const bool grow0 = mx[0] > m[0] + kLazy, grow1 = mx[1] > m[1] + kLazy;
+      float alpha[2] = {1.f, 1.f};
+      if (__builtin_amdgcn_ballot_w64(grow0 || grow1)) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const float m_new = (i ? grow1 : grow0) ? mx[i] : m[i];
+          alpha[i] = __builtin_amdgcn_exp2f(m[i] - m_new);
+          const float dm = m_new - mo[i];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             s[i][0][r] -= dm;
@@ -723,23 +739,18 @@ void latent_attn_pair_kernel(AttnArgs a) {
           }
           m[i] = m_new;
         }
-        hand_f[i * 64 + lane] = alpha;
-        if constexpr (kSumMfma) {
+      }
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            s[i][0][r] = __builtin_amdgcn_exp2f(s[i][0][r]);
-            s[i][1][r] = __builtin_amdgcn_exp2f(s[i][1][r]);
-          }
-        } else {
-          float ls = 0.f;
+      for (int i = 0; i < 2; ++i) hand_f[i * 64 + lane] = alpha[i];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            s[i][0][r] = __builtin_amdgcn_exp2f(s[i][0][r]);
-            s[i][1][r] = __builtin_amdgcn_exp2f(s[i][1][r]);
-            ls += s[i][0][r] + s[i][1][r];
-          }
-          l[i] += ls;
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          s[i][0][r] = __builtin_amdgcn_exp2f(s[i][0][r]);
+          s[i][1][r] = __builtin_amdgcn_exp2f(s[i][1][r]);
         }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -749,7 +760,6 @@ void latent_attn_pair_kernel(AttnArgs a) {
             for (int e = 0; e < 8; ++e) v[e] = (__bf16)s[i][kb][8 * jj + e];
             *reinterpret_cast<bf16x8*>(hand_p + ((4 * i + 2 * kb + jj) * 64 + lane) * 8) = v;
           }
-      }
     };
 
     __syncthreads();               // tile 0 published
@@ -776,13 +786,6 @@ void latent_attn_pair_kernel(AttnArgs a) {
     }
     __syncthreads();
     __syncthreads();
-    if constexpr (!kSumMfma) {
-      if (live) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) hand_f[i * 64 + lane] = 1.f / sum_across_halves(l[i]);
-      }
-    }
-    __syncthreads();               // 1 / l handed over
     if constexpr (!kFold) {
       stage_w_v_up();
       __syncthreads();
@@ -846,11 +849,10 @@ void latent_attn_pair_kernel(AttnArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int t = 0; t < kLatTiles; ++t) o[i][t] = f32x16{};
-  f32x16 osum[2] = {f32x16{}, f32x16{}};
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)(qi == 0 ? 1.f : 0.f);
+  // row sums l of both units over this lane's keys, from the bf16 P^T
+  float lsum[2] = {0.f, 0.f};
 
+  const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
   bf16x8 pb[2][4];        // P^T of the tile being accumulated: [unit][(key block, 16-key step)]
   // C^T fragment f = g * kLatTiles + t of a tile: key group g = (key block,
   // 16-key step), latent block t; two transpose reads.
@@ -862,11 +864,9 @@ void latent_attn_pair_kernel(AttnArgs a) {
     const bf16x4 hi = lds_tr4(Kb + v_off2);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
-  // O^T += C^T P^T for both units: kFrags fragments, each feeding two MFMAs
-  // (+2 row-sum MFMAs per key group at narrow latents); fragments 0 and 1
-  // come in already read, later ones are read two fragments ahead.
-  // fragments 0 and 1 are read into the ring fr (slot f % 3) before the
-  // phase's barrier; later ones are read two fragments ahead
+  // O^T += C^T P^T for both units: kFrags fragments, each feeding two MFMAs.
+  // Fragments 0 and 1 are read into the ring fr (slot f % 3) before the
+  // phase's barrier; later ones are read two fragments ahead.
   bf16x8 fr[3];
   auto accumulate = [&](const bf16_t* K) {
 #pragma unroll
@@ -875,19 +875,13 @@ void latent_attn_pair_kernel(AttnArgs a) {
       const int g = f / kLatTiles, t = f % kLatTiles;
       o[0][t] = mfma32(fr[f % 3], pb[0][g], o[0][t]);
       o[1][t] = mfma32(fr[f % 3], pb[1][g], o[1][t]);
-      if constexpr (kSumMfma) {
-        if (t == kLatTiles - 1) {
-          osum[0] = mfma32(ones, pb[0][g], osum[0]);
-          osum[1] = mfma32(ones, pb[1][g], osum[1]);
-        }
-      }
     }
 #pragma unroll
     for (int f = 0; f < kFrags - 2; ++f) {
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kSumMfma ? 12 : 4, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
   };
 
   issue_tile(0);
@@ -934,8 +928,22 @@ void latent_attn_pair_kernel(AttnArgs a) {
           o[0][t] *= al0;
           o[1][t] *= al1;
         }
-        osum[0] *= al0;
-        osum[1] *= al1;
+        lsum[0] *= al0;
+        lsum[1] *= al1;
+      }
+      // row sums of P^T(j-1): a lane's 32 bf16 values per unit (8 keys of
+      // each 16-key step, one query), by dot products with (1, 1)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        float part[2] = {0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          part[g & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i][g], pb[i][g], 0, 1), one2, part[g & 1], false);
+          part[g & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i][g], pb[i][g], 2, 3), one2, part[g & 1], false);
+          part[g & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i][g], pb[i][g], 4, 5), one2, part[g & 1], false);
+          part[g & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i][g], pb[i][g], 6, 7), one2, part[g & 1], false);
+        }
+        lsum[i] += part[0] + part[1];
       }
       __syncthreads();
       // B(j): P.C of tile j-1
@@ -953,14 +961,10 @@ void latent_attn_pair_kernel(AttnArgs a) {
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();                 // 1 / l handed over
+  // lanes l and l + 32 hold the sums over the two key halves of one query
   float inv[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    // osum register 0: row 0 (the sum) in lanes 0-31, row 4 (zero) in lanes 32-63
-    if constexpr (kSumMfma) inv[i] = 1.f / sum_across_halves(osum[i][0]);
-    else inv[i] = hand_f[i * 64 + lane];
-  }
+  for (int i = 0; i < 2; ++i) inv[i] = 1.f / sum_across_halves(lsum[i]);
 
   if constexpr (kFold) {
     // olat = O / l; register 8 jj + e of latent tile t holds latent dim
