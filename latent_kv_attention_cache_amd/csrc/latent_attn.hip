@@ -135,7 +135,13 @@ void latent_attn_kernel(AttnArgs a) {
   constexpr int kLoadsPerWave = Sh::kLoadsPerWave;
   constexpr int kFeatSteps = Sh::kFeatSteps;
   constexpr int kLatTiles = Sh::kLatTiles;
-  __shared__ __attribute__((aligned(16))) bf16_t kt[kBufs * kTileElems];
+  // At narrow latents one phase covers kSub 64-key sub-tiles (128 keys), so
+  // the two barriers and the phase starts of a step are spread over twice the
+  // work; the sub-tiles keep the 64-key LDS layout, kBufs * kSub buffers.
+  constexpr int kSub = DC <= 64 ? 2 : 1;
+  constexpr int kNB = kBufs * kSub;                 // sub-tile buffers
+  static_assert(kNB * kTileElems * 2 <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) bf16_t kt[kNB * kTileElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -191,36 +197,43 @@ void latent_attn_kernel(AttnArgs a) {
   }
 
   const T* cache = static_cast<const T*>(a.cache) + ((size_t)b * a.cache_rows + k0) * kRow;
-  const int ntiles = (nk + kKT - 1) / kKT;
+  constexpr int kTileKeys = kKT * kSub;             // keys per step
+  const int ntiles = (nk + kTileKeys - 1) / kTileKeys;
+  // sub-tile st of the window sits in buffer st % kNB
+  auto sub_buf = [&](int st) { return kt + (st % kNB) * kTileElems; };
 
   // ---- tile staging (X waves only). Wave-wide load n moves chunk column n:
-  // lane r reads features 8n .. 8n+7 of key 64 j + r into slot n * kSlots + r.
-  // Keys past the window are clamped to the last valid key (finite data; their
-  // scores are masked).
+  // lane r reads features 8n .. 8n+7 of key 64 st + r (sub-tile st) into slot
+  // n * kSlots + r. Keys past the window are clamped to the last valid key
+  // (finite data; their scores are masked).
   const uint32_t kt_lds = (uint32_t)(uintptr_t)(VMLA_LDS bf16_t*)kt;
   auto issue_tile = [&](int j) {
-    const int buf = j % kBufs;
-    const int kg = min(j * kKT + lane, nk - 1);
     const int wv = __builtin_amdgcn_readfirstlane(wave);   // scalar load index and LDS address
 #pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i) {
-      const int n = wv + kLoaders * i;
-      if (Sh::kChunks % kLoaders != 0 && n >= Sh::kChunks) continue;   // wave-uniform
-      if constexpr (std::is_same_v<T, bf16_t>) {
-        dma16(cache, (uint32_t)(kg * (kRow * 2)) + (uint32_t)(16 * n),
-              kt_lds + 2u * (uint32_t)(buf * kTileElems + n * kSlots * 8));
-      } else {
-        const T* src = cache + (size_t)kg * kRow + 8 * n;
-        *reinterpret_cast<uint4*>(kt + buf * kTileElems + (n * kSlots + lane) * 8) = load8_bf16<T>(src);
+    for (int sb = 0; sb < kSub; ++sb) {
+      const int st = j * kSub + sb;
+      const int buf = st % kNB;
+      const int kg = min(st * kKT + lane, nk - 1);
+#pragma unroll
+      for (int i = 0; i < kLoadsPerWave; ++i) {
+        const int n = wv + kLoaders * i;
+        if (Sh::kChunks % kLoaders != 0 && n >= Sh::kChunks) continue;   // wave-uniform
+        if constexpr (std::is_same_v<T, bf16_t>) {
+          dma16(cache, (uint32_t)(kg * (kRow * 2)) + (uint32_t)(16 * n),
+                kt_lds + 2u * (uint32_t)(buf * kTileElems + n * kSlots * 8));
+        } else {
+          const T* src = cache + (size_t)kg * kRow + 8 * n;
+          *reinterpret_cast<uint4*>(kt + buf * kTileElems + (n * kSlots + lane) * 8) = load8_bf16<T>(src);
+        }
       }
     }
   };
 
-  // Read-time RoPE of this loading wave's k_R column of tile j (kRot only).
-  auto rotate_tile = [&](int j) {
+  // Read-time RoPE of this loading wave's k_R column of sub-tile st (kRot only).
+  auto rotate_sub = [&](int st) {
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    bf16_t* p = kt + (j % kBufs) * kTileElems + ((kDC / 8 + wv) * kSlots + lane) * 8;
-    const int kg = k0 + min(j * kKT + lane, nk - 1);        // cache slot
+    bf16_t* p = sub_buf(st) + ((kDC / 8 + wv) * kSlots + lane) * 8;
+    const int kg = k0 + min(st * kKT + lane, nk - 1);       // cache slot
     int n_in, ww;
     const int fs = div_small(kg, a.tokens_per_frame, a.inv_tokens_per_frame, &n_in);
     const int hh = div_small(n_in, a.grid_w, a.inv_grid_w, &ww);
@@ -243,6 +256,10 @@ void latent_attn_kernel(AttnArgs a) {
       o[q] = pack2(a0 * cs - a1 * sn, a0 * sn + a1 * cs);
     }
     *reinterpret_cast<uint4*>(p) = uint4{o[0], o[1], o[2], o[3]};
+  };
+  auto rotate_tile = [&](int j) {
+#pragma unroll
+    for (int sb = 0; sb < kSub; ++sb) rotate_sub(j * kSub + sb);
   };
 
   // Per-lane LDS element offsets (relative to a tile) of the operand reads; a
@@ -275,78 +292,100 @@ void latent_attn_kernel(AttnArgs a) {
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)(qi == 0 ? 1.f : 0.f);
-  f32x16 s0, s1;          // S^T of the current tile: register r holds key 32 kb + 8(r/4) + 4 half + r%4
-  bf16x8 pb[2][2];        // P^T of the previous tile, bf16, per (key block, 16-key step)
+  // S^T of the current step, per sub-tile and key block: register r holds
+  // key 32 kb + 8(r/4) + 4 half + r%4 of the sub-tile
+  f32x16 s[kSub][2];
+  bf16x8 pb[kSub][2][2];  // P^T of the previous step, bf16, per (sub-tile, key block, 16-key step)
 
-  // O^T += C^T(tile) P^T: 24 MFMAs, 48 transpose reads issued two MFMAs ahead.
-  auto accumulate = [&](const bf16_t* K) {
+  // O^T += C^T(step j) P^T: 4 kLatTiles MFMAs per sub-tile (24 at d_c 192),
+  // the transpose reads issued two MFMAs ahead.
+  auto accumulate = [&](int j) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int sb = 0; sb < kSub; ++sb) {
+      const bf16_t* K = sub_buf(j * kSub + sb);
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const bf16_t* Kb = K + (kb * 32 + jj * 16) * 8;
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int t = 0; t < kLatTiles; ++t) {
-          const bf16x4 lo = lds_tr4(Kb + v_off1 + 4 * kSlots * 8 * t);
-          const bf16x4 hi = lds_tr4(Kb + v_off2 + 4 * kSlots * 8 * t);
-          const bf16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[t] = mfma32(av, pb[kb][jj], o[t]);
+        for (int jj = 0; jj < 2; ++jj) {
+          const bf16_t* Kb = K + (kb * 32 + jj * 16) * 8;
+#pragma unroll
+          for (int t = 0; t < kLatTiles; ++t) {
+            const bf16x4 lo = lds_tr4(Kb + v_off1 + 4 * kSlots * 8 * t);
+            const bf16x4 hi = lds_tr4(Kb + v_off2 + 4 * kSlots * 8 * t);
+            const bf16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            o[t] = mfma32(av, pb[sb][kb][jj], o[t]);
+          }
+          if constexpr (kSumMfma) osum = mfma32(ones, pb[sb][kb][jj], osum);
         }
-        if constexpr (kSumMfma) osum = mfma32(ones, pb[kb][jj], osum);
       }
     }
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 4 * kLatTiles - 2; ++i) {
+    for (int i = 0; i < 4 * kLatTiles * kSub - 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kSumMfma ? 6 : 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 + (kSumMfma ? 4 * kSub : 0), 0);
   };
-  // S^T of one tile: 28 MFMAs, 28 row reads issued two steps ahead.
-  // The score accumulators start at -mo, mo = the reference max m (0 before
-  // the first tile): the MFMAs deliver s - m, and the softmax needs no
-  // subtraction unless m moves.
-  auto scores = [&](const bf16_t* K) {
+  // S^T of one step: 2 kFeatSteps MFMAs per sub-tile (28 at d_c 192), the row
+  // reads issued two feature steps ahead. The score accumulators start at
+  // -mo, mo = the reference max m (0 before the first tile): the MFMAs deliver
+  // s - m, and the softmax needs no subtraction unless m moves.
+  auto scores = [&](int j) {
     const float mo = m > -INFINITY ? -m : 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s0[r] = mo;
-      s1[r] = mo;
-    }
+    for (int sb = 0; sb < kSub; ++sb)
 #pragma unroll
-    for (int ks = 0; ks < kFeatSteps; ++ks) {
-      const int off = a_base + 2 * kSlots * 8 * ks;
-      const bf16x8 a0 = lds_row8(K + off);
-      const bf16x8 a1 = lds_row8(K + off + 32 * 8);
-      s0 = mfma32(a0, qf[ks], s0);
-      s1 = mfma32(a1, qf[ks], s1);
+      for (int r = 0; r < 16; ++r) {
+        s[sb][0][r] = mo;
+        s[sb][1][r] = mo;
+      }
+#pragma unroll
+    for (int sb = 0; sb < kSub; ++sb) {
+      const bf16_t* K = sub_buf(j * kSub + sb);
+#pragma unroll
+      for (int ks = 0; ks < kFeatSteps; ++ks) {
+        const int off = a_base + 2 * kSlots * 8 * ks;
+        const bf16x8 a0 = lds_row8(K + off);
+        const bf16x8 a1 = lds_row8(K + off + 32 * 8);
+        s[sb][0] = mfma32(a0, qf[ks], s[sb][0]);
+        s[sb][1] = mfma32(a1, qf[ks], s[sb][1]);
+      }
     }
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 1);
 #pragma unroll
-    for (int i = 0; i < kFeatSteps - 2; ++i) {
+    for (int i = 0; i < kFeatSteps * kSub - 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 1);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
     }
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 1);
   };
-  // Online softmax of the current tile; leaves P^T (bf16) in pb.
+  // Online softmax of the current step; leaves P^T (bf16) in pb.
   auto softmax = [&](int key0) {
-    if (key0 + kKT > nk) {       // the keys end inside this tile (wave-uniform)
-      // register r of key block kb holds key key0 + 32 kb + 8(r/4) + 4 half + r%4
-      const int lim = nk - key0 - 4 * half;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int k = 8 * (r >> 2) + (r & 3);
-        if (k >= lim) s0[r] = -INFINITY;
-        if (k + 32 >= lim) s1[r] = -INFINITY;
+    for (int sb = 0; sb < kSub; ++sb) {
+      const int ks0 = key0 + sb * kKT;          // first key of the sub-tile
+      if (ks0 + kKT > nk) {        // the keys end inside this sub-tile (wave-uniform)
+        // register r of key block kb holds key ks0 + 32 kb + 8(r/4) + 4 half + r%4
+        const int lim = nk - ks0 - 4 * half;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int k = 8 * (r >> 2) + (r & 3);
+          if (k >= lim) s[sb][0][r] = -INFINITY;
+          if (k + 32 >= lim) s[sb][1][r] = -INFINITY;
+        }
       }
     }
     // the registers hold s - mo with mo = m (0 before the first tile)
     const float mo = m > -INFINITY ? m : 0.f;
-    float mx = fmaxf(s0[0], s1[0]);
+    float mx = -INFINITY;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    for (int sb = 0; sb < kSub; ++sb) {
+      float ms = fmaxf(s[sb][0][0], s[sb][1][0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) ms = fmaxf(ms, fmaxf(s[sb][0][r], s[sb][1][r]));
+      mx = sb == 0 ? ms : fmaxf(mx, ms);
+    }
     mx = max_across_halves(mx) + mo;
     // Lazy rescaling: the reference max only moves when a score exceeds it by
     // more than 2^kLazy, so exp2(s - m) <= 2^kLazy stays exact in fp32/bf16 and
@@ -361,35 +400,42 @@ void latent_attn_kernel(AttnArgs a) {
       for (int t = 0; t < kLatTiles; ++t) o[t] *= alpha;
       const float dm = m_new - mo;             // scores to the new reference
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] -= dm;
-        s1[r] -= dm;
-      }
+      for (int sb = 0; sb < kSub; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[sb][0][r] -= dm;
+          s[sb][1][r] -= dm;
+        }
       m = m_new;
     }
     if constexpr (kSumMfma) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] = __builtin_amdgcn_exp2f(s0[r]);
-        s1[r] = __builtin_amdgcn_exp2f(s1[r]);
-      }
+      for (int sb = 0; sb < kSub; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[sb][0][r] = __builtin_amdgcn_exp2f(s[sb][0][r]);
+          s[sb][1][r] = __builtin_amdgcn_exp2f(s[sb][1][r]);
+        }
     } else {
       float ls = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] = __builtin_amdgcn_exp2f(s0[r]);
-        s1[r] = __builtin_amdgcn_exp2f(s1[r]);
-        ls += s0[r] + s1[r];
-      }
+      for (int sb = 0; sb < kSub; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[sb][0][r] = __builtin_amdgcn_exp2f(s[sb][0][r]);
+          s[sb][1][r] = __builtin_amdgcn_exp2f(s[sb][1][r]);
+          ls += s[sb][0][r] + s[sb][1][r];
+        }
       l += ls;
     }
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int sb = 0; sb < kSub; ++sb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pb[0][jj][e] = (__bf16)s0[8 * jj + e];
-        pb[1][jj][e] = (__bf16)s1[8 * jj + e];
-      }
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pb[sb][kb][jj][e] = (__bf16)s[sb][kb][8 * jj + e];
   };
 
   if (!lag) {
@@ -416,8 +462,8 @@ void latent_attn_kernel(AttnArgs a) {
       if ((q & 1) == 0) {          // matrix phase for tile jt
         __builtin_amdgcn_s_setprio(1);
         if (live) {
-          if (jt >= 1) accumulate(kt + ((jt - 1) % kBufs) * kTileElems);
-          if (jt < ntiles) scores(kt + (jt % kBufs) * kTileElems);
+          if (jt >= 1) accumulate(jt - 1);
+          if (jt < ntiles) scores(jt);
         }
         __builtin_amdgcn_s_setprio(0);
       } else if (jt < ntiles) {    // vector phase for tile jt
@@ -428,7 +474,7 @@ void latent_attn_kernel(AttnArgs a) {
           }
           if (jt + 2 < ntiles) issue_tile(jt + 2);
         }
-        if (live) softmax(jt * kKT);
+        if (live) softmax(jt * kTileKeys);
       }
     }
     __syncthreads();

@@ -57,6 +57,21 @@ def test_chunk_causal_latent_small(gh, gw, F, C, W, B, dt):
         compare(got[b], _reference(r, F, W, b), f"latent clip F={F} C={C} W={W} b={b}", per_head_axis=1)
 
 
+@pytest.mark.parametrize("d_c", [64, 128])
+@pytest.mark.parametrize("gh,gw,F,C,W,B,dt", [CASES[0], CASES[4]])
+def test_chunk_causal_latent_narrow_latents(d_c, gh, gw, F, C, W, B, dt):
+    # the latent route at d_c 64 (two 64-key sub-tiles per step) and 128
+    print(f"[case] latent chunk-causal d_c={d_c} grid {gh}x{gw} F={F} C={C} W={W} B={B} {dt}", flush=True)
+    w = custom(gh, gw, window_frames=F, chunk_frames=C, t_first=0, batch=B, dtype=dt).with_(d_c=d_c)
+    r, x = _clip_run(w, F)
+    out = vm.vmla_chunk_causal_attention(r.cache, x, r.dw["w_q"], r.dw["w_k_up"], r.dw["w_v_up"],
+                                         F, C, W, dims=r.dims)
+    got = _np(out)
+    for b in range(B):
+        compare(got[b], _reference(r, F, W, b), f"latent clip d_c={d_c} F={F} C={C} W={W} b={b}",
+                per_head_axis=1)
+
+
 @pytest.mark.parametrize("gh,gw,F,C,W,B,dt", CASES)
 def test_chunk_causal_explicit_small(gh, gw, F, C, W, B, dt):
     print(f"[case] explicit chunk-causal grid {gh}x{gw} F={F} C={C} W={W} B={B} {dt}", flush=True)
