@@ -35,8 +35,9 @@
 // lane ends up with four consecutive columns of one token row.
 //
 // Pipeline: a round is two 32-deep stages (one per team); LDS holds kRing
-// rounds (3 at the default widths, 48 KB each), filled by 16-byte LDS-DMA
-// loads kRing - 1 rounds ahead, one barrier per round. The loads of a round
+// rounds (3 of 48 KB for ranges of 160 rows at the default widths, 4 for
+// ranges of up to 64 rows, whose rounds take 32-37 KB), filled by 16-byte
+// LDS-DMA loads kRing - 1 rounds ahead, one barrier per round. The loads of a round
 // are spread evenly over the eight waves (six each at the default widths) and
 // issued between the matrix instructions; each costs a scalar base update
 // only (fixed lane offsets). LDS layouts of a round:
@@ -109,7 +110,10 @@ struct Tile {
   static constexpr int kRoundElems = kXElems + 2 * WS::kWElems;
   static constexpr int kRoundLoads = kXLoads + 2 * kWStageLoads;
   static constexpr int kLPW = (kRoundLoads + kWaves - 1) / kWaves;   // loads per wave per round
-  static constexpr int kRing = 3 * kRoundElems * 2 <= kLdsBytes ? 3 : 2;   // rounds held in LDS
+  // rounds held in LDS: 4 where they fit with a margin for the RoPE table
+  // (one or two row blocks per wave), else 3, else 2
+  static constexpr int kRing = 4 * kRoundElems * 2 <= kLdsBytes - 1024 ? 4
+                               : (3 * kRoundElems * 2 <= kLdsBytes ? 3 : 2);
   static constexpr int kRingElems = kRing * kRoundElems;
   // epilogue LDS: the RoPE table (its own array, for the whole kernel); five
   // ints of row info per row (batch element, slot, t, h, w) at kRiOff, past
@@ -284,8 +288,8 @@ void append_kernel(AppendArgs a) {
   // the last round's data into buffers that are not read again, so the round
   // body has no branch; every wave issues kLPW loads per round.
   for (int r = 0; r < nrounds; ++r) {
-    if constexpr (kRing == 3) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kLPW) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // round r has landed
+    // round r has landed: the loads of the kRing - 2 later rounds may be in flight
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"((kRing - 2) * kLPW) : "memory");
     __syncthreads();
     const int rn = min(r + kRing - 1, nrounds - 1);           // source round of the loads
     const bf16_t* S = smem + (r % kRing) * Tl::kRoundElems;
