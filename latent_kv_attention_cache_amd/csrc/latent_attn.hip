@@ -39,9 +39,7 @@
 // Tile buffers. Tile t is read in phases 2t .. 2t+3 (X scores, Y scores, X and Y
 // P.C). The X waves fetch tile t+2 during their vector phase 2t+1 into the
 // buffer of tile t-2 (four buffers) and make sure it has landed before the
-// barrier that precedes its first reader (phase 2t+4). At d_c = 64, where a
-// phase of one 64-key tile is short next to its barriers, a "tile" of this
-// schedule is two 64-key sub-tiles in the same layout (eight buffers).
+// barrier that precedes its first reader (phase 2t+4).
 //
 // LDS tile layout, chunk-major: the 16-byte chunk c (features 8c .. 8c+7) of
 // key row r sits at slot c * 68 + r. One wave-wide LDS-DMA load moves chunk c of
