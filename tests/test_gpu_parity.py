@@ -63,6 +63,19 @@ def test_key_count_sweep(grid_h, grid_w, window, t_first):
 
 
 @pytest.mark.parametrize("grid_h,grid_w", [
+    (1, 1), (8, 8), (5, 13), (1, 127), (8, 16), (3, 43), (12, 16), (1, 193),
+])
+def test_key_count_sweep_two_sub_tiles(grid_h, grid_w):
+    # d_c = 64 runs two 64-key sub-tiles per step: N_k = 1, 64, 65, 127, 128,
+    # 129, 192, 193 end inside the first or the second sub-tile of a step, or
+    # exactly at a step boundary
+    w = custom(grid_h, grid_w, window_frames=1, chunk_frames=1, t_first=0).with_(d_c=64)
+    r = Run(w)
+    out = _sync_np(r.chunk_step())
+    compare(out[0], r.reference(), f"d_c=64 N_k={w.n_k}", per_head_axis=1)
+
+
+@pytest.mark.parametrize("grid_h,grid_w", [
     (8, 32),      # 256 queries: 8 units of 32 per head, one head per workgroup
     (1, 257),     # 257: 9 units, the last with one row; workgroups span two heads
     (10, 29),     # 290: 10 units, the last with two rows
