@@ -13,9 +13,11 @@
 // (72 or 136): more than the 256 registers of a wave when two waves share a
 // SIMD. Here a workgroup is four waves, one per SIMD, each with the SIMD's
 // whole register file (the O^T accumulators live in the accumulation
-// registers). Without a partner wave there is no ping-pong: a wave runs the
-// scores, the softmax and P.C of a tile in turn, while the next tile streams
-// into the second LDS buffer.
+// registers). Without a partner wave there is no ping-pong; at d_c = 256 a
+// wave instead pipelines its own tiles: the exps, row sums and bf16 packing of
+// tile j - 1 run between the score MFMAs of tile j (a wave's vector work next
+// to its own MFMAs costs little), then P.C of tile j - 1, then the max and
+// rescale decision of tile j, while tile j + 1 streams into a third buffer.
 //
 // Work split. Units of 32 queries of one head, numbered head-major with the
 // units of a head padded to a multiple of the units per workgroup, so that a
@@ -33,12 +35,12 @@
 //
 // Tile. 64 keys, chunk-major and padded in LDS as in latent_attn_kernel (chunk
 // c of key row r at slot c * 68 + r), copied by 16-byte LDS-DMA loads that all
-// four waves share; two buffers (78 KB at d_c = 256, 148 KB at 512).
+// four waves share; three buffers at d_c = 256 (117 KB), two at 512 (148 KB).
 //
-// Per tile, per wave: S^T = K Qhat^T (2 x (d_c + 32) / 16 MFMAs 32x32x16),
-// softmax of its 64 keys with the lazy reference max, P^T packed to bf16 in
-// place, O^T += C^T P^T (d_c / 32 x 4 MFMAs) with C^T read by the LDS
-// transpose read. One barrier per tile.
+// Per tile, per wave: S^T = K Qhat^T (2 x (d_c + 32) / 16 MFMAs 32x32x16, in
+// four accumulation chains at d_c = 256), softmax of its 64 keys with the lazy
+// reference max, P^T packed to bf16 in place, O^T += C^T P^T (d_c / 32 x 4
+// MFMAs) with C^T read by the LDS transpose read. One barrier per tile.
 #include <type_traits>
 
 #include "device_common.h"
@@ -74,7 +76,10 @@ struct WideShape {
   // pair exchange area after the tile buffers: maxima [wave][lane] (fp32)
   // and packed P^T [wave][step][lane] (16 bytes)
   static constexpr int kXchElems = kPair ? (kWaves * 64 * 4 + kWaves * 2 * 64 * 16) / 2 : 0;
-  static_assert(2 * kTileElems * 2 + kXchElems * 2 <= 160 * 1024, "two tile buffers in LDS");
+  // one wave per unit pipelines tiles (C^T of tile j - 1, K of tile j, tile
+  // j + 1 in flight): three buffers; the wave pair keeps two
+  static constexpr int kBufs = kPair ? 2 : 3;
+  static_assert(kBufs * kTileElems * 2 + kXchElems * 2 <= 160 * 1024, "tile buffers in LDS");
   static_assert((kPair ? DC / 2 : DC) * kVLd <= 2 * kTileElems, "staged W_V_up rows fit the tile buffers");
 };
 
@@ -92,7 +97,7 @@ void latent_attn_wide_kernel(AttnArgs a) {
   constexpr int kFeatSteps = Sh::kFeatSteps;
   constexpr int kOTiles = Sh::kOTiles;
   constexpr int kUnitsWG = Sh::kUnitsWG;
-  __shared__ __attribute__((aligned(16))) bf16_t kt[2 * kTileElems + Sh::kXchElems];
+  __shared__ __attribute__((aligned(16))) bf16_t kt[Sh::kBufs * kTileElems + Sh::kXchElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -134,7 +139,7 @@ void latent_attn_wide_kernel(AttnArgs a) {
     for (int i = 0; i < Sh::kLoadsPerWave; ++i) {
       const int n = wv + kWaves * i;
       dma16(cache, (uint32_t)(kg * (kRow * 2)) + (uint32_t)(16 * n),
-            kt_lds + 2u * (uint32_t)((j & 1) * kTileElems + n * kSlots * 8));
+            kt_lds + 2u * (uint32_t)((j % Sh::kBufs) * kTileElems + n * kSlots * 8));
     }
   };
 
@@ -252,91 +257,147 @@ void latent_attn_wide_kernel(AttnArgs a) {
     l += xmax[partner * 64 + lane];
     __syncthreads();                               // the exchange area is free again
   } else {
-    for (int jt = 0; jt < ntiles; ++jt) {
-      if (jt + 1 < ntiles) issue_tile(jt + 1);     // into the buffer read in tile jt - 1
-      const bf16_t* K = kt + (jt & 1) * kTileElems;
-      if (live) {
-        // S^T of the tile: register r of key block kb holds key 32 kb + 8(r/4) + 4 half + r%4
-        f32x16 s0 = f32x16{}, s1 = f32x16{};
-  #pragma unroll
-        for (int ks = 0; ks < kFeatSteps; ++ks) {
-          const int off = a_base + 2 * kSlots * 8 * ks;
-          s0 = mfma32(lds_row8(K + off), qf[ks], s0);
-          s1 = mfma32(lds_row8(K + off + 32 * 8), qf[ks], s1);
+    // Software pipeline over tiles. Iteration jt issues the score MFMAs of tile
+    // jt with the exps, row sums and bf16 packing of tile jt - 1 spread between
+    // them (one wave per SIMD, so the exps sit between this wave's own MFMAs),
+    // then P.C of tile jt - 1, then the max and lazy rescale of tile jt.
+    // S^T of tile jt sits in set jt % 2: register r of key block kb holds key
+    // 32 kb + 8(r/4) + 4 half + r%4.
+    f32x16 sc[2][2];
+    bf16x8 pb[2][2];
+    auto buf = [&](int j) { return kt + (j % Sh::kBufs) * kTileElems; };
+    // items n0 .. n1 - 1 of set Q: exp of register n % 16 of key block n / 16
+    // against the reference max, its row sum, and every eighth a bf16 fragment
+    float ls[2] = {0.f, 0.f};
+    auto items = [&](auto qc, int n0, int n1) {
+      constexpr int Q = decltype(qc)::value;
+#pragma unroll
+      for (int n = n0; n < n1; ++n) {
+        const int kb = n / 16, r = n % 16;
+        sc[Q][kb][r] = __builtin_amdgcn_exp2f(sc[Q][kb][r] - m);
+        ls[n & 1] += sc[Q][kb][r];
+        if (r % 8 == 7) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pb[kb][r / 8][e] = (__bf16)sc[Q][kb][8 * (r / 8) + e];
         }
-        // operand reads run four steps ahead of the MFMAs (one wave per SIMD: the LDS latency is not hidden by a partner wave)
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
-  #pragma unroll
-        for (int i = 0; i < kFeatSteps - 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+    };
+    // S^T of tile j into set P; with kExp the items of set P ^ 1 between the
+    // 2 kFeatSteps MFMAs. Operand rows are read kAhead feature steps ahead.
+    constexpr int kAhead = 3;
+    auto scores = [&](auto pc, auto ec, const bf16_t* K) {
+      constexpr int P = decltype(pc)::value;
+      constexpr bool kExp = decltype(ec)::value;
+      constexpr int nm = 2 * kFeatSteps;
+      // four accumulation chains: even feature steps into sc, odd ones into
+      // sx, added at the end (two dependent chains leave the matrix core
+      // waiting on each MFMA's result)
+      f32x16 sx[2];
+      sc[P][0] = f32x16{};
+      sc[P][1] = f32x16{};
+      sx[0] = f32x16{};
+      sx[1] = f32x16{};
+      bf16x8 fa[kAhead + 1][2];
+#pragma unroll
+      for (int ks = 0; ks < kAhead; ++ks) {
+        fa[ks][0] = lds_row8(K + a_base + 2 * kSlots * 8 * ks);
+        fa[ks][1] = lds_row8(K + a_base + 2 * kSlots * 8 * ks + 32 * 8);
+      }
+#pragma unroll
+      for (int ks = 0; ks < kFeatSteps; ++ks) {
+        if (ks + kAhead < kFeatSteps) {
+          fa[(ks + kAhead) % (kAhead + 1)][0] = lds_row8(K + a_base + 2 * kSlots * 8 * (ks + kAhead));
+          fa[(ks + kAhead) % (kAhead + 1)][1] = lds_row8(K + a_base + 2 * kSlots * 8 * (ks + kAhead) + 32 * 8);
         }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 0);
-        const int key0 = jt * kKT;
-        if (key0 + kKT > nk) {
-          const int lim = nk - key0 - 4 * half;
-  #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int k = 8 * (r >> 2) + (r & 3);
-            if (k >= lim) s0[r] = -INFINITY;
-            if (k + 32 >= lim) s1[r] = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if (ks & 1) sx[kb] = mfma32(fa[ks % (kAhead + 1)][kb], qf[ks], sx[kb]);
+          else sc[P][kb] = mfma32(fa[ks % (kAhead + 1)][kb], qf[ks], sc[P][kb]);
+          if constexpr (kExp) items(std::integral_constant<int, P ^ 1>{}, 32 * (2 * ks + kb) / nm, 32 * (2 * ks + kb + 1) / nm);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      sc[P][0] += sx[0];
+      sc[P][1] += sx[1];
+    };
+    // O^T += C^T(tile) P^T
+    auto accumulate = [&](const bf16_t* K) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const bf16_t* Kb = K + (kb * 32 + jj * 16) * 8;
+#pragma unroll
+          for (int t = 0; t < kOTiles; ++t) {
+            const int ct = 4 * kSlots * 8 * t;
+            const bf16x4 lo = lds_tr4(Kb + v_off1 + ct);
+            const bf16x4 hi = lds_tr4(Kb + v_off2 + ct);
+            o[t] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb[kb][jj], o[t]);
           }
         }
-        float mx = fmaxf(s0[0], s1[0]);
-  #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-        mx = max_across_halves(mx);
-        const bool grow = mx > m + kLazy;
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-          const float m_new = grow ? mx : m;
-          const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-          l *= alpha;
-  #pragma unroll
-          for (int t = 0; t < kOTiles; ++t) o[t] *= alpha;
-          m = m_new;
-        }
-        float ls = 0.f;
-        bf16x8 pb[2][2];
-  #pragma unroll
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 1);
+#pragma unroll
+      for (int i = 0; i < 4 * kOTiles - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 1);
+    };
+    // mask, max and lazy rescale of tile j (set P)
+    auto decide = [&](auto pc, int j) {
+      constexpr int P = decltype(pc)::value;
+      const int key0 = j * kKT;
+      if (key0 + kKT > nk) {
+        const int lim = nk - key0 - 4 * half;
+#pragma unroll
         for (int r = 0; r < 16; ++r) {
-          s0[r] = __builtin_amdgcn_exp2f(s0[r] - m);
-          s1[r] = __builtin_amdgcn_exp2f(s1[r] - m);
-          ls += s0[r] + s1[r];
+          const int k = 8 * (r >> 2) + (r & 3);
+          if (k >= lim) sc[P][0][r] = -INFINITY;
+          if (k + 32 >= lim) sc[P][1][r] = -INFINITY;
         }
-        l += ls;
-  #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-  #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            pb[0][jj][e] = (__bf16)s0[8 * jj + e];
-            pb[1][jj][e] = (__bf16)s1[8 * jj + e];
-          }
-        // O^T += C^T(tile) P^T
-  #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-  #pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const bf16_t* Kb = K + (kb * 32 + jj * 16) * 8;
-  #pragma unroll
-            for (int t = 0; t < kOTiles; ++t) {
-              const int ct = 4 * kSlots * 8 * (t + kOTiles * lat_half);
-              const bf16x4 lo = lds_tr4(Kb + v_off1 + ct);
-              const bf16x4 hi = lds_tr4(Kb + v_off2 + ct);
-              o[t] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb[kb][jj], o[t]);
-            }
-          }
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 1);
-  #pragma unroll
-        for (int i = 0; i < 4 * kOTiles - 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+      }
+      float mx = fmaxf(sc[P][0][0], sc[P][1][0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[P][0][r], sc[P][1][r]));
+      mx = max_across_halves(mx);
+      const bool grow = mx > m + kLazy;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int t = 0; t < kOTiles; ++t) o[t] *= alpha;
+        m = m_new;
+      }
+    };
+    auto iteration = [&](auto pc, auto ec, int jt) {
+      constexpr int P = decltype(pc)::value;
+      constexpr bool kExp = decltype(ec)::value;
+      if (jt + 1 < ntiles) issue_tile(jt + 1);     // into the buffer of tile jt - 2
+      if (live) {
+        scores(pc, ec, buf(jt));
+        if constexpr (kExp) {
+          l += ls[0] + ls[1];
+          ls[0] = ls[1] = 0.f;
+          accumulate(buf(jt - 1));
         }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 1);
+        decide(pc, jt);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of tile jt + 1
-      __syncthreads();                                    // tile jt + 1 complete, buffer jt free
+      __syncthreads();                                    // tile jt + 1 complete, tile jt - 2 free
+    };
+    iteration(std::integral_constant<int, 0>{}, std::false_type{}, 0);
+    for (int jt = 1; jt < ntiles; jt += 2) {
+      iteration(std::integral_constant<int, 1>{}, std::true_type{}, jt);
+      if (jt + 1 < ntiles) iteration(std::integral_constant<int, 0>{}, std::true_type{}, jt + 1);
     }
-
+    if (live) {                                     // the last tile's exps and P.C
+      if ((ntiles - 1) & 1) items(std::integral_constant<int, 1>{}, 0, 32);
+      else items(std::integral_constant<int, 0>{}, 0, 32);
+      l += ls[0] + ls[1];
+      accumulate(buf(ntiles - 1));
+    }
+    __syncthreads();                                // every tile read before the staging
   }
 
   // ---- epilogue: out = (O / l) @ W_V_up[h]. The W_V_up[h] rows of a latent
