@@ -171,6 +171,12 @@ void append_kernel(AppendArgs a) {
   const T* wd = static_cast<const T*>(a.w_down);
   const T* wr = static_cast<const T*>(a.w_kr);
   const int nrounds = a.d_model / (2 * kSK);
+  // Each workgroup runs the rounds in its own rotated order, starting at
+  // round rot: workgroups are dealt round-robin to the 8 XCDs, so the 32 or
+  // so on one XCD start at different rounds and read different weight lines
+  // from its L2 at any moment (about 1 % faster at the batch-8 chunk shape
+  // than all starting at round 0). The fp32 sums only change order.
+  const int rot = (int)((blockIdx.x / 8) % (unsigned)nrounds);
 
   // Load n of a round (0 <= n < kRoundLoads): first the x loads (8 rows of
   // 128 bytes each: both stages' k columns, so every load reads whole cache
@@ -212,7 +218,8 @@ void append_kernel(AppendArgs a) {
 #pragma unroll
     for (int i = 0; i < kLPW; ++i) {
       if (i < i0 || i >= i1) continue;
-      const int k0 = kind[i] == 0 ? rs * 2 * kSK : (2 * rs + half[i]) * kSK;
+      const int rk = rs + rot < nrounds ? rs + rot : rs + rot - nrounds;   // round of the data
+      const int k0 = kind[i] == 0 ? rk * 2 * kSK : (2 * rk + half[i]) * kSK;
       bf16_t* dst = base + ldst[i];
       if constexpr (kBf16) {
         const bf16_t* src = kind[i] == 0 ? xw + k0 : (kind[i] == 1 ? wd + (size_t)k0 * DC
