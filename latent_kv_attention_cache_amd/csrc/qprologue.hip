@@ -12,19 +12,21 @@
 // with the token's (t, h, w) (App. D.3). Folding log2 e into the scale lets the
 // attention kernel use exp2 directly.
 //
-// Tile: 128 query rows (batch x tokens flattened, so a tile may span two batch
-// elements) x two heads (256 columns of W_Q). Per output the L2 traffic of the
-// projection is (1/128 + 1/256) of the operand bytes. Eight waves, two per
-// SIMD (one wave's LDS and barrier waits overlap the other's MFMAs): wave
-// (rh, hh) computes rows 32 rh .. 32 rh + 31 and the 128 columns of head hh of
+// Tile: 128 query rows (256 for large grids; batch x tokens flattened, so a
+// tile may span two batch elements) x two heads (256 columns of W_Q). Per
+// output the L2 traffic of the projection is (1/128 + 1/256) of the operand
+// bytes (1/256 + 1/256 with 256-row tiles). Eight waves, two per SIMD (one
+// wave's LDS and barrier waits overlap the other's MFMAs): wave (rh, hh)
+// computes rows R rh .. R rh + R - 1 (R = 32 or 64) and the 128 columns of head hh of
 // the pair with v_mfma_f32_16x16x32_bf16 as out^T = W^T x^T, so that
 // a lane holds four consecutive columns of one row (a RoPE pair sits in one
-// lane). The d_model contraction runs as a 3-stage pipeline of 64-deep slices
-// of x (row-major, chunk-swizzled) and W_Q (row-major, 512-byte rows, chunk c
-// of row k at position c ^ 2 t(k), t(k) = (k & 3) | bit3(k) << 2, so that a
+// lane). The d_model contraction runs as a pipeline of 64-deep slices of x
+// (row-major, chunk-swizzled) and W_Q (row-major, 512-byte rows, chunk c of
+// row k at position c ^ 2 t(k), t(k) = (k & 3) | bit3(k) << 2, so that a
 // transposed operand read of 32 lanes, rows k0 .. k0+3 and k0+8 .. k0+11,
-// covers all 64 banks once), fetched by LDS-DMA two stages ahead; each wave
-// issues its share of the next loads between its MFMAs.
+// covers all 64 banks once), three stages in LDS fetched by LDS-DMA two
+// stages ahead (256-row tiles: two stages, one ahead); each wave issues its
+// share of the next loads between its MFMAs.
 //
 // Epilogue, per wave and in registers: RoPE on the 32 rope columns and their
 // store; q_nope goes to LDS as bf16, and q_lat^T = W_K_up[h] q_nope^T by MFMA
@@ -39,24 +41,32 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsT = 128;                       // query rows per workgroup
-constexpr int kNRB = 2;                           // 16-row blocks per wave
-constexpr int kRowsW = 16 * kNRB;                 // query rows per wave
 constexpr int kHeadsT = 2;                        // heads per workgroup
 constexpr int kColsT = kHeadsT * kDHead;          // 256 columns of W_Q
 constexpr int kCB = kDHead / 16;                  // 8 column blocks per wave
-constexpr int kXElems = kRowsT * kStageK;         // x slice of a stage
-constexpr int kXLoads = kXElems * 2 / 1024;       // 16 wave-wide 1 KB loads
 constexpr int kWElems = kStageK * kColsT;         // W_Q slice of a stage
 constexpr int kWLoads = kWElems * 2 / 1024;       // 32
-constexpr int kStageElems = kXElems + kWElems;
-constexpr int kStages = 3;
-constexpr int kXPerWave = kXLoads / kWaves;       // 2
 constexpr int kWPerWave = kWLoads / kWaves;       // 4
-constexpr int kL = kXPerWave + kWPerWave;         // loads per wave per stage
 constexpr int kWChunks = kColsT / 8;              // 32 chunks per W_Q tile row
-static_assert(kXLoads % kWaves == 0 && kWLoads % kWaves == 0, "loads split evenly");
-static_assert(kStages * kStageElems * 2 <= 160 * 1024, "LDS budget");
+static_assert(kWLoads % kWaves == 0, "loads split evenly");
+
+// Row tile of NRB 16-row blocks per wave: 128 rows (NRB = 2, three stages in
+// LDS) or, for grids of more than two rounds of workgroups, 256 rows (NRB = 4,
+// two stages: each W_Q fragment read from LDS then feeds twice the MFMAs).
+template <int NRB>
+struct QTile {
+  static constexpr int kNRB = NRB;                          // 16-row blocks per wave
+  static constexpr int kRowsW = 16 * NRB;                   // query rows per wave
+  static constexpr int kRowsT = 4 * kRowsW;                 // query rows per workgroup
+  static constexpr int kXElems = kRowsT * kStageK;          // x slice of a stage
+  static constexpr int kXLoads = kXElems * 2 / 1024;        // wave-wide 1 KB loads
+  static constexpr int kStageElems = kXElems + kWElems;
+  static constexpr int kStages = NRB == 2 ? 3 : 2;
+  static constexpr int kXPerWave = kXLoads / kWaves;
+  static constexpr int kL = kXPerWave + kWPerWave;          // loads per wave per stage
+  static_assert(kXLoads % kWaves == 0, "loads split evenly");
+  static_assert(kStages * kStageElems * 2 <= 160 * 1024, "LDS budget");
+};
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -65,9 +75,13 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // chunk permutation mask of W_Q tile row k (an involution on the chunks of a row)
 __device__ __forceinline__ int swz_q(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
 
-template <typename T, int DC, int DN>
+template <typename T, int DC, int DN, int NRB>
 __global__ __launch_bounds__(kThreads)
 void qprologue_kernel(QArgs a) {
+  using QT = QTile<NRB>;
+  constexpr int kNRB = QT::kNRB, kRowsW = QT::kRowsW, kRowsT = QT::kRowsT;
+  constexpr int kXElems = QT::kXElems, kStageElems = QT::kStageElems, kStages = QT::kStages;
+  constexpr int kXPerWave = QT::kXPerWave, kL = QT::kL;
   constexpr int kDC = DC;                   // content width (192 by default; 64, 128 in the sweep)
   constexpr int kDNope = DN;                // NoPE width of a head (96 by default)
   constexpr int kRow = DC + kDHead - DN;    // Qhat row: [q_lat (DC) | q_rope (128 - DN)]
@@ -283,7 +297,7 @@ void qprologue_kernel(QArgs a) {
       }
     }
   }
-  // q_nope of this wave's 32 rows to LDS: qn[row][0..DN-1] (bf16)
+  // q_nope of this wave's kRowsW rows to LDS: qn[row][0..DN-1] (bf16)
   bf16_t* qn = smem + wv * kRowsW * kQnLd;
 #pragma unroll
   for (int rb = 0; rb < kNRB; ++rb)
@@ -318,40 +332,58 @@ void qprologue_kernel(QArgs a) {
   }
 }
 
-template <int DC, int DN>
+template <int DC, int DN, int NRB>
 void launch_t(const QArgs& a, bool f32, dim3 grid, hipStream_t s) {
-  if (f32) hipLaunchKernelGGL((qprologue_kernel<float, DC, DN>), grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL((qprologue_kernel<bf16_t, DC, DN>), grid, dim3(kThreads), 0, s, a);
+  if (f32) hipLaunchKernelGGL((qprologue_kernel<float, DC, DN, NRB>), grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((qprologue_kernel<bf16_t, DC, DN, NRB>), grid, dim3(kThreads), 0, s, a);
 }
 
-}  // namespace
-
-hipError_t launch_qprologue(const QArgs& a, bool f32, hipStream_t s) {
+template <int NRB>
+hipError_t launch_nrb(const QArgs& a, bool f32, hipStream_t s) {
   const int64_t M = (int64_t)a.batch * a.n_q;
-  const int64_t n_rt = (M + kRowsT - 1) / kRowsT;
+  const int64_t n_rt = (M + QTile<NRB>::kRowsT - 1) / QTile<NRB>::kRowsT;
   const int n_hp = (a.n_heads + kHeadsT - 1) / kHeadsT;
   const dim3 grid((unsigned)(8 * n_hp * ((n_rt + 7) / 8)));
   if (a.d_rope != kDRope) {                 // split variants: d_c = kDC
     switch (a.d_rope) {
-      case 16: launch_t<kDC, 112>(a, f32, grid, s); break;
-      case 64: launch_t<kDC, 64>(a, f32, grid, s); break;
-      case 96: launch_t<kDC, 32>(a, f32, grid, s); break;
+      case 16: launch_t<kDC, 112, NRB>(a, f32, grid, s); break;
+      case 64: launch_t<kDC, 64, NRB>(a, f32, grid, s); break;
+      case 96: launch_t<kDC, 32, NRB>(a, f32, grid, s); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
   switch (a.d_c) {
-    case 64: launch_t<64, kDNope>(a, f32, grid, s); break;
-    case 128: launch_t<128, kDNope>(a, f32, grid, s); break;
+    case 64: launch_t<64, kDNope, NRB>(a, f32, grid, s); break;
+    case 128: launch_t<128, kDNope, NRB>(a, f32, grid, s); break;
     case 256:
     case 512:                                 // wide latents: bf16 storage only
       if (f32) return hipErrorInvalidValue;
-      if (a.d_c == 256) hipLaunchKernelGGL((qprologue_kernel<bf16_t, 256, kDNope>), grid, dim3(kThreads), 0, s, a);
-      else hipLaunchKernelGGL((qprologue_kernel<bf16_t, 512, kDNope>), grid, dim3(kThreads), 0, s, a);
+      if (a.d_c == 256) hipLaunchKernelGGL((qprologue_kernel<bf16_t, 256, kDNope, NRB>), grid, dim3(kThreads), 0, s, a);
+      else hipLaunchKernelGGL((qprologue_kernel<bf16_t, 512, kDNope, NRB>), grid, dim3(kThreads), 0, s, a);
       break;
-    default: launch_t<kDC, kDNope>(a, f32, grid, s); break;
+    default: launch_t<kDC, kDNope, NRB>(a, f32, grid, s); break;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+// 256-row tiles (bf16 sources) once the 128-row grid would take more than two
+// rounds of the device's compute units (batch 8 of the 4680-token chunk: 12%
+// faster; batch 1 keeps 222 workgroups of 128 rows on 256 CUs).
+hipError_t launch_qprologue(const QArgs& a, bool f32, hipStream_t s) {
+  if (!f32) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int64_t M = (int64_t)a.batch * a.n_q;
+    const int64_t n_hp = (a.n_heads + kHeadsT - 1) / kHeadsT;
+    if ((M + QTile<2>::kRowsT - 1) / QTile<2>::kRowsT * n_hp > 2 * (int64_t)cus) return launch_nrb<4>(a, f32, s);
+  }
+  return launch_nrb<2>(a, f32, s);
 }
 
 }  // namespace vmla

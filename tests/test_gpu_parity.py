@@ -300,3 +300,16 @@ def test_large_batch_small_grid():
     for b in (0, 1, 17, 31):
         compare(out[b], r.reference(b=b), f"B=32 b={b}", per_head_axis=1)
         compare(r.cache_rows(5, 2, b=b), r.append_reference(5, 2, b=b), f"B=32 cache b={b}")
+
+
+def test_query_prologue_tall_tiles():
+    # 12 x 930 = 11,160 query rows: 88 row tiles of 128 x 6 head pairs = 528
+    # workgroups, more than two rounds of 256 compute units, so the query
+    # prologue runs its 256-row tiles; tiles span batch-element boundaries and
+    # the last one holds 152 rows. Outputs of the first, a middle and the last
+    # batch element are compared in full.
+    w = custom(30, 31, window_frames=2, chunk_frames=1, t_first=1, batch=12)
+    r = Run(w)
+    out = _sync_np(r.chunk_step())
+    for b in (0, 5, 11):
+        compare(out[b], r.reference(b=b), f"tall tiles b={b}", per_head_axis=1)
