@@ -25,8 +25,9 @@
 // row k at position c ^ 2 t(k), t(k) = (k & 3) | bit3(k) << 2, so that a
 // transposed operand read of 32 lanes, rows k0 .. k0+3 and k0+8 .. k0+11,
 // covers all 64 banks once), three stages in LDS fetched by LDS-DMA two
-// stages ahead (256-row tiles: two stages, one ahead); each wave issues its
-// share of the next loads between its MFMAs.
+// stages ahead, each wave issuing its share of the next loads between its
+// MFMAs (256-row tiles: two stages, the next one's loads all issued as the
+// current one starts).
 //
 // Epilogue, per wave and in registers: RoPE on the 32 rope columns and their
 // store; q_nope goes to LDS as bf16, and q_lat^T = W_K_up[h] q_nope^T by MFMA
@@ -221,7 +222,11 @@ void qprologue_kernel(QArgs a) {
         bf16x8 an = av;
         if (q + 1 < 2 * kNRB) an = lds_row8(X + a_off[(q + 1) % kNRB][(q + 1) / kNRB]);
         if (kk == 0 && rb == kNRB - 1) read_w(1, b1);
-        issue(s + kStages - 1, sn, q * kL / (2 * kNRB), (q + 1) * kL / (2 * kNRB));
+        if constexpr (kStages == 2) {       // one stage ahead: all loads at its start
+          if (q == 0) issue(s + kStages - 1, sn, 0, kL);
+        } else {
+          issue(s + kStages - 1, sn, q * kL / (2 * kNRB), (q + 1) * kL / (2 * kNRB));
+        }
 #pragma unroll
         for (int cb = 0; cb < kCB; ++cb)
           acc[rb][cb] = mfma16(kk == 0 ? b0[cb] : b1[cb], av, acc[rb][cb]);
