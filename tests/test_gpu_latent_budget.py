@@ -128,3 +128,19 @@ def test_wide_wan_shape_sampled_rows(d_c):
     idx = np.unique(np.concatenate([[0, 127, 128, w.n_q - 1], rng.choice(w.n_q, 28, replace=False)]))
     compare(out[0, idx], r.reference(query_tokens=idx), f"d_c={d_c} Wan sampled", per_head_axis=1)
     compare(r.cache_rows(18, 3), r.append_reference(18, 3), f"d_c={d_c} Wan chunk rows")
+
+
+@pytest.mark.parametrize("d_c", [64, 128, 256, 512])
+def test_query_prologue_tall_tiles(d_c):
+    # 12 x 930 query rows: more than two rounds of 128-row prologue
+    # workgroups, so the query prologue runs its 256-row tiles at this width;
+    # sampled rows of the first and the last batch element (whose last rows
+    # sit in the final, 152-row tile)
+    print(f"[case] d_c {d_c} tall prologue tiles", flush=True)
+    w = custom(30, 31, window_frames=2, chunk_frames=1, t_first=1, batch=12).with_(d_c=d_c)
+    r = Run(w)
+    out = _np(r.chunk_step())
+    rng = np.random.default_rng(70 + d_c)
+    for b in (0, 11):
+        idx = np.unique(np.concatenate([[0, 31, 32, 255, 256, w.n_q - 1], rng.choice(w.n_q, 40, replace=False)]))
+        compare(out[b, idx], r.reference(b=b, query_tokens=idx), f"d_c={d_c} tall tiles b={b}", per_head_axis=1)

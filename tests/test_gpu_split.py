@@ -76,3 +76,19 @@ def test_split_wan_shape_sampled_rows(d_rope):
     compare(got[0, idx], ref, f"split {d_rope} Wan latent, {len(idx)} rows", per_head_axis=1)
     compare(_np(_explicit(r, w))[0, idx], ref, f"split {d_rope} Wan explicit", per_head_axis=1)
     compare(r.cache_rows(18, 3), r.append_reference(18, 3), f"split {d_rope} Wan chunk rows")
+
+
+@pytest.mark.parametrize("d_rope", [16, 64, 96])
+def test_split_query_prologue_tall_tiles(d_rope):
+    # 12 x 930 query rows: the query prologue runs its 256-row tiles with the
+    # split variant's NoPE/RoPE widths; sampled rows of the first and the last
+    # batch element
+    print(f"[case] split {128 - d_rope}/{d_rope} tall prologue tiles", flush=True)
+    w = split_variant(custom(30, 31, window_frames=2, chunk_frames=1, t_first=1, batch=12), d_rope)
+    r = Run(w)
+    got = _np(r.chunk_step())
+    rng = np.random.default_rng(90 + d_rope)
+    for b in (0, 11):
+        idx = np.unique(np.concatenate([[0, 255, 256, w.n_q - 1], rng.choice(w.n_q, 28, replace=False)]))
+        compare(got[b, idx], r.reference(b=b, query_tokens=idx), f"split {d_rope} tall tiles b={b}",
+                per_head_axis=1)
