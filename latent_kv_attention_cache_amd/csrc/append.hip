@@ -423,13 +423,20 @@ void append_kernel(AppendArgs a) {
     }
   }
   __syncthreads();
+  // Non-temporal 16-byte stores: every workgroup writes its rows at the end of
+  // the kernel, and streaming them out as they are issued (rather than
+  // leaving up to 16.8 MB of dirty lines in the L2s at the kernel's end) made
+  // the batch-8 append ~7 % faster; the attention that reads the rows next
+  // measured the same.
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   T* cache = static_cast<T*>(a.cache);
   constexpr int kPer = 16 / sizeof(T);      // elements per 16-byte store
   constexpr int kChunksRow = kRow / kPer;
   for (int c = tid; c < rows * kChunksRow; c += kThreads) {
     const int row = c / kChunksRow, cc = c - row * kChunksRow;
     T* dst = cache + ((size_t)ri[5 * row] * cache_rows + ri[5 * row + 1]) * kRow + kPer * cc;
-    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(&ot[row * kOutLd + kPer * cc]);
+    __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(&ot[row * kOutLd + kPer * cc]),
+                                reinterpret_cast<u32x4_t*>(dst));
   }
 }
 
