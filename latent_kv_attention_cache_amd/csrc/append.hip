@@ -171,12 +171,14 @@ void append_kernel(AppendArgs a) {
   const T* wd = static_cast<const T*>(a.w_down);
   const T* wr = static_cast<const T*>(a.w_kr);
   const int nrounds = a.d_model / (2 * kSK);
-  // Each workgroup runs the rounds in its own rotated order, starting at
-  // round rot: workgroups are dealt round-robin to the 8 XCDs, so the 32 or
-  // so on one XCD start at different rounds and read different weight lines
-  // from its L2 at any moment (about 1 % faster at the batch-8 chunk shape
-  // than all starting at round 0). The fp32 sums only change order.
-  const int rot = (int)((blockIdx.x / 8) % (unsigned)nrounds);
+  // With ranges of three or more row blocks per wave, each workgroup runs
+  // the rounds in its own rotated order, starting at round rot: workgroups
+  // are dealt round-robin to the 8 XCDs, so the 32 or so on one XCD start at
+  // different rounds and read different weight lines from its L2 at any
+  // moment (about 1 % faster at the batch-8 chunk shape than all starting at
+  // round 0; 2 % slower for the 32-row ranges of a batch-1 chunk, which keep
+  // the plain order). The fp32 sums only change order.
+  const int rot = NRB >= 3 ? (int)((blockIdx.x / 8) % (unsigned)nrounds) : 0;
 
   // Load n of a round (0 <= n < kRoundLoads): first the x loads (8 rows of
   // 128 bytes each: both stages' k columns, so every load reads whole cache
