@@ -278,8 +278,9 @@ def _noise_sets(w, dims, n_sets, dev, seed, layer=False):
 def append_cold(dev, reps=60):
     """The append at the batch-8 chunk shape (8 x 4680 tokens, 132.5 MB of
     algorithmic traffic) on 30 rotating buffer sets (7 GB, far beyond the 256 MB
-    Infinity Cache), timed with HIP events on the launch stream: the HBM-graded
-    append figure."""
+    Infinity Cache), timed with one pair of HIP events on the launch stream
+    around 60 back-to-back launches (each on the next buffer set): the
+    HBM-graded append figure, the average launch duration."""
     import torch
     import latent_kv_attention_cache_amd as vm
     from workloads import config
@@ -290,23 +291,24 @@ def append_cold(dev, reps=60):
     for i in range(10):
         x, dw, cache = sets[i % len(sets)]
         vm.vmla_cache_append(cache, x, dw["w_down"], dw["w_kr"], w.t_first, w.chunk_frames, dims=dims)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    # one event pair over the back-to-back launches: the average launch
+    # duration, with no event packets between the kernels
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
     for i in range(reps):
         x, dw, cache = sets[i % len(sets)]
-        ev[i][0].record(stream)
         vm.vmla_cache_append(cache, x, dw["w_down"], dw["w_kr"], w.t_first, w.chunk_frames, dims=dims)
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
-    med = us[len(us) // 2]
+    us = e0.elapsed_time(e1) * 1e3 / reps
     nbytes = work(w)["bytes_append"]
     del sets
     torch.cuda.empty_cache()
-    gbs = nbytes / (med * 1e-6) / 1e9
-    log(f"[bench] cold append (B=8, 4680 tokens, 30 buffer sets): {med:.1f} us = {gbs:.0f} GB/s")
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"[bench] cold append (B=8, 4680 tokens, 30 buffer sets): {us:.1f} us = {gbs:.0f} GB/s")
     return {"workload": "append at the batch-8 chunk shape: 8 x 4680 tokens, 30 rotating buffer sets "
                         "(7 GB, cold: not served by the Infinity Cache)",
-            "bound": "hbm", "us": round(med, 2), "bytes_per_launch": nbytes, "achieved": round(gbs, 1),
+            "bound": "hbm", "us": round(us, 2), "bytes_per_launch": nbytes, "achieved": round(gbs, 1),
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
@@ -572,19 +574,21 @@ def main():
     }
     log(f"[bench] ms/step {ms_step:.4f}  kernels {k_ms}  attention {attn_tflops:.1f} TFLOP/s")
     _add_measured_peak(result["roofline"], result["append_roofline"])
+    if args.config == 2 and not (args.long_horizon or args.layer or args.explicit) and args.d_c == 192 \
+            and args.split == 32:
+        # the HBM-graded append figure: the batch-8 shape on cold buffers, timed
+        # while the GPU is still under load and before the CPU baseline occupies
+        # the host
+        ac = append_cold(dev)
+        ac["measured_peak"] = result["append_roofline"]["measured_peak"]
+        ac["frac_of_measured_peak"] = round(ac["achieved"] / ac["measured_peak"], 4)
+        result["append_cold"] = ac
     if not args.no_cpu_baseline and args.config == 2:
         xh = lambda t: xs[t]  # noqa: E731
         result["cpu_baseline"] = cpu_baseline(w, wts, xh, wk["step"], mix)
     elif not args.no_cpu_baseline and args.config in (3, 4) and not (args.layer or args.explicit) \
             and args.d_c == 192 and args.split == 32:
         result["cpu_baseline"] = cpu_baseline_sampled(w)
-    if args.config == 2 and not (args.long_horizon or args.layer or args.explicit) and args.d_c == 192 \
-            and args.split == 32:
-        # the HBM-graded append figure: the batch-8 shape on cold buffers
-        ac = append_cold(dev)
-        ac["measured_peak"] = result["append_roofline"]["measured_peak"]
-        ac["frac_of_measured_peak"] = round(ac["achieved"] / ac["measured_peak"], 4)
-        result["append_cold"] = ac
     if args.long_horizon:
         result["config"]["workload"] = ("Wan-1.3B-shaped chunk-layer, long rollout: B=1, 30x52 "
                                         "grid, 3-frame query chunk at t=18..20 over one sink frame "
